@@ -1,0 +1,354 @@
+"""Python face of the C ABI: torch tensors in, device pointers out.
+
+Argument marshalling only - every step of the optimizer runs in the HIP
+library.  Tensors must live on the current HIP device; work is enqueued on
+the current torch stream (or the one given) and nothing is synchronised.
+Workspaces are torch allocations on the same stream.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib as L
+
+_DTYPES = {torch.float32: L.MO_F32, torch.bfloat16: L.MO_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)") from None
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> C.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _dense(t: torch.Tensor, name: str) -> None:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _matrix(t: torch.Tensor, name: str) -> int:
+    """Row stride of a row-major 2-D (possibly row-sliced) tensor."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+# ---------------------------------------------------------------------------
+def muon_momentum(grads: Sequence[Optional[torch.Tensor]], momenta: Sequence[torch.Tensor],
+                  dirs: Optional[Sequence[Optional[torch.Tensor]]] = None, mu: float = 0.95,
+                  nesterov: bool = True, stream=None) -> None:
+    """B <- mu B + G; D <- G + mu B (or B).  A None gradient skips its item."""
+    n = len(momenta)
+    dirs = list(dirs) if dirs is not None else [None] * n
+    items = (L.MomentumItem * max(n, 1))()
+    dev = None
+    for i, (g, b, d) in enumerate(zip(grads, momenta, dirs)):
+        if b.dtype != torch.float32:
+            raise TypeError("momentum buffers are fp32")
+        _dense(b, "momentum")
+        items[i].momentum = _ptr(b)
+        items[i].numel = b.numel()
+        if g is not None:
+            _dense(g, "grad")
+            items[i].grad = _ptr(g)
+            items[i].grad_dtype = _dt(g)
+        if d is not None:
+            _dense(d, "dir")
+            items[i].dir = _ptr(d)
+            items[i].dir_dtype = _dt(d)
+        dev = b.device
+    if n == 0:
+        return
+    ws = _workspace(L.lib().muon_momentum_workspace_bytes(n), dev)
+    L.check("muon_momentum", L.lib().muon_momentum(items, n, mu, int(bool(nesterov)),
+                                                   C.c_void_p(ws.data_ptr()), ws.numel(),
+                                                   _stream(stream)))
+
+
+def _coeff_array(coeffs) -> Tuple[C.Array, int]:
+    rows = [tuple(float(x) for x in r) for r in coeffs]
+    flat = (C.c_float * (3 * len(rows)))(*[x for r in rows for x in r])
+    return flat, len(rows)
+
+
+PRECISIONS = {"bf16": L.MO_NS_BF16, "fp32": L.MO_NS_F32}
+
+
+def ns_items(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor]):
+    n = len(inputs)
+    items = (L.NsItem * max(n, 1))()
+    for i, (x, y) in enumerate(zip(inputs, outputs)):
+        if x.shape != y.shape:
+            raise ValueError("input / output shape mismatch")
+        items[i].inp = _ptr(x)
+        items[i].out = _ptr(y)
+        items[i].rows, items[i].cols = x.shape
+        items[i].ld_in = _matrix(x, "input")
+        items[i].ld_out = _matrix(y, "output")
+        items[i].in_dtype = _dt(x)
+        items[i].out_dtype = _dt(y)
+    return items
+
+
+def ns_workspace_bytes(inputs: Sequence[torch.Tensor], precision: str = "bf16") -> int:
+    items = ns_items(inputs, inputs)
+    return int(L.lib().ns_workspace_bytes(items, len(inputs), PRECISIONS[precision]))
+
+
+def ns_orthogonalize_batched(inputs: Sequence[torch.Tensor],
+                             outputs: Optional[Sequence[torch.Tensor]] = None,
+                             coeffs=((1.5, -0.5, 0.0),) * 5, precision: str = "bf16",
+                             stream=None, workspace: Optional[torch.Tensor] = None):
+    """Newton-Schulz orthogonalisation of independent 2-D matrices.
+
+    Returns ``outputs`` (new tensors shaped and typed like the inputs when
+    not given).  ``coeffs`` is a sequence of per-iteration (a, b, c).
+    """
+    if outputs is None:
+        outputs = [torch.empty_like(x) for x in inputs]
+    n = len(inputs)
+    items = ns_items(inputs, outputs)
+    flat, steps = _coeff_array(coeffs)
+    prec = PRECISIONS[precision]
+    need = int(L.lib().ns_workspace_bytes(items, n, prec))
+    if workspace is None or workspace.numel() < need:
+        workspace = _workspace(need, inputs[0].device)
+    L.check("ns_orthogonalize_batched",
+            L.lib().ns_orthogonalize_batched(items, n, flat, steps, prec,
+                                             C.c_void_p(workspace.data_ptr()),
+                                             workspace.numel(), _stream(stream)))
+    return outputs
+
+
+def normuon_rownorm(O: torch.Tensor, v: torch.Tensor, beta2: float = 0.95, eps: float = 1e-8,
+                    stream=None) -> None:
+    if v.dtype != torch.float32 or v.numel() != O.shape[0]:
+        raise ValueError("v must be fp32 with one entry per row")
+    ld = _matrix(O, "O")
+    L.check("normuon_rownorm",
+            L.lib().normuon_rownorm(_ptr(O), _dt(O), O.shape[0], O.shape[1], ld, _ptr(v), beta2,
+                                    eps, _stream(stream)))
+
+
+def muon_update(W: torch.Tensor, U: torch.Tensor, lr: float, wd: float = 0.0,
+                scale: float = 1.0, stream=None) -> None:
+    if W.shape != U.shape:
+        raise ValueError("W / U shape mismatch")
+    L.check("muon_update",
+            L.lib().muon_update(_ptr(W), _dt(W), _ptr(U), _dt(U), W.shape[0], W.shape[1],
+                                _matrix(W, "W"), _matrix(U, "U"), lr, wd, scale,
+                                _stream(stream)))
+
+
+def adamw_clip_step(params: Sequence[torch.Tensor], grads: Sequence[Optional[torch.Tensor]],
+                    exp_avgs: Sequence[torch.Tensor], exp_avg_sqs: Sequence[torch.Tensor],
+                    steps: Sequence[int], lr: float, beta1: float = 0.9, beta2: float = 0.95,
+                    eps: float = 1e-8, weight_decay=0.0, max_norm: float = 1.0,
+                    norm_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Joint clipped AdamW step; ``weight_decay`` is a float or one per param."""
+    n = len(params)
+    wds = list(weight_decay) if isinstance(weight_decay, (list, tuple)) else [weight_decay] * n
+    items = (L.AdamwItem * max(n, 1))()
+    for i in range(n):
+        p, g, m, v = params[i], grads[i], exp_avgs[i], exp_avg_sqs[i]
+        for t, nm in ((p, "param"), (m, "exp_avg"), (v, "exp_avg_sq")):
+            _dense(t, nm)
+        if m.dtype != torch.float32 or v.dtype != torch.float32:
+            raise TypeError("AdamW moments are fp32")
+        items[i].param = _ptr(p)
+        items[i].exp_avg = _ptr(m)
+        items[i].exp_avg_sq = _ptr(v)
+        items[i].numel = p.numel()
+        items[i].dtype = _dt(p)
+        items[i].step = int(steps[i])
+        items[i].weight_decay = float(wds[i])
+        if g is not None:
+            _dense(g, "grad")
+            if g.dtype != p.dtype:
+                raise TypeError("grad dtype must match the param dtype")
+            items[i].grad = _ptr(g)
+    if norm_out is not None and (norm_out.dtype != torch.float64 or norm_out.numel() < 1):
+        raise TypeError("norm_out must be a float64 device tensor")
+    dev = params[0].device if n else torch.device("cuda")
+    ws = _workspace(L.lib().adamw_workspace_bytes(items, n), dev)
+    L.check("adamw_clip_step",
+            L.lib().adamw_clip_step(items, n, lr, beta1, beta2, eps, max_norm, _ptr(norm_out),
+                                    C.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# Host-only: routing and view expansion
+# ---------------------------------------------------------------------------
+def make_desc(name: str, shape: Sequence[int], role: str = "matrix", no_decay: bool = False,
+              requires_grad: bool = True, ident: Optional[int] = None,
+              view: Optional[Sequence[int]] = None,
+              split: Optional[Sequence[int]] = None) -> L.ParamDesc:
+    d = L.ParamDesc()
+    d.name = name.encode()
+    d.ident = ident if ident is not None else (hash(name) & 0x7FFFFFFFFFFFFFFF)
+    if len(shape) > L.MO_MAX_NDIM:
+        raise ValueError("too many dims")
+    d.ndim = len(shape)
+    for i, s in enumerate(shape):
+        d.shape[i] = int(s)
+    d.role = L.ROLE_CODES[role]
+    d.no_decay = int(bool(no_decay))
+    d.requires_grad = int(bool(requires_grad))
+    if view is not None:
+        if len(view) > L.MO_MAX_NDIM:
+            raise ValueError("view rank above the ABI maximum")
+        d.view_ndim = len(view)
+        for i, s in enumerate(view):
+            d.view[i] = int(s)
+    if split is not None:
+        if len(split) > L.MO_MAX_SPLIT:
+            raise ValueError("too many split sizes")
+        d.nsplit = len(split)
+        for i, s in enumerate(split):
+            d.split[i] = int(s)
+    return d
+
+
+def route(descs: Sequence[L.ParamDesc]) -> Tuple[List[Tuple[int, int, int, int]], int]:
+    n = len(descs)
+    arr = (L.ParamDesc * max(n, 1))(*descs)
+    out = (L.RouteOut * max(n, 1))()
+    ng = C.c_int32(0)
+    L.check("mo_route", L.lib().mo_route(arr, n, out, C.byref(ng)))
+    return [(o.algorithm, o.decay, o.group, o.nslices) for o in out[:n]], ng.value
+
+
+def expand_view(rows: int, cols: int, view: Optional[Sequence[int]] = None,
+                split: Optional[Sequence[int]] = None) -> List[Tuple[int, int, int]]:
+    v = list(view or [])
+    s = list(split or [])
+    va = (C.c_int64 * max(len(v), 1))(*v)
+    sa = (C.c_int64 * max(len(s), 1))(*s)
+    cnt = C.c_int32(0)
+    st = L.lib().mo_expand_view(rows, cols, len(v), va, len(s), sa, None, 0, C.byref(cnt))
+    if st not in (L.MO_OK, L.MO_EINVAL):
+        L.check("mo_expand_view", st)
+    out = (C.c_int64 * max(3 * cnt.value, 3))()
+    L.check("mo_expand_view", L.lib().mo_expand_view(rows, cols, len(v), va, len(s), sa, out,
+                                                     cnt.value, C.byref(cnt)))
+    return [(out[3 * i], out[3 * i + 1], out[3 * i + 2]) for i in range(cnt.value)]
+
+
+# ---------------------------------------------------------------------------
+# Plan + grouped step
+# ---------------------------------------------------------------------------
+def make_hparams(muon_lr=0.01, muon_wd=0.0, mu=0.95, nesterov=True, coeffs=((1.5, -0.5, 0.0),) * 5,
+                 ns_precision="bf16", normuon=False, normuon_beta2=0.95, normuon_eps=1e-8,
+                 adamw_lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, adamw_wd=0.0,
+                 max_norm=1.0) -> L.HParams:
+    h = L.HParams()
+    h.muon_lr, h.muon_wd, h.mu, h.nesterov = muon_lr, muon_wd, mu, int(bool(nesterov))
+    rows = [tuple(r) for r in coeffs]
+    if not 1 <= len(rows) <= L.MO_NS_MAX_STEPS:
+        raise ValueError("coefficient table must have 1..64 rows")
+    h.ns_steps = len(rows)
+    for k, (a, b, c) in enumerate(rows):
+        h.ns_coeffs[k][0], h.ns_coeffs[k][1], h.ns_coeffs[k][2] = a, b, c
+    h.ns_precision = PRECISIONS[ns_precision]
+    h.normuon, h.normuon_beta2, h.normuon_eps = int(bool(normuon)), normuon_beta2, normuon_eps
+    h.adamw_lr, h.beta1, h.beta2, h.eps = adamw_lr, beta1, beta2, eps
+    h.adamw_wd, h.max_norm = adamw_wd, max_norm
+    return h
+
+
+class Plan:
+    """Owns a C plan over a parameter table; ``step()`` runs one hybrid step.
+
+    ``entries``: dicts with ``desc`` (a ParamDesc from ``make_desc``), ``param``,
+    ``grad`` (or None) and the states the routing needs: ``momentum`` (and
+    ``normuon_v`` with NorMuon) for Muon params, ``exp_avg`` / ``exp_avg_sq``
+    for AdamW params.  The tensors must stay alive and in place.
+    """
+
+    def __init__(self, entries: Sequence[dict], hparams: L.HParams):
+        n = len(entries)
+        self._keep = list(entries)
+        arr = (L.Param * max(n, 1))()
+        for i, e in enumerate(entries):
+            arr[i].desc = e["desc"]
+            arr[i].param = _ptr(e.get("param"))
+            arr[i].grad = _ptr(e.get("grad"))
+            if e.get("param") is not None:
+                arr[i].dtype = _dt(e["param"])
+            for k in ("momentum", "normuon_v", "exp_avg", "exp_avg_sq"):
+                t = e.get(k)
+                if t is not None and t.dtype != torch.float32:
+                    raise TypeError(f"{k} must be fp32")
+                setattr(arr[i], k, _ptr(t))
+        self._hp = hparams
+        h = C.c_void_p()
+        L.check("mo_plan_create", L.lib().mo_plan_create(arr, n, C.byref(hparams), C.byref(h)))
+        self._h = h
+        self.n = n
+        self._ws: Optional[torch.Tensor] = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            L.lib().mo_plan_destroy(h)
+            self._h = None
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(L.lib().mo_plan_workspace_bytes(self._h))
+
+    def routes(self):
+        out = (L.RouteOut * max(self.n, 1))()
+        L.check("mo_plan_route", L.lib().mo_plan_route(self._h, out, self.n))
+        return [(o.algorithm, o.decay, o.group, o.nslices) for o in out[:self.n]]
+
+    def slices(self):
+        k = L.lib().mo_plan_num_slices(self._h)
+        out = (C.c_int64 * max(4 * k, 4))()
+        L.check("mo_plan_slices", L.lib().mo_plan_slices(self._h, out, k))
+        return [tuple(out[4 * i:4 * i + 4]) for i in range(k)]
+
+    def get_steps(self) -> List[int]:
+        out = (C.c_int32 * max(self.n, 1))()
+        L.check("mo_plan_get_steps", L.lib().mo_plan_get_steps(self._h, out, self.n))
+        return list(out[:self.n])
+
+    def set_steps(self, steps: Sequence[int]) -> None:
+        arr = (C.c_int32 * max(self.n, 1))(*[int(s) for s in steps])
+        L.check("mo_plan_set_steps", L.lib().mo_plan_set_steps(self._h, arr, self.n))
+
+    def workspace(self, device) -> torch.Tensor:
+        if self._ws is None or self._ws.numel() < self.workspace_bytes:
+            self._ws = _workspace(self.workspace_bytes, device)
+        return self._ws
+
+    def step(self, muon_lr: Optional[float] = None, adamw_lr: Optional[float] = None,
+             norm_out: Optional[torch.Tensor] = None, stream=None,
+             workspace: Optional[torch.Tensor] = None) -> None:
+        a = L.StepArgs()
+        a.muon_lr = -1.0 if muon_lr is None else float(muon_lr)
+        a.adamw_lr = -1.0 if adamw_lr is None else float(adamw_lr)
+        a.norm_out = _ptr(norm_out)
+        if workspace is None:
+            dev = next(e["param"].device for e in self._keep if e.get("param") is not None)
+            workspace = self.workspace(dev)
+        L.check("mo_grouped_step",
+                L.lib().mo_grouped_step(self._h, C.byref(a), C.c_void_p(workspace.data_ptr()),
+                                        workspace.numel(), _stream(stream)))

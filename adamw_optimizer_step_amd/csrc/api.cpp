@@ -1,0 +1,281 @@
+// C entry points of the individual optimizer stages.  Each validates all of
+// its arguments before enqueueing anything, copies its descriptor table into
+// the caller's workspace and launches one kernel per stage on `stream`.
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "host.hpp"
+
+using namespace mo;
+
+namespace {
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+mo_status upload(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  return stage_upload(dst, src, bytes, st);
+}
+
+mo_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MO_OK;
+  if (!ws) return fail(MO_EWORKSPACE, "workspace of %zu bytes required", need);
+  if (reinterpret_cast<uintptr_t>(ws) & 255u)
+    return fail(MO_EALIGN, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MO_EWORKSPACE, "workspace has %zu bytes, %zu required", have, need);
+  return MO_OK;
+}
+
+// ----- momentum --------------------------------------------------------------
+size_t momentum_table_bytes(int32_t n) { return align_up(sizeof(MomSeg) * (n > 0 ? n : 0), 256); }
+
+// ----- NS workspace layout ---------------------------------------------------
+struct NsWs {
+  NsTables tabs;
+  size_t tab = 0, partials = 0, scale = 0, fin = 0, pool = 0, total = 0;
+};
+
+NsWs ns_ws_layout(const NsLayout& L) {
+  NsWs w;
+  w.tabs = ns_table_offsets(L);
+  WsCursor c;
+  w.tab = c.take(w.tabs.bytes);
+  w.fin = c.take(sizeof(FinalItem) * L.n);
+  w.partials = c.take(sizeof(StatPartial) * L.prep_tiles);
+  w.scale = c.take(sizeof(float) * L.n);
+  w.pool = c.take(static_cast<size_t>(L.pool_elems) * L.elem);
+  w.total = align_up(c.off, 256);
+  return w;
+}
+
+mo_status validate_ns_items(const mo_ns_item* items, int32_t n, int32_t precision) {
+  if (n <= 0 || !items) return fail(MO_EINVAL, "no Newton-Schulz items");
+  if (precision != MO_NS_BF16 && precision != MO_NS_F32)
+    return fail(MO_EINVAL, "unknown precision %d", precision);
+  for (int32_t i = 0; i < n; ++i) {
+    const mo_ns_item& it = items[i];
+    if (!it.in || !it.out) return fail(MO_EINVAL, "item %d: NULL pointer", i);
+    if (!valid_dtype(it.in_dtype) || !valid_dtype(it.out_dtype))
+      return fail(MO_EDTYPE, "item %d: bad dtype", i);
+    if (it.rows < 1 || it.cols < 1 || it.rows > 65536 || it.cols > 65536)
+      return fail(MO_ESHAPE, "item %d: shape (%lld, %lld) outside [1, 65536]", i,
+                  (long long)it.rows, (long long)it.cols);
+    if (it.ld_in < it.cols || it.ld_out < it.cols)
+      return fail(MO_ESHAPE, "item %d: row stride smaller than cols", i);
+  }
+  return MO_OK;
+}
+
+void ns_layout_from_items(const mo_ns_item* items, int32_t n, int32_t precision, bool need_a,
+                          NsLayout& L) {
+  std::vector<int64_t> r(n), c(n);
+  for (int32_t i = 0; i < n; ++i) { r[i] = items[i].rows; c[i] = items[i].cols; }
+  build_ns_layout(L, r.data(), c.data(), n, precision == MO_NS_F32 ? 4 : 2, need_a);
+}
+
+// ----- AdamW -----------------------------------------------------------------
+struct AdamWs {
+  size_t tab = 0, partials = 0, scal = 0, total = 0;
+  int64_t nblocks = 0;
+  int nseg = 0;
+};
+
+AdamWs adam_ws_layout(const mo_adamw_item* items, int32_t n) {
+  AdamWs w;
+  for (int32_t i = 0; i < n; ++i)
+    if (items[i].grad && items[i].numel > 0) {
+      w.nblocks += ceil_div(items[i].numel, kEltPerBlock);
+      ++w.nseg;
+    }
+  WsCursor c;
+  w.tab = c.take(sizeof(AdamSeg) * w.nseg);
+  w.partials = c.take(sizeof(double) * w.nblocks);
+  w.scal = c.take(2 * sizeof(double));
+  w.total = align_up(c.off, 256);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t muon_momentum_workspace_bytes(int32_t n) { return momentum_table_bytes(n); }
+
+mo_status muon_momentum(const mo_momentum_item* items, int32_t n, float mu, int32_t nesterov,
+                        void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (n < 0 || (n > 0 && !items)) return fail(MO_EINVAL, "bad item list");
+  if (!std::isfinite(mu)) return fail(MO_EINVAL, "mu must be finite");
+  std::vector<MomSeg> segs;
+  int64_t nblocks = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const mo_momentum_item& it = items[i];
+    if (it.numel < 0) return fail(MO_EINVAL, "item %d: negative numel", i);
+    if (!it.grad || it.numel == 0) continue;
+    if (!it.momentum) return fail(MO_EINVAL, "item %d: NULL momentum", i);
+    if (!valid_dtype(it.grad_dtype) || (it.dir && !valid_dtype(it.dir_dtype)))
+      return fail(MO_EDTYPE, "item %d: bad dtype", i);
+    if (!aligned16(it.grad) || !aligned16(it.momentum) || (it.dir && !aligned16(it.dir)))
+      return fail(MO_EALIGN, "item %d: pointers must be 16-byte aligned", i);
+    MomSeg s;
+    s.g = it.grad; s.b = it.momentum; s.d = it.dir; s.numel = it.numel; s.start = nblocks;
+    s.gdt = it.grad_dtype; s.ddt = it.dir ? it.dir_dtype : MO_F32; s.vec = 1; s.pad = 0;
+    nblocks += ceil_div(it.numel, kEltPerBlock);
+    segs.push_back(s);
+  }
+  if (segs.empty()) return MO_OK;
+  mo_status s = check_ws(ws, ws_bytes, momentum_table_bytes(static_cast<int32_t>(segs.size())));
+  if (s != MO_OK) return s;
+  hipStream_t st = as_stream(stream);
+  if ((s = upload(ws, segs.data(), segs.size() * sizeof(MomSeg), st)) != MO_OK) return s;
+  return launch_momentum(static_cast<const MomSeg*>(ws), static_cast<int>(segs.size()), nblocks,
+                         mu, nesterov, nullptr, st);
+}
+
+size_t ns_workspace_bytes(const mo_ns_item* items, int32_t n, int32_t precision) {
+  if (validate_ns_items(items, n, precision) != MO_OK) return 0;
+  NsLayout L;
+  ns_layout_from_items(items, n, precision, true, L);
+  return ns_ws_layout(L).total;
+}
+
+mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const float* coeffs,
+                                   int32_t steps, int32_t precision, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  clear_error();
+  mo_status s = validate_ns_items(items, n, precision);
+  if (s != MO_OK) return s;
+  if (steps < 1 || steps > MO_NS_MAX_STEPS || !coeffs)
+    return fail(MO_EINVAL, "steps must be in [1, %d] with a coefficient table", MO_NS_MAX_STEPS);
+  bool need_a = false;
+  for (int k = 0; k < 3 * steps; ++k)
+    if (!std::isfinite(coeffs[k])) return fail(MO_EINVAL, "non-finite coefficient");
+  for (int k = 0; k < steps; ++k) need_a |= coeffs[3 * k + 2] != 0.f;
+  NsLayout L;
+  ns_layout_from_items(items, n, precision, need_a, L);
+  const NsWs W = ns_ws_layout(L);
+  // The size query assumes the quintic-capable layout, which is never smaller.
+  if ((s = check_ws(ws, ws_bytes, W.total)) != MO_OK) return s;
+
+  char* base = static_cast<char*>(ws);
+  std::vector<FinalItem> fin(n);
+  int64_t rows = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    PrepItem& p = L.prep[i];
+    p.in = items[i].in;
+    p.ld_in = items[i].ld_in;
+    p.in_dt = items[i].in_dtype;
+    p.stat_begin = p.start;
+    p.stat_end = p.start + static_cast<int64_t>(p.rp / kPrepTile) * p.tiles_c;
+    FinalItem& f = fin[i];
+    f.out = items[i].out;
+    f.ld_out = items[i].ld_out;
+    f.src = L.final_off(i, steps);
+    f.ld_src = L.final_ld(i);
+    f.rows = static_cast<int32_t>(items[i].rows);
+    f.cols = static_cast<int32_t>(items[i].cols);
+    f.out_dt = items[i].out_dtype;
+    f.start = rows;
+    rows += items[i].rows;
+  }
+  std::vector<char> tab;
+  ns_pack_tables(L, W.tabs, tab);
+  hipStream_t st = as_stream(stream);
+  if ((s = upload(base + W.tab, tab.data(), tab.size(), st)) != MO_OK) return s;
+  if ((s = upload(base + W.fin, fin.data(), fin.size() * sizeof(FinalItem), st)) != MO_OK) return s;
+  const PrepItem* dprep = reinterpret_cast<const PrepItem*>(base + W.tab + W.tabs.prep);
+  StatPartial* partials = reinterpret_cast<StatPartial*>(base + W.partials);
+  float* scale = reinterpret_cast<float*>(base + W.scale);
+  void* pool = base + W.pool;
+  if ((s = launch_ns_stats(dprep, n, L.prep_tiles, partials, st)) != MO_OK) return s;
+  if ((s = launch_ns_scale(dprep, n, partials, scale, st)) != MO_OK) return s;
+  if ((s = launch_ns_prep(dprep, n, L.prep_tiles, scale, pool, L.elem, st)) != MO_OK) return s;
+  if ((s = ns_run_iterations(L, base + W.tab, W.tabs, pool, coeffs, steps, st)) != MO_OK) return s;
+  return launch_ns_final(reinterpret_cast<const FinalItem*>(base + W.fin), n, rows, pool, L.elem,
+                         st);
+}
+
+mo_status normuon_rownorm(void* O, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                          float* v, float beta2, float eps, void* stream) {
+  clear_error();
+  if (!O || !v) return fail(MO_EINVAL, "NULL pointer");
+  if (!valid_dtype(dtype)) return fail(MO_EDTYPE, "bad dtype");
+  if (rows < 0 || cols < 1 || ld < cols || rows > (int64_t(1) << 31) || cols > (1 << 30))
+    return fail(MO_ESHAPE, "bad shape");
+  if (!std::isfinite(beta2) || !std::isfinite(eps)) return fail(MO_EINVAL, "bad hyper-parameter");
+  RowSeg one;
+  std::memset(&one, 0, sizeof(one));
+  one.o = O; one.nv = v; one.ld_o = ld; one.rows = static_cast<int32_t>(rows);
+  one.cols = static_cast<int32_t>(cols); one.o_dt = dtype; one.w_dt = dtype; one.scale = 1.f;
+  return launch_rows(kRowNormInPlace, nullptr, 0, one, rows, 0.f, beta2, eps,
+                     as_stream(stream));
+}
+
+mo_status muon_update(void* W, int32_t w_dtype, const void* U, int32_t u_dtype, int64_t rows,
+                      int64_t cols, int64_t ld_w, int64_t ld_u, float lr, float wd, float scale,
+                      void* stream) {
+  clear_error();
+  if (!W || !U) return fail(MO_EINVAL, "NULL pointer");
+  if (!valid_dtype(w_dtype) || !valid_dtype(u_dtype)) return fail(MO_EDTYPE, "bad dtype");
+  if (rows < 0 || cols < 1 || ld_w < cols || ld_u < cols || rows > (int64_t(1) << 31) ||
+      cols > (1 << 30))
+    return fail(MO_ESHAPE, "bad shape");
+  if (!std::isfinite(lr) || !std::isfinite(wd) || !std::isfinite(scale))
+    return fail(MO_EINVAL, "bad hyper-parameter");
+  RowSeg one;
+  std::memset(&one, 0, sizeof(one));
+  one.w = W; one.o = const_cast<void*>(U); one.ld_w = ld_w; one.ld_o = ld_u;
+  one.rows = static_cast<int32_t>(rows); one.cols = static_cast<int32_t>(cols);
+  one.w_dt = w_dtype; one.o_dt = u_dtype; one.scale = scale; one.wd = wd;
+  return launch_rows(kRowUpdate, nullptr, 0, one, rows, lr, 0.f, 0.f, as_stream(stream));
+}
+
+size_t adamw_workspace_bytes(const mo_adamw_item* items, int32_t n) {
+  if (n < 0 || (n > 0 && !items)) return 0;
+  return adam_ws_layout(items, n).total;
+}
+
+mo_status adamw_clip_step(const mo_adamw_item* items, int32_t n, float lr, float beta1,
+                          float beta2, float eps, float max_norm, double* norm_out, void* ws,
+                          size_t ws_bytes, void* stream) {
+  clear_error();
+  if (n < 0 || (n > 0 && !items)) return fail(MO_EINVAL, "bad item list");
+  if (!std::isfinite(lr) || !std::isfinite(beta1) || !std::isfinite(beta2) ||
+      !std::isfinite(eps) || beta1 < 0.f || beta1 >= 1.f || beta2 < 0.f || beta2 >= 1.f ||
+      std::isnan(max_norm))
+    return fail(MO_EINVAL, "bad hyper-parameter");
+  std::vector<AdamSeg> segs;
+  int64_t nblocks = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const mo_adamw_item& it = items[i];
+    if (it.numel < 0) return fail(MO_EINVAL, "item %d: negative numel", i);
+    if (!it.grad || it.numel == 0) continue;
+    if (!it.param || !it.exp_avg || !it.exp_avg_sq) return fail(MO_EINVAL, "item %d: NULL", i);
+    if (!valid_dtype(it.dtype)) return fail(MO_EDTYPE, "item %d: bad dtype", i);
+    if (it.step < 1) return fail(MO_EINVAL, "item %d: step must be >= 1", i);
+    if (!std::isfinite(it.weight_decay)) return fail(MO_EINVAL, "item %d: bad decay", i);
+    if (!aligned16(it.param) || !aligned16(it.grad) || !aligned16(it.exp_avg) ||
+        !aligned16(it.exp_avg_sq))
+      return fail(MO_EALIGN, "item %d: pointers must be 16-byte aligned", i);
+    AdamSeg s;
+    s.p = it.param; s.g = it.grad; s.m = it.exp_avg; s.v = it.exp_avg_sq; s.numel = it.numel;
+    s.start = nblocks; s.dt = it.dtype; s.t0 = it.step; s.wd = it.weight_decay; s.pad = 0.f;
+    nblocks += ceil_div(it.numel, kEltPerBlock);
+    segs.push_back(s);
+  }
+  const AdamWs W = adam_ws_layout(items, n);
+  mo_status s = check_ws(ws, ws_bytes, W.total);
+  if (s != MO_OK) return s;
+  hipStream_t st = as_stream(stream);
+  char* base = static_cast<char*>(ws);
+  double* partials = reinterpret_cast<double*>(base + W.partials);
+  double* scal = reinterpret_cast<double*>(base + W.scal);
+  const AdamSeg* dsegs = reinterpret_cast<const AdamSeg*>(base + W.tab);
+  if ((s = upload(base + W.tab, segs.data(), segs.size() * sizeof(AdamSeg), st)) != MO_OK) return s;
+  const int nseg = static_cast<int>(segs.size());
+  if ((s = launch_adam_sumsq(dsegs, nseg, nblocks, partials, st)) != MO_OK) return s;
+  if ((s = launch_adam_norm(partials, nblocks, max_norm, scal, norm_out, st)) != MO_OK) return s;
+  return launch_adam_apply(dsegs, nseg, nblocks, scal, lr, beta1, beta2, eps, 0, st);
+}
+
+}  // extern "C"

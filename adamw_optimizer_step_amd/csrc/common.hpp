@@ -1,0 +1,163 @@
+// Shared host/device helpers of the hybrid Muon + AdamW library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstddef>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/muon_adamw.h"
+
+namespace mo {
+
+// ---------------------------------------------------------------------------
+// Error reporting (thread-local message, status returned to the caller)
+// ---------------------------------------------------------------------------
+mo_status fail(mo_status s, const char* fmt, ...);
+void clear_error();
+
+#define MO_HIP_TRY(expr)                                                          \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess)                                                         \
+      return ::mo::fail(MO_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));  \
+  } while (0)
+
+#define MO_LAUNCH_CHECK(name)                                                     \
+  do {                                                                            \
+    hipError_t e_ = hipGetLastError();                                            \
+    if (e_ != hipSuccess)                                                         \
+      return ::mo::fail(MO_EHIP, "launch of %s failed: %s", name,                 \
+                        hipGetErrorString(e_));                                   \
+  } while (0)
+
+inline bool valid_dtype(int32_t d) { return d == MO_F32 || d == MO_BF16; }
+inline size_t dtype_size(int32_t d) { return d == MO_F32 ? 4 : 2; }
+__host__ __device__ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Bump allocator over the caller's workspace (offsets only; no memory touched).
+struct WsCursor {
+  size_t off = 0;
+  size_t take(size_t bytes, size_t align = 256) {
+    off = align_up(off, align);
+    size_t at = off;
+    off += bytes;
+    return at;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float load_as_f32(const void* p, int64_t i, int32_t dt) {
+  return dt == MO_F32 ? static_cast<const float*>(p)[i]
+                      : bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+__device__ __forceinline__ void store_from_f32(void* p, int64_t i, int32_t dt, float v) {
+  if (dt == MO_F32)
+    static_cast<float*>(p)[i] = v;
+  else
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+}
+
+// 8 consecutive elements <-> 8 floats.  Pointers must be 16-byte aligned.
+__device__ __forceinline__ void load8(const void* p, int64_t i, int32_t dt, float* v) {
+  if (dt == MO_F32) {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
+    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void store8(void* p, int64_t i, int32_t dt, const float* v) {
+  if (dt == MO_F32) {
+    float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + i);
+    q[0] = make_float4(v[0], v[1], v[2], v[3]);
+    q[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    uint4 u;
+    u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    u.z = f32_to_bf16(v[4]) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
+    u.w = f32_to_bf16(v[6]) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = u;
+  }
+}
+
+__device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Largest index p in [0, n) with start[p] <= key (start ascending, start[0] == 0).
+template <typename S, typename K>
+__device__ __forceinline__ int find_segment(const S* segs, int n, K key) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].start <= key) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Per-block partial statistics of a Newton-Schulz input (max |d| and sum d^2).
+struct StatPartial {
+  float amax;
+  float pad;
+  double sumsq;
+};
+
+// Block-wide reduction of (amax, sumsq) over 256 threads in a fixed order.
+__device__ __forceinline__ void block_stat_reduce(float amax, double ss, StatPartial* out) {
+  __shared__ float s_amax[4];
+  __shared__ double s_ss[4];
+  amax = wave_max(amax);
+  ss = wave_sum(ss);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) { s_amax[w] = amax; s_ss[w] = ss; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    StatPartial p;
+    p.amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+    p.pad = 0.f;
+    p.sumsq = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+    *out = p;
+  }
+}
+
+}  // namespace mo

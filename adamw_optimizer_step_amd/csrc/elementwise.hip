@@ -1,0 +1,342 @@
+// Memory-bound kernels: Muon momentum, AdamW with the global-norm clip, and
+// the row kernels (NorMuon row normalisation, scaled Muon update).
+//
+// All are HBM-bound streaming passes: 8 elements (16-byte bf16 / 2 x 16-byte
+// fp32 vectors) per thread per iteration, 8192 elements per 256-thread block,
+// one launch over every tensor of a call (segment table + binary search).
+#include "kernels.hpp"
+
+namespace mo {
+
+namespace {
+
+// (1 - beta^t) by binary exponentiation in fp64 (t >= 1).
+__device__ double one_minus_pow(double beta, int t) {
+  double r = 1.0, b = beta;
+  while (t > 0) {
+    if (t & 1) r *= b;
+    b *= b;
+    t >>= 1;
+  }
+  return 1.0 - r;
+}
+
+// ---------------------------------------------------------------------------
+// Momentum: B <- mu B + G ; D <- G + mu B (Nesterov) or B.
+// (OMN "Dual-Manifold Optimization", Muon-path paragraph; NorMuon eq. (1).)
+// ---------------------------------------------------------------------------
+template <bool kStats>
+__global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict__ segs, int nseg,
+                                                       float mu, int nesterov,
+                                                       StatPartial* __restrict__ stats) {
+  const int64_t blk = blockIdx.x;
+  const MomSeg sg = segs[find_segment(segs, nseg, blk)];
+  const int64_t base = (blk - sg.start) * kEltPerBlock;
+  float amax = 0.f;
+  double ss = 0.0;
+#pragma unroll 1
+  for (int it = 0; it < kEltIters; ++it) {
+    const int64_t e0 = base + static_cast<int64_t>(it) * kThreads * kEltPerThread +
+                       threadIdx.x * kEltPerThread;
+    if (e0 >= sg.numel) break;
+    float g[8], b[8], d[8];
+    const int cnt = sg.numel - e0 >= 8 ? 8 : static_cast<int>(sg.numel - e0);
+    const bool vec = cnt == 8 && sg.vec;
+    if (vec) {
+      load8(sg.g, e0, sg.gdt, g);
+      load8(sg.b, e0, MO_F32, b);
+    } else {
+      for (int k = 0; k < 8; ++k) {
+        g[k] = k < cnt ? load_as_f32(sg.g, e0 + k, sg.gdt) : 0.f;
+        b[k] = k < cnt ? sg.b[e0 + k] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      b[k] = mu * b[k] + g[k];
+      d[k] = nesterov ? g[k] + mu * b[k] : b[k];
+    }
+    if (vec) {
+      store8(sg.b, e0, MO_F32, b);
+      if (sg.d) store8(sg.d, e0, sg.ddt, d);
+    } else {
+      for (int k = 0; k < cnt; ++k) {
+        sg.b[e0 + k] = b[k];
+        if (sg.d) store_from_f32(sg.d, e0 + k, sg.ddt, d[k]);
+      }
+    }
+    if (kStats) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        // statistics of the value as stored
+        const float dv = sg.ddt == MO_BF16 ? bf16_to_f32(f32_to_bf16(d[k])) : d[k];
+        const float a = k < cnt ? fabsf(dv) : 0.f;
+        amax = fmaxf(amax, a);
+        ss += static_cast<double>(a) * a;
+      }
+    }
+  }
+  if (kStats) block_stat_reduce(amax, ss, &stats[blk]);
+}
+
+// ---------------------------------------------------------------------------
+// AdamW (OMN page, recipe paragraph; Qwen3.8 optimizer notes, Adam/AdamW).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_adam_sumsq(const AdamSeg* __restrict__ segs, int nseg,
+                                                         double* __restrict__ partials) {
+  const int64_t blk = blockIdx.x;
+  const AdamSeg sg = segs[find_segment(segs, nseg, blk)];
+  const int64_t base = (blk - sg.start) * kEltPerBlock;
+  double ss = 0.0;
+#pragma unroll 1
+  for (int it = 0; it < kEltIters; ++it) {
+    const int64_t e0 = base + static_cast<int64_t>(it) * kThreads * kEltPerThread +
+                       threadIdx.x * kEltPerThread;
+    if (e0 >= sg.numel) break;
+    float g[8];
+    const int cnt = sg.numel - e0 >= 8 ? 8 : static_cast<int>(sg.numel - e0);
+    if (cnt == 8) {
+      load8(sg.g, e0, sg.dt, g);
+    } else {
+      for (int k = 0; k < 8; ++k) g[k] = k < cnt ? load_as_f32(sg.g, e0 + k, sg.dt) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ss += static_cast<double>(g[k]) * g[k];
+  }
+  __shared__ double s_ss[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blk] = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+}
+
+__global__ __launch_bounds__(kThreads) void k_adam_norm(const double* __restrict__ partials,
+                                                        int64_t n, float max_norm,
+                                                        double* __restrict__ scal,
+                                                        double* __restrict__ norm_out) {
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) s += partials[i];
+  __shared__ double s_ss[4];
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double T = sqrt((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]));
+    const double kappa = (max_norm > 0.f && T > static_cast<double>(max_norm))
+                             ? static_cast<double>(max_norm) / T
+                             : 1.0;
+    scal[0] = T;
+    reinterpret_cast<float*>(scal + 1)[0] = static_cast<float>(kappa);
+    if (norm_out) *norm_out = T;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_adam_apply(const AdamSeg* __restrict__ segs, int nseg,
+                                                         const double* __restrict__ scal, float lr,
+                                                         float beta1, float beta2, float eps,
+                                                         int32_t tdelta) {
+  const int64_t blk = blockIdx.x;
+  const AdamSeg sg = segs[find_segment(segs, nseg, blk)];
+  const int64_t base = (blk - sg.start) * kEltPerBlock;
+  const float kappa = reinterpret_cast<const float*>(scal + 1)[0];
+  const int t = sg.t0 + tdelta;
+  const double bc1 = one_minus_pow(beta1, t);
+  const double bc2 = one_minus_pow(beta2, t);
+  const float step = static_cast<float>(lr / bc1);
+  const float ibc2 = static_cast<float>(1.0 / sqrt(bc2));
+  const float decay = 1.f - lr * sg.wd;
+  const float omb1 = 1.f - beta1, omb2 = 1.f - beta2;
+#pragma unroll 1
+  for (int it = 0; it < kEltIters; ++it) {
+    const int64_t e0 = base + static_cast<int64_t>(it) * kThreads * kEltPerThread +
+                       threadIdx.x * kEltPerThread;
+    if (e0 >= sg.numel) break;
+    float g[8], w[8], m[8], v[8];
+    const int cnt = sg.numel - e0 >= 8 ? 8 : static_cast<int>(sg.numel - e0);
+    if (cnt == 8) {
+      load8(sg.g, e0, sg.dt, g);
+      load8(sg.p, e0, sg.dt, w);
+      load8(sg.m, e0, MO_F32, m);
+      load8(sg.v, e0, MO_F32, v);
+    } else {
+      for (int k = 0; k < 8; ++k) {
+        const bool in = k < cnt;
+        g[k] = in ? load_as_f32(sg.g, e0 + k, sg.dt) : 0.f;
+        w[k] = in ? load_as_f32(sg.p, e0 + k, sg.dt) : 0.f;
+        m[k] = in ? sg.m[e0 + k] : 0.f;
+        v[k] = in ? sg.v[e0 + k] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float gk = kappa * g[k];
+      m[k] = beta1 * m[k] + omb1 * gk;
+      v[k] = beta2 * v[k] + omb2 * gk * gk;
+      const float denom = sqrtf(v[k]) * ibc2 + eps;
+      w[k] = w[k] * decay - step * (m[k] / denom);
+    }
+    if (cnt == 8) {
+      store8(sg.p, e0, sg.dt, w);
+      store8(sg.m, e0, MO_F32, m);
+      store8(sg.v, e0, MO_F32, v);
+    } else {
+      for (int k = 0; k < cnt; ++k) {
+        store_from_f32(sg.p, e0 + k, sg.dt, w[k]);
+        sg.m[e0 + k] = m[k];
+        sg.v[e0 + k] = v[k];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Row kernels: one wavefront per row.
+//   NorMuon (NorMuon paper section 3.1): ms = mean_j O_ij^2,
+//     v_i <- beta2 v_i + (1 - beta2) ms, O_ij <- O_ij / (sqrt(v_i) + eps).
+//   Update (NorMuon eq. (3); OMN rectangular-scaling paragraph):
+//     W <- W (1 - lr wd) - lr scale O.
+// ---------------------------------------------------------------------------
+template <int kMode>
+__global__ __launch_bounds__(kThreads) void k_rows(const RowSeg* __restrict__ segs, int nseg,
+                                                   RowSeg one, int64_t total_rows, float lr,
+                                                   float beta2, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= total_rows) return;
+  // nseg == 0: a single matrix passed by value
+  const RowSeg sg = nseg == 0 ? one : segs[find_segment(segs, nseg, row)];
+  const int64_t r = row - sg.start;
+  const int cols = sg.cols;
+  const int64_t obase = r * sg.ld_o;
+  const int64_t wbase = r * sg.ld_w;
+  // vector path when every row start is 16-byte aligned and cols % 8 == 0
+  const bool vec_o = (cols % 8 == 0) && ((sg.ld_o * (sg.o_dt == MO_F32 ? 4 : 2)) % 16 == 0) &&
+                     aligned16(sg.o);
+  const bool vec_w = (cols % 8 == 0) && ((sg.ld_w * (sg.w_dt == MO_F32 ? 4 : 2)) % 16 == 0) &&
+                     aligned16(sg.w);
+  float inv = 1.f;
+  if (kMode != kRowUpdate) {
+    double ss = 0.0;
+    if (vec_o) {
+      for (int c0 = lane * 8; c0 < cols; c0 += 64 * 8) {
+        float o[8];
+        load8(sg.o, obase + c0, sg.o_dt, o);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ss += static_cast<double>(o[k]) * o[k];
+      }
+    } else {
+      for (int c = lane; c < cols; c += 64) {
+        const float o = load_as_f32(sg.o, obase + c, sg.o_dt);
+        ss += static_cast<double>(o) * o;
+      }
+    }
+    ss = wave_sum(ss);
+    const double ms = ss / cols;
+    const float vnew = static_cast<float>(beta2 * static_cast<double>(sg.nv[r]) +
+                                          (1.0 - beta2) * ms);
+    if (lane == 0) sg.nv[r] = vnew;
+    inv = 1.f / (sqrtf(vnew) + eps);
+  }
+  if (kMode == kRowNormInPlace) {
+    if (vec_o) {
+      for (int c0 = lane * 8; c0 < cols; c0 += 64 * 8) {
+        float o[8];
+        load8(sg.o, obase + c0, sg.o_dt, o);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] *= inv;
+        store8(sg.o, obase + c0, sg.o_dt, o);
+      }
+    } else {
+      for (int c = lane; c < cols; c += 64)
+        store_from_f32(sg.o, obase + c, sg.o_dt, load_as_f32(sg.o, obase + c, sg.o_dt) * inv);
+    }
+    return;
+  }
+  const float decay = 1.f - lr * sg.wd;
+  const float coef = lr * sg.scale * inv;
+  if (vec_o && vec_w) {
+    for (int c0 = lane * 8; c0 < cols; c0 += 64 * 8) {
+      float o[8], w[8];
+      load8(sg.o, obase + c0, sg.o_dt, o);
+      load8(sg.w, wbase + c0, sg.w_dt, w);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) w[k] = w[k] * decay - coef * o[k];
+      store8(sg.w, wbase + c0, sg.w_dt, w);
+    }
+  } else {
+    for (int c = lane; c < cols; c += 64) {
+      const float o = load_as_f32(sg.o, obase + c, sg.o_dt);
+      const float w = load_as_f32(sg.w, wbase + c, sg.w_dt);
+      store_from_f32(sg.w, wbase + c, sg.w_dt, w * decay - coef * o);
+    }
+  }
+}
+
+}  // namespace
+
+mo_status launch_momentum(const MomSeg* segs, int nseg, int64_t nblocks, float mu, int nesterov,
+                          StatPartial* stats, hipStream_t st) {
+  if (nblocks <= 0) return MO_OK;
+  KTimer tm(MO_KC_MOMENTUM, st);
+  if (stats)
+    k_momentum<true><<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(
+        segs, nseg, mu, nesterov, stats);
+  else
+    k_momentum<false><<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(
+        segs, nseg, mu, nesterov, nullptr);
+  MO_LAUNCH_CHECK("k_momentum");
+  return MO_OK;
+}
+
+mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, double* partials,
+                            hipStream_t st) {
+  if (nblocks <= 0) return MO_OK;
+  KTimer tm(MO_KC_ADAM_SUMSQ, st);
+  k_adam_sumsq<<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(segs, nseg,
+                                                                               partials);
+  MO_LAUNCH_CHECK("k_adam_sumsq");
+  return MO_OK;
+}
+
+mo_status launch_adam_norm(const double* partials, int64_t nblocks, float max_norm, double* scal,
+                           double* norm_out, hipStream_t st) {
+  KTimer tm(MO_KC_ADAM_NORM, st);
+  k_adam_norm<<<dim3(1), dim3(kThreads), 0, st>>>(partials, nblocks, max_norm, scal, norm_out);
+  MO_LAUNCH_CHECK("k_adam_norm");
+  return MO_OK;
+}
+
+mo_status launch_adam_apply(const AdamSeg* segs, int nseg, int64_t nblocks, const double* scal,
+                            float lr, float beta1, float beta2, float eps, int32_t tdelta,
+                            hipStream_t st) {
+  if (nblocks <= 0) return MO_OK;
+  KTimer tm(MO_KC_ADAM_APPLY, st);
+  k_adam_apply<<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(
+      segs, nseg, scal, lr, beta1, beta2, eps, tdelta);
+  MO_LAUNCH_CHECK("k_adam_apply");
+  return MO_OK;
+}
+
+mo_status launch_rows(int32_t mode, const RowSeg* segs, int nseg, const RowSeg& one,
+                      int64_t total_rows, float lr, float beta2, float eps, hipStream_t st) {
+  if (total_rows <= 0) return MO_OK;
+  const unsigned grid = static_cast<unsigned>(ceil_div(total_rows, kThreads / 64));
+  KTimer tm(MO_KC_ROWS, st);
+  switch (mode) {
+    case kRowUpdate:
+      k_rows<kRowUpdate><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, beta2, eps);
+      break;
+    case kRowNormUpdate:
+      k_rows<kRowNormUpdate><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, beta2,
+                                                         eps);
+      break;
+    default:
+      k_rows<kRowNormInPlace><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, beta2,
+                                                          eps);
+      break;
+  }
+  MO_LAUNCH_CHECK("k_rows");
+  return MO_OK;
+}
+
+}  // namespace mo

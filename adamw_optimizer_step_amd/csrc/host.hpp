@@ -1,0 +1,59 @@
+// Host-side declarations shared by the library's translation units.
+#pragma once
+
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace mo {
+
+struct Slice {
+  int64_t off;   // first stored row
+  int64_t rows;
+  int64_t cols;
+};
+
+mo_status expand_view(int64_t rows, int64_t cols, int32_t view_ndim, const int64_t* view,
+                      int32_t nsplit, const int64_t* split, std::vector<Slice>& out);
+mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* ngroups);
+
+// Newton-Schulz layout of a batch of independent matrices: padded pool
+// buffers per matrix and the GEMM / prep problem tables (pool offsets only;
+// device pointers and statistics ranges are filled by the caller).
+struct NsLayout {
+  int elem = 2;
+  bool need_a = false;
+  int n = 0;
+  std::vector<PrepItem> prep;
+  std::vector<GemmProb> gram_p, gram_a, square, upd0, upd1;
+  int64_t prep_tiles = 0, gram_tiles = 0, square_tiles = 0, upd_tiles = 0;
+  std::vector<int64_t> x_off, xt_off0, xt_off1;
+  std::vector<int32_t> tall, sp, lp;
+  int64_t pool_elems = 0;
+
+  // stored-orientation buffer of the final iterate and its row stride
+  int64_t final_off(int i, int steps) const {
+    return tall[i] ? (steps % 2 ? xt_off1[i] : xt_off0[i]) : x_off[i];
+  }
+  int32_t final_ld(int i) const { return tall[i] ? sp[i] : lp[i]; }
+};
+
+void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
+                     bool need_a);
+
+// Byte offsets of the device tables inside one contiguous table block.
+struct NsTables {
+  size_t prep = 0, gram_p = 0, gram_a = 0, square = 0, upd0 = 0, upd1 = 0, bytes = 0;
+};
+NsTables ns_table_offsets(const NsLayout& L);
+void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf);
+
+// Asynchronous host -> device copy through a pinned staging buffer; `src`
+// may be released when this returns.
+mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st);
+
+// Enqueue the Newton-Schulz iterations on the prepared pool.
+mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
+                            const float* coeffs, int steps, hipStream_t st);
+
+}  // namespace mo

@@ -1,0 +1,153 @@
+// Device descriptor tables and launchers of the gfx950 kernels.
+//
+// Every kernel reads its per-item descriptors from a table in device memory
+// (inside the caller's workspace or a plan-owned buffer) and finds its item
+// with a binary search over the items' first-block (or first-row) indices,
+// so one launch covers any number of tensors or matrices.
+#pragma once
+
+#include "common.hpp"
+
+namespace mo {
+
+constexpr int kThreads = 256;
+
+// Scope guard: while timing is enabled (mo_timing_enable), brackets the
+// launch issued inside its scope with HIP events on `st`.
+class KTimer {
+ public:
+  KTimer(int cls, hipStream_t st);
+  ~KTimer();
+  KTimer(const KTimer&) = delete;
+  KTimer& operator=(const KTimer&) = delete;
+
+ private:
+  int cls_;
+  hipStream_t st_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+  bool active_ = false;
+};
+
+// ----- momentum (elementwise, 8192 elements per block) ----------------------
+constexpr int kEltPerThread = 8;
+constexpr int kEltIters = 4;
+constexpr int kEltPerBlock = kThreads * kEltPerThread * kEltIters;
+
+struct MomSeg {
+  const void* g;       // gradient (grad dtype)
+  float* b;            // momentum buffer (fp32, in-out)
+  void* d;             // direction out (dir dtype) or nullptr
+  int64_t numel;
+  int64_t start;       // first block of this segment
+  int32_t gdt, ddt;
+  int32_t vec;         // g, b, d all 16-byte aligned: vector path
+  int32_t pad;
+};
+
+// stats != nullptr: per-block (amax, sum d^2) of the written direction, one
+// StatPartial per block at stats[block].
+mo_status launch_momentum(const MomSeg* segs, int nseg, int64_t nblocks, float mu, int nesterov,
+                          StatPartial* stats, hipStream_t st);
+
+// ----- AdamW ------------------------------------------------------------------
+struct AdamSeg {
+  void* p;             // param (dtype)
+  const void* g;       // grad (dtype)
+  float* m;
+  float* v;
+  int64_t numel;
+  int64_t start;       // first block
+  int32_t dt;
+  int32_t t0;          // step number for tdelta == 0
+  float wd;
+  float pad;
+};
+
+mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, double* partials,
+                            hipStream_t st);
+// Reduces partials -> T (fp64) and kappa (fp32) at scal[0], (float*)&scal[1].
+mo_status launch_adam_norm(const double* partials, int64_t nblocks, float max_norm, double* scal,
+                           double* norm_out, hipStream_t st);
+mo_status launch_adam_apply(const AdamSeg* segs, int nseg, int64_t nblocks, const double* scal,
+                            float lr, float beta1, float beta2, float eps, int32_t tdelta,
+                            hipStream_t st);
+
+// ----- row kernels: NorMuon row normalisation and the scaled Muon update -----
+enum RowMode : int32_t {
+  kRowUpdate = 0,          // W <- W (1 - lr wd) - lr scale O
+  kRowNormUpdate = 1,      // NorMuon on O's rows, then the update
+  kRowNormInPlace = 2      // NorMuon on O's rows, written back to O
+};
+
+struct RowSeg {
+  void* w;                 // weight rows (kRowNormInPlace: unused)
+  void* o;                 // O rows (read; written back for kRowNormInPlace)
+  float* nv;               // NorMuon v (fp32, one per row) or nullptr
+  int64_t ld_w, ld_o;
+  int64_t start;           // first global row index of this segment
+  int32_t rows, cols;
+  int32_t w_dt, o_dt;
+  float scale;             // shape scale
+  float wd;                // decoupled decay of this matrix's group
+};
+
+// nseg == 0: `one` is the only matrix (passed by value, no table needed).
+mo_status launch_rows(int32_t mode, const RowSeg* segs, int nseg, const RowSeg& one,
+                      int64_t total_rows, float lr, float beta2, float eps, hipStream_t st);
+
+// ----- Newton-Schulz ------------------------------------------------------------
+constexpr int kPrepTile = 64;   // prep / stats tile edge
+constexpr int kGemmTile = 128;  // GEMM tile edge (M and N); matrices are padded to it
+
+struct PrepItem {
+  const void* in;          // D in stored orientation, rows r x cols c, stride ld_in
+  int64_t ld_in;
+  int64_t sbuf;            // pool offset of the stored-orientation buffer (rp x cp)
+  int64_t stbuf;           // pool offset of the transposed buffer (cp x rp)
+  int64_t start;           // first prep tile of this item
+  int64_t stat_begin;      // partial-statistics range of this item
+  int64_t stat_end;
+  int32_t r, c;
+  int32_t rp, cp;          // padded (multiples of kGemmTile)
+  int32_t tiles_c;         // cp / kPrepTile
+  int32_t in_dt;
+};
+
+struct GemmProb {
+  int64_t a_off, b_off;    // operand pool offsets (row-major, K contiguous)
+  int64_t c_off;           // direct output
+  int64_t ct_off;          // transposed output, -1 = none
+  int64_t e_off;           // epilogue input (same layout as c), -1 = none
+  int32_t lda, ldb, ldc, ldct, lde;
+  int32_t K;
+  int32_t tiles_m, tiles_n;
+  int32_t sym;             // only tiles (i <= j); mirror written through ct
+  int32_t start;           // first tile of this problem
+};
+
+struct FinalItem {         // NS output copy (stored orientation)
+  void* out;
+  int64_t ld_out;
+  int64_t src;             // pool offset of the stored-orientation buffer
+  int64_t start;           // first row
+  int32_t rows, cols;
+  int32_t ld_src;
+  int32_t out_dt;
+};
+
+// Statistics of D over the prep tiles -> partials[tile].
+mo_status launch_ns_stats(const PrepItem* items, int n, int64_t ntiles, StatPartial* partials,
+                          hipStream_t st);
+// Per-item scale = 1 / (alpha (||D||/alpha + 1e-7)), alpha = max(amax, 1e-7).
+mo_status launch_ns_scale(const PrepItem* items, int n, const StatPartial* partials,
+                          float* scale, hipStream_t st);
+// X0 (scaled, padded, both orientations) into the pool.  elem = 2 (bf16) or 4.
+mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const float* scale,
+                         void* pool, int elem, hipStream_t st);
+// One batched GEMM phase:  out = c0 * E + c1 * (A_op B_op^T).
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, void* pool, int elem,
+                         float c0, float c1, int has_e, hipStream_t st);
+mo_status launch_ns_final(const FinalItem* items, int n, int64_t total_rows, const void* pool,
+                          int elem, hipStream_t st);
+
+}  // namespace mo

@@ -1,0 +1,371 @@
+// Plan (routing + slice table + workspace layout) and the grouped hybrid
+// Muon + AdamW step.
+//
+// One step enqueues, on the caller's stream and without host synchronisation:
+//   k_momentum   over every Muon slice (B, D and per-block D statistics)
+//   k_ns_scale   per slice (max-abs / Frobenius scale from those statistics)
+//   k_ns_prep    X0 in both orientations into the padded pool
+//   k_ns_gemm    2 (cubic) or 3 launches per Newton-Schulz iteration
+//   k_rows       NorMuon (optional) + shape scale + weight update per row
+//   k_adam_*     sum of squares, clip factor, AdamW update
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "host.hpp"
+
+using namespace mo;
+
+struct mo_plan {
+  struct SliceRec {
+    int32_t param;
+    int64_t off, rows, cols;
+  };
+  std::vector<mo_param> params;
+  mo_hparams hp;
+  std::vector<mo_route_out> routes;
+  std::vector<SliceRec> slices;     // all Muon slices, in param order
+  std::vector<SliceRec> active;     // slices of Muon params with a gradient
+  std::vector<int32_t> steps;       // AdamW step counters (per param)
+  int32_t ddt = MO_BF16;            // direction / pool dtype
+  bool need_a = false;
+
+  NsLayout ns;
+  // workspace layout (byte offsets)
+  std::vector<size_t> d_off;        // per param: direction buffer (Muon with grad)
+  size_t ws_stats = 0, ws_scale = 0, ws_adam_partials = 0, ws_adam_scal = 0, ws_pool = 0;
+  size_t ws_total = 0;
+  int64_t mom_blocks = 0, adam_blocks = 0, total_rows = 0;
+  int n_adam = 0;
+
+  // plan-owned device tables
+  NsTables nst;
+  size_t tab_mom = 0, tab_ns = 0, tab_rows = 0, tab_adam = 0, tab_bytes = 0;
+  char* dtab = nullptr;
+  int device = -1;
+  std::vector<char> htab;
+  void* uploaded_ws = nullptr;
+  bool dirty = true;
+  int32_t tdelta = 0;
+};
+
+namespace {
+
+mo_status build_plan(mo_plan* P) {
+  const int32_t n = static_cast<int32_t>(P->params.size());
+  std::vector<mo_param_desc> descs(n);
+  for (int32_t i = 0; i < n; ++i) descs[i] = P->params[i].desc;
+  P->routes.assign(n, mo_route_out{});
+  int32_t ng = 0;
+  mo_status s = route(descs.data(), n, P->routes.data(), &ng);
+  if (s != MO_OK) return s;
+  const mo_hparams& hp = P->hp;
+  P->ddt = hp.ns_precision == MO_NS_F32 ? MO_F32 : MO_BF16;
+  P->need_a = false;
+  for (int k = 0; k < hp.ns_steps; ++k) P->need_a |= hp.ns_coeffs[k][2] != 0.f;
+  P->steps.assign(n, 0);
+
+  WsCursor ws;
+  std::vector<Slice> sl;
+  P->d_off.assign(n, 0);
+  for (int32_t i = 0; i < n; ++i) {
+    const mo_param& p = P->params[i];
+    const mo_route_out& r = P->routes[i];
+    if (r.algorithm == MO_ALG_SKIP) continue;
+    if (!p.param) return fail(MO_EINVAL, "param %d: NULL param pointer", i);
+    if (!valid_dtype(p.dtype)) return fail(MO_EDTYPE, "param %d: bad dtype", i);
+    int64_t numel = 1;
+    for (int k = 0; k < p.desc.ndim; ++k) numel *= p.desc.shape[k];
+    if (r.algorithm == MO_ALG_MUON) {
+      const int64_t R = p.desc.shape[0], C = p.desc.shape[1];
+      if (R > 65536 || C > 65536) return fail(MO_ESHAPE, "param %d: dims above 65536", i);
+      if (!p.momentum) return fail(MO_EINVAL, "param %d: Muon needs a momentum buffer", i);
+      if (hp.normuon && !p.normuon_v) return fail(MO_EINVAL, "param %d: NorMuon needs v", i);
+      // The routing key's view (the parameter's registered view) defines the slices.
+      s = expand_view(R, C, p.desc.view_ndim, p.desc.view, p.desc.nsplit, p.desc.split, sl);
+      if (s != MO_OK) return s;
+      for (const Slice& x : sl) {
+        P->slices.push_back({i, x.off, x.rows, x.cols});
+        if (p.grad) P->active.push_back({i, x.off, x.rows, x.cols});
+      }
+      if (p.grad) P->d_off[i] = ws.take(static_cast<size_t>(numel) * dtype_size(P->ddt));
+    } else {
+      if (!p.exp_avg || !p.exp_avg_sq) return fail(MO_EINVAL, "param %d: AdamW needs m and v", i);
+      if (p.grad && numel > 0) {
+        if (!aligned16(p.param) || !aligned16(p.grad) || !aligned16(p.exp_avg) ||
+            !aligned16(p.exp_avg_sq))
+          return fail(MO_EALIGN, "param %d: AdamW pointers must be 16-byte aligned", i);
+        P->adam_blocks += ceil_div(numel, kEltPerBlock);
+        ++P->n_adam;
+      }
+    }
+  }
+  // momentum blocks per active slice (one statistics partial per block)
+  for (const auto& a : P->active) P->mom_blocks += ceil_div(a.rows * a.cols, kEltPerBlock);
+  std::vector<int64_t> rr, cc;
+  for (const auto& a : P->active) { rr.push_back(a.rows); cc.push_back(a.cols); P->total_rows += a.rows; }
+  build_ns_layout(P->ns, rr.data(), cc.data(), static_cast<int>(rr.size()),
+                  P->ddt == MO_F32 ? 4 : 2, P->need_a);
+  P->ws_stats = ws.take(sizeof(StatPartial) * P->mom_blocks);
+  P->ws_scale = ws.take(sizeof(float) * P->active.size());
+  P->ws_adam_partials = ws.take(sizeof(double) * P->adam_blocks);
+  P->ws_adam_scal = ws.take(2 * sizeof(double));
+  P->ws_pool = ws.take(static_cast<size_t>(P->ns.pool_elems) * P->ns.elem);
+  P->ws_total = align_up(ws.off, 256);
+
+  P->nst = ns_table_offsets(P->ns);
+  WsCursor t;
+  P->tab_mom = t.take(sizeof(MomSeg) * P->active.size());
+  P->tab_ns = t.take(P->nst.bytes);
+  P->tab_rows = t.take(sizeof(RowSeg) * P->active.size());
+  P->tab_adam = t.take(sizeof(AdamSeg) * P->n_adam);
+  P->tab_bytes = align_up(t.off, 256);
+  return MO_OK;
+}
+
+// Fill the device tables (absolute pointers into `ws`) and upload them.
+mo_status upload_tables(mo_plan* P, char* ws, hipStream_t st) {
+  const mo_hparams& hp = P->hp;
+  int dev = 0;
+  MO_HIP_TRY(hipGetDevice(&dev));
+  if (P->dtab && P->device != dev) {
+    return fail(MO_EINVAL, "plan was first used on device %d, now on %d", P->device, dev);
+  }
+  if (!P->dtab && P->tab_bytes) {
+    MO_HIP_TRY(hipMalloc(reinterpret_cast<void**>(&P->dtab), P->tab_bytes));
+    P->device = dev;
+  }
+  P->htab.assign(P->tab_bytes, 0);
+  char* h = P->htab.data();
+  const size_t esz = dtype_size(P->ddt);
+  char* pool = ws + P->ws_pool;
+  // momentum segments = active slices; NS prep items read D from the workspace
+  MomSeg* mom = reinterpret_cast<MomSeg*>(h + P->tab_mom);
+  RowSeg* rows = reinterpret_cast<RowSeg*>(h + P->tab_rows);
+  int64_t blk = 0, row = 0;
+  for (size_t k = 0; k < P->active.size(); ++k) {
+    const auto& a = P->active[k];
+    const mo_param& p = P->params[a.param];
+    const int64_t e0 = a.off * a.cols, numel = a.rows * a.cols;
+    MomSeg& m = mom[k];
+    m.g = static_cast<const char*>(p.grad) + e0 * dtype_size(p.dtype);
+    m.b = p.momentum + e0;
+    m.d = ws + P->d_off[a.param] + e0 * esz;
+    m.numel = numel;
+    m.start = blk;
+    m.gdt = p.dtype;
+    m.ddt = P->ddt;
+    m.vec = aligned16(m.g) && aligned16(m.b) && aligned16(m.d);
+    m.pad = 0;
+    PrepItem& pi = P->ns.prep[k];
+    pi.in = m.d;
+    pi.ld_in = a.cols;
+    pi.in_dt = P->ddt;
+    pi.stat_begin = blk;
+    blk += ceil_div(numel, kEltPerBlock);
+    pi.stat_end = blk;
+    RowSeg& r = rows[k];
+    std::memset(&r, 0, sizeof(r));
+    r.w = static_cast<char*>(p.param) + e0 * dtype_size(p.dtype);
+    r.o = pool + P->ns.final_off(static_cast<int>(k), hp.ns_steps) * esz;
+    r.nv = hp.normuon ? p.normuon_v + a.off : nullptr;
+    r.ld_w = a.cols;
+    r.ld_o = P->ns.final_ld(static_cast<int>(k));
+    r.start = row;
+    r.rows = static_cast<int32_t>(a.rows);
+    r.cols = static_cast<int32_t>(a.cols);
+    r.w_dt = p.dtype;
+    r.o_dt = P->ddt;
+    r.scale = static_cast<float>(std::sqrt(std::max(1.0, static_cast<double>(a.rows) / a.cols)));
+    r.wd = P->routes[a.param].decay ? hp.muon_wd : 0.f;
+    row += a.rows;
+  }
+  std::vector<char> nsbuf;
+  ns_pack_tables(P->ns, P->nst, nsbuf);
+  if (!nsbuf.empty()) std::memcpy(h + P->tab_ns, nsbuf.data(), nsbuf.size());
+  AdamSeg* ad = reinterpret_cast<AdamSeg*>(h + P->tab_adam);
+  int64_t ablk = 0;
+  int j = 0;
+  for (size_t i = 0; i < P->params.size(); ++i) {
+    const mo_param& p = P->params[i];
+    if (P->routes[i].algorithm != MO_ALG_ADAMW || !p.grad) continue;
+    int64_t numel = 1;
+    for (int k = 0; k < p.desc.ndim; ++k) numel *= p.desc.shape[k];
+    if (numel == 0) continue;
+    AdamSeg& s = ad[j++];
+    s.p = p.param; s.g = p.grad; s.m = p.exp_avg; s.v = p.exp_avg_sq; s.numel = numel;
+    s.start = ablk; s.dt = p.dtype; s.t0 = P->steps[i] + 1;
+    s.wd = P->routes[i].decay ? hp.adamw_wd : 0.f;
+    s.pad = 0.f;
+    ablk += ceil_div(numel, kEltPerBlock);
+  }
+  if (P->tab_bytes) {
+    mo_status s = stage_upload(P->dtab, h, P->tab_bytes, st);
+    if (s != MO_OK) return s;
+  }
+  P->uploaded_ws = ws;
+  P->dirty = false;
+  P->tdelta = 0;
+  return MO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mo_status mo_plan_create(const mo_param* params, int32_t n, const mo_hparams* hp,
+                         mo_plan** out) {
+  clear_error();
+  if (!out || !hp || n < 0 || (n > 0 && !params)) return fail(MO_EINVAL, "bad arguments");
+  *out = nullptr;
+  if (hp->ns_steps < 1 || hp->ns_steps > MO_NS_MAX_STEPS)
+    return fail(MO_EINVAL, "ns_steps must be in [1, %d]", MO_NS_MAX_STEPS);
+  if (hp->ns_precision != MO_NS_BF16 && hp->ns_precision != MO_NS_F32)
+    return fail(MO_EINVAL, "bad ns_precision");
+  const float checks[] = {hp->muon_lr, hp->muon_wd, hp->mu, hp->normuon_beta2, hp->normuon_eps,
+                          hp->adamw_lr, hp->beta1, hp->beta2, hp->eps, hp->adamw_wd};
+  for (float c : checks)
+    if (!std::isfinite(c)) return fail(MO_EINVAL, "non-finite hyper-parameter");
+  if (hp->beta1 < 0.f || hp->beta1 >= 1.f || hp->beta2 < 0.f || hp->beta2 >= 1.f)
+    return fail(MO_EINVAL, "betas must be in [0, 1)");
+  if (std::isnan(hp->max_norm)) return fail(MO_EINVAL, "max_norm is NaN");
+  for (int k = 0; k < hp->ns_steps; ++k)
+    for (int j = 0; j < 3; ++j)
+      if (!std::isfinite(hp->ns_coeffs[k][j])) return fail(MO_EINVAL, "non-finite coefficient");
+  mo_plan* P = new (std::nothrow) mo_plan();
+  if (!P) return fail(MO_EINVAL, "out of host memory");
+  P->params.assign(params, params + n);
+  P->hp = *hp;
+  mo_status s = build_plan(P);
+  if (s != MO_OK) {
+    delete P;
+    return s;
+  }
+  *out = P;
+  return MO_OK;
+}
+
+void mo_plan_destroy(mo_plan* plan) {
+  if (!plan) return;
+  if (plan->dtab) (void)hipFree(plan->dtab);
+  delete plan;
+}
+
+size_t mo_plan_workspace_bytes(const mo_plan* plan) { return plan ? plan->ws_total : 0; }
+
+mo_status mo_plan_route(const mo_plan* plan, mo_route_out* out, int32_t n) {
+  clear_error();
+  if (!plan || !out || n < static_cast<int32_t>(plan->routes.size()))
+    return fail(MO_EINVAL, "bad arguments");
+  std::memcpy(out, plan->routes.data(), plan->routes.size() * sizeof(mo_route_out));
+  return MO_OK;
+}
+
+int32_t mo_plan_num_slices(const mo_plan* plan) {
+  return plan ? static_cast<int32_t>(plan->slices.size()) : 0;
+}
+
+mo_status mo_plan_slices(const mo_plan* plan, int64_t* out4, int32_t max_slices) {
+  clear_error();
+  if (!plan || !out4 || max_slices < static_cast<int32_t>(plan->slices.size()))
+    return fail(MO_EINVAL, "bad arguments");
+  for (size_t k = 0; k < plan->slices.size(); ++k) {
+    out4[4 * k] = plan->slices[k].param;
+    out4[4 * k + 1] = plan->slices[k].off;
+    out4[4 * k + 2] = plan->slices[k].rows;
+    out4[4 * k + 3] = plan->slices[k].cols;
+  }
+  return MO_OK;
+}
+
+mo_status mo_plan_get_steps(const mo_plan* plan, int32_t* steps, int32_t n) {
+  clear_error();
+  if (!plan || !steps || n < static_cast<int32_t>(plan->steps.size()))
+    return fail(MO_EINVAL, "bad arguments");
+  std::memcpy(steps, plan->steps.data(), plan->steps.size() * sizeof(int32_t));
+  return MO_OK;
+}
+
+mo_status mo_plan_set_steps(mo_plan* plan, const int32_t* steps, int32_t n) {
+  clear_error();
+  if (!plan || !steps || n < static_cast<int32_t>(plan->steps.size()))
+    return fail(MO_EINVAL, "bad arguments");
+  for (size_t i = 0; i < plan->steps.size(); ++i)
+    if (steps[i] < 0) return fail(MO_EINVAL, "negative step counter");
+  std::memcpy(plan->steps.data(), steps, plan->steps.size() * sizeof(int32_t));
+  plan->dirty = true;
+  return MO_OK;
+}
+
+mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t ws_bytes,
+                          void* stream) {
+  clear_error();
+  if (!P) return fail(MO_EINVAL, "NULL plan");
+  if (P->ws_total) {
+    if (!ws) return fail(MO_EWORKSPACE, "workspace of %zu bytes required", P->ws_total);
+    if (reinterpret_cast<uintptr_t>(ws) & 255u)
+      return fail(MO_EALIGN, "workspace must be 256-byte aligned");
+    if (ws_bytes < P->ws_total)
+      return fail(MO_EWORKSPACE, "workspace has %zu bytes, %zu required", ws_bytes, P->ws_total);
+  }
+  const mo_hparams& hp = P->hp;
+  const float muon_lr = args && args->muon_lr >= 0.f ? args->muon_lr : hp.muon_lr;
+  const float adamw_lr = args && args->adamw_lr >= 0.f ? args->adamw_lr : hp.adamw_lr;
+  if (!std::isfinite(muon_lr) || !std::isfinite(adamw_lr))
+    return fail(MO_EINVAL, "non-finite learning rate");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  mo_status s;
+  if (P->dirty || P->uploaded_ws != ws) {
+    if ((s = upload_tables(P, base, st)) != MO_OK) return s;
+  }
+  const int nsl = static_cast<int>(P->active.size());
+  if (nsl > 0) {
+    StatPartial* stats = reinterpret_cast<StatPartial*>(base + P->ws_stats);
+    float* scale = reinterpret_cast<float*>(base + P->ws_scale);
+    void* pool = base + P->ws_pool;
+    const char* dns = P->dtab + P->tab_ns;
+    const PrepItem* dprep = reinterpret_cast<const PrepItem*>(dns + P->nst.prep);
+    if ((s = launch_momentum(reinterpret_cast<const MomSeg*>(P->dtab + P->tab_mom), nsl,
+                             P->mom_blocks, hp.mu, hp.nesterov, stats, st)) != MO_OK)
+      return s;
+    if ((s = launch_ns_scale(dprep, nsl, stats, scale, st)) != MO_OK) return s;
+    if ((s = launch_ns_prep(dprep, nsl, P->ns.prep_tiles, scale, pool, P->ns.elem, st)) != MO_OK)
+      return s;
+    float coeffs[3 * MO_NS_MAX_STEPS];
+    for (int k = 0; k < hp.ns_steps; ++k)
+      for (int j = 0; j < 3; ++j) coeffs[3 * k + j] = hp.ns_coeffs[k][j];
+    if ((s = ns_run_iterations(P->ns, dns, P->nst, pool, coeffs, hp.ns_steps, st)) != MO_OK)
+      return s;
+    RowSeg none;
+    std::memset(&none, 0, sizeof(none));
+    if ((s = launch_rows(hp.normuon ? kRowNormUpdate : kRowUpdate,
+                         reinterpret_cast<const RowSeg*>(P->dtab + P->tab_rows), nsl, none,
+                         P->total_rows, muon_lr, hp.normuon_beta2, hp.normuon_eps, st)) != MO_OK)
+      return s;
+  }
+  if (P->n_adam > 0) {
+    const AdamSeg* dad = reinterpret_cast<const AdamSeg*>(P->dtab + P->tab_adam);
+    double* partials = reinterpret_cast<double*>(base + P->ws_adam_partials);
+    double* scal = reinterpret_cast<double*>(base + P->ws_adam_scal);
+    if ((s = launch_adam_sumsq(dad, P->n_adam, P->adam_blocks, partials, st)) != MO_OK) return s;
+    if ((s = launch_adam_norm(partials, P->adam_blocks, hp.max_norm, scal,
+                              args ? args->norm_out : nullptr, st)) != MO_OK)
+      return s;
+    if ((s = launch_adam_apply(dad, P->n_adam, P->adam_blocks, scal, adamw_lr, hp.beta1,
+                               hp.beta2, hp.eps, P->tdelta, st)) != MO_OK)
+      return s;
+  } else if (args && args->norm_out) {
+    // no AdamW gradient: report T = 0 (a kernel write, not a memset node)
+    if ((s = launch_adam_norm(nullptr, 0, hp.max_norm,
+                              reinterpret_cast<double*>(base + P->ws_adam_scal), args->norm_out,
+                              st)) != MO_OK)
+      return s;
+  }
+  for (size_t i = 0; i < P->params.size(); ++i)
+    if (P->routes[i].algorithm == MO_ALG_ADAMW && P->params[i].grad) ++P->steps[i];
+  ++P->tdelta;
+  return MO_OK;
+}
+
+}  // extern "C"

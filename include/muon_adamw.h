@@ -1,0 +1,348 @@
+/*
+ * muon_adamw.h - C ABI of the MI355X (gfx950) hybrid Muon + AdamW optimizer step.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers are DEVICE pointers owned by the caller; descriptor arrays
+ *   (items, params, coefficient tables, descs) are HOST pointers read during
+ *   the call only.  The library never allocates tensor memory.  Scratch space
+ *   is the caller's workspace (`ws`, `ws_bytes`, device, 256-byte aligned);
+ *   each entry point that needs one has a *_workspace_bytes() query.
+ * - Every computing call enqueues on `stream` (a hipStream_t; NULL = the
+ *   default stream) and returns without synchronising.
+ * - Everything is validated before anything is enqueued: a non-MO_OK status
+ *   means no tensor was modified.  mo_last_error() then holds a message
+ *   (thread-local).  No C++ exception crosses this boundary.
+ * - Storage dtypes: MO_F32 (IEEE binary32) and MO_BF16 (upper half of a
+ *   binary32; conversions round to nearest, ties to even).  Optimizer states
+ *   (momentum, exp_avg, exp_avg_sq, NorMuon v) are always fp32.
+ * - Matrices are row-major; `ld` is the row stride in elements.  Vector loads
+ *   need 16-byte aligned base pointers (MO_EALIGN otherwise).
+ * - Calls that share a workspace must be ordered on one stream.
+ */
+#ifndef MUON_ADAMW_H
+#define MUON_ADAMW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mo_status {
+  MO_OK = 0,
+  MO_EINVAL = 1,      /* bad argument (NULL pointer, negative size, bad hyper-parameter) */
+  MO_ESHAPE = 2,      /* view / split does not match the stored shape */
+  MO_ECONFLICT = 3,   /* two different views registered for one parameter identity */
+  MO_EEMPTY = 4,      /* no trainable parameter */
+  MO_EDTYPE = 5,      /* unsupported dtype */
+  MO_EWORKSPACE = 6,  /* workspace missing or too small */
+  MO_EHIP = 7,        /* a HIP runtime call failed */
+  MO_EALIGN = 8       /* pointer not 16-byte aligned */
+} mo_status;
+
+typedef enum mo_dtype { MO_F32 = 0, MO_BF16 = 1 } mo_dtype;
+
+/* Arithmetic of the Newton-Schulz products: bf16 operands with fp32
+ * accumulation (MFMA bf16), or fp32 operands with fp32 accumulation. */
+typedef enum mo_ns_precision { MO_NS_BF16 = 0, MO_NS_F32 = 1 } mo_ns_precision;
+
+typedef enum mo_role { MO_ROLE_MATRIX = 0, MO_ROLE_EMBEDDING = 1, MO_ROLE_HEAD = 2,
+                       MO_ROLE_NORM = 3 } mo_role;
+
+typedef enum mo_algorithm { MO_ALG_SKIP = -1, MO_ALG_ADAMW = 0, MO_ALG_MUON = 1 } mo_algorithm;
+
+#define MO_MAX_NDIM 8
+#define MO_MAX_SPLIT 8
+#define MO_NS_MAX_STEPS 64
+
+const char* mo_status_str(mo_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* mo_last_error(void);
+/* Library version string. */
+const char* mo_version(void);
+/* sizeof() of the ABI structs, for binding self-checks: 0 mo_momentum_item,
+ * 1 mo_ns_item, 2 mo_adamw_item, 3 mo_param_desc, 4 mo_route_out, 5 mo_param,
+ * 6 mo_hparams, 7 mo_step_args; 0 for any other index. */
+size_t mo_abi_struct_size(int32_t which);
+
+/* ------------------------------------------------------------------------
+ * muon_momentum - Muon momentum buffer and Nesterov direction.
+ *
+ * Per item, elementwise:  B <- mu * B + G;  D <- G + mu * B (nesterov != 0,
+ * using the updated B) or D <- B (nesterov == 0).
+ * Source: OMN "Dual-Manifold Optimization" page, Muon-path paragraph (buffer
+ * accumulating gradients at 0.95, Nesterov-style direction adding the scaled
+ * buffer back to the gradient, zeros-initialised buffer); NorMuon paper,
+ * section 2.2, eq. (1).
+ *   grad      device, `grad_dtype`, numel elements, read only.  NULL = no
+ *             gradient this step: the item is skipped (buffer untouched).
+ *   momentum  device fp32, numel elements, updated in place.
+ *   dir       device, `dir_dtype`, numel elements, written.  May be NULL
+ *             (only the buffer is updated).
+ * Workspace: muon_momentum_workspace_bytes(n) bytes (descriptor table).
+ * ------------------------------------------------------------------------ */
+typedef struct mo_momentum_item {
+  const void* grad;
+  float* momentum;
+  void* dir;
+  int64_t numel;
+  int32_t grad_dtype;
+  int32_t dir_dtype;
+} mo_momentum_item;
+
+size_t muon_momentum_workspace_bytes(int32_t n);
+mo_status muon_momentum(const mo_momentum_item* items, int32_t n, float mu, int32_t nesterov,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * ns_orthogonalize_batched - Newton-Schulz orthogonalisation of many
+ * independent matrices.
+ *
+ * Per item (one independent matrix D of rows x cols, e.g. one slice of a
+ * registered view):
+ *   alpha = max(max|D|, 1e-7);  X = D / alpha;  X <- X / (||X||_F + 1e-7);
+ *   if rows > cols: X <- X^T   (the Gram is formed on the short side);
+ *   for k in 0..steps-1, (a, b, c) = coeffs[k]:
+ *       A = X X^T;  X <- a X + (b A + c A A) X;
+ *   orientation restored; out = X (in out_dtype).
+ * Source: OMN page, Muon-path paragraphs (fp32 direction, max-abs rescale
+ * clamped at 1e-7, Frobenius normalisation with epsilon, transpose when tall,
+ * five polynomial iterations, orientation restored); NorMuon paper section
+ * 2.2 eq. (5) for the (a, b, c) iteration; MuonClip page, "Newton-Schulz
+ * Orthogonalization", for the cubic set (1.5, -0.5, 0).
+ *   items[i].in   device, in_dtype, rows x cols with row stride ld_in.
+ *   items[i].out  device, out_dtype, rows x cols with row stride ld_out; may
+ *                 alias `in` (the input is fully consumed first).
+ *   coeffs        host, [steps][3] floats (a, b, c) per iteration,
+ *                 1 <= steps <= MO_NS_MAX_STEPS.
+ *   precision     mo_ns_precision.
+ * Workspace: ns_workspace_bytes(items, n, precision).  All sizes must be >= 1
+ * and cols, rows <= 65536.
+ * ------------------------------------------------------------------------ */
+typedef struct mo_ns_item {
+  const void* in;
+  void* out;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld_in;
+  int64_t ld_out;
+  int32_t in_dtype;
+  int32_t out_dtype;
+} mo_ns_item;
+
+size_t ns_workspace_bytes(const mo_ns_item* items, int32_t n, int32_t precision);
+mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const float* coeffs,
+                                   int32_t steps, int32_t precision, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * normuon_rownorm - NorMuon per-row second-moment normalisation, in place.
+ *
+ * For each row i of O (rows x cols, stride ld):
+ *   ms_i = (1/cols) sum_j O_ij^2;  v_i <- beta2 v_i + (1 - beta2) ms_i;
+ *   O_ij <- O_ij / (sqrt(v_i) + eps).
+ * Source: NorMuon paper, section 3.1 (per-neuron second moment v in R^m,
+ * mean square of each row of O_t, EMA with decay beta2, row-wise
+ * normalisation after orthogonalisation).  v_0 = 0 is the caller's zeroed
+ * buffer; no bias correction.
+ *   O  device, dtype, updated in place.   v  device fp32 [rows], in-out.
+ * ------------------------------------------------------------------------ */
+mo_status normuon_rownorm(void* O, int32_t dtype, int64_t rows, int64_t cols, int64_t ld,
+                          float* v, float beta2, float eps, void* stream);
+
+/* ------------------------------------------------------------------------
+ * muon_update - scaled Muon weight update.
+ *
+ *   W <- W (1 - lr wd) - lr * scale * U      (rows x cols)
+ * with scale normally sqrt(max(1, rows/cols)) of the independent matrix.
+ * Source: NorMuon paper section 2.2 eq. (3); OMN page, rectangular-scaling
+ * paragraph (sqrt(max(1, m/n)), m x n in out-by-in orientation); decoupled
+ * weight decay is zero in the OMN recipe (weight-decay paragraph).
+ *   W  device, w_dtype, stride ld_w, in place.   U  device, u_dtype, ld_u.
+ * ------------------------------------------------------------------------ */
+mo_status muon_update(void* W, int32_t w_dtype, const void* U, int32_t u_dtype, int64_t rows,
+                      int64_t cols, int64_t ld_w, int64_t ld_u, float lr, float wd, float scale,
+                      void* stream);
+
+/* ------------------------------------------------------------------------
+ * adamw_clip_step - AdamW over a set of parameters with one global-norm clip.
+ *
+ *   T = sqrt(sum over every item with a gradient of sum G^2)   (fp64)
+ *   kappa = max_norm / T if max_norm > 0 and T > max_norm, else 1
+ *   per element: g = kappa G;  m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2;
+ *   W <- W (1 - lr wd) - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ * Source: OMN page, recipe paragraph (betas (0.90, 0.95), epsilon 1e-8,
+ * clipping at 1.0 over AdamW parameters only, zero decay); Qwen3.8 optimizer
+ * notes, Adam / AdamW background (bias-corrected moments, decoupled decay).
+ *   items[i].param       device, dtype, numel, in place.
+ *   items[i].grad        device, dtype, numel, read only; NULL = skipped
+ *                        (not in T, param and moments untouched).
+ *   items[i].exp_avg     device fp32 m;  items[i].exp_avg_sq  device fp32 v.
+ *   items[i].step        t >= 1 of this update (caller increments).
+ *   items[i].weight_decay  decoupled decay of the item's group.
+ *   norm_out             device fp64 scalar receiving T (nullable).
+ * Workspace: adamw_workspace_bytes(items, n).
+ * ------------------------------------------------------------------------ */
+typedef struct mo_adamw_item {
+  void* param;
+  const void* grad;
+  float* exp_avg;
+  float* exp_avg_sq;
+  int64_t numel;
+  int32_t dtype;
+  int32_t step;
+  float weight_decay;
+  float reserved;
+} mo_adamw_item;
+
+size_t adamw_workspace_bytes(const mo_adamw_item* items, int32_t n);
+mo_status adamw_clip_step(const mo_adamw_item* items, int32_t n, float lr, float beta1,
+                          float beta2, float eps, float max_norm, double* norm_out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host-only: routing predicate and view expansion (no GPU needed).
+ *
+ * mo_route follows the kimi-k3 "build_parameter_groups" page ("Exclusion and
+ * decay rules"; "Classification happens once per original parameter
+ * identity"), with the OMN page's routing paragraph for the embedding:
+ *   requires_grad == 0, or an identity already seen    -> MO_ALG_SKIP
+ *   ndim < 2 or no_decay                               -> AdamW, decay 0
+ *   ndim == 2 and role not embedding/head              -> Muon (view, split), decay 1
+ *   otherwise                                          -> AdamW, decay 1
+ * Groups are keyed by (algorithm, view, split, decay) in order of first
+ * appearance; out[i].group is the group index (-1 when skipped).  Views are
+ * validated ("Recording independent matrix geometry"): MO_ESHAPE for a bad
+ * view or split, MO_ECONFLICT for two views on one identity, MO_EEMPTY when
+ * nothing is trainable.
+ * ------------------------------------------------------------------------ */
+typedef struct mo_param_desc {
+  const char* name;       /* informational, may be NULL */
+  int64_t ident;          /* parameter identity: tied parameters share it */
+  int32_t ndim;
+  int32_t role;           /* mo_role */
+  int64_t shape[MO_MAX_NDIM];
+  int32_t no_decay;
+  int32_t requires_grad;
+  int32_t view_ndim;      /* 0 = no view */
+  int32_t nsplit;         /* 0 = no split */
+  int64_t view[MO_MAX_NDIM];
+  int64_t split[MO_MAX_SPLIT];
+} mo_param_desc;
+
+typedef struct mo_route_out {
+  int32_t algorithm;      /* mo_algorithm */
+  int32_t decay;          /* 0 / 1 */
+  int32_t group;          /* group index or -1 */
+  int32_t nslices;        /* independent matrices (Muon), 0 otherwise */
+} mo_route_out;
+
+mo_status mo_route(const mo_param_desc* descs, int32_t n, mo_route_out* out, int32_t* ngroups);
+
+/* Independent sub-matrices of a stored (rows, cols) weight under a view
+ * (view_ndim == 0: the whole weight).  Writes (row_offset, rows, cols)
+ * triples to out_slices[3*k ...]; *nslices receives the count even when it
+ * exceeds max_slices (then MO_EINVAL).  Source: kimi-k3 page, "The layout
+ * declarations are literal" (leading view axes flatten row-major onto the
+ * stored rows; split sizes cut each view matrix's rows). */
+mo_status mo_expand_view(int64_t rows, int64_t cols, int32_t view_ndim, const int64_t* view,
+                         int32_t nsplit, const int64_t* split, int64_t* out_slices,
+                         int32_t max_slices, int32_t* nslices);
+
+/* ------------------------------------------------------------------------
+ * Plan + grouped hybrid step over a parameter-group table.
+ *
+ * mo_plan_create routes `params` (mo_route), expands Muon views into
+ * independent slices and sizes the workspace; it is host-only.  The plan
+ * keeps the tensor pointers given here; its small device-side descriptor
+ * tables are allocated and uploaded on the first mo_grouped_step call and
+ * freed by mo_plan_destroy.
+ *
+ * mo_grouped_step runs one full hybrid step on `stream`:
+ *   Muon params with a grad: muon_momentum -> per-slice Newton-Schulz ->
+ *     [NorMuon row normalisation] -> shape scale -> update (lr, wd if the
+ *     routing key decays);
+ *   AdamW params with a grad: adamw_clip_step over all of them jointly
+ *     (decay only for decaying groups); the per-parameter step counter t is
+ *     kept by the plan and incremented after each call.
+ * Sources: as for the individual entry points above; the ordering of NorMuon
+ * before the shape scale is this library's reading (the pages do not order
+ * them).
+ * ------------------------------------------------------------------------ */
+typedef struct mo_param {
+  mo_param_desc desc;
+  void* param;            /* device W (dtype) */
+  const void* grad;       /* device G (dtype); NULL = no gradient (skipped) */
+  int32_t dtype;          /* mo_dtype of W and G */
+  int32_t reserved;
+  float* momentum;        /* Muon: fp32, numel */
+  float* normuon_v;       /* Muon with NorMuon: fp32, rows; else NULL */
+  float* exp_avg;         /* AdamW: fp32, numel */
+  float* exp_avg_sq;      /* AdamW: fp32, numel */
+} mo_param;
+
+typedef struct mo_hparams {
+  float muon_lr;
+  float muon_wd;
+  float mu;
+  int32_t nesterov;
+  int32_t ns_steps;
+  int32_t ns_precision;                       /* mo_ns_precision */
+  float ns_coeffs[MO_NS_MAX_STEPS][3];        /* (a, b, c) per iteration */
+  int32_t normuon;
+  float normuon_beta2;
+  float normuon_eps;
+  float adamw_lr;
+  float beta1;
+  float beta2;
+  float eps;
+  float adamw_wd;
+  float max_norm;
+} mo_hparams;
+
+typedef struct mo_step_args {
+  float muon_lr;          /* < 0: use the plan's hparams */
+  float adamw_lr;         /* < 0: use the plan's hparams */
+  double* norm_out;       /* device fp64 scalar receiving the AdamW pre-clip norm T (nullable) */
+} mo_step_args;
+
+typedef struct mo_plan mo_plan;
+
+mo_status mo_plan_create(const mo_param* params, int32_t n, const mo_hparams* hp,
+                         mo_plan** out);
+void mo_plan_destroy(mo_plan* plan);
+size_t mo_plan_workspace_bytes(const mo_plan* plan);
+/* Host queries for tests: routing of each param and the slice table. */
+mo_status mo_plan_route(const mo_plan* plan, mo_route_out* out, int32_t n);
+int32_t mo_plan_num_slices(const mo_plan* plan);
+/* (param index, row_offset, rows, cols) per slice. */
+mo_status mo_plan_slices(const mo_plan* plan, int64_t* out4, int32_t max_slices);
+/* AdamW step counters (per param, plan order; 0 for non-AdamW). */
+mo_status mo_plan_get_steps(const mo_plan* plan, int32_t* steps, int32_t n);
+mo_status mo_plan_set_steps(mo_plan* plan, const int32_t* steps, int32_t n);
+mo_status mo_grouped_step(mo_plan* plan, const mo_step_args* args, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing (diagnostics).  While enabled, every kernel launch of this
+ * library is bracketed by two HIP events recorded on the launch's own
+ * stream.  mo_timing_read waits for the recorded events of one kernel class
+ * and returns their summed duration (ms) and launch count.  Enabling (on=1)
+ * or disabling (on=0) clears earlier records.  Host thread safe.
+ * ------------------------------------------------------------------------ */
+typedef enum mo_kernel_class {
+  MO_KC_MOMENTUM = 0, MO_KC_NS_STATS = 1, MO_KC_NS_SCALE = 2, MO_KC_NS_PREP = 3,
+  MO_KC_NS_GEMM = 4, MO_KC_NS_FINAL = 5, MO_KC_ROWS = 6, MO_KC_ADAM_SUMSQ = 7,
+  MO_KC_ADAM_NORM = 8, MO_KC_ADAM_APPLY = 9, MO_KC_COUNT = 10
+} mo_kernel_class;
+
+mo_status mo_timing_enable(int32_t on);
+mo_status mo_timing_read(int32_t kclass, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_ADAMW_H */

@@ -1,0 +1,187 @@
+"""GPU parity of the grouped hybrid step (mo_grouped_step) against the oracle's
+hybrid step, plus the fused-versus-separate gate/up invariant."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from adamw_optimizer_step_amd import _lib as L
+from adamw_optimizer_step_amd import api
+from oracle import muon as omuon
+from oracle.hybrid import HybridState, HyperParams, hybrid_step
+from oracle.routing import descs_from_specs
+from oracle.views import expand
+
+from gpu_common import (NS_BF16_MAXABS, NS_BF16_RELFRO, NS_F32_MAXABS, REL_F32,
+                        assert_bf16_close, f64, rel_inf, require_gpu, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def build_entries(w: wl.Workload, normuon: bool, init=None):
+    """Device tensors for a workload: W from the seeded init, zero states."""
+    entries = []
+    routes, _ = api.route([api.make_desc(p.name, p.shape, p.role, p.no_decay,
+                                         p.requires_grad, i, p.view, p.split)
+                           for i, p in enumerate(w.params)])
+    for i, (p, r) in enumerate(zip(w.params, routes)):
+        W0 = wl.init_weight(w, i) if init is None else init[i]
+        e = {"desc": api.make_desc(p.name, p.shape, p.role, p.no_decay, p.requires_grad, i,
+                                   p.view, p.split),
+             "param": to_dev(W0, p.dtype),
+             "grad": torch.zeros(p.shape, dtype=TORCH_DT[p.dtype], device="cuda"),
+             "route": r}
+        if r[0] == L.MO_ALG_MUON:
+            e["momentum"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
+            if normuon:
+                e["normuon_v"] = torch.zeros(p.shape[0], dtype=torch.float32, device="cuda")
+        elif r[0] == L.MO_ALG_ADAMW:
+            e["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
+            e["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
+        entries.append(e)
+    return entries
+
+
+def _oracle_setup(w):
+    descs = descs_from_specs(w.params)
+    for d, p in zip(descs, w.params):
+        d["dtype"] = p.dtype
+    return descs
+
+
+@pytest.mark.parametrize("precision", ["fp32", "bf16"])
+def test_grouped_tiny_three_steps(precision):
+    w = wl.tiny_routing()
+    ents = build_entries(w, normuon=False)
+    coeffs = wl.coeff_table("cubic")
+    plan = api.Plan(ents, api.make_hparams(coeffs=coeffs, ns_precision=precision))
+    descs = _oracle_setup(w)
+    st = HybridState()
+    hp = HyperParams(coeffs=coeffs)
+    Wref = {p.name: f64(e["param"]) for p, e in zip(w.params, ents)}
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    tol_ns = NS_F32_MAXABS if precision == "fp32" else NS_BF16_MAXABS
+    for step in (1, 2, 3):
+        G = {}
+        for i, (p, e) in enumerate(zip(w.params, ents)):
+            g = wl.grad(w, i, step)
+            e["grad"].copy_(to_dev(g, p.dtype))
+            G[p.name] = wl.from_storage(g, p.dtype).astype(np.float64)
+        Wold = {p.name: f64(e["param"]) for p, e in zip(w.params, ents)}
+        plan.step(norm_out=norm)
+        out = hybrid_step(descs, Wref, G, st, hp, keep_outputs=True)
+        assert abs(f64(norm)[0] - out["T"]) <= 1e-12 * out["T"]
+        for p, e in zip(w.params, ents):
+            got = f64(e["param"])
+            if p.name in out["muon"]:
+                res = out["muon"][p.name]
+                assert rel_inf(f64(e["momentum"]), res["B"]) <= REL_F32
+                dgot, dref = got - Wold[p.name], -0.01 * res["U"]
+                for off, r, c in expand(p.shape, p.view, p.split):
+                    sc = math.sqrt(max(1.0, r / c))
+                    err = np.abs(dgot[off:off + r] - dref[off:off + r]).max()
+                    assert err <= 0.01 * sc * tol_ns + 1e-7, (p.name, off, err)
+            else:
+                dgot, dref = got - Wold[p.name], out["W"][p.name] - Wold[p.name]
+                tol = REL_F32 * np.abs(dref).max() + 2 ** -23 * np.abs(got).max()
+                assert np.max(np.abs(dgot - dref)) <= tol, p.name
+                assert rel_inf(f64(e["exp_avg"]), st.m[p.name]) <= REL_F32
+                assert rel_inf(f64(e["exp_avg_sq"]), st.v[p.name]) <= REL_F32
+            Wref[p.name] = got.copy()     # continue both sides from the stored weights
+    assert plan.get_steps() == [3, 0, 0, 0, 3]
+
+
+def _small_decoder(fused: bool, normuon: bool, dtype="bf16"):
+    d, ffn = 64, 96
+    ps = [wl.ParamSpec("embed", (256, d), dtype, wl.ROLE_EMBEDDING, no_decay=True),
+          wl.ParamSpec("norm1", (d,), dtype, wl.ROLE_NORM, no_decay=True),
+          wl.ParamSpec("q", (d, d), dtype)]
+    if fused:
+        ps.append(wl.ParamSpec("gate_up", (2 * ffn, d), dtype, view=(2, ffn, d)))
+    else:
+        ps += [wl.ParamSpec("gate", (ffn, d), dtype), wl.ParamSpec("up", (ffn, d), dtype)]
+    ps.append(wl.ParamSpec("down", (d, ffn), dtype))
+    return wl.Workload("small_decoder", 7, tuple(ps), grad_std=1e-3, normuon=normuon)
+
+
+def _run_small(fused, normuon, steps=2, precision="bf16"):
+    w = _small_decoder(fused, normuon)
+    # identical data for the fused and separate layouts: build the fused
+    # weights by stacking the separate ones
+    sep = _small_decoder(False, normuon)
+    init_sep = [wl.init_weight(sep, i) for i in range(len(sep.params))]
+    grads_sep = {t: [wl.grad(sep, i, t) for i in range(len(sep.params))]
+                 for t in range(1, steps + 1)}
+    def fuse(arrs):
+        return arrs[:3] + [np.concatenate([arrs[3], arrs[4]], axis=0), arrs[5]] if fused else arrs
+    ents = build_entries(w, normuon, init=fuse(init_sep))
+    plan = api.Plan(ents, api.make_hparams(ns_precision=precision, normuon=normuon))
+    for t in range(1, steps + 1):
+        for e, g, p in zip(ents, fuse(grads_sep[t]), w.params):
+            e["grad"].copy_(to_dev(g, p.dtype))
+        plan.step()
+    return w, ents, init_sep, grads_sep
+
+
+@pytest.mark.parametrize("normuon", [False, True])
+def test_fused_gate_up_equals_separate(normuon):
+    _, fused, _, _ = _run_small(True, normuon)
+    _, sep, _, _ = _run_small(False, normuon)
+    fw = f64(fused[3]["param"])
+    assert np.array_equal(fw[:96], f64(sep[3]["param"]))
+    assert np.array_equal(fw[96:], f64(sep[4]["param"]))
+    if normuon:
+        fv = f64(fused[3]["normuon_v"])
+        assert np.array_equal(fv[:96], f64(sep[3]["normuon_v"]))
+        assert np.array_equal(fv[96:], f64(sep[4]["normuon_v"]))
+    for a, b in ((0, 0), (2, 2), (4, 5)):
+        assert np.array_equal(f64(fused[a]["param"]), f64(sep[b]["param"]))
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp32"])
+def test_grouped_normuon_parity(precision):
+    steps = 2
+    w, ents, init, grads = _run_small(False, True, steps=steps, precision=precision)
+    descs = _oracle_setup(w)
+    st = HybridState()
+    hp = HyperParams(normuon=True)
+    W = {p.name: wl.from_storage(init[i], p.dtype).astype(np.float64)
+         for i, p in enumerate(w.params)}
+    for t in range(1, steps + 1):
+        G = {p.name: wl.from_storage(grads[t][i], p.dtype).astype(np.float64)
+             for i, p in enumerate(w.params)}
+        out = hybrid_step(descs, W, G, st, hp, keep_outputs=True)
+        W = out["W"]
+    relfro = NS_BF16_RELFRO if precision == "bf16" else 1e-4
+    for i, (p, e) in enumerate(zip(w.params, ents)):
+        got = f64(e["param"])
+        W0 = wl.from_storage(init[i], p.dtype).astype(np.float64)
+        if p.name in st.B:
+            assert rel_inf(f64(e["momentum"]), st.B[p.name]) <= REL_F32
+            # NorMuon v follows the NS output's row norms: relative, per row
+            vr = st.nv[p.name]
+            assert np.max(np.abs(f64(e["normuon_v"]) - vr) / vr) <= 4 * relfro
+            dgot, dref = got - W0, W[p.name] - W0
+            # total update over the steps, relative Frobenius; bf16 storage
+            # of W adds at most half an ulp per step
+            assert np.linalg.norm(dgot - dref) / np.linalg.norm(dref) <= 2 * relfro + 2e-2
+        else:
+            assert_bf16_close(got, W[p.name], extra=bf16_extra(W[p.name]))
+
+
+def bf16_extra(x):
+    # two AdamW steps each rounded to bf16: allow one more ulp of drift
+    from gpu_common import bf16_ulp
+    return bf16_ulp(x)

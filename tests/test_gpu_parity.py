@@ -1,0 +1,242 @@
+"""GPU parity: every entry point of the HIP library against the fp64 oracle,
+on seeded inputs that span several tiles / blocks and ragged tails."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from adamw_optimizer_step_amd import api
+from oracle import adamw as oadamw
+from oracle import muon as omuon
+
+from gpu_common import (REL_F32, assert_bf16_close, assert_ns_close, f64, rel_inf,
+                        require_gpu, storage_draw, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+# --- momentum -----------------------------------------------------------------
+
+@pytest.mark.parametrize("gdt,ddt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_momentum_parity(gdt, ddt):
+    sizes = [1, 7, 8, 8192 * 2 + 5, 3 * 8192, 1000]
+    G = [storage_draw(11, 1, i, (n,), 1.0, gdt) for i, n in enumerate(sizes)]
+    B0 = [wl.draw_f32(11, 0, i, (n,), 1.0) for i, n in enumerate(sizes)]
+    g_d = [to_dev(g, gdt) for g in G]
+    b_d = [to_dev(b, "f32") for b in B0]
+    d_d = [torch.empty(n, dtype=torch.float32 if ddt == "f32" else torch.bfloat16,
+                       device="cuda") for n in sizes]
+    skip = 4                               # the 1000-element item has no gradient
+    grads = [None if i == skip else g for i, g in enumerate(g_d)]
+    api.muon_momentum(grads, b_d, d_d, mu=0.95, nesterov=True)
+    for i in range(len(sizes)):
+        if i == skip:
+            assert np.array_equal(f64(b_d[i]), B0[i].astype(np.float64))
+            continue
+        gref = wl.from_storage(G[i], gdt).astype(np.float64)
+        Bref, Dref = omuon.momentum(B0[i].astype(np.float64), gref, 0.95)
+        assert rel_inf(f64(b_d[i]), Bref) <= REL_F32
+        if ddt == "f32":
+            assert rel_inf(f64(d_d[i]), Dref) <= REL_F32
+        else:
+            assert_bf16_close(f64(d_d[i]), Dref)
+
+
+def test_momentum_no_nesterov_and_no_dir():
+    n = 20000
+    G = storage_draw(12, 1, 0, (n,), 1.0, "f32")
+    b = torch.zeros(n, device="cuda")
+    d = torch.empty(n, device="cuda")
+    api.muon_momentum([to_dev(G, "f32")], [b], [d], mu=0.9, nesterov=False)
+    np.testing.assert_array_equal(f64(b), f64(d))
+    b2 = torch.zeros(n, device="cuda")
+    api.muon_momentum([to_dev(G, "f32")], [b2], None, mu=0.9)
+    np.testing.assert_array_equal(f64(b2), f64(b))
+
+
+# --- Newton-Schulz ---------------------------------------------------------------
+
+NS_SHAPES = [(4, 8), (16, 8), (6, 8), (300, 200), (130, 700), (256, 256), (1, 64), (64, 1),
+             (129, 129), (520, 300)]
+
+
+def _ns_case(shapes, dtype, seed, std=1.0):
+    mats = [storage_draw(seed, 1, i, s, std, dtype) for i, s in enumerate(shapes)]
+    return mats, [to_dev(m, dtype) for m in mats]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind", ["cubic", "quintic"])
+def test_ns_parity_ragged_shapes(precision, kind):
+    dtype = "bf16" if precision == "bf16" else "f32"
+    mats, dev = _ns_case(NS_SHAPES, dtype, 21)
+    coeffs = wl.coeff_table(kind)
+    outs = api.ns_orthogonalize_batched(dev, coeffs=coeffs, precision=precision)
+    for m, o in zip(mats, outs):
+        ref = omuon.newton_schulz(wl.from_storage(m, dtype).astype(np.float64), coeffs)
+        assert_ns_close(f64(o), ref, precision)
+
+
+def test_ns_strided_views_and_fp32_output():
+    # row slabs of a larger weight, as a view / split produces them
+    W = storage_draw(22, 1, 0, (20, 72), 1.0, "bf16")
+    Wd = to_dev(W, "bf16")
+    parts = [Wd[0:4, :70], Wd[4:10, :70], Wd[10:20, 2:72]]
+    outs = [torch.empty(p.shape, dtype=torch.float32, device="cuda") for p in parts]
+    api.ns_orthogonalize_batched(parts, outs, coeffs=wl.coeff_table("cubic"))
+    Wf = wl.from_storage(W, "bf16").astype(np.float64)
+    for (r0, r1, c0, c1), o in zip([(0, 4, 0, 70), (4, 10, 0, 70), (10, 20, 2, 72)], outs):
+        ref = omuon.newton_schulz(Wf[r0:r1, c0:c1], wl.coeff_table("cubic"))
+        assert_ns_close(f64(o), ref, "bf16")
+
+
+def test_ns_degenerate_inputs():
+    z = torch.zeros(33, 17, dtype=torch.bfloat16, device="cuda")
+    u = torch.linspace(-1, 1, 40, device="cuda")
+    r1 = (u[:, None] * torch.linspace(0.5, 2, 24, device="cuda")[None, :]).float()
+    tiny = torch.full((5, 9), 1e-30, dtype=torch.float32, device="cuda")
+    outs = api.ns_orthogonalize_batched([z, r1, tiny], coeffs=wl.coeff_table("cubic"),
+                                        precision="fp32")
+    assert torch.all(outs[0] == 0)
+    ref = omuon.newton_schulz(f64(r1), wl.coeff_table("cubic"))
+    assert_ns_close(f64(outs[1]), ref, "fp32")
+    np.testing.assert_allclose(f64(outs[1]), f64(r1) / np.linalg.norm(f64(r1)), atol=1e-4)
+    ref = omuon.newton_schulz(f64(tiny), wl.coeff_table("cubic"))
+    assert np.all(np.isfinite(f64(outs[2])))
+    assert_ns_close(f64(outs[2]), ref, "fp32")
+
+
+def test_ns_prescribed_spectrum_spike():
+    # ill-conditioned input: rank-8 spike at 100x on top of the noise
+    w = wl.ns_sweep(384, 200, "quintic")
+    G = wl.spiked_grad(w, 0, 1)
+    outs = api.ns_orthogonalize_batched([to_dev(G, "bf16")], coeffs=wl.coeff_table("quintic"))
+    ref = omuon.newton_schulz(wl.from_storage(G, "bf16").astype(np.float64),
+                              wl.coeff_table("quintic"))
+    assert_ns_close(f64(outs[0]), ref, "bf16")
+
+
+def test_ns_slice_independence():
+    mats, dev = _ns_case([(64, 96), (64, 96), (40, 96)], "bf16", 23)
+    a = [f64(o) for o in api.ns_orthogonalize_batched(dev)]
+    dev[1].mul_(-3.0)
+    b = [f64(o) for o in api.ns_orthogonalize_batched(dev)]
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[2], b[2])
+    assert not np.array_equal(a[1], b[1])
+
+
+def test_ns_deterministic():
+    _, dev = _ns_case([(200, 300), (517, 64)], "bf16", 24)
+    a = [f64(o) for o in api.ns_orthogonalize_batched(dev)]
+    b = [f64(o) for o in api.ns_orthogonalize_batched(dev)]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+# --- NorMuon row normalisation and update ------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_normuon_rownorm_parity(dtype):
+    rows, cols, ld = 37, 300, 320
+    O = storage_draw(31, 1, 0, (rows, ld), 0.05, dtype)
+    v0 = np.abs(wl.draw_f32(31, 0, 1, (rows,), 1e-3))
+    Od = to_dev(O, dtype)
+    vd = to_dev(v0, "f32")
+    api.normuon_rownorm(Od[:, :cols], vd, 0.95, 1e-8)
+    Of = wl.from_storage(O, dtype).astype(np.float64)
+    Oref, vref = omuon.normuon_rownorm(Of[:, :cols], v0.astype(np.float64), 0.95, 1e-8)
+    assert rel_inf(f64(vd), vref) <= REL_F32
+    got = f64(Od)
+    np.testing.assert_array_equal(got[:, cols:], Of[:, cols:])  # padding untouched
+    if dtype == "f32":
+        assert rel_inf(got[:, :cols], Oref) <= REL_F32
+    else:
+        assert_bf16_close(got[:, :cols], Oref)
+
+
+@pytest.mark.parametrize("wdt,udt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+def test_muon_update_parity(wdt, udt):
+    rows, cols = 50, 136
+    W = storage_draw(32, 0, 0, (rows, cols), 0.02, wdt)
+    U = storage_draw(32, 1, 1, (rows, cols), 0.03, udt)
+    Wd = to_dev(W, wdt)
+    api.muon_update(Wd, to_dev(U, udt), lr=0.01, wd=0.1, scale=1.6583)
+    Wf = wl.from_storage(W, wdt).astype(np.float64)
+    ref = omuon.apply_update(Wf, 1.6583 * wl.from_storage(U, udt).astype(np.float64), 0.01, 0.1)
+    if wdt == "f32":
+        # the update within 1e-6 (normwise), plus the fp32 rounding of W
+        dref = ref - Wf
+        tol = REL_F32 * np.abs(dref).max() + 2 ** -23 * np.abs(ref).max()
+        assert np.max(np.abs(f64(Wd) - ref)) <= tol
+    else:
+        assert_bf16_close(f64(Wd), ref)
+
+
+# --- AdamW -------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,std", [("f32", 1.0), ("bf16", 1e-3), ("bf16", 1.0)])
+def test_adamw_clip_parity_three_steps(dtype, std):
+    sizes = [8, 512, 8192 + 3, 2 * 8192, 100]
+    P = [storage_draw(41, 0, i, (n,), 0.02, dtype) for i, n in enumerate(sizes)]
+    Pd = [to_dev(p, dtype) for p in P]
+    m = [torch.zeros(n, device="cuda") for n in sizes]
+    v = [torch.zeros(n, device="cuda") for n in sizes]
+    Wref = [wl.from_storage(p, dtype).astype(np.float64) for p in P]
+    mref = [np.zeros(n) for n in sizes]
+    vref = [np.zeros(n) for n in sizes]
+    wds = [0.0, 0.1, 0.0, 0.0, 0.0]
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for t in (1, 2, 3):
+        G = [storage_draw(41, t, i, (n,), std, dtype) for i, n in enumerate(sizes)]
+        gdev = [to_dev(g, dtype) for g in G]
+        gdev[4] = None if t == 2 else gdev[4]            # a skipped gradient at t = 2
+        steps = [t, t, t, t, t if t == 1 else t - 1]
+        api.adamw_clip_step(Pd, gdev, m, v, steps, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8,
+                            weight_decay=wds, max_norm=1.0, norm_out=norm)
+        items = []
+        for i in range(len(sizes)):
+            g = None if gdev[i] is None else wl.from_storage(G[i], dtype).astype(np.float64)
+            items.append({"W": Wref[i], "G": g, "m": mref[i], "v": vref[i], "t": steps[i],
+                          "wd": wds[i]})
+        out, T, kappa = oadamw.adamw_clip_step(items, 3e-4, 0.9, 0.95, 1e-8, 0.0, 1.0)
+        assert abs(f64(norm)[0] - T) <= 1e-12 * T
+        for i, res in enumerate(out):
+            if res is None:
+                continue
+            Wn, mref[i], vref[i] = res
+            assert rel_inf(f64(m[i]), mref[i]) <= REL_F32
+            assert rel_inf(f64(v[i]), vref[i]) <= REL_F32
+            got = f64(Pd[i])
+            if dtype == "f32":
+                # fp32 weights: the update itself within 1e-6, plus rounding of W
+                dref = Wn - Wref[i]
+                dgot = got - Wref[i]
+                tol = REL_F32 * np.abs(dref).max() + 2 ** -23 * np.abs(Wn).max()
+                assert np.max(np.abs(dgot - dref)) <= tol
+                Wref[i] = got.copy()
+            else:
+                assert_bf16_close(got, Wn)
+                Wref[i] = got.copy()          # continue from the stored bf16 weights
+
+
+def test_adamw_clip_inactive_and_norm():
+    n = 4096
+    G = storage_draw(42, 1, 0, (n,), 1e-3, "bf16")       # T ~ 0.064 < 1: no clipping
+    p = to_dev(storage_draw(42, 0, 0, (n,), 0.02, "bf16"), "bf16")
+    m, v = torch.zeros(n, device="cuda"), torch.zeros(n, device="cuda")
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    api.adamw_clip_step([p], [to_dev(G, "bf16")], [m], [v], [1], lr=1e-3, norm_out=norm)
+    g = wl.from_storage(G, "bf16").astype(np.float64)
+    T = math.sqrt(np.sum(g * g))
+    assert T < 1.0 and abs(f64(norm)[0] - T) <= 1e-12
+    assert rel_inf(f64(m), 0.1 * g) <= REL_F32

@@ -31,13 +31,16 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     NaN maps to a quiet NaN; infinities and overflow to +-inf follow IEEE RNE.
     """
     a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = (u + 0x7FFF + lsb) >> 16
+    u = a.view(np.uint32)
+    # finite values stay below 0xff800000 + 0x8000, so 32-bit sums cannot wrap
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
     out = r.astype(np.uint16)
     nan = np.isnan(a)
     if nan.any():
-        out = np.where(nan, np.uint16(0x7FC0), out)
+        out[nan] = np.uint16(0x7FC0)
     return out.reshape(a.shape)
 
 
@@ -304,6 +307,27 @@ def draw_f32(config_seed: int, step: int, tensor_index: int, shape: Sequence[int
     if std != 1.0:
         x *= np.float32(std)
     return x
+
+
+def device_seed(config_seed: int, step: int, tensor_index: int) -> int:
+    """64-bit seed of the on-device stream for (config, step, tensor)."""
+    ss = np.random.SeedSequence([int(config_seed), int(step), int(tensor_index), 0xD5])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & np.uint64(0x7FFFFFFFFFFFFFFF))
+
+
+def draw_device(config_seed: int, step: int, tensor_index: int, shape: Sequence[int],
+                std: float, dtype: str, device="cuda"):
+    """Seeded draw made on the GPU with torch's Philox generator (full-size
+    workloads, where host generation would take minutes).  Drawn in fp32,
+    scaled, then rounded to the storage dtype by torch (round to nearest even).
+    Read the tensor back to give the oracle exactly the same bytes."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(device_seed(config_seed, step, tensor_index))
+    x = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x if dtype == "f32" else x.to(torch.bfloat16)
 
 
 def init_weight(w: Workload, index: int) -> np.ndarray:
