@@ -115,7 +115,7 @@ def cpu_baseline(w, coeffs, normuon, budget_s: float):
     adam_elems = 0
     for i, p in enumerate(w.params):
         if len(p.shape) == 2 and p.role == "matrix":
-            key = tuple(sorted((r, c)) for _, r, c in expand(p.shape, p.view, p.split))
+            key = tuple(tuple(sorted((r, c))) for _, r, c in expand(p.shape, p.view, p.split))
             shapes.setdefault(key, [i, 0])[1] += 1
         else:
             adam_elems += p.numel

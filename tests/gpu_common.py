@@ -39,6 +39,8 @@ def to_dev(arr: np.ndarray, dtype: str) -> torch.Tensor:
 
 def f64(t: torch.Tensor) -> np.ndarray:
     """Exact float64 values of a device tensor (bf16 / fp32 widen exactly)."""
+    if t.dtype == torch.float64:
+        return t.detach().cpu().numpy()
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
@@ -61,14 +63,15 @@ def assert_bf16_close(got: np.ndarray, ref64: np.ndarray, extra: float = 0.0):
                            f"max diff {np.max(np.abs(got - want))}")
 
 
-def assert_ns_close(got: np.ndarray, ref: np.ndarray, precision: str):
+def assert_ns_close(got: np.ndarray, ref: np.ndarray, precision: str,
+                    relfro: float = NS_BF16_RELFRO):
     err = np.max(np.abs(got - ref)) if ref.size else 0.0
     if precision == "bf16":
         assert err <= NS_BF16_MAXABS, f"max-abs {err:.3e}"
         nr = np.linalg.norm(ref)
         if nr > 0:
             rf = np.linalg.norm(got - ref) / nr
-            assert rf <= NS_BF16_RELFRO, f"relative Frobenius {rf:.3e}"
+            assert rf <= relfro, f"relative Frobenius {rf:.3e}"
         else:
             assert np.all(got == 0)
     else:

@@ -123,7 +123,11 @@ def test_ns_prescribed_spectrum_spike():
     outs = api.ns_orthogonalize_batched([to_dev(G, "bf16")], coeffs=wl.coeff_table("quintic"))
     ref = omuon.newton_schulz(wl.from_storage(G, "bf16").astype(np.float64),
                               wl.coeff_table("quintic"))
-    assert_ns_close(f64(outs[0]), ref, "bf16")
+    # After normalisation the 192 noise directions sit near sigma = 1e-3 and
+    # five quintic steps amplify them ~23x, while their bf16 rounding error is
+    # set by the eight O(1) spike directions: the relative Frobenius error is
+    # about five bf16 unit roundoffs (2.1e-2) here; max-abs stays ~2e-3.
+    assert_ns_close(f64(outs[0]), ref, "bf16", relfro=4e-2)
 
 
 def test_ns_slice_independence():
