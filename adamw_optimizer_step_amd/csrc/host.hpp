@@ -19,14 +19,25 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
 
 // Newton-Schulz layout of a batch of independent matrices: padded pool
 // buffers per matrix and the GEMM / prep problem tables (pool offsets only;
-// device pointers and statistics ranges are filled by the caller).
+// device pointers and statistics ranges are filled by the caller).  Matrices
+// are bucketed by GEMM tile size: short side >= kBigTileMinS -> 256 x 256
+// tiles, otherwise 128 x 128; each bucket has its own tables and launches.
+constexpr int kBigTile = 256;
+constexpr int kBigTileMinS = 512;
+
+struct NsBucket {
+  int tile = kGemmTile;
+  std::vector<GemmProb> gram_p, gram_a, square, upd0, upd1;
+  int64_t gram_tiles = 0, square_tiles = 0, upd_tiles = 0;
+};
+
 struct NsLayout {
   int elem = 2;
   bool need_a = false;
   int n = 0;
   std::vector<PrepItem> prep;
-  std::vector<GemmProb> gram_p, gram_a, square, upd0, upd1;
-  int64_t prep_tiles = 0, gram_tiles = 0, square_tiles = 0, upd_tiles = 0;
+  std::vector<NsBucket> buckets;
+  int64_t prep_tiles = 0;
   std::vector<int64_t> x_off, xt_off0, xt_off1;
   std::vector<int32_t> tall, sp, lp;
   int64_t pool_elems = 0;
@@ -42,8 +53,12 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
                      bool need_a);
 
 // Byte offsets of the device tables inside one contiguous table block.
+struct NsBucketTables {
+  size_t gram_p = 0, gram_a = 0, square = 0, upd0 = 0, upd1 = 0;
+};
 struct NsTables {
-  size_t prep = 0, gram_p = 0, gram_a = 0, square = 0, upd0 = 0, upd1 = 0, bytes = 0;
+  size_t prep = 0, bytes = 0;
+  std::vector<NsBucketTables> b;
 };
 NsTables ns_table_offsets(const NsLayout& L);
 void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf);

@@ -97,7 +97,7 @@ mo_status launch_rows(int32_t mode, const RowSeg* segs, int nseg, const RowSeg& 
 
 // ----- Newton-Schulz ------------------------------------------------------------
 constexpr int kPrepTile = 64;   // prep / stats tile edge
-constexpr int kGemmTile = 128;  // GEMM tile edge (M and N); matrices are padded to it
+constexpr int kGemmTile = 128;  // small GEMM tile edge (M and N); matrices are padded to their tile
 
 struct PrepItem {
   const void* in;          // D in stored orientation, rows r x cols c, stride ld_in
@@ -118,11 +118,13 @@ struct GemmProb {
   int64_t c_off;           // direct output
   int64_t ct_off;          // transposed output, -1 = none
   int64_t e_off;           // epilogue input (same layout as c), -1 = none
-  int32_t lda, ldb, ldc, ldct, lde;
+  int64_t et_off;          // epilogue input in the transposed layout (for ct)
+  int32_t lda, ldb, ldc, ldct, lde, ldet;
   int32_t K;
   int32_t tiles_m, tiles_n;
   int32_t sym;             // only tiles (i <= j); mirror written through ct
   int32_t start;           // first tile of this problem
+  int32_t pad;
 };
 
 struct FinalItem {         // NS output copy (stored orientation)
@@ -144,9 +146,10 @@ mo_status launch_ns_scale(const PrepItem* items, int n, const StatPartial* parti
 // X0 (scaled, padded, both orientations) into the pool.  elem = 2 (bf16) or 4.
 mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const float* scale,
                          void* pool, int elem, hipStream_t st);
-// One batched GEMM phase:  out = c0 * E + c1 * (A_op B_op^T).
-mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, void* pool, int elem,
-                         float c0, float c1, int has_e, hipStream_t st);
+// One batched GEMM phase:  out = c0 * E + c1 * (A_op B_op^T), with square
+// workgroup tiles of edge `tile` (128 or 256; the problems' padding).
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, void* pool,
+                         int elem, float c0, float c1, int has_e, hipStream_t st);
 mo_status launch_ns_final(const FinalItem* items, int n, int64_t total_rows, const void* pool,
                           int elem, hipStream_t st);
 

@@ -12,6 +12,8 @@
 // The update writes X' in place and its transpose into the other X^T buffer.
 // Zero padding stays zero through every product, so no bounds checks are
 // needed inside the GEMM.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace mo {
@@ -127,20 +129,64 @@ __global__ __launch_bounds__(kThreads) void k_ns_final(const FinalItem* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Batched NT GEMM on MFMA: 128 x 128 tile per 256-thread workgroup, 4 waves
-// in 2 x 2, each wave 64 x 64 = 2 x 2 blocks of the 32x32 MFMA.  K is staged
-// through LDS 128 bytes of every row at a time (64 bf16 / 32 fp32) with a
-// 16-byte XOR swizzle, double-buffered; the next K slab is prefetched into
-// registers while the current one is multiplied.
+// Batched NT GEMM on MFMA (32x32x16 bf16, or 32x32x2 fp32), templated on the
+// workgroup tile BM x BN and the wave grid WM x WN (64 * WM * WN threads).
+// Each wave owns a (BM/WM) x (BN/WN) sub-tile of FM x FN 32x32 blocks.  K is
+// staged through LDS 128 bytes of every row at a time (64 bf16 / 32 fp32),
+// double-buffered, with the next slab prefetched into registers while the
+// current one is multiplied.  The LDS traffic per MFMA falls as the wave
+// sub-tile grows: (FM + FN) fragment reads feed FM * FN MFMAs.
 // ---------------------------------------------------------------------------
 constexpr int kRowBytes = 128;
-constexpr int kStageBytes = 2 * kGemmTile * kRowBytes;   // A + B slabs: 32 KiB
-constexpr int kCsLd = 132;                               // epilogue tile stride (floats)
-constexpr int kLdsBytes = kGemmTile * kCsLd * 4;         // 66 KiB (>= 2 stages)
-static_assert(kLdsBytes >= 2 * kStageBytes, "epilogue tile must cover both stages");
 
+// 16-byte chunk c of LDS row `row` lives at chunk c ^ f(row), f(r) = (r + r/8)
+// mod 8: any 8 consecutive rows, and the 8 rows of one parity among any 16
+// consecutive rows, see distinct chunks, so the MFMA operand reads (32 rows,
+// one chunk) are conflict-free for both 128-byte and 256-byte bank windows.
 __device__ __forceinline__ int swz(int row, int c16) {
-  return row * kRowBytes + ((c16 ^ (row & 7)) << 4);
+  return row * kRowBytes + ((c16 ^ ((row + (row >> 3)) & 7)) << 4);
+}
+
+// Tile order inside one problem.  Non-symmetric problems go by groups of 8
+// tile-rows (column-major inside a group), so the workgroups resident at one
+// time share both operand row blocks; symmetric problems (upper triangle
+// only) go by 4 x 4 super-tiles of the triangle.
+constexpr int kGroupRows = 8;
+constexpr int kSuper = 4;
+
+__device__ __forceinline__ void decode_tile(int t, int tm, int tn, int sym, int& ti, int& tj) {
+  if (!sym) {
+    const int per = kGroupRows * tn;
+    const int g = t / per;
+    const int first = g * kGroupRows;
+    const int gsz = min(tm - first, kGroupRows);
+    const int r = t - g * per;
+    ti = first + r % gsz;
+    tj = r / gsz;
+    return;
+  }
+  const int ts = (tm + kSuper - 1) / kSuper;
+  for (int bi = 0; bi < ts; ++bi) {
+    const int hi = min(kSuper, tm - bi * kSuper);
+    for (int bj = bi; bj < ts; ++bj) {
+      const int wj = min(kSuper, tm - bj * kSuper);
+      const int cnt = bi == bj ? hi * (hi + 1) / 2 : hi * wj;
+      if (t < cnt) {
+        if (bi == bj) {
+          int i = 0, len = hi;
+          while (t >= len) { t -= len; ++i; --len; }
+          ti = bi * kSuper + i;
+          tj = bi * kSuper + i + t;
+        } else {
+          ti = bi * kSuper + t / wj;
+          tj = bj * kSuper + t % wj;
+        }
+        return;
+      }
+      t -= cnt;
+    }
+  }
+  ti = tj = 0;  // unreachable for t inside the problem's tile count
 }
 
 template <typename T>
@@ -199,11 +245,87 @@ __device__ __forceinline__ void st8<float>(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void k_ns_gemm(const GemmProb* __restrict__ probs,
-                                                         int nprob, T* __restrict__ pool,
-                                                         float c0, float c1, int has_e) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+__device__ __forceinline__ void ld4(const T* p, float* v);
+template <>
+__device__ __forceinline__ void ld4<uint16_t>(const uint16_t* p, float* v) {
+  const u32x2 u = *reinterpret_cast<const u32x2*>(p);
+  v[0] = __uint_as_float(u[0] << 16);
+  v[1] = __uint_as_float(u[0] & 0xffff0000u);
+  v[2] = __uint_as_float(u[1] << 16);
+  v[3] = __uint_as_float(u[1] & 0xffff0000u);
+}
+template <>
+__device__ __forceinline__ void ld4<float>(const float* p, float* v) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) v[k] = a[k];
+}
+
+template <typename T>
+__device__ __forceinline__ void st4(T* p, const float* v);
+template <>
+__device__ __forceinline__ void st4<uint16_t>(uint16_t* p, const float* v) {
+  u32x2 u;
+  u[0] = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+  u[1] = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+  *reinterpret_cast<u32x2*>(p) = u;
+}
+template <>
+__device__ __forceinline__ void st4<float>(float* p, const float* v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+
+template <int N>
+using Int = std::integral_constant<int, N>;
+
+// f(Int<I>{}), ..., f(Int<N-1>{}) with compile-time indices.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// MFMA q = 0..NM-1 via mfma(Int<q>), each followed by its share of the NS
+// memory instructions other(Int<s>), spread evenly, in a fenced fixed order.
+template <int Q, int NM, int NS, typename F, typename G>
+__device__ __forceinline__ void mfma_interleave(F&& mfma, G&& other) {
+  if constexpr (Q < NM) {
+    mfma(Int<Q>{});
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<(Q * NS) / NM, ((Q + 1) * NS) / NM>(other);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_interleave<Q + 1, NM, NS>(mfma, other);
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+struct GemmCfg {
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
+  static constexpr int FM = kWaveM / 32, FN = kWaveN / 32;
+  static constexpr int kRowsPerPass = kThreads / 8;        // 8 x 16-byte chunks per row
+  static constexpr int kPassA = BM / kRowsPerPass, kPassB = BN / kRowsPerPass;
+  static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+  static constexpr int kBandLd = BN + 4;                    // epilogue band stride (floats)
+  static constexpr int kBandBytes = kWaveM * kBandLd * 4;   // one wave-row band of C
+  static constexpr int kLdsBytes =
+      2 * kStageBytes > kBandBytes ? 2 * kStageBytes : kBandBytes;
+  static_assert(FM >= 1 && FN >= 1 && kPassA >= 1 && kPassB >= 1, "bad tile");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
+};
+
+template <typename T, int BM, int BN, int WM, int WN, int MINW>
+__global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
+    const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1,
+    int has_e) {
+  using C = GemmCfg<BM, BN, WM, WN>;
+  constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
+  __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8
   // XCDs; give each XCD a contiguous run of logical tiles so neighbouring
   // tiles (which share operand rows) meet in the same L2.
@@ -211,142 +333,224 @@ __global__ __launch_bounds__(kThreads, 2) void k_ns_gemm(const GemmProb* __restr
   const int q8 = G >> 3, r8 = G & 7, xcd = bid & 7;
   const int tile = xcd * q8 + min(xcd, r8) + (bid >> 3);
   const GemmProb pr = probs[find_segment(probs, nprob, tile)];
-  int t = tile - pr.start, ti, tj;
-  if (pr.sym) {
-    ti = 0;
-    int len = pr.tiles_m;
-    while (t >= len) { t -= len; ++ti; --len; }
-    tj = ti + t;
-  } else {
-    ti = t / pr.tiles_n;
-    tj = t - ti * pr.tiles_n;
-  }
+  int ti, tj;
+  decode_tile(tile - pr.start, pr.tiles_m, pr.tiles_n, pr.sym, ti, tj);
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int fr = lane & 31, fg = lane >> 5;
   const int lrow = tid >> 3, lc = tid & 7;
-  const size_t lda_b = static_cast<size_t>(pr.lda) * sizeof(T);
-  const size_t ldb_b = static_cast<size_t>(pr.ldb) * sizeof(T);
-  const char* ag = reinterpret_cast<const char*>(pool + pr.a_off) +
-                   static_cast<size_t>(ti) * kGemmTile * lda_b + lrow * lda_b + lc * 16;
-  const char* bg = reinterpret_cast<const char*>(pool + pr.b_off) +
-                   static_cast<size_t>(tj) * kGemmTile * ldb_b + lrow * ldb_b + lc * 16;
+  static_assert(FM % 2 == 0 && FN % 2 == 0, "wave tiles span an even number of 32-row blocks");
+  static_assert(C::kRowsPerPass % 32 == 0, "slab rows per pass must keep the swizzle phase");
 
-  u32x4 ra[4], rb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ra[q] = *reinterpret_cast<const u32x4*>(ag + q * 32 * lda_b);
-    rb[q] = *reinterpret_cast<const u32x4*>(bg + q * 32 * ldb_b);
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    *reinterpret_cast<u32x4*>(smem + swz(lrow + 32 * q, lc)) = ra[q];
-    *reinterpret_cast<u32x4*>(smem + kGemmTile * kRowBytes + swz(lrow + 32 * q, lc)) = rb[q];
-  }
-  __syncthreads();
+  // Global -> register loads through buffer resources spanning this tile's
+  // operand rows (hardware range-checked): one per-thread VGPR offset, the
+  // row-pass and K-slab offsets go into the scalar soffset.
+  const uint32_t lda_b = static_cast<uint32_t>(pr.lda) * sizeof(T);
+  const uint32_t ldb_b = static_cast<uint32_t>(pr.ldb) * sizeof(T);
+  const char* abase = reinterpret_cast<const char*>(pool + pr.a_off) +
+                      static_cast<size_t>(ti) * BM * lda_b;
+  const char* bbase = reinterpret_cast<const char*>(pool + pr.b_off) +
+                      static_cast<size_t>(tj) * BN * ldb_b;
+  const auto rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0,
+                                                     static_cast<int>(BM * lda_b), 0x00020000);
+  const auto rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bbase), 0,
+                                                     static_cast<int>(BN * ldb_b), 0x00020000);
+  const int voa = static_cast<int>(lrow * lda_b) + lc * 16;
+  const int vob = static_cast<int>(lrow * ldb_b) + lc * 16;
 
-  f32x16 acc[2][2];
+  // LDS slab layout: row r, 16-byte chunk c at r * 128 + ((c ^ f(r)) << 4),
+  // f(r) = (r + r / 8) & 7.  Rows 32 apart differ in f by 4 (mod 8), so every
+  // address below is a per-thread base plus a compile-time immediate.
+  const int f_l = (lrow + (lrow >> 3)) & 7;
+  const int st_base = lrow * kRowBytes;
+  auto st_chunk = [&](int q) __attribute__((always_inline)) {
+    return (lc ^ ((f_l + 4 * ((q * C::kRowsPerPass / 32) & 1)) & 7)) << 4;
+  };
+  const int f_r = (fr + (fr >> 3)) & 7;
+  const int rd_a = (wm * C::kWaveM + fr) * kRowBytes;
+  const int rd_b = BM * kRowBytes + (wn * C::kWaveN + fr) * kRowBytes;
+  auto rd_chunk = [&](int ks, int parity) __attribute__((always_inline)) {
+    return ((ks * 2 + fg) ^ ((f_r + 4 * parity) & 7)) << 4;
+  };
+
+  u32x4 ra[C::kPassA], rb[C::kPassB];
+  // q-th 16-byte global load / LDS store of a slab (A rows first, then B)
+  auto gload_one = [&](int kt, auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    if constexpr (q < C::kPassA)
+      ra[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rsa, voa, q * C::kRowsPerPass * lda_b + kt * kRowBytes, 0));
+    else
+      rb[q - C::kPassA] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rsb, vob, (q - C::kPassA) * C::kRowsPerPass * ldb_b + kt * kRowBytes, 0));
+  };
+  auto lstore_one = [&](int stage, auto qc) __attribute__((always_inline)) {
+    constexpr int q = decltype(qc)::value;
+    if constexpr (q < C::kPassA)
+      *reinterpret_cast<u32x4*>(smem + stage * C::kStageBytes + st_base + st_chunk(q) +
+                                q * C::kRowsPerPass * kRowBytes) = ra[q];
+    else
+      *reinterpret_cast<u32x4*>(smem + stage * C::kStageBytes + BM * kRowBytes + st_base +
+                                st_chunk(q - C::kPassA) +
+                                (q - C::kPassA) * C::kRowsPerPass * kRowBytes) = rb[q - C::kPassA];
+  };
+  constexpr int kStores = C::kPassA + C::kPassB;
+  auto gload = [&](int kt) __attribute__((always_inline)) {
+    static_for<0, kStores>([&](auto qc) __attribute__((always_inline)) { gload_one(kt, qc); });
+  };
+  auto lstore = [&](int stage) __attribute__((always_inline)) {
+    static_for<0, kStores>([&](auto qc) __attribute__((always_inline)) { lstore_one(stage, qc); });
+  };
+
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
-  const int KT = pr.K / (kRowBytes / static_cast<int>(sizeof(T)));
-  for (int kt = 0; kt < KT; ++kt) {
-    const bool more = kt + 1 < KT;
-    if (more) {
-      ag += kRowBytes;
-      bg += kRowBytes;
+  // Operand fragments of one k-substep (32 bytes of every row); two sets so
+  // that the reads of substep ks+1 are in flight while ks is multiplied.
+  u32x4 av[2][FM], bv[2][FN];
+  auto fload = [&](int stage, int ks, auto setc) __attribute__((always_inline)) {
+    constexpr int set = decltype(setc)::value;
+    const char* base = smem + stage * C::kStageBytes;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ra[q] = *reinterpret_cast<const u32x4*>(ag + q * 32 * lda_b);
-        rb[q] = *reinterpret_cast<const u32x4*>(bg + q * 32 * ldb_b);
-      }
-    }
-    const char* as = smem + (kt & 1) * kStageBytes;
-    const char* bs = as + kGemmTile * kRowBytes;
+    for (int mi = 0; mi < FM; ++mi)
+      av[set][mi] = *reinterpret_cast<const u32x4*>(base + rd_a + mi * 32 * kRowBytes +
+                                                    rd_chunk(ks, mi & 1));
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 av[2], bv[2];
+    for (int ni = 0; ni < FN; ++ni)
+      bv[set][ni] = *reinterpret_cast<const u32x4*>(base + rd_b + ni * 32 * kRowBytes +
+                                                    rd_chunk(ks, ni & 1));
+  };
+  auto mfma_block = [&](auto setc) __attribute__((always_inline)) {
+    constexpr int set = decltype(setc)::value;
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        av[mi] = *reinterpret_cast<const u32x4*>(as + swz(wm * 64 + mi * 32 + fr, ks * 2 + fg));
+    for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bv[ni] = *reinterpret_cast<const u32x4*>(bs + swz(wn * 64 + ni * 32 + fr, ks * 2 + fg));
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) mma<T>(av[mi], bv[ni], acc[mi][ni]);
-    }
-    if (more) {
-      char* nas = smem + ((kt + 1) & 1) * kStageBytes;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        *reinterpret_cast<u32x4*>(nas + swz(lrow + 32 * q, lc)) = ra[q];
-        *reinterpret_cast<u32x4*>(nas + kGemmTile * kRowBytes + swz(lrow + 32 * q, lc)) = rb[q];
-      }
-    }
-    __syncthreads();
-  }
+      for (int ni = 0; ni < FN; ++ni) mma<T>(av[set][mi], bv[set][ni], acc[mi][ni]);
+  };
+  // MFMAs of one substep with `other` (kStores memory instructions) spread
+  // evenly between them.
+  auto mfma_block_with = [&](auto setc, auto&& other) __attribute__((always_inline)) {
+    constexpr int set = decltype(setc)::value;
+    mfma_interleave<0, FM * FN, kStores>(
+        [&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          mma<T>(av[set][q / FN], bv[set][q % FN], acc[q / FN][q % FN]);
+        },
+        other);
+  };
 
-  // Epilogue: stage the fp32 tile in LDS, then coalesced direct (and
-  // transposed) stores.  32x32 MFMA output: lane l holds column l % 32 and
+  // Software pipeline over K slabs (4 substeps of 16 k each).  Per slab:
+  //   ks0: read frags ks1                   | MFMAs ks0
+  //   ks1: read frags ks2                   | MFMAs ks1, interleaved with the
+  //        LDS store of slab k+1 (registers -> other stage)
+  //   ks2: read frags ks3                   | MFMAs ks2, interleaved with the
+  //        global loads of slab k+2
+  //   barrier (slab k+1 complete in LDS; slab k fully read)
+  //   ks3: read frags ks0 of slab k+1       | MFMAs ks3
+  // The barrier and the next slab's first LDS reads overlap MFMA work, and
+  // the fences keep each region's reads ahead of its MFMAs.
+  const int KT = pr.K / (kRowBytes / static_cast<int>(sizeof(T)));
+  gload(0);
+  lstore(0);
+  if (KT > 1) gload(1);
+  __syncthreads();
+  fload(0, 0, Int<0>{});
+  for (int kt = 0; kt < KT; ++kt) {
+    const int stage = kt & 1;
+    const bool more = kt + 1 < KT;
+    fload(stage, 1, Int<1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(Int<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    fload(stage, 2, Int<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(Int<1>{});
+    if (more) lstore(stage ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    fload(stage, 3, Int<1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(Int<0>{});
+    if (kt + 2 < KT) gload(kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    if (more) fload(stage ^ 1, 0, Int<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_block(Int<1>{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+
+  // Epilogue, one band of kWaveM rows (one row of waves) at a time: the
+  // band's waves stage their fp32 accumulators in LDS, then all threads make
+  // coalesced direct stores (with the E term) and, when asked, write the
+  // values back for the transposed stores.  32x32 MFMA output: lane l holds column l % 32 and
   // rows 8 (v / 4) + 4 (l / 32) + v % 4 for v = 0..15.
   float* cs = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int i = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * fg + (v & 3);
-        const int j = wn * 64 + ni * 32 + fr;
-        cs[i * kCsLd + j] = acc[mi][ni][v];
-      }
-  __syncthreads();
   const bool need_t = pr.ct_off >= 0 && !(pr.sym && ti == tj);
-  T* cg = pool + pr.c_off + static_cast<size_t>(ti) * kGemmTile * pr.ldc + tj * kGemmTile;
-  const T* eg = has_e ? pool + pr.e_off + static_cast<size_t>(ti) * kGemmTile * pr.lde +
-                            tj * kGemmTile
-                      : nullptr;
-#pragma unroll 2
-  for (int p = 0; p < (kGemmTile * kGemmTile) / (kThreads * 8); ++p) {
-    const int idx = p * kThreads + tid;
-    const int i = idx >> 4, j = (idx & 15) * 8;
-    float v[8];
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(cs + i * kCsLd + j);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(cs + i * kCsLd + j + 4);
+  constexpr int BR = C::kWaveM;
+  constexpr int kIters = (BR * BN) / (NT * 8);
+#pragma unroll 1
+  for (int band = 0; band < WM; ++band) {
+    const int row0 = ti * BM + band * BR;
+    T* cg = pool + pr.c_off + static_cast<size_t>(row0) * pr.ldc + tj * BN;
+    const T* eg = has_e ? pool + pr.e_off + static_cast<size_t>(row0) * pr.lde + tj * BN
+                        : nullptr;
+    if (wm == band) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) { v[k] = c1 * x0[k]; v[4 + k] = c1 * x1[k]; }
-    if (has_e) {
-      float e[8];
-      ld8<T>(eg + static_cast<size_t>(i) * pr.lde + j, e);
+      for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] += c0 * e[k];
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int i = mi * 32 + 8 * (v >> 2) + 4 * fg + (v & 3);
+            const int j = wn * C::kWaveN + ni * 32 + fr;
+            cs[i * C::kBandLd + j] = acc[mi][ni][v];
+          }
     }
-    st8<T>(cg + static_cast<size_t>(i) * pr.ldc + j, v);
-    if (need_t) {
-      *reinterpret_cast<f32x4*>(cs + i * kCsLd + j) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(cs + i * kCsLd + j + 4) = f32x4{v[4], v[5], v[6], v[7]};
-    }
-  }
-  if (need_t) {
     __syncthreads();
-    T* ctg = pool + pr.ct_off + static_cast<size_t>(tj) * kGemmTile * pr.ldct + ti * kGemmTile;
 #pragma unroll 2
-    for (int p = 0; p < (kGemmTile * kGemmTile) / (kThreads * 8); ++p) {
-      const int idx = p * kThreads + tid;
-      const int j = idx & (kGemmTile - 1), i = (idx >> 7) * 8;
+    for (int p = 0; p < kIters; ++p) {
+      const int idx = p * NT + tid;
+      const int i = idx / (BN / 8), j = (idx % (BN / 8)) * 8;
       float v[8];
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(cs + i * C::kBandLd + j);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(cs + i * C::kBandLd + j + 4);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = cs[(i + k) * kCsLd + j];
-      st8<T>(ctg + static_cast<size_t>(j) * pr.ldct + i, v);
+      for (int k = 0; k < 4; ++k) { v[k] = c1 * x0[k]; v[4 + k] = c1 * x1[k]; }
+      if (has_e) {
+        float e[8];
+        ld8<T>(eg + static_cast<size_t>(i) * pr.lde + j, e);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] += c0 * e[k];
+      }
+      st8<T>(cg + static_cast<size_t>(i) * pr.ldc + j, v);
+      if (need_t) {
+        *reinterpret_cast<f32x4*>(cs + i * C::kBandLd + j) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(cs + i * C::kBandLd + j + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      }
     }
+    if (need_t) {
+      __syncthreads();
+      T* ctg = pool + pr.ct_off + static_cast<size_t>(tj) * BN * pr.ldct + row0;
+#pragma unroll
+      for (int p = 0; p < kIters; ++p) {
+        const int idx = p * NT + tid;
+        const int j = idx % BN, i = (idx / BN) * 8;
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = cs[(i + k) * C::kBandLd + j];
+        st8<T>(ctg + static_cast<size_t>(j) * pr.ldct + i, v);
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -384,16 +588,28 @@ mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const flo
   return MO_OK;
 }
 
-mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, void* pool, int elem,
-                         float c0, float c1, int has_e, hipStream_t st) {
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, void* pool,
+                         int elem, float c0, float c1, int has_e, hipStream_t st) {
   if (ntiles <= 0) return MO_OK;
   KTimer tm(MO_KC_NS_GEMM, st);
-  if (elem == 2)
-    k_ns_gemm<uint16_t><<<dim3(static_cast<unsigned>(ntiles)), kThreads, 0, st>>>(
-        probs, n, static_cast<uint16_t*>(pool), c0, c1, has_e);
-  else
-    k_ns_gemm<float><<<dim3(static_cast<unsigned>(ntiles)), kThreads, 0, st>>>(
-        probs, n, static_cast<float*>(pool), c0, c1, has_e);
+  const dim3 grid(static_cast<unsigned>(ntiles));
+  if (tile == 256) {
+    if (elem == 2)
+      k_ns_gemm<uint16_t, 256, 256, 2, 4, 2><<<grid, 512, 0, st>>>(
+          probs, n, static_cast<uint16_t*>(pool), c0, c1, has_e);
+    else
+      k_ns_gemm<float, 256, 256, 2, 4, 2><<<grid, 512, 0, st>>>(
+          probs, n, static_cast<float*>(pool), c0, c1, has_e);
+  } else if (tile == 128) {
+    if (elem == 2)
+      k_ns_gemm<uint16_t, 128, 128, 2, 2, 2><<<grid, 256, 0, st>>>(
+          probs, n, static_cast<uint16_t*>(pool), c0, c1, has_e);
+    else
+      k_ns_gemm<float, 128, 128, 2, 2, 2><<<grid, 256, 0, st>>>(
+          probs, n, static_cast<float*>(pool), c0, c1, has_e);
+  } else {
+    return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);
+  }
   MO_LAUNCH_CHECK("k_ns_gemm");
   return MO_OK;
 }

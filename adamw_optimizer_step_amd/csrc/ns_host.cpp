@@ -7,14 +7,15 @@
 namespace mo {
 
 namespace {
-int32_t pad_tile(int64_t x) { return static_cast<int32_t>(ceil_div(x, kGemmTile) * kGemmTile); }
+int32_t pad_to(int64_t x, int t) { return static_cast<int32_t>(ceil_div(x, t) * t); }
 
-GemmProb make_prob(int64_t a, int64_t b, int64_t c, int64_t ct, int64_t e, int32_t lda,
-                   int32_t ldb, int32_t ldc, int32_t ldct, int32_t lde, int32_t K, int32_t tm,
-                   int32_t tn, int32_t sym, int64_t& start) {
+GemmProb make_prob(int64_t a, int64_t b, int64_t c, int64_t ct, int64_t e, int64_t et,
+                   int32_t lda, int32_t ldb, int32_t ldc, int32_t ldct, int32_t lde, int32_t ldet,
+                   int32_t K, int32_t tm, int32_t tn, int32_t sym, int64_t& start) {
   GemmProb p;
-  p.a_off = a; p.b_off = b; p.c_off = c; p.ct_off = ct; p.e_off = e;
-  p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ldct = ldct; p.lde = lde;
+  std::memset(&p, 0, sizeof(p));
+  p.a_off = a; p.b_off = b; p.c_off = c; p.ct_off = ct; p.e_off = e; p.et_off = et;
+  p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ldct = ldct; p.lde = lde; p.ldet = ldet;
   p.K = K; p.tiles_m = tm; p.tiles_n = tn; p.sym = sym;
   p.start = static_cast<int32_t>(start);
   start += sym ? static_cast<int64_t>(tm) * (tm + 1) / 2 : static_cast<int64_t>(tm) * tn;
@@ -28,12 +29,18 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
   L.elem = elem;
   L.need_a = need_a;
   L.n = n;
+  L.buckets.resize(2);
+  L.buckets[0].tile = kGemmTile;
+  L.buckets[1].tile = kBigTile;
   int64_t pool = 0;
   auto take = [&pool](int64_t elems) { int64_t at = pool; pool += elems; return at; };
   for (int i = 0; i < n; ++i) {
     const int64_t r = rows[i], c = cols[i];
     const bool tall = r > c;
-    const int32_t sp = pad_tile(tall ? c : r), lp = pad_tile(tall ? r : c);
+    const int64_t s_ = tall ? c : r, l_ = tall ? r : c;
+    NsBucket& B = L.buckets[s_ >= kBigTileMinS ? 1 : 0];
+    const int tile = B.tile;
+    const int32_t sp = pad_to(s_, tile), lp = pad_to(l_, tile);
     const int64_t x = take(static_cast<int64_t>(sp) * lp);
     const int64_t xt0 = take(static_cast<int64_t>(lp) * sp);
     const int64_t xt1 = take(static_cast<int64_t>(lp) * sp);
@@ -59,20 +66,23 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     L.prep_tiles += static_cast<int64_t>(pi.rp / kPrepTile) * pi.tiles_c;
     L.prep.push_back(pi);
 
-    const int32_t ts = sp / kGemmTile, tl = lp / kGemmTile;
-    // Gram X X^T (K = l) into P (scaled by b) or into A.
-    L.gram_p.push_back(make_prob(x, x, p, p, -1, lp, lp, sp, sp, 0, lp, ts, ts, 1, L.gram_tiles));
+    const int32_t ts = sp / tile, tl = lp / tile;
+    // Gram X X^T (K = l) into P (scaled by b) or into A; mirror tiles through ct.
+    B.gram_p.push_back(make_prob(x, x, p, p, -1, -1, lp, lp, sp, sp, 0, 0, lp, ts, ts, 1,
+                                 B.gram_tiles));
     if (need_a) {
-      int64_t t = L.gram_p.back().start;
-      L.gram_a.push_back(make_prob(x, x, a, a, -1, lp, lp, sp, sp, 0, lp, ts, ts, 1, t));
-      L.square.push_back(make_prob(a, a, p, p, a, sp, sp, sp, sp, sp, sp, ts, ts, 1,
-                                   L.square_tiles));
+      int64_t t = B.gram_p.back().start;
+      B.gram_a.push_back(make_prob(x, x, a, a, -1, -1, lp, lp, sp, sp, 0, 0, lp, ts, ts, 1, t));
+      // P = b A + c A A; A is exactly symmetric, so it is its own transposed E
+      B.square.push_back(make_prob(a, a, p, p, a, a, sp, sp, sp, sp, sp, sp, sp, ts, ts, 1,
+                                   B.square_tiles));
     }
     // Update X <- a X + P X: A_op = P (s x s), B_op = Xt (l x s), K = s;
-    // X written in place, X^T into the other buffer.
-    int64_t t0 = L.upd_tiles;
-    L.upd0.push_back(make_prob(p, xt0, x, xt1, x, sp, sp, lp, sp, lp, sp, ts, tl, 0, t0));
-    L.upd1.push_back(make_prob(p, xt1, x, xt0, x, sp, sp, lp, sp, lp, sp, ts, tl, 0, L.upd_tiles));
+    // X written in place (E = X), X^T into the other buffer (E^T = current X^T).
+    int64_t t0 = B.upd_tiles;
+    B.upd0.push_back(make_prob(p, xt0, x, xt1, x, xt0, sp, sp, lp, sp, lp, sp, sp, ts, tl, 0, t0));
+    B.upd1.push_back(make_prob(p, xt1, x, xt0, x, xt1, sp, sp, lp, sp, lp, sp, sp, ts, tl, 0,
+                               B.upd_tiles));
   }
   L.pool_elems = pool;
 }
@@ -81,11 +91,15 @@ NsTables ns_table_offsets(const NsLayout& L) {
   NsTables T;
   WsCursor c;
   T.prep = c.take(L.prep.size() * sizeof(PrepItem), 64);
-  T.gram_p = c.take(L.gram_p.size() * sizeof(GemmProb), 64);
-  T.gram_a = c.take(L.gram_a.size() * sizeof(GemmProb), 64);
-  T.square = c.take(L.square.size() * sizeof(GemmProb), 64);
-  T.upd0 = c.take(L.upd0.size() * sizeof(GemmProb), 64);
-  T.upd1 = c.take(L.upd1.size() * sizeof(GemmProb), 64);
+  for (const NsBucket& B : L.buckets) {
+    NsBucketTables b;
+    b.gram_p = c.take(B.gram_p.size() * sizeof(GemmProb), 64);
+    b.gram_a = c.take(B.gram_a.size() * sizeof(GemmProb), 64);
+    b.square = c.take(B.square.size() * sizeof(GemmProb), 64);
+    b.upd0 = c.take(B.upd0.size() * sizeof(GemmProb), 64);
+    b.upd1 = c.take(B.upd1.size() * sizeof(GemmProb), 64);
+    T.b.push_back(b);
+  }
   T.bytes = align_up(c.off, 256);
   return T;
 }
@@ -96,35 +110,52 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
     if (bytes) std::memcpy(buf.data() + off, src, bytes);
   };
   put(T.prep, L.prep.data(), L.prep.size() * sizeof(PrepItem));
-  put(T.gram_p, L.gram_p.data(), L.gram_p.size() * sizeof(GemmProb));
-  put(T.gram_a, L.gram_a.data(), L.gram_a.size() * sizeof(GemmProb));
-  put(T.square, L.square.data(), L.square.size() * sizeof(GemmProb));
-  put(T.upd0, L.upd0.data(), L.upd0.size() * sizeof(GemmProb));
-  put(T.upd1, L.upd1.data(), L.upd1.size() * sizeof(GemmProb));
+  for (size_t k = 0; k < L.buckets.size(); ++k) {
+    const NsBucket& B = L.buckets[k];
+    const NsBucketTables& b = T.b[k];
+    put(b.gram_p, B.gram_p.data(), B.gram_p.size() * sizeof(GemmProb));
+    put(b.gram_a, B.gram_a.data(), B.gram_a.size() * sizeof(GemmProb));
+    put(b.square, B.square.data(), B.square.size() * sizeof(GemmProb));
+    put(b.upd0, B.upd0.data(), B.upd0.size() * sizeof(GemmProb));
+    put(b.upd1, B.upd1.data(), B.upd1.size() * sizeof(GemmProb));
+  }
 }
 
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* coeffs, int steps, hipStream_t st) {
-  const GemmProb* gram_p = reinterpret_cast<const GemmProb*>(dtab + T.gram_p);
-  const GemmProb* gram_a = reinterpret_cast<const GemmProb*>(dtab + T.gram_a);
-  const GemmProb* square = reinterpret_cast<const GemmProb*>(dtab + T.square);
-  const GemmProb* upd[2] = {reinterpret_cast<const GemmProb*>(dtab + T.upd0),
-                            reinterpret_cast<const GemmProb*>(dtab + T.upd1)};
   for (int k = 0; k < steps; ++k) {
     const float a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
-    mo_status s;
-    if (c == 0.f || !L.need_a) {
-      // P = b X X^T   (cubic-type step)
-      s = launch_ns_gemm(gram_p, L.n, L.gram_tiles, pool, L.elem, 0.f, b, 0, st);
-    } else {
-      // A = X X^T;  P = b A + c A A
-      s = launch_ns_gemm(gram_a, L.n, L.gram_tiles, pool, L.elem, 0.f, 1.f, 0, st);
-      if (s == MO_OK) s = launch_ns_gemm(square, L.n, L.square_tiles, pool, L.elem, b, c, 1, st);
+    const bool cubic_step = c == 0.f || !L.need_a;
+    // phase 1: P = b X X^T (cubic-type step), or A = X X^T then P = b A + c A A
+    for (size_t q = 0; q < L.buckets.size(); ++q) {
+      const NsBucket& B = L.buckets[q];
+      if (B.gram_p.empty()) continue;
+      const NsBucketTables& tb = T.b[q];
+      const int n = static_cast<int>(B.gram_p.size());
+      mo_status s;
+      if (cubic_step) {
+        s = launch_ns_gemm(reinterpret_cast<const GemmProb*>(dtab + tb.gram_p), n, B.gram_tiles,
+                           B.tile, pool, L.elem, 0.f, b, 0, st);
+      } else {
+        s = launch_ns_gemm(reinterpret_cast<const GemmProb*>(dtab + tb.gram_a), n, B.gram_tiles,
+                           B.tile, pool, L.elem, 0.f, 1.f, 0, st);
+        if (s == MO_OK)
+          s = launch_ns_gemm(reinterpret_cast<const GemmProb*>(dtab + tb.square), n,
+                             B.square_tiles, B.tile, pool, L.elem, b, c, 1, st);
+      }
+      if (s != MO_OK) return s;
     }
-    if (s != MO_OK) return s;
-    // X <- a X + P X
-    s = launch_ns_gemm(upd[k & 1], L.n, L.upd_tiles, pool, L.elem, a, 1.f, 1, st);
-    if (s != MO_OK) return s;
+    // phase 2: X <- a X + P X
+    for (size_t q = 0; q < L.buckets.size(); ++q) {
+      const NsBucket& B = L.buckets[q];
+      if (B.upd0.empty()) continue;
+      const NsBucketTables& tb = T.b[q];
+      const size_t off = (k & 1) ? tb.upd1 : tb.upd0;
+      mo_status s = launch_ns_gemm(reinterpret_cast<const GemmProb*>(dtab + off),
+                                   static_cast<int>(B.upd0.size()), B.upd_tiles, B.tile, pool,
+                                   L.elem, a, 1.f, 1, st);
+      if (s != MO_OK) return s;
+    }
   }
   return MO_OK;
 }

@@ -87,6 +87,22 @@ def test_ns_parity_ragged_shapes(precision, kind):
         assert_ns_close(f64(o), ref, precision)
 
 
+# short side >= 512 goes to the 256 x 256 tile bucket; mixed with small ones
+NS_BIG_SHAPES = [(520, 600), (1100, 530), (512, 512), (768, 2050), (40, 90), (300, 200)]
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp32"])
+@pytest.mark.parametrize("kind", ["cubic", "quintic"])
+def test_ns_parity_big_tiles(precision, kind):
+    dtype = "bf16" if precision == "bf16" else "f32"
+    mats, dev = _ns_case(NS_BIG_SHAPES, dtype, 25)
+    coeffs = wl.coeff_table(kind)
+    outs = api.ns_orthogonalize_batched(dev, coeffs=coeffs, precision=precision)
+    for m, o in zip(mats, outs):
+        ref = omuon.newton_schulz(wl.from_storage(m, dtype).astype(np.float64), coeffs)
+        assert_ns_close(f64(o), ref, precision)
+
+
 def test_ns_strided_views_and_fp32_output():
     # row slabs of a larger weight, as a view / split produces them
     W = storage_draw(22, 1, 0, (20, 72), 1.0, "bf16")
