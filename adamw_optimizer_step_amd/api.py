@@ -303,6 +303,7 @@ class Plan:
         self._h = h
         self.n = n
         self._ws: Optional[torch.Tensor] = None
+        self._slices = None
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -320,10 +321,13 @@ class Plan:
         return [(o.algorithm, o.decay, o.group, o.nslices) for o in out[:self.n]]
 
     def slices(self):
-        k = L.lib().mo_plan_num_slices(self._h)
-        out = (C.c_int64 * max(4 * k, 4))()
-        L.check("mo_plan_slices", L.lib().mo_plan_slices(self._h, out, k))
-        return [tuple(out[4 * i:4 * i + 4]) for i in range(k)]
+        """(param index, row offset, rows, cols) per Muon slice (fixed at creation)."""
+        if self._slices is None:
+            k = L.lib().mo_plan_num_slices(self._h)
+            out = (C.c_int64 * max(4 * k, 4))()
+            L.check("mo_plan_slices", L.lib().mo_plan_slices(self._h, out, k))
+            self._slices = [tuple(out[4 * i:4 * i + 4]) for i in range(k)]
+        return list(self._slices)
 
     def get_steps(self) -> List[int]:
         out = (C.c_int32 * max(self.n, 1))()
@@ -333,6 +337,25 @@ class Plan:
     def set_steps(self, steps: Sequence[int]) -> None:
         arr = (C.c_int32 * max(self.n, 1))(*[int(s) for s in steps])
         L.check("mo_plan_set_steps", L.lib().mo_plan_set_steps(self._h, arr, self.n))
+
+    def ns_output(self, slice_index: int, workspace: Optional[torch.Tensor] = None
+                  ) -> torch.Tensor:
+        """View into the workspace of one slice's Newton-Schulz output O after
+        the last step: (rows, cols) in the stored orientation, bf16 or fp32."""
+        ws = self._ws if workspace is None else workspace
+        if ws is None:
+            raise ValueError("ns_output: the plan has no workspace yet")
+        o, ld, dt = C.c_void_p(), C.c_int64(), C.c_int32()
+        L.check("mo_plan_ns_output",
+                L.lib().mo_plan_ns_output(self._h, int(slice_index), C.c_void_p(ws.data_ptr()),
+                                          C.byref(o), C.byref(ld), C.byref(dt)))
+        _, _, rows, cols = self._slices[slice_index] if self._slices else \
+            self.slices()[slice_index]
+        esz = 4 if dt.value == L.MO_F32 else 2
+        off = o.value - ws.data_ptr()
+        flat = ws[off:off + ((rows - 1) * ld.value + cols) * esz]
+        flat = flat.view(torch.float32 if esz == 4 else torch.bfloat16)
+        return flat.as_strided((rows, cols), (ld.value, 1))
 
     def workspace(self, device) -> torch.Tensor:
         if self._ws is None or self._ws.numel() < self.workspace_bytes:

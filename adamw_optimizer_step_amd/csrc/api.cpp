@@ -278,4 +278,16 @@ mo_status adamw_clip_step(const mo_adamw_item* items, int32_t n, float lr, float
   return launch_adam_apply(dsegs, nseg, nblocks, scal, lr, beta1, beta2, eps, 0, st);
 }
 
+mo_status mo_diag_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  clear_error();
+  if (bytes < 0 || bytes % 16 != 0 || (bytes > 0 && (!src || !dst)))
+    return fail(MO_EINVAL, "copy of %lld bytes: need non-NULL pointers and a multiple of 16",
+                static_cast<long long>(bytes));
+  if (!aligned16(src) || !aligned16(dst)) return fail(MO_EALIGN, "copy pointers must be 16-byte aligned");
+  const char* a = static_cast<const char*>(src);
+  const char* b = static_cast<const char*>(dst);
+  if (bytes > 0 && a < b + bytes && b < a + bytes) return fail(MO_EINVAL, "copy ranges overlap");
+  return launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -339,4 +339,26 @@ mo_status launch_rows(int32_t mode, const RowSeg* segs, int nseg, const RowSeg& 
   return MO_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Plain device copy of a known byte count (16-byte loads and stores, grid
+// stride): the reference point that scales hardware byte counters.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_diag_copy(const uint4* __restrict__ src,
+                                                        uint4* __restrict__ dst, int64_t n16) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16;
+       i += stride)
+    dst[i] = src[i];
+}
+
+mo_status launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
+  if (bytes <= 0) return MO_OK;
+  const int64_t n16 = bytes / 16;
+  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(ceil_div(n16, kThreads), 8192));
+  k_diag_copy<<<grid, kThreads, 0, st>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst),
+                                          n16);
+  MO_LAUNCH_CHECK("k_diag_copy");
+  return MO_OK;
+}
+
 }  // namespace mo

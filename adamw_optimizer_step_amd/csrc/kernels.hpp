@@ -92,6 +92,7 @@ struct RowSeg {
 };
 
 // nseg == 0: `one` is the only matrix (passed by value, no table needed).
+mo_status launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 mo_status launch_rows(int32_t mode, const RowSeg* segs, int nseg, const RowSeg& one,
                       int64_t total_rows, float lr, float beta2, float eps, hipStream_t st);
 

@@ -290,19 +290,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// MFMA q = 0..NM-1 via mfma(Int<q>), each followed by its share of the NS
-// memory instructions other(Int<s>), spread evenly, in a fenced fixed order.
-template <int Q, int NM, int NS, typename F, typename G>
-__device__ __forceinline__ void mfma_interleave(F&& mfma, G&& other) {
-  if constexpr (Q < NM) {
-    mfma(Int<Q>{});
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<(Q * NS) / NM, ((Q + 1) * NS) / NM>(other);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_interleave<Q + 1, NM, NS>(mfma, other);
-  }
-}
-
 template <int BM, int BN, int WM, int WN>
 struct GemmCfg {
   static constexpr int kThreads = 64 * WM * WN;
@@ -435,28 +422,16 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni) mma<T>(av[set][mi], bv[set][ni], acc[mi][ni]);
   };
-  // MFMAs of one substep with `other` (kStores memory instructions) spread
-  // evenly between them.
-  auto mfma_block_with = [&](auto setc, auto&& other) __attribute__((always_inline)) {
-    constexpr int set = decltype(setc)::value;
-    mfma_interleave<0, FM * FN, kStores>(
-        [&](auto qc) __attribute__((always_inline)) {
-          constexpr int q = decltype(qc)::value;
-          mma<T>(av[set][q / FN], bv[set][q % FN], acc[q / FN][q % FN]);
-        },
-        other);
-  };
-
-  // Software pipeline over K slabs (4 substeps of 16 k each).  Per slab:
-  //   ks0: read frags ks1                   | MFMAs ks0
-  //   ks1: read frags ks2                   | MFMAs ks1, interleaved with the
-  //        LDS store of slab k+1 (registers -> other stage)
-  //   ks2: read frags ks3                   | MFMAs ks2, interleaved with the
-  //        global loads of slab k+2
+  // Software pipeline over K slabs (4 substeps of 16 k each), alternating
+  // two fragment register sets.  Per slab:
+  //   read frags ks1              | MFMAs ks0
+  //   read frags ks2              | MFMAs ks1, then LDS store of slab k+1
+  //                               |   (registers -> the other stage)
+  //   read frags ks3              | MFMAs ks2, then global loads of slab k+2
   //   barrier (slab k+1 complete in LDS; slab k fully read)
-  //   ks3: read frags ks0 of slab k+1       | MFMAs ks3
-  // The barrier and the next slab's first LDS reads overlap MFMA work, and
-  // the fences keep each region's reads ahead of its MFMAs.
+  //   read frags ks0 of slab k+1  | MFMAs ks3
+  // The scheduling fences keep each region's LDS reads issued ahead of the
+  // MFMAs that hide them.
   const int KT = pr.K / (kRowBytes / static_cast<int>(sizeof(T)));
   gload(0);
   lstore(0);

@@ -297,6 +297,28 @@ mo_status mo_plan_set_steps(mo_plan* plan, const int32_t* steps, int32_t n) {
   return MO_OK;
 }
 
+mo_status mo_plan_ns_output(const mo_plan* P, int32_t slice, const void* ws, void** o,
+                            int64_t* ld, int32_t* dtype) {
+  clear_error();
+  if (!P || !ws || !o || !ld || !dtype) return fail(MO_EINVAL, "bad arguments");
+  if (slice < 0 || slice >= static_cast<int32_t>(P->slices.size()))
+    return fail(MO_EINVAL, "slice %d out of range", slice);
+  if (P->uploaded_ws != ws || P->tdelta == 0)
+    return fail(MO_EINVAL, "no grouped step has run on this workspace");
+  const int32_t param = P->slices[slice].param;
+  if (!P->params[param].grad) return fail(MO_EINVAL, "slice %d: param has no gradient", slice);
+  // active slices are the slices of params with a gradient, in the same order
+  int k = 0;
+  for (int32_t i = 0; i < slice; ++i)
+    if (P->params[P->slices[i].param].grad) ++k;
+  const size_t esz = dtype_size(P->ddt);
+  *o = const_cast<char*>(static_cast<const char*>(ws)) + P->ws_pool +
+       P->ns.final_off(k, P->hp.ns_steps) * esz;
+  *ld = P->ns.final_ld(k);
+  *dtype = P->ddt;
+  return MO_OK;
+}
+
 mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t ws_bytes,
                           void* stream) {
   clear_error();

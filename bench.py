@@ -155,6 +155,22 @@ def cpu_baseline(w, coeffs, normuon, budget_s: float):
                        f"{spent:.1f}s of Muon work measured")}
 
 
+def counted_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none for
+    this workload or the kernel's sources have changed since it was taken."""
+    from adamw_optimizer_step_amd import profiling
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"{kernel}_{workload}_traffic.md")
+    s = profiling.read_summary(path)
+    if not s or s.get("workload") != workload:
+        return None
+    if s.get("source_digest") != profiling.source_digest(kernel):
+        log(f"{path}: counters predate the current {kernel} sources; traffic = null")
+        return None
+    return float(s["fetch_bytes_per_launch"]) + float(s["write_bytes_per_launch"])
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +182,9 @@ def main() -> int:
     ap.add_argument("--timing-steps", type=int, default=3)
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", type=int, default=1024, metavar="MIB",
+                    help="size of the plain device copy (k_diag_copy) that calibrates "
+                         "byte counters and gives the copy bandwidth (0 = skip)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -253,6 +272,30 @@ def main() -> int:
     if "rows" in kern:
         hbm["update"] = round(muon_elems * (3 * elt) / (kern["rows"]["ms_per_step"] * 1e-3) / 1e9,
                               1)
+
+    # plain copy of known size: counter calibration and practical HBM ceiling
+    copy_gbs = None
+    if args.copy_calibration > 0:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        stream = torch.cuda.current_stream().cuda_stream
+        L.check("mo_diag_copy", lib.mo_diag_copy(C.c_void_p(src.data_ptr()),
+                                                 C.c_void_p(dst.data_ptr()), nbytes,
+                                                 C.c_void_p(stream)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.check("mo_diag_copy", lib.mo_diag_copy(C.c_void_p(src.data_ptr()),
+                                                 C.c_void_p(dst.data_ptr()), nbytes,
+                                                 C.c_void_p(stream)))
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbs = round(2 * nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        hbm["copy"] = copy_gbs
+        del src, dst
+
+    if roofline is not None:
+        roofline["traffic"] = counted_traffic("k_ns_gemm", w.key)
 
     cpu = None
     if args.cpu_budget > 0:

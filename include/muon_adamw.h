@@ -324,6 +324,18 @@ mo_status mo_plan_get_steps(const mo_plan* plan, int32_t* steps, int32_t n);
 mo_status mo_plan_set_steps(mo_plan* plan, const int32_t* steps, int32_t n);
 mo_status mo_grouped_step(mo_plan* plan, const mo_step_args* args, void* ws, size_t ws_bytes,
                           void* stream);
+/* Where the last grouped step left the Newton-Schulz output O of one slice
+ * (the point the NorMuon paper section 2.2 calls O_t: after the iterations,
+ * before NorMuon, the shape scale and the learning rate).  `slice` indexes
+ * mo_plan_slices' table; `ws` is the workspace that step used.  On success
+ * *o is a device pointer inside `ws` to a (rows, cols) row-major matrix in
+ * the stored orientation with row stride *ld elements and element type
+ * *dtype (MO_BF16 or MO_F32, the NS precision's storage).  The values stay
+ * valid until the next step or ns call on that workspace.  Host only; no
+ * device work.  MO_EINVAL for a bad index, a slice whose param had no
+ * gradient, or a plan that has not run a step on `ws`. */
+mo_status mo_plan_ns_output(const mo_plan* plan, int32_t slice, const void* ws, void** o,
+                            int64_t* ld, int32_t* dtype);
 
 /* ------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel launch of this
@@ -340,6 +352,14 @@ typedef enum mo_kernel_class {
 
 mo_status mo_timing_enable(int32_t on);
 mo_status mo_timing_read(int32_t kclass, double* total_ms, int64_t* launches);
+
+/* Plain device-to-device copy of `bytes` bytes by a kernel of this library
+ * (k_diag_copy), enqueued on `stream`: a transfer of known size against which
+ * hardware byte counters (FETCH_SIZE, WRITE_SIZE) are calibrated.  `src` and
+ * `dst` are device pointers, 16-byte aligned, not overlapping; `bytes` is a
+ * multiple of 16.  MO_EINVAL / MO_EALIGN otherwise.  Not part of the
+ * optimizer step. */
+mo_status mo_diag_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }
