@@ -22,12 +22,19 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
 // device pointers and statistics ranges are filled by the caller).  Matrices
 // are bucketed by GEMM tile size: short side >= kBigTileMinS -> 256 x 256
 // tiles, otherwise 128 x 128; each bucket has its own tables and launches.
+//
+// Per matrix (s = short side, l = long side, both padded to the tile): two
+// iterate buffers X0, X1 (s x l, short-side rows) used in turn, P (s x s) and,
+// for tables with a quintic-type row, A (s x s).  Iteration k reads X[k % 2]
+// and writes X[(k + 1) % 2]; the last iteration of a tall matrix writes its
+// result transposed (stored orientation, l x s) into that buffer instead.
 constexpr int kBigTile = 256;
 constexpr int kBigTileMinS = 512;
 
 struct NsBucket {
   int tile = kGemmTile;
-  std::vector<GemmProb> gram_p, gram_a, square, upd0, upd1;
+  // [parity of the iteration]; fin = the update of the last iteration
+  std::vector<GemmProb> gram_p[2], gram_a[2], square, upd[2], fin[2];
   int64_t gram_tiles = 0, square_tiles = 0, upd_tiles = 0;
 };
 
@@ -38,14 +45,12 @@ struct NsLayout {
   std::vector<PrepItem> prep;
   std::vector<NsBucket> buckets;
   int64_t prep_tiles = 0;
-  std::vector<int64_t> x_off, xt_off0, xt_off1;
+  std::vector<int64_t> x_off[2];
   std::vector<int32_t> tall, sp, lp;
   int64_t pool_elems = 0;
 
-  // stored-orientation buffer of the final iterate and its row stride
-  int64_t final_off(int i, int steps) const {
-    return tall[i] ? (steps % 2 ? xt_off1[i] : xt_off0[i]) : x_off[i];
-  }
+  // buffer of the final iterate (stored orientation) and its row stride
+  int64_t final_off(int i, int steps) const { return x_off[steps & 1][i]; }
   int32_t final_ld(int i) const { return tall[i] ? sp[i] : lp[i]; }
 };
 
@@ -54,7 +59,7 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
 
 // Byte offsets of the device tables inside one contiguous table block.
 struct NsBucketTables {
-  size_t gram_p = 0, gram_a = 0, square = 0, upd0 = 0, upd1 = 0;
+  size_t gram_p[2] = {0, 0}, gram_a[2] = {0, 0}, square = 0, upd[2] = {0, 0}, fin[2] = {0, 0};
 };
 struct NsTables {
   size_t prep = 0, bytes = 0;

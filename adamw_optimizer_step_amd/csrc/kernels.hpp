@@ -103,8 +103,8 @@ constexpr int kGemmTile = 128;  // small GEMM tile edge (M and N); matrices are 
 struct PrepItem {
   const void* in;          // D in stored orientation, rows r x cols c, stride ld_in
   int64_t ld_in;
-  int64_t sbuf;            // pool offset of the stored-orientation buffer (rp x cp)
-  int64_t stbuf;           // pool offset of the transposed buffer (cp x rp)
+  int64_t sbuf;            // pool offset of the stored-orientation copy (rp x cp), -1 = none
+  int64_t stbuf;           // pool offset of the transposed copy (cp x rp), -1 = none
   int64_t start;           // first prep tile of this item
   int64_t stat_begin;      // partial-statistics range of this item
   int64_t stat_end;
@@ -115,17 +115,17 @@ struct PrepItem {
 };
 
 struct GemmProb {
-  int64_t a_off, b_off;    // operand pool offsets (row-major, K contiguous)
-  int64_t c_off;           // direct output
-  int64_t ct_off;          // transposed output, -1 = none
+  int64_t a_off;           // A operand: M x K row-major (K contiguous)
+  int64_t b_off;           // B operand: N x K row-major, or K x N row-major when the
+                           // launch reads B K-major
+  int64_t c_off;           // direct output (M x N), -1 = none
+  int64_t ct_off;          // transposed output (N x M), -1 = none
   int64_t e_off;           // epilogue input (same layout as c), -1 = none
-  int64_t et_off;          // epilogue input in the transposed layout (for ct)
-  int32_t lda, ldb, ldc, ldct, lde, ldet;
+  int32_t lda, ldb, ldc, ldct, lde;
   int32_t K;
   int32_t tiles_m, tiles_n;
   int32_t sym;             // only tiles (i <= j); mirror written through ct
   int32_t start;           // first tile of this problem
-  int32_t pad;
 };
 
 struct FinalItem {         // NS output copy (stored orientation)
@@ -149,8 +149,9 @@ mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const flo
                          void* pool, int elem, hipStream_t st);
 // One batched GEMM phase:  out = c0 * E + c1 * (A_op B_op^T), with square
 // workgroup tiles of edge `tile` (128 or 256; the problems' padding).
-mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, void* pool,
-                         int elem, float c0, float c1, int has_e, hipStream_t st);
+// bk = 1: B is read K-major (K x N row-major) through LDS transpose reads.
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
+                         void* pool, int elem, float c0, float c1, int has_e, hipStream_t st);
 mo_status launch_ns_final(const FinalItem* items, int n, int64_t total_rows, const void* pool,
                           int elem, hipStream_t st);
 

@@ -98,9 +98,10 @@ __global__ __launch_bounds__(kThreads) void k_ns_prep(const PrepItem* __restrict
     if (row < it.r && col < it.c)
       v = load_as_f32(it.in, static_cast<int64_t>(row) * it.ld_in + col, it.in_dt) * s;
     const T e = to_elem<T>(v);
-    sb[static_cast<int64_t>(row) * it.cp + col] = e;
+    if (it.sbuf >= 0) sb[static_cast<int64_t>(row) * it.cp + col] = e;
     tile_s[lr][tx] = e;
   }
+  if (it.stbuf < 0) return;  // uniform over the block
   __syncthreads();
   for (int q = 0; q < kPrepTile / 4; ++q) {
     const int lc = ty + 4 * q;  // column of the stored tile = row of the transpose
@@ -189,6 +190,8 @@ __device__ __forceinline__ void decode_tile(int t, int tm, int tn, int sym, int&
   ti = tj = 0;  // unreachable for t inside the problem's tile count
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 template <typename T>
 __device__ __forceinline__ void mma(const u32x4& a, const u32x4& b, f32x16& acc);
 
@@ -245,8 +248,6 @@ __device__ __forceinline__ void st8<float>(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
 template <typename T>
 __device__ __forceinline__ void ld4(const T* p, float* v);
 template <>
@@ -290,27 +291,51 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <typename T, int BM, int BN, int WM, int WN, bool BK>
 struct GemmCfg {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int FM = kWaveM / 32, FN = kWaveN / 32;
+  static constexpr int kSlabK = kRowBytes / static_cast<int>(sizeof(T));  // k per slab
   static constexpr int kRowsPerPass = kThreads / 8;        // 8 x 16-byte chunks per row
-  static constexpr int kPassA = BM / kRowsPerPass, kPassB = BN / kRowsPerPass;
-  static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+  static constexpr int kPassA = BM / kRowsPerPass;
+  // B stored N x K: like A.  B stored K x N (BK): kSlabK rows of BN elements,
+  // each padded by 64 bytes so that the transpose reads of 4 consecutive
+  // rows fall into distinct banks.
+  static constexpr int kBkRowBytes = BN * static_cast<int>(sizeof(T)) + 64;
+  static constexpr int kBkChunksPerRow = BN * static_cast<int>(sizeof(T)) / 16;
+  static constexpr int kBkRowsPerPass = kThreads / kBkChunksPerRow;
+  static constexpr int kPassB = BK ? kSlabK / kBkRowsPerPass : BN / kRowsPerPass;
+  static constexpr int kBStageBytes = BK ? kSlabK * kBkRowBytes : BN * kRowBytes;
+  static constexpr int kStageBytes = BM * kRowBytes + kBStageBytes;
   static constexpr int kBandLd = BN + 4;                    // epilogue band stride (floats)
   static constexpr int kBandBytes = kWaveM * kBandLd * 4;   // one wave-row band of C
   static constexpr int kLdsBytes =
       2 * kStageBytes > kBandBytes ? 2 * kStageBytes : kBandBytes;
   static_assert(FM >= 1 && FN >= 1 && kPassA >= 1 && kPassB >= 1, "bad tile");
+  static_assert(!BK || kBkRowsPerPass * kPassB == kSlabK, "K-major B slab split");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
-template <typename T, int BM, int BN, int WM, int WN, int MINW>
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives element
+// (i & 3) of the 4-element words addressed by lanes 4e + (i >> 2), e = 0..3.
+// With lane j pointing at row k0 + (j >> 2), columns n0 + 4 (j & 3) .. + 3 of
+// a K x N row-major array, lane i therefore gets column n0 + i, rows
+// k0 .. k0 + 3: an MFMA B fragment piece read from K-major data.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) char*)(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK>
 __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1,
     int has_e) {
-  using C = GemmCfg<BM, BN, WM, WN>;
+  using C = GemmCfg<T, BM, BN, WM, WN, BK>;
   constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8
@@ -338,18 +363,32 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   const uint32_t ldb_b = static_cast<uint32_t>(pr.ldb) * sizeof(T);
   const char* abase = reinterpret_cast<const char*>(pool + pr.a_off) +
                       static_cast<size_t>(ti) * BM * lda_b;
-  const char* bbase = reinterpret_cast<const char*>(pool + pr.b_off) +
-                      static_cast<size_t>(tj) * BN * ldb_b;
   const auto rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0,
                                                      static_cast<int>(BM * lda_b), 0x00020000);
-  const auto rsb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bbase), 0,
-                                                     static_cast<int>(BN * ldb_b), 0x00020000);
   const int voa = static_cast<int>(lrow * lda_b) + lc * 16;
-  const int vob = static_cast<int>(lrow * ldb_b) + lc * 16;
+  // B stored N x K: rows tj*BN.. of B, like A.  B stored K x N: columns
+  // tj*BN.. of every row; the resource moves with the K slab, so offsets stay
+  // below kSlabK rows whatever the matrix size.
+  const char* bbase = BK ? reinterpret_cast<const char*>(pool + pr.b_off + tj * BN)
+                         : reinterpret_cast<const char*>(pool + pr.b_off) +
+                               static_cast<size_t>(tj) * BN * ldb_b;
+  const int bk_row = tid / C::kBkChunksPerRow, bk_c = tid % C::kBkChunksPerRow;
+  const int vob = BK ? static_cast<int>(bk_row * ldb_b) + bk_c * 16
+                     : static_cast<int>(lrow * ldb_b) + lc * 16;
+  auto rsb_at = [&](int kt) __attribute__((always_inline)) {
+    if constexpr (BK)
+      return __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(bbase) + static_cast<size_t>(kt) * C::kSlabK * ldb_b, 0,
+          static_cast<int>(C::kSlabK * ldb_b), 0x00020000);
+    else
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bbase), 0,
+                                               static_cast<int>(BN * ldb_b), 0x00020000);
+  };
 
-  // LDS slab layout: row r, 16-byte chunk c at r * 128 + ((c ^ f(r)) << 4),
-  // f(r) = (r + r / 8) & 7.  Rows 32 apart differ in f by 4 (mod 8), so every
-  // address below is a per-thread base plus a compile-time immediate.
+  // LDS slab layout of A (and of B stored N x K): row r, 16-byte chunk c at
+  // r * 128 + ((c ^ f(r)) << 4), f(r) = (r + r / 8) & 7.  Rows 32 apart
+  // differ in f by 4 (mod 8), so every address below is a per-thread base
+  // plus a compile-time immediate.  B stored K x N: row k at k * kBkRowBytes.
   const int f_l = (lrow + (lrow >> 3)) & 7;
   const int st_base = lrow * kRowBytes;
   auto st_chunk = [&](int q) __attribute__((always_inline)) {
@@ -361,14 +400,27 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   auto rd_chunk = [&](int ks, int parity) __attribute__((always_inline)) {
     return ((ks * 2 + fg) ^ ((f_r + 4 * parity) & 7)) << 4;
   };
+  const int st_bk = BM * kRowBytes + bk_row * C::kBkRowBytes + bk_c * 16;
+  // transpose-read base (bf16): lane j of 16-lane group g reads row
+  // 8 (g / 2) + (j / 4) + 4 h of the substep, columns 16 (g % 2) + 4 (j % 4).
+  // fp32: lane reads rows 4 fg + e, column fr.
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int rd_bk = sizeof(T) == 2
+                        ? BM * kRowBytes + (8 * (g16 >> 1) + (j16 >> 2)) * C::kBkRowBytes +
+                              (wn * C::kWaveN + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2
+                        : BM * kRowBytes + 4 * fg * C::kBkRowBytes + (wn * C::kWaveN + fr) * 4;
 
   u32x4 ra[C::kPassA], rb[C::kPassB];
   // q-th 16-byte global load / LDS store of a slab (A rows first, then B)
-  auto gload_one = [&](int kt, auto qc) __attribute__((always_inline)) {
+  auto gload_one = [&](int kt, auto rsb, auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
     if constexpr (q < C::kPassA)
       ra[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                             rsa, voa, q * C::kRowsPerPass * lda_b + kt * kRowBytes, 0));
+    else if constexpr (BK)
+      rb[q - C::kPassA] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rsb, vob, (q - C::kPassA) * C::kBkRowsPerPass * ldb_b, 0));
     else
       rb[q - C::kPassA] = __builtin_bit_cast(
           u32x4, __builtin_amdgcn_raw_buffer_load_b128(
@@ -376,17 +428,22 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   };
   auto lstore_one = [&](int stage, auto qc) __attribute__((always_inline)) {
     constexpr int q = decltype(qc)::value;
+    char* sb = smem + stage * C::kStageBytes;
     if constexpr (q < C::kPassA)
-      *reinterpret_cast<u32x4*>(smem + stage * C::kStageBytes + st_base + st_chunk(q) +
-                                q * C::kRowsPerPass * kRowBytes) = ra[q];
+      *reinterpret_cast<u32x4*>(sb + st_base + st_chunk(q) + q * C::kRowsPerPass * kRowBytes) =
+          ra[q];
+    else if constexpr (BK)
+      *reinterpret_cast<u32x4*>(sb + st_bk + (q - C::kPassA) * C::kBkRowsPerPass *
+                                                 C::kBkRowBytes) = rb[q - C::kPassA];
     else
-      *reinterpret_cast<u32x4*>(smem + stage * C::kStageBytes + BM * kRowBytes + st_base +
-                                st_chunk(q - C::kPassA) +
+      *reinterpret_cast<u32x4*>(sb + BM * kRowBytes + st_base + st_chunk(q - C::kPassA) +
                                 (q - C::kPassA) * C::kRowsPerPass * kRowBytes) = rb[q - C::kPassA];
   };
   constexpr int kStores = C::kPassA + C::kPassB;
   auto gload = [&](int kt) __attribute__((always_inline)) {
-    static_for<0, kStores>([&](auto qc) __attribute__((always_inline)) { gload_one(kt, qc); });
+    const auto rsb = rsb_at(kt);
+    static_for<0, kStores>(
+        [&](auto qc) __attribute__((always_inline)) { gload_one(kt, rsb, qc); });
   };
   auto lstore = [&](int stage) __attribute__((always_inline)) {
     static_for<0, kStores>([&](auto qc) __attribute__((always_inline)) { lstore_one(stage, qc); });
@@ -410,10 +467,28 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     for (int mi = 0; mi < FM; ++mi)
       av[set][mi] = *reinterpret_cast<const u32x4*>(base + rd_a + mi * 32 * kRowBytes +
                                                     rd_chunk(ks, mi & 1));
+    if constexpr (!BK) {
 #pragma unroll
-    for (int ni = 0; ni < FN; ++ni)
-      bv[set][ni] = *reinterpret_cast<const u32x4*>(base + rd_b + ni * 32 * kRowBytes +
-                                                    rd_chunk(ks, ni & 1));
+      for (int ni = 0; ni < FN; ++ni)
+        bv[set][ni] = *reinterpret_cast<const u32x4*>(base + rd_b + ni * 32 * kRowBytes +
+                                                      rd_chunk(ks, ni & 1));
+    } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) {
+        const char* p = base + rd_bk + ks * 16 * C::kBkRowBytes + ni * 64;
+        const u32x2 lo = lds_read_tr16(p);
+        const u32x2 hi = lds_read_tr16(p + 4 * C::kBkRowBytes);
+        bv[set][ni] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    } else {
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) {
+        const char* p = base + rd_bk + ks * 8 * C::kBkRowBytes + ni * 128;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          bv[set][ni][e] = *reinterpret_cast<const uint32_t*>(p + e * C::kBkRowBytes);
+      }
+    }
   };
   auto mfma_block = [&](auto setc) __attribute__((always_inline)) {
     constexpr int set = decltype(setc)::value;
@@ -432,7 +507,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   //   read frags ks0 of slab k+1  | MFMAs ks3
   // The scheduling fences keep each region's LDS reads issued ahead of the
   // MFMAs that hide them.
-  const int KT = pr.K / (kRowBytes / static_cast<int>(sizeof(T)));
+  const int KT = pr.K / C::kSlabK;
   gload(0);
   lstore(0);
   if (KT > 1) gload(1);
@@ -469,13 +544,14 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   // values back for the transposed stores.  32x32 MFMA output: lane l holds column l % 32 and
   // rows 8 (v / 4) + 4 (l / 32) + v % 4 for v = 0..15.
   float* cs = reinterpret_cast<float*>(smem);
+  const bool need_c = pr.c_off >= 0;
   const bool need_t = pr.ct_off >= 0 && !(pr.sym && ti == tj);
   constexpr int BR = C::kWaveM;
   constexpr int kIters = (BR * BN) / (NT * 8);
 #pragma unroll 1
   for (int band = 0; band < WM; ++band) {
     const int row0 = ti * BM + band * BR;
-    T* cg = pool + pr.c_off + static_cast<size_t>(row0) * pr.ldc + tj * BN;
+    T* cg = need_c ? pool + pr.c_off + static_cast<size_t>(row0) * pr.ldc + tj * BN : nullptr;
     const T* eg = has_e ? pool + pr.e_off + static_cast<size_t>(row0) * pr.lde + tj * BN
                         : nullptr;
     if (wm == band) {
@@ -506,7 +582,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] += c0 * e[k];
       }
-      st8<T>(cg + static_cast<size_t>(i) * pr.ldc + j, v);
+      if (need_c) st8<T>(cg + static_cast<size_t>(i) * pr.ldc + j, v);
       if (need_t) {
         *reinterpret_cast<f32x4*>(cs + i * C::kBandLd + j) = f32x4{v[0], v[1], v[2], v[3]};
         *reinterpret_cast<f32x4*>(cs + i * C::kBandLd + j + 4) = f32x4{v[4], v[5], v[6], v[7]};
@@ -563,25 +639,35 @@ mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const flo
   return MO_OK;
 }
 
-mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, void* pool,
-                         int elem, float c0, float c1, int has_e, hipStream_t st) {
+template <typename T, int BM, int WM, int WN>
+void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
+                       float c1, int has_e, hipStream_t st) {
+  constexpr int NT = 64 * WM * WN;
+  if (bk)
+    k_ns_gemm<T, BM, BM, WM, WN, 2, true><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e);
+  else
+    k_ns_gemm<T, BM, BM, WM, WN, 2, false><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e);
+}
+
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
+                         void* pool, int elem, float c0, float c1, int has_e, hipStream_t st) {
   if (ntiles <= 0) return MO_OK;
   KTimer tm(MO_KC_NS_GEMM, st);
   const dim3 grid(static_cast<unsigned>(ntiles));
   if (tile == 256) {
     if (elem == 2)
-      k_ns_gemm<uint16_t, 256, 256, 2, 4, 2><<<grid, 512, 0, st>>>(
-          probs, n, static_cast<uint16_t*>(pool), c0, c1, has_e);
+      launch_gemm_shape<uint16_t, 256, 2, 4>(probs, n, grid, bk, static_cast<uint16_t*>(pool), c0,
+                                             c1, has_e, st);
     else
-      k_ns_gemm<float, 256, 256, 2, 4, 2><<<grid, 512, 0, st>>>(
-          probs, n, static_cast<float*>(pool), c0, c1, has_e);
+      launch_gemm_shape<float, 256, 2, 4>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
+                                          has_e, st);
   } else if (tile == 128) {
     if (elem == 2)
-      k_ns_gemm<uint16_t, 128, 128, 2, 2, 2><<<grid, 256, 0, st>>>(
-          probs, n, static_cast<uint16_t*>(pool), c0, c1, has_e);
+      launch_gemm_shape<uint16_t, 128, 2, 2>(probs, n, grid, bk, static_cast<uint16_t*>(pool), c0,
+                                             c1, has_e, st);
     else
-      k_ns_gemm<float, 128, 128, 2, 2, 2><<<grid, 256, 0, st>>>(
-          probs, n, static_cast<float*>(pool), c0, c1, has_e);
+      launch_gemm_shape<float, 128, 2, 2>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
+                                          has_e, st);
   } else {
     return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);
   }
