@@ -140,19 +140,19 @@ __global__ __launch_bounds__(kThreads) void k_ns_final(const FinalItem* __restri
 // ---------------------------------------------------------------------------
 constexpr int kRowBytes = 128;
 
-// 16-byte chunk c of LDS row `row` lives at chunk c ^ f(row), f(r) = (r + r/8)
-// mod 8: any 8 consecutive rows, and the 8 rows of one parity among any 16
-// consecutive rows, see distinct chunks, so the MFMA operand reads (32 rows,
-// one chunk) are conflict-free for both 128-byte and 256-byte bank windows.
-__device__ __forceinline__ int swz(int row, int c16) {
-  return row * kRowBytes + ((c16 ^ ((row + (row >> 3)) & 7)) << 4);
-}
-
+// LDS slabs of 128-byte rows: 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7).  The LDS has 64 four-byte banks, so rows r and r + 1 of
+// an aligned pair fill one 256-byte bank line; XOR-ing bits 1..3 of the row
+// spreads the 32 rows x one chunk of an MFMA operand read (and the 8 lanes per
+// row of a slab store) over all banks.  Measured on gfx950 with the LDS bank
+// conflict counter: no conflict cycles for these reads, where the row-parity
+// swizzle (r + r / 8) & 7 doubles their cycles.
 // Tile order inside one problem.  Non-symmetric problems go by groups of 8
 // tile-rows (column-major inside a group), so the workgroups resident at one
 // time share both operand row blocks; symmetric problems (upper triangle
 // only) go by 4 x 4 super-tiles of the triangle.
 constexpr int kGroupRows = 8;
+constexpr int kXcdChunk = 32;
 constexpr int kSuper = 4;
 
 __device__ __forceinline__ void decode_tile(int t, int tm, int tn, int sym, int& ti, int& tj) {
@@ -191,6 +191,32 @@ __device__ __forceinline__ void decode_tile(int t, int tm, int tn, int sym, int&
 }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Buffer resource (raw, stride 0) over `bytes` bytes from `base`; accesses
+// past the range read zero instead of faulting.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) & 0xffffu, bytes,
+               0x00020000u};
+}
+
+// Direct-to-LDS load (buffer_load_dwordx4 ... lds): lane i's 16 bytes from
+// base + voff + soff land at LDS byte lds_byte + 16 i.  M0, which carries the
+// LDS address, is saved and restored around it.  The compiler does not see
+// this as an LDS store: the caller waits for the vector memory counter and
+// synchronises the workgroup before the data is read.
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t lds_byte, int voff,
+                                          int soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_byte), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
 
 template <typename T>
 __device__ __forceinline__ void mma(const u32x4& a, const u32x4& b, f32x16& acc);
@@ -294,26 +320,29 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <typename T, int BM, int BN, int WM, int WN, bool BK>
 struct GemmCfg {
   static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int FM = kWaveM / 32, FN = kWaveN / 32;
   static constexpr int kSlabK = kRowBytes / static_cast<int>(sizeof(T));  // k per slab
-  static constexpr int kRowsPerPass = kThreads / 8;        // 8 x 16-byte chunks per row
-  static constexpr int kPassA = BM / kRowsPerPass;
-  // B stored N x K: like A.  B stored K x N (BK): kSlabK rows of BN elements,
-  // each padded by 64 bytes so that the transpose reads of 4 consecutive
-  // rows fall into distinct banks.
-  static constexpr int kBkRowBytes = BN * static_cast<int>(sizeof(T)) + 64;
-  static constexpr int kBkChunksPerRow = BN * static_cast<int>(sizeof(T)) / 16;
-  static constexpr int kBkRowsPerPass = kThreads / kBkChunksPerRow;
-  static constexpr int kPassB = BK ? kSlabK / kBkRowsPerPass : BN / kRowsPerPass;
+  // Slabs are filled by direct-to-LDS loads: one instruction moves 64 lanes x
+  // 16 bytes into 1 KiB of contiguous LDS.  A (and B stored N x K): 8 rows of
+  // 128 bytes per instruction.  B stored K x N (BK): rows of BN elements.
+  static constexpr int kBkRowBytes = BN * static_cast<int>(sizeof(T));
+  static constexpr int kBkRowsPerInst = 1024 / kBkRowBytes;
+  static constexpr int kBkChunksPerRow = kBkRowBytes / 16;
+  static constexpr int kInstA = BM * kRowBytes / 1024 / kWaves;    // per wave and slab
   static constexpr int kBStageBytes = BK ? kSlabK * kBkRowBytes : BN * kRowBytes;
+  static constexpr int kInstB = kBStageBytes / 1024 / kWaves;
   static constexpr int kStageBytes = BM * kRowBytes + kBStageBytes;
   static constexpr int kBandLd = BN + 4;                    // epilogue band stride (floats)
-  static constexpr int kBandBytes = kWaveM * kBandLd * 4;   // one wave-row band of C
+  static constexpr int kBandBytes = kWaveM / 2 * kBandLd * 4;   // one epilogue band of C
   static constexpr int kLdsBytes =
       2 * kStageBytes > kBandBytes ? 2 * kStageBytes : kBandBytes;
-  static_assert(FM >= 1 && FN >= 1 && kPassA >= 1 && kPassB >= 1, "bad tile");
-  static_assert(!BK || kBkRowsPerPass * kPassB == kSlabK, "K-major B slab split");
+  static_assert(FM >= 1 && FN >= 1 && kInstA >= 1 && kInstB >= 1, "bad tile");
+  static_assert(kInstA * kWaves * 1024 == BM * kRowBytes, "A slab split");
+  static_assert(kInstB * kWaves * 1024 == kBStageBytes, "B slab split");
+  static_assert(!BK || (kBkRowsPerInst >= 1 && kBkRowsPerInst * kBkRowBytes == 1024),
+                "K-major B rows per instruction");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
@@ -339,11 +368,21 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8
-  // XCDs; give each XCD a contiguous run of logical tiles so neighbouring
-  // tiles (which share operand rows) meet in the same L2.
+  // XCDs.  Each XCD receives chunks of kXcdChunk consecutive logical tiles
+  // (neighbouring tiles share operand panels in that XCD's L2), the chunks
+  // dealt round-robin so that every XCD gets a similar mix of long and short
+  // problems; the last partial round is split into contiguous runs.
   const int G = gridDim.x, bid = blockIdx.x;
-  const int q8 = G >> 3, r8 = G & 7, xcd = bid & 7;
-  const int tile = xcd * q8 + min(xcd, r8) + (bid >> 3);
+  const int xcd = bid & 7, ord = bid >> 3;
+  const int full = G / (8 * kXcdChunk);
+  int tile;
+  if (ord < full * kXcdChunk) {
+    tile = ((ord / kXcdChunk) * 8 + xcd) * kXcdChunk + ord % kXcdChunk;
+  } else {
+    const int rest = G - full * 8 * kXcdChunk;
+    const int q8 = rest >> 3, r8 = rest & 7;
+    tile = full * 8 * kXcdChunk + xcd * q8 + min(xcd, r8) + (ord - full * kXcdChunk);
+  }
   const GemmProb pr = probs[find_segment(probs, nprob, tile)];
   int ti, tj;
   decode_tile(tile - pr.start, pr.tiles_m, pr.tiles_n, pr.sym, ti, tj);
@@ -352,102 +391,101 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int fr = lane & 31, fg = lane >> 5;
-  const int lrow = tid >> 3, lc = tid & 7;
   static_assert(FM % 2 == 0 && FN % 2 == 0, "wave tiles span an even number of 32-row blocks");
-  static_assert(C::kRowsPerPass % 32 == 0, "slab rows per pass must keep the swizzle phase");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
 
-  // Global -> register loads through buffer resources spanning this tile's
-  // operand rows (hardware range-checked): one per-thread VGPR offset, the
-  // row-pass and K-slab offsets go into the scalar soffset.
+  // Global -> LDS through buffer resources (hardware range-checked).  A (and
+  // B stored N x K) spans this tile's operand rows; the K slab goes into the
+  // scalar offset.  B stored K x N spans the columns tj*BN.. of the slab's
+  // kSlabK rows; its resource moves with the slab so offsets stay small.
   const uint32_t lda_b = static_cast<uint32_t>(pr.lda) * sizeof(T);
   const uint32_t ldb_b = static_cast<uint32_t>(pr.ldb) * sizeof(T);
   const char* abase = reinterpret_cast<const char*>(pool + pr.a_off) +
                       static_cast<size_t>(ti) * BM * lda_b;
-  const auto rsa = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(abase), 0,
-                                                     static_cast<int>(BM * lda_b), 0x00020000);
-  const int voa = static_cast<int>(lrow * lda_b) + lc * 16;
-  // B stored N x K: rows tj*BN.. of B, like A.  B stored K x N: columns
-  // tj*BN.. of every row; the resource moves with the K slab, so offsets stay
-  // below kSlabK rows whatever the matrix size.
+  const u32x4 rsa = buffer_rsrc(abase, BM * lda_b);
   const char* bbase = BK ? reinterpret_cast<const char*>(pool + pr.b_off + tj * BN)
                          : reinterpret_cast<const char*>(pool + pr.b_off) +
                                static_cast<size_t>(tj) * BN * ldb_b;
-  const int bk_row = tid / C::kBkChunksPerRow, bk_c = tid % C::kBkChunksPerRow;
-  const int vob = BK ? static_cast<int>(bk_row * ldb_b) + bk_c * 16
-                     : static_cast<int>(lrow * ldb_b) + lc * 16;
   auto rsb_at = [&](int kt) __attribute__((always_inline)) {
     if constexpr (BK)
-      return __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<char*>(bbase) + static_cast<size_t>(kt) * C::kSlabK * ldb_b, 0,
-          static_cast<int>(C::kSlabK * ldb_b), 0x00020000);
+      return buffer_rsrc(bbase + static_cast<size_t>(kt) * C::kSlabK * ldb_b, C::kSlabK * ldb_b);
     else
-      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(bbase), 0,
-                                               static_cast<int>(BN * ldb_b), 0x00020000);
+      return buffer_rsrc(bbase, BN * ldb_b);
   };
 
-  // LDS slab layout of A (and of B stored N x K): row r, 16-byte chunk c at
-  // r * 128 + ((c ^ f(r)) << 4), f(r) = (r + r / 8) & 7.  Rows 32 apart
-  // differ in f by 4 (mod 8), so every address below is a per-thread base
-  // plus a compile-time immediate.  B stored K x N: row k at k * kBkRowBytes.
-  const int f_l = (lrow + (lrow >> 3)) & 7;
-  const int st_base = lrow * kRowBytes;
-  auto st_chunk = [&](int q) __attribute__((always_inline)) {
-    return (lc ^ ((f_l + 4 * ((q * C::kRowsPerPass / 32) & 1)) & 7)) << 4;
+  // LDS slab layout (128-byte rows): 16-byte chunk c of row r sits at chunk
+  // c ^ ((r >> 1) & 7).  Load instruction q of this wave fills rows
+  // 8 (wave * kInst + q) .. + 7; lane i lands at row + i / 8, physical chunk
+  // i % 8, so it fetches logical chunk (i % 8) ^ ((row >> 1) & 7).  With
+  // kInst even, that swizzle depends on q only through q & 1.
+  static_assert(C::kInstA % 2 == 0 && (BK || C::kInstB % 2 == 0), "instruction parity");
+  auto nt_voff = [&](uint32_t ld_b, int par) __attribute__((always_inline)) {
+    const int row = lane >> 3;  // row inside the instruction's 8
+    const int chunk = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+    return static_cast<int>(row * ld_b) + chunk * 16;
   };
-  const int f_r = (fr + (fr >> 3)) & 7;
+  const int voa0 = nt_voff(lda_b, 0), voa1 = nt_voff(lda_b, 1);
+  const int vobn0 = nt_voff(ldb_b, 0), vobn1 = nt_voff(ldb_b, 1);
+  // B stored K x N: row r of the slab (kBkRowBytes bytes) holds 16-byte chunk
+  // c at c ^ ((r & 3) << 2) (bf16; the four rows read together by a
+  // transpose read then use four different 64-byte bank windows).
+  auto bk_swz = [](int r) __attribute__((always_inline)) {
+    return sizeof(T) == 2 ? (r & 3) << 2 : 0;
+  };
+  int vobk[C::kInstB];
+#pragma unroll
+  for (int q = 0; q < C::kInstB; ++q) {
+    const int row = (wv * C::kInstB + q) * C::kBkRowsPerInst + lane / C::kBkChunksPerRow;
+    const int chunk = (lane % C::kBkChunksPerRow) ^ bk_swz(row);
+    vobk[q] = BK ? static_cast<int>(row * ldb_b) + chunk * 16 : 0;
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
+  // all direct-to-LDS loads of slab kt into `stage`
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    const uint32_t sb = lds0 + stage * C::kStageBytes;
+#pragma unroll
+    for (int q = 0; q < C::kInstA; ++q) {
+      const int t = wv * C::kInstA + q;
+      lds_dma16(rsa, sb + t * 1024, (q & 1) ? voa1 : voa0, t * 8 * lda_b + kt * kRowBytes);
+    }
+    const u32x4 rsb = rsb_at(kt);
+#pragma unroll
+    for (int q = 0; q < C::kInstB; ++q) {
+      const int t = wv * C::kInstB + q;
+      if constexpr (BK)
+        lds_dma16(rsb, sb + BM * kRowBytes + t * 1024, vobk[q], 0);
+      else
+        lds_dma16(rsb, sb + BM * kRowBytes + t * 1024, (q & 1) ? vobn1 : vobn0,
+                  t * 8 * ldb_b + kt * kRowBytes);
+    }
+  };
+
+  // Fragment reads.  A / NxK B: lane reads row (wave row base + fr), logical
+  // chunk 2 ks + fg; row offsets are multiples of 16, so the swizzle is a
+  // per-thread constant.  KxN B (bf16): transpose reads, lane j of 16-lane
+  // group g covering rows 16 ks + 8 (g / 2) + 4 h + j / 4 and columns
+  // wn * kWaveN + 32 ni + 16 (g % 2) + 4 (j % 4); fp32: rows 8 ks + 4 fg + e,
+  // column wn * kWaveN + 32 ni + fr.
+  const int f_r = (fr >> 1) & 7;
   const int rd_a = (wm * C::kWaveM + fr) * kRowBytes;
   const int rd_b = BM * kRowBytes + (wn * C::kWaveN + fr) * kRowBytes;
-  auto rd_chunk = [&](int ks, int parity) __attribute__((always_inline)) {
-    return ((ks * 2 + fg) ^ ((f_r + 4 * parity) & 7)) << 4;
+  auto rd_chunk = [&](int ks) __attribute__((always_inline)) {
+    return ((ks * 2 + fg) ^ f_r) << 4;
   };
-  const int st_bk = BM * kRowBytes + bk_row * C::kBkRowBytes + bk_c * 16;
-  // transpose-read base (bf16): lane j of 16-lane group g reads row
-  // 8 (g / 2) + (j / 4) + 4 h of the substep, columns 16 (g % 2) + 4 (j % 4).
-  // fp32: lane reads rows 4 fg + e, column fr.
   const int g16 = lane >> 4, j16 = lane & 15;
-  const int rd_bk = sizeof(T) == 2
-                        ? BM * kRowBytes + (8 * (g16 >> 1) + (j16 >> 2)) * C::kBkRowBytes +
-                              (wn * C::kWaveN + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2
-                        : BM * kRowBytes + 4 * fg * C::kBkRowBytes + (wn * C::kWaveN + fr) * 4;
-
-  u32x4 ra[C::kPassA], rb[C::kPassB];
-  // q-th 16-byte global load / LDS store of a slab (A rows first, then B)
-  auto gload_one = [&](int kt, auto rsb, auto qc) __attribute__((always_inline)) {
-    constexpr int q = decltype(qc)::value;
-    if constexpr (q < C::kPassA)
-      ra[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rsa, voa, q * C::kRowsPerPass * lda_b + kt * kRowBytes, 0));
-    else if constexpr (BK)
-      rb[q - C::kPassA] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     rsb, vob, (q - C::kPassA) * C::kBkRowsPerPass * ldb_b, 0));
-    else
-      rb[q - C::kPassA] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     rsb, vob, (q - C::kPassA) * C::kRowsPerPass * ldb_b + kt * kRowBytes, 0));
-  };
-  auto lstore_one = [&](int stage, auto qc) __attribute__((always_inline)) {
-    constexpr int q = decltype(qc)::value;
-    char* sb = smem + stage * C::kStageBytes;
-    if constexpr (q < C::kPassA)
-      *reinterpret_cast<u32x4*>(sb + st_base + st_chunk(q) + q * C::kRowsPerPass * kRowBytes) =
-          ra[q];
-    else if constexpr (BK)
-      *reinterpret_cast<u32x4*>(sb + st_bk + (q - C::kPassA) * C::kBkRowsPerPass *
-                                                 C::kBkRowBytes) = rb[q - C::kPassA];
-    else
-      *reinterpret_cast<u32x4*>(sb + BM * kRowBytes + st_base + st_chunk(q - C::kPassA) +
-                                (q - C::kPassA) * C::kRowsPerPass * kRowBytes) = rb[q - C::kPassA];
-  };
-  constexpr int kStores = C::kPassA + C::kPassB;
-  auto gload = [&](int kt) __attribute__((always_inline)) {
-    const auto rsb = rsb_at(kt);
-    static_for<0, kStores>(
-        [&](auto qc) __attribute__((always_inline)) { gload_one(kt, rsb, qc); });
-  };
-  auto lstore = [&](int stage) __attribute__((always_inline)) {
-    static_for<0, kStores>([&](auto qc) __attribute__((always_inline)) { lstore_one(stage, qc); });
-  };
+  int rd_bk[FN];
+#pragma unroll
+  for (int ni = 0; ni < FN; ++ni) {
+    if constexpr (sizeof(T) == 2) {
+      const int row = 8 * (g16 >> 1) + (j16 >> 2);
+      const int colb = (wn * C::kWaveN + ni * 32 + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+      rd_bk[ni] = BM * kRowBytes + row * C::kBkRowBytes +
+                  (((colb >> 4) ^ bk_swz(row)) << 4) + (colb & 15);
+    } else {
+      rd_bk[ni] = BM * kRowBytes + 4 * fg * C::kBkRowBytes + (wn * C::kWaveN + ni * 32 + fr) * 4;
+    }
+  }
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -466,16 +504,16 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi)
       av[set][mi] = *reinterpret_cast<const u32x4*>(base + rd_a + mi * 32 * kRowBytes +
-                                                    rd_chunk(ks, mi & 1));
+                                                    rd_chunk(ks));
     if constexpr (!BK) {
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni)
         bv[set][ni] = *reinterpret_cast<const u32x4*>(base + rd_b + ni * 32 * kRowBytes +
-                                                      rd_chunk(ks, ni & 1));
+                                                      rd_chunk(ks));
     } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni) {
-        const char* p = base + rd_bk + ks * 16 * C::kBkRowBytes + ni * 64;
+        const char* p = base + rd_bk[ni] + ks * 16 * C::kBkRowBytes;
         const u32x2 lo = lds_read_tr16(p);
         const u32x2 hi = lds_read_tr16(p + 4 * C::kBkRowBytes);
         bv[set][ni] = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -483,7 +521,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     } else {
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni) {
-        const char* p = base + rd_bk + ks * 8 * C::kBkRowBytes + ni * 128;
+        const char* p = base + rd_bk[ni] + ks * 8 * C::kBkRowBytes;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           bv[set][ni][e] = *reinterpret_cast<const uint32_t*>(p + e * C::kBkRowBytes);
@@ -497,25 +535,31 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni) mma<T>(av[set][mi], bv[set][ni], acc[mi][ni]);
   };
+  // vmcnt(0) lgkmcnt(0): this wave's direct-to-LDS loads have landed (they
+  // are counted by the vector memory counter) and its LDS reads of the stage
+  // that the next loads overwrite have completed.
+  auto wait_loads = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0070);
+  };
   // Software pipeline over K slabs (4 substeps of 16 k each), alternating
-  // two fragment register sets.  Per slab:
+  // two fragment register sets and two LDS stages.  Per slab kt:
+  //   loads of slab kt+1 into the other stage (its last readers passed the
+  //   previous barrier)
   //   read frags ks1              | MFMAs ks0
-  //   read frags ks2              | MFMAs ks1, then LDS store of slab k+1
-  //                               |   (registers -> the other stage)
-  //   read frags ks3              | MFMAs ks2, then global loads of slab k+2
-  //   barrier (slab k+1 complete in LDS; slab k fully read)
-  //   read frags ks0 of slab k+1  | MFMAs ks3
-  // The scheduling fences keep each region's LDS reads issued ahead of the
-  // MFMAs that hide them.
+  //   read frags ks2              | MFMAs ks1
+  //   read frags ks3              | MFMAs ks2
+  //   wait for this wave's loads; barrier (slab kt+1 in LDS, slab kt read)
+  //   read frags ks0 of slab kt+1 | MFMAs ks3
   const int KT = pr.K / C::kSlabK;
-  gload(0);
-  lstore(0);
-  if (KT > 1) gload(1);
+  issue(0, 0);
+  wait_loads();
   __syncthreads();
   fload(0, 0, Int<0>{});
   for (int kt = 0; kt < KT; ++kt) {
     const int stage = kt & 1;
     const bool more = kt + 1 < KT;
+    if (more) issue(kt + 1, stage ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
     fload(stage, 1, Int<1>{});
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(Int<0>{});
@@ -523,13 +567,12 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     fload(stage, 2, Int<0>{});
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(Int<1>{});
-    if (more) lstore(stage ^ 1);
     __builtin_amdgcn_sched_barrier(0);
     fload(stage, 3, Int<1>{});
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(Int<0>{});
-    if (kt + 2 < KT) gload(kt + 2);
     __builtin_amdgcn_sched_barrier(0);
+    wait_loads();
     __syncthreads();
     if (more) fload(stage ^ 1, 0, Int<0>{});
     __builtin_amdgcn_sched_barrier(0);
@@ -538,36 +581,52 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   }
   __syncthreads();
 
-  // Epilogue, one band of kWaveM rows (one row of waves) at a time: the
-  // band's waves stage their fp32 accumulators in LDS, then all threads make
-  // coalesced direct stores (with the E term) and, when asked, write the
-  // values back for the transposed stores.  32x32 MFMA output: lane l holds column l % 32 and
-  // rows 8 (v / 4) + 4 (l / 32) + v % 4 for v = 0..15.
+  // Epilogue, one band of kWaveM / 2 rows (half of one row of waves) at a
+  // time: the band's waves stage their fp32 accumulators in LDS, then all
+  // threads make coalesced direct stores (with the E term) and, when asked,
+  // write the values back for the transposed stores.  bf16 E values of the
+  // band are all requested before the staging (one memory round trip per
+  // band).  32x32 MFMA output: lane l holds column l % 32 and rows
+  // 8 (v / 4) + 4 (l / 32) + v % 4 for v = 0..15.
   float* cs = reinterpret_cast<float*>(smem);
   const bool need_c = pr.c_off >= 0;
   const bool need_t = pr.ct_off >= 0 && !(pr.sym && ti == tj);
-  constexpr int BR = C::kWaveM;
+  constexpr int HM = FM / 2;                 // 32-row blocks per band
+  constexpr int BR = HM * 32;                // band rows
   constexpr int kIters = (BR * BN) / (NT * 8);
+  static_assert(FM % 2 == 0 && kIters >= 1 && (BR * BN) % (NT * 8) == 0, "epilogue split");
 #pragma unroll 1
-  for (int band = 0; band < WM; ++band) {
+  for (int band = 0; band < 2 * WM; ++band) {
     const int row0 = ti * BM + band * BR;
     T* cg = need_c ? pool + pr.c_off + static_cast<size_t>(row0) * pr.ldc + tj * BN : nullptr;
     const T* eg = has_e ? pool + pr.e_off + static_cast<size_t>(row0) * pr.lde + tj * BN
                         : nullptr;
-    if (wm == band) {
+    u32x4 er[kIters];
+    if constexpr (sizeof(T) == 2) {
+      if (has_e) {
 #pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
+        for (int p = 0; p < kIters; ++p) {
+          const int idx = p * NT + tid;
+          const int i = idx / (BN / 8), j = (idx % (BN / 8)) * 8;
+          er[p] = *reinterpret_cast<const u32x4*>(eg + static_cast<size_t>(i) * pr.lde + j);
+        }
+      }
+    }
+    if (wm == (band >> 1)) {
+      const int h = band & 1;
+#pragma unroll
+      for (int hm = 0; hm < HM; ++hm)
 #pragma unroll
         for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int i = mi * 32 + 8 * (v >> 2) + 4 * fg + (v & 3);
+            const int i = hm * 32 + 8 * (v >> 2) + 4 * fg + (v & 3);
             const int j = wn * C::kWaveN + ni * 32 + fr;
-            cs[i * C::kBandLd + j] = acc[mi][ni][v];
+            cs[i * C::kBandLd + j] = h ? acc[HM + hm][ni][v] : acc[hm][ni][v];
           }
     }
     __syncthreads();
-#pragma unroll 2
+#pragma unroll
     for (int p = 0; p < kIters; ++p) {
       const int idx = p * NT + tid;
       const int i = idx / (BN / 8), j = (idx % (BN / 8)) * 8;
@@ -578,7 +637,15 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
       for (int k = 0; k < 4; ++k) { v[k] = c1 * x0[k]; v[4 + k] = c1 * x1[k]; }
       if (has_e) {
         float e[8];
-        ld8<T>(eg + static_cast<size_t>(i) * pr.lde + j, e);
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            e[2 * k] = __uint_as_float(er[p][k] << 16);
+            e[2 * k + 1] = __uint_as_float(er[p][k] & 0xffff0000u);
+          }
+        } else {
+          ld8<T>(eg + static_cast<size_t>(i) * pr.lde + j, e);
+        }
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] += c0 * e[k];
       }

@@ -1,5 +1,6 @@
 // Host side of the Newton-Schulz path: pool layout, problem tables and the
 // iteration driver.
+#include <algorithm>
 #include <cstring>
 
 #include "host.hpp"
@@ -23,6 +24,18 @@ GemmProb make_prob(int64_t a, int64_t b, int64_t c, int64_t ct, int64_t e, int32
 
 int64_t tiles_of(int32_t tm, int32_t tn, bool sym) {
   return sym ? static_cast<int64_t>(tm) * (tm + 1) / 2 : static_cast<int64_t>(tm) * tn;
+}
+
+// Longest tiles (largest K) first, then renumber the first-tile indices: the
+// short tiles fill the end of the launch.
+void order_by_k(std::vector<GemmProb>& v) {
+  std::stable_sort(v.begin(), v.end(),
+                   [](const GemmProb& a, const GemmProb& b) { return a.K > b.K; });
+  int64_t start = 0;
+  for (GemmProb& p : v) {
+    p.start = static_cast<int32_t>(start);
+    start += tiles_of(p.tiles_m, p.tiles_n, p.sym != 0);
+  }
 }
 }  // namespace
 
@@ -96,6 +109,15 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     }
     B.gram_tiles += tiles_of(ts, ts, true);
     B.upd_tiles += tiles_of(ts, tl, false);
+  }
+  for (NsBucket& B : L.buckets) {
+    for (int q = 0; q < 2; ++q) {
+      order_by_k(B.gram_p[q]);
+      order_by_k(B.gram_a[q]);
+      order_by_k(B.upd[q]);
+      order_by_k(B.fin[q]);
+    }
+    order_by_k(B.square);
   }
   L.pool_elems = pool;
 }
