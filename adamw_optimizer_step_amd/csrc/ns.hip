@@ -138,15 +138,13 @@ __global__ __launch_bounds__(kThreads) void k_ns_final(const FinalItem* __restri
 // current one is multiplied.  The LDS traffic per MFMA falls as the wave
 // sub-tile grows: (FM + FN) fragment reads feed FM * FN MFMAs.
 // ---------------------------------------------------------------------------
-constexpr int kRowBytes = 128;
-
-// LDS slabs of 128-byte rows: 16-byte chunk c of row r sits at chunk
-// c ^ ((r >> 1) & 7).  The LDS has 64 four-byte banks, so rows r and r + 1 of
-// an aligned pair fill one 256-byte bank line; XOR-ing bits 1..3 of the row
-// spreads the 32 rows x one chunk of an MFMA operand read (and the 8 lanes per
-// row of a slab store) over all banks.  Measured on gfx950 with the LDS bank
-// conflict counter: no conflict cycles for these reads, where the row-parity
-// swizzle (r + r / 8) & 7 doubles their cycles.
+// LDS slabs of kRowB-byte rows (one K slab of A, or of B stored N x K):
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> kSh) & (chunks - 1)) with
+// kSh = log2(256 / kRowB).  The LDS has 64 four-byte banks; the rows that
+// share one 256-byte bank line differ in the bits below kSh, and XOR-ing the
+// next bits spreads the 32 rows x one chunk of an MFMA operand read over all
+// banks.  Measured on gfx950 with the LDS bank-conflict counter: no conflict
+// cycles for these reads, where a row-parity swizzle doubles their cycles.
 // Tile order inside one problem.  Non-symmetric problems go by groups of 8
 // tile-rows (column-major inside a group), so the workgroups resident at one
 // time share both operand row blocks; symmetric problems (upper triangle
@@ -323,26 +321,35 @@ struct GemmCfg {
   static constexpr int kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int FM = kWaveM / 32, FN = kWaveN / 32;
-  static constexpr int kSlabK = kRowBytes / static_cast<int>(sizeof(T));  // k per slab
+  // K slab: 64-byte rows (32 bf16 / 16 fp32 of k), 4 LDS stages, 3 in flight
+  static constexpr int kRowB = 64;
+  static constexpr int kStages = 4;
+  static constexpr int kSub = kRowB / 32;                   // 16-k substeps per slab
+  static constexpr int kChunks = kRowB / 16;                // 16-byte chunks per row
+  static constexpr int kSh = kRowB == 64 ? 2 : 1;           // swizzle shift
+  static constexpr int kSlabK = kRowB / static_cast<int>(sizeof(T));
   // Slabs are filled by direct-to-LDS loads: one instruction moves 64 lanes x
-  // 16 bytes into 1 KiB of contiguous LDS.  A (and B stored N x K): 8 rows of
-  // 128 bytes per instruction.  B stored K x N (BK): rows of BN elements.
+  // 16 bytes into 1 KiB of contiguous LDS.  A (and B stored N x K): 1024 / kRowB
+  // rows per instruction.  B stored K x N (BK): rows of BN elements.
+  static constexpr int kRowsPerInst = 1024 / kRowB;
   static constexpr int kBkRowBytes = BN * static_cast<int>(sizeof(T));
   static constexpr int kBkRowsPerInst = 1024 / kBkRowBytes;
   static constexpr int kBkChunksPerRow = kBkRowBytes / 16;
-  static constexpr int kInstA = BM * kRowBytes / 1024 / kWaves;    // per wave and slab
-  static constexpr int kBStageBytes = BK ? kSlabK * kBkRowBytes : BN * kRowBytes;
+  static constexpr int kInstA = BM * kRowB / 1024 / kWaves;    // per wave and slab
+  static constexpr int kBStageBytes = BK ? kSlabK * kBkRowBytes : BN * kRowB;
   static constexpr int kInstB = kBStageBytes / 1024 / kWaves;
-  static constexpr int kStageBytes = BM * kRowBytes + kBStageBytes;
+  static constexpr int kInst = kInstA + kInstB;
+  static constexpr int kStageBytes = BM * kRowB + kBStageBytes;
   static constexpr int kBandLd = BN + 4;                    // epilogue band stride (floats)
   static constexpr int kBandBytes = kWaveM / 2 * kBandLd * 4;   // one epilogue band of C
   static constexpr int kLdsBytes =
-      2 * kStageBytes > kBandBytes ? 2 * kStageBytes : kBandBytes;
+      kStages * kStageBytes > kBandBytes ? kStages * kStageBytes : kBandBytes;
   static_assert(FM >= 1 && FN >= 1 && kInstA >= 1 && kInstB >= 1, "bad tile");
-  static_assert(kInstA * kWaves * 1024 == BM * kRowBytes, "A slab split");
+  static_assert(kInstA * kWaves * 1024 == BM * kRowB, "A slab split");
   static_assert(kInstB * kWaves * 1024 == kBStageBytes, "B slab split");
   static_assert(!BK || (kBkRowsPerInst >= 1 && kBkRowsPerInst * kBkRowBytes == 1024),
                 "K-major B rows per instruction");
+  static_assert(kInst <= 7, "vector-memory wait counts below assume at most 7 loads per slab");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
@@ -413,63 +420,61 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
       return buffer_rsrc(bbase, BN * ldb_b);
   };
 
-  // LDS slab layout (128-byte rows): 16-byte chunk c of row r sits at chunk
-  // c ^ ((r >> 1) & 7).  Load instruction q of this wave fills rows
-  // 8 (wave * kInst + q) .. + 7; lane i lands at row + i / 8, physical chunk
-  // i % 8, so it fetches logical chunk (i % 8) ^ ((row >> 1) & 7).  With
-  // kInst even, that swizzle depends on q only through q & 1.
-  static_assert(C::kInstA % 2 == 0 && (BK || C::kInstB % 2 == 0), "instruction parity");
-  auto nt_voff = [&](uint32_t ld_b, int par) __attribute__((always_inline)) {
-    const int row = lane >> 3;  // row inside the instruction's 8
-    const int chunk = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
-    return static_cast<int>(row * ld_b) + chunk * 16;
+  // LDS slab layout (kRowB-byte rows): chunk c of row r at chunk
+  // c ^ swz(r).  Load instruction t of the workgroup fills rows
+  // kRowsPerInst * t .. + kRowsPerInst - 1; lane i lands at row + i / kChunks,
+  // physical chunk i % kChunks, so it fetches logical chunk
+  // (i % kChunks) ^ swz(row).
+  auto swz = [](int r) __attribute__((always_inline)) {
+    return (r >> C::kSh) & (C::kChunks - 1);
   };
-  const int voa0 = nt_voff(lda_b, 0), voa1 = nt_voff(lda_b, 1);
-  const int vobn0 = nt_voff(ldb_b, 0), vobn1 = nt_voff(ldb_b, 1);
+  int voa[C::kInstA], vob[C::kInstB];
+#pragma unroll
+  for (int q = 0; q < C::kInstA; ++q) {
+    const int row = (wv * C::kInstA + q) * C::kRowsPerInst + lane / C::kChunks;
+    voa[q] = static_cast<int>(row * lda_b) + (((lane % C::kChunks) ^ swz(row)) << 4);
+  }
   // B stored K x N: row r of the slab (kBkRowBytes bytes) holds 16-byte chunk
   // c at c ^ ((r & 3) << 2) (bf16; the four rows read together by a
   // transpose read then use four different 64-byte bank windows).
   auto bk_swz = [](int r) __attribute__((always_inline)) {
     return sizeof(T) == 2 ? (r & 3) << 2 : 0;
   };
-  int vobk[C::kInstB];
 #pragma unroll
   for (int q = 0; q < C::kInstB; ++q) {
-    const int row = (wv * C::kInstB + q) * C::kBkRowsPerInst + lane / C::kBkChunksPerRow;
-    const int chunk = (lane % C::kBkChunksPerRow) ^ bk_swz(row);
-    vobk[q] = BK ? static_cast<int>(row * ldb_b) + chunk * 16 : 0;
+    if constexpr (BK) {
+      const int row = (wv * C::kInstB + q) * C::kBkRowsPerInst + lane / C::kBkChunksPerRow;
+      vob[q] = static_cast<int>(row * ldb_b) +
+               (((lane % C::kBkChunksPerRow) ^ bk_swz(row)) << 4);
+    } else {
+      const int row = (wv * C::kInstB + q) * C::kRowsPerInst + lane / C::kChunks;
+      vob[q] = static_cast<int>(row * ldb_b) + (((lane % C::kChunks) ^ swz(row)) << 4);
+    }
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
-  // all direct-to-LDS loads of slab kt into `stage`
+  // all direct-to-LDS loads of slab kt into `stage` (kInst per wave)
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
     const uint32_t sb = lds0 + stage * C::kStageBytes;
 #pragma unroll
-    for (int q = 0; q < C::kInstA; ++q) {
-      const int t = wv * C::kInstA + q;
-      lds_dma16(rsa, sb + t * 1024, (q & 1) ? voa1 : voa0, t * 8 * lda_b + kt * kRowBytes);
-    }
+    for (int q = 0; q < C::kInstA; ++q)
+      lds_dma16(rsa, sb + (wv * C::kInstA + q) * 1024, voa[q], kt * C::kRowB);
     const u32x4 rsb = rsb_at(kt);
 #pragma unroll
-    for (int q = 0; q < C::kInstB; ++q) {
-      const int t = wv * C::kInstB + q;
-      if constexpr (BK)
-        lds_dma16(rsb, sb + BM * kRowBytes + t * 1024, vobk[q], 0);
-      else
-        lds_dma16(rsb, sb + BM * kRowBytes + t * 1024, (q & 1) ? vobn1 : vobn0,
-                  t * 8 * ldb_b + kt * kRowBytes);
-    }
+    for (int q = 0; q < C::kInstB; ++q)
+      lds_dma16(rsb, sb + BM * C::kRowB + (wv * C::kInstB + q) * 1024, vob[q],
+                BK ? 0 : kt * C::kRowB);
   };
 
   // Fragment reads.  A / NxK B: lane reads row (wave row base + fr), logical
-  // chunk 2 ks + fg; row offsets are multiples of 16, so the swizzle is a
-  // per-thread constant.  KxN B (bf16): transpose reads, lane j of 16-lane
-  // group g covering rows 16 ks + 8 (g / 2) + 4 h + j / 4 and columns
-  // wn * kWaveN + 32 ni + 16 (g % 2) + 4 (j % 4); fp32: rows 8 ks + 4 fg + e,
-  // column wn * kWaveN + 32 ni + fr.
-  const int f_r = (fr >> 1) & 7;
-  const int rd_a = (wm * C::kWaveM + fr) * kRowBytes;
-  const int rd_b = BM * kRowBytes + (wn * C::kWaveN + fr) * kRowBytes;
+  // chunk 2 ks + fg; the row offsets added are multiples of 32, so the
+  // swizzle is a per-thread constant.  KxN B (bf16): transpose reads, lane j
+  // of 16-lane group g covering rows 16 ks + 8 (g / 2) + 4 h + j / 4 and
+  // columns wn * kWaveN + 32 ni + 16 (g % 2) + 4 (j % 4); fp32: rows
+  // 8 ks + 4 fg + e, column wn * kWaveN + 32 ni + fr.
+  const int f_r = swz(fr);
+  const int rd_a = (wm * C::kWaveM + fr) * C::kRowB;
+  const int rd_b = BM * C::kRowB + (wn * C::kWaveN + fr) * C::kRowB;
   auto rd_chunk = [&](int ks) __attribute__((always_inline)) {
     return ((ks * 2 + fg) ^ f_r) << 4;
   };
@@ -480,10 +485,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     if constexpr (sizeof(T) == 2) {
       const int row = 8 * (g16 >> 1) + (j16 >> 2);
       const int colb = (wn * C::kWaveN + ni * 32 + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
-      rd_bk[ni] = BM * kRowBytes + row * C::kBkRowBytes +
+      rd_bk[ni] = BM * C::kRowB + row * C::kBkRowBytes +
                   (((colb >> 4) ^ bk_swz(row)) << 4) + (colb & 15);
     } else {
-      rd_bk[ni] = BM * kRowBytes + 4 * fg * C::kBkRowBytes + (wn * C::kWaveN + ni * 32 + fr) * 4;
+      rd_bk[ni] = BM * C::kRowB + 4 * fg * C::kBkRowBytes + (wn * C::kWaveN + ni * 32 + fr) * 4;
     }
   }
 
@@ -496,19 +501,19 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
       for (int v = 0; v < 16; ++v) acc[mi][ni][v] = 0.f;
 
   // Operand fragments of one k-substep (32 bytes of every row); two sets so
-  // that the reads of substep ks+1 are in flight while ks is multiplied.
+  // that the reads of the next substep are in flight while one is multiplied.
   u32x4 av[2][FM], bv[2][FN];
   auto fload = [&](int stage, int ks, auto setc) __attribute__((always_inline)) {
     constexpr int set = decltype(setc)::value;
     const char* base = smem + stage * C::kStageBytes;
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi)
-      av[set][mi] = *reinterpret_cast<const u32x4*>(base + rd_a + mi * 32 * kRowBytes +
+      av[set][mi] = *reinterpret_cast<const u32x4*>(base + rd_a + mi * 32 * C::kRowB +
                                                     rd_chunk(ks));
     if constexpr (!BK) {
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni)
-        bv[set][ni] = *reinterpret_cast<const u32x4*>(base + rd_b + ni * 32 * kRowBytes +
+        bv[set][ni] = *reinterpret_cast<const u32x4*>(base + rd_b + ni * 32 * C::kRowB +
                                                       rd_chunk(ks));
     } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -535,46 +540,46 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
 #pragma unroll
       for (int ni = 0; ni < FN; ++ni) mma<T>(av[set][mi], bv[set][ni], acc[mi][ni]);
   };
-  // vmcnt(0) lgkmcnt(0): this wave's direct-to-LDS loads have landed (they
-  // are counted by the vector memory counter) and its LDS reads of the stage
-  // that the next loads overwrite have completed.
-  auto wait_loads = []() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0070);
+  // Wait until this wave's loads of all but the `younger` most recent slabs
+  // have landed (the direct-to-LDS loads are counted by the vector memory
+  // counter, kInst per slab, completing in order) and its LDS reads are done
+  // (the stage they read is refilled after the next barrier).
+  auto wait_slab = [](int younger) __attribute__((always_inline)) {
+    static_assert(2 * C::kInst <= 15, "vmcnt immediate");
+    if (younger >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0070 | (2 * C::kInst));
+    else if (younger == 1)
+      __builtin_amdgcn_s_waitcnt(0x0070 | C::kInst);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);
   };
-  // Software pipeline over K slabs (4 substeps of 16 k each), alternating
-  // two fragment register sets and two LDS stages.  Per slab kt:
-  //   loads of slab kt+1 into the other stage (its last readers passed the
-  //   previous barrier)
+  // Software pipeline over K slabs (kSub = 2 substeps of 16 k), two fragment
+  // register sets, kStages = 4 LDS stages with the loads of 3 slabs in flight.
+  // Per slab kt:
+  //   loads of slab kt+3 into stage (kt+3) % 4 (last read in slab kt-1,
+  //   which ended with a barrier)
   //   read frags ks1              | MFMAs ks0
-  //   read frags ks2              | MFMAs ks1
-  //   read frags ks3              | MFMAs ks2
-  //   wait for this wave's loads; barrier (slab kt+1 in LDS, slab kt read)
-  //   read frags ks0 of slab kt+1 | MFMAs ks3
+  //   wait for slab kt+1; barrier
+  //   read frags ks0 of slab kt+1 | MFMAs ks1
+  static_assert(C::kSub == 2, "pipeline below is written for two substeps per slab");
   const int KT = pr.K / C::kSlabK;
-  issue(0, 0);
-  wait_loads();
+  const int pre = KT < C::kStages - 1 ? KT : C::kStages - 1;
+  for (int k = 0; k < pre; ++k) issue(k, k);
+  wait_slab(pre - 1);
   __syncthreads();
   fload(0, 0, Int<0>{});
   for (int kt = 0; kt < KT; ++kt) {
-    const int stage = kt & 1;
-    const bool more = kt + 1 < KT;
-    if (more) issue(kt + 1, stage ^ 1);
+    const int stage = kt & (C::kStages - 1);
+    if (kt + C::kStages - 1 < KT) issue(kt + C::kStages - 1, (kt + C::kStages - 1) & (C::kStages - 1));
     __builtin_amdgcn_sched_barrier(0);
     fload(stage, 1, Int<1>{});
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(Int<0>{});
     __builtin_amdgcn_sched_barrier(0);
-    fload(stage, 2, Int<0>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_block(Int<1>{});
-    __builtin_amdgcn_sched_barrier(0);
-    fload(stage, 3, Int<1>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_block(Int<0>{});
-    __builtin_amdgcn_sched_barrier(0);
-    wait_loads();
+    const int last = min(KT - 1, kt + C::kStages - 1);
+    wait_slab(last - (kt + 1));
     __syncthreads();
-    if (more) fload(stage ^ 1, 0, Int<0>{});
+    if (kt + 1 < KT) fload((kt + 1) & (C::kStages - 1), 0, Int<0>{});
     __builtin_amdgcn_sched_barrier(0);
     mfma_block(Int<1>{});
     __builtin_amdgcn_sched_barrier(0);
@@ -584,9 +589,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   // Epilogue, one band of kWaveM / 2 rows (half of one row of waves) at a
   // time: the band's waves stage their fp32 accumulators in LDS, then all
   // threads make coalesced direct stores (with the E term) and, when asked,
-  // write the values back for the transposed stores.  bf16 E values of the
-  // band are all requested before the staging (one memory round trip per
-  // band).  32x32 MFMA output: lane l holds column l % 32 and rows
+  // write the values back for the transposed stores.  32x32 MFMA output: lane l holds column l % 32 and rows
   // 8 (v / 4) + 4 (l / 32) + v % 4 for v = 0..15.
   float* cs = reinterpret_cast<float*>(smem);
   const bool need_c = pr.c_off >= 0;
@@ -595,23 +598,30 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   constexpr int BR = HM * 32;                // band rows
   constexpr int kIters = (BR * BN) / (NT * 8);
   static_assert(FM % 2 == 0 && kIters >= 1 && (BR * BN) % (NT * 8) == 0, "epilogue split");
-#pragma unroll 1
+  // bf16: the whole tile's E values are requested before the first store
+  // (the compiler orders a load after every earlier store it cannot prove
+  // disjoint, so loads issued between bands would wait for their stores).
+  u32x4 er[2 * WM][kIters];
+  if constexpr (sizeof(T) == 2) {
+    if (has_e) {
+#pragma unroll
+      for (int band = 0; band < 2 * WM; ++band) {
+        const T* eg = pool + pr.e_off + static_cast<size_t>(ti * BM + band * BR) * pr.lde + tj * BN;
+#pragma unroll
+        for (int p = 0; p < kIters; ++p) {
+          const int idx = p * NT + tid;
+          const int i = idx / (BN / 8), j = (idx % (BN / 8)) * 8;
+          er[band][p] = *reinterpret_cast<const u32x4*>(eg + static_cast<size_t>(i) * pr.lde + j);
+        }
+      }
+    }
+  }
+#pragma unroll
   for (int band = 0; band < 2 * WM; ++band) {
     const int row0 = ti * BM + band * BR;
     T* cg = need_c ? pool + pr.c_off + static_cast<size_t>(row0) * pr.ldc + tj * BN : nullptr;
     const T* eg = has_e ? pool + pr.e_off + static_cast<size_t>(row0) * pr.lde + tj * BN
                         : nullptr;
-    u32x4 er[kIters];
-    if constexpr (sizeof(T) == 2) {
-      if (has_e) {
-#pragma unroll
-        for (int p = 0; p < kIters; ++p) {
-          const int idx = p * NT + tid;
-          const int i = idx / (BN / 8), j = (idx % (BN / 8)) * 8;
-          er[p] = *reinterpret_cast<const u32x4*>(eg + static_cast<size_t>(i) * pr.lde + j);
-        }
-      }
-    }
     if (wm == (band >> 1)) {
       const int h = band & 1;
 #pragma unroll
@@ -640,8 +650,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            e[2 * k] = __uint_as_float(er[p][k] << 16);
-            e[2 * k + 1] = __uint_as_float(er[p][k] & 0xffff0000u);
+            e[2 * k] = __uint_as_float(er[band][p][k] << 16);
+            e[2 * k + 1] = __uint_as_float(er[band][p][k] & 0xffff0000u);
           }
         } else {
           ld8<T>(eg + static_cast<size_t>(i) * pr.lde + j, e);
