@@ -256,20 +256,29 @@ __device__ __forceinline__ void ld8<float>(const float* p, float* v) {
   for (int k = 0; k < 4; ++k) { v[k] = a[k]; v[4 + k] = b[k]; }
 }
 
-template <typename T>
-__device__ __forceinline__ void st8(T* p, const float* v);
-template <>
-__device__ __forceinline__ void st8<uint16_t>(uint16_t* p, const float* v) {
-  u32x4 u;
+// 8 values to 8 consecutive elements; NT = non-temporal (streaming) stores,
+// for outputs that the same launch does not read again.
+template <typename T, bool NT = false>
+__device__ __forceinline__ void st8(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4 u;
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    u[k] = f32_to_bf16(v[2 * k]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * k + 1])) << 16);
-  *reinterpret_cast<u32x4*>(p) = u;
-}
-template <>
-__device__ __forceinline__ void st8<float>(float* p, const float* v) {
-  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    for (int k = 0; k < 4; ++k)
+      u[k] = f32_to_bf16(v[2 * k]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * k + 1])) << 16);
+    if constexpr (NT)
+      __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
+    else
+      *reinterpret_cast<u32x4*>(p) = u;
+  } else {
+    const f32x4 a{v[0], v[1], v[2], v[3]}, b{v[4], v[5], v[6], v[7]};
+    if constexpr (NT) {
+      __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+      __builtin_nontemporal_store(b, reinterpret_cast<f32x4*>(p + 4));
+    } else {
+      *reinterpret_cast<f32x4*>(p) = a;
+      *reinterpret_cast<f32x4*>(p + 4) = b;
+    }
+  }
 }
 
 template <typename T>
@@ -659,7 +668,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] += c0 * e[k];
       }
-      if (need_c) st8<T>(cg + static_cast<size_t>(i) * pr.ldc + j, v);
+      // the update's output is read only by the next launch: stream it past
+      // L2, which holds this launch's operand panels (the Gram's stores are
+      // kept: its mirror writes rely on write combining in L2)
+      if (need_c) st8<T, BK>(cg + static_cast<size_t>(i) * pr.ldc + j, v);
       if (need_t) {
         *reinterpret_cast<f32x4*>(cs + i * C::kBandLd + j) = f32x4{v[0], v[1], v[2], v[3]};
         *reinterpret_cast<f32x4*>(cs + i * C::kBandLd + j + 4) = f32x4{v[4], v[5], v[6], v[7]};
