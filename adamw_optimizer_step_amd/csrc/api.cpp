@@ -165,6 +165,7 @@ mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const flo
     p.in = items[i].in;
     p.ld_in = items[i].ld_in;
     p.in_dt = items[i].in_dtype;
+    p.vec = aligned16(p.in) && (p.ld_in * dtype_size(p.in_dt)) % 16 == 0;
     p.stat_begin = p.start;
     p.stat_end = p.start + static_cast<int64_t>(p.rp / kPrepTile) * p.tiles_c;
     FinalItem& f = fin[i];

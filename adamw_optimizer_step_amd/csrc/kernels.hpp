@@ -112,6 +112,8 @@ struct PrepItem {
   int32_t rp, cp;          // padded (multiples of kGemmTile)
   int32_t tiles_c;         // cp / kPrepTile
   int32_t in_dt;
+  int32_t vec;             // rows of `in` allow 16-byte loads of 8 elements
+  int32_t pad;
 };
 
 struct GemmProb {

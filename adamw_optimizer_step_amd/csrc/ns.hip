@@ -77,39 +77,6 @@ template <>
 __device__ __forceinline__ float to_elem<float>(float v) { return v; }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_ns_prep(const PrepItem* __restrict__ items, int n,
-                                                      const float* __restrict__ scale,
-                                                      T* __restrict__ pool) {
-  __shared__ T tile_s[kPrepTile][kPrepTile + 1];
-  const int64_t tile = blockIdx.x;
-  const int idx = find_segment(items, n, tile);
-  const PrepItem it = items[idx];
-  const float s = scale[idx];
-  const int64_t lt = tile - it.start;
-  const int r0 = static_cast<int>(lt / it.tiles_c) * kPrepTile;
-  const int c0 = static_cast<int>(lt % it.tiles_c) * kPrepTile;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  T* sb = pool + it.sbuf;
-  T* st = pool + it.stbuf;
-  for (int q = 0; q < kPrepTile / 4; ++q) {
-    const int lr = ty + 4 * q;
-    const int row = r0 + lr, col = c0 + tx;
-    float v = 0.f;
-    if (row < it.r && col < it.c)
-      v = load_as_f32(it.in, static_cast<int64_t>(row) * it.ld_in + col, it.in_dt) * s;
-    const T e = to_elem<T>(v);
-    if (it.sbuf >= 0) sb[static_cast<int64_t>(row) * it.cp + col] = e;
-    tile_s[lr][tx] = e;
-  }
-  if (it.stbuf < 0) return;  // uniform over the block
-  __syncthreads();
-  for (int q = 0; q < kPrepTile / 4; ++q) {
-    const int lc = ty + 4 * q;  // column of the stored tile = row of the transpose
-    st[static_cast<int64_t>(c0 + lc) * it.rp + r0 + tx] = tile_s[tx][lc];
-  }
-}
-
-template <typename T>
 __global__ __launch_bounds__(kThreads) void k_ns_final(const FinalItem* __restrict__ items, int n,
                                                        int64_t total_rows,
                                                        const T* __restrict__ pool) {
@@ -310,6 +277,68 @@ __device__ __forceinline__ void st4<uint16_t>(uint16_t* p, const float* v) {
 template <>
 __device__ __forceinline__ void st4<float>(float* p, const float* v) {
   *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+
+template <typename T>
+__device__ __forceinline__ float from_elem(T v);
+template <>
+__device__ __forceinline__ float from_elem<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+template <>
+__device__ __forceinline__ float from_elem<float>(float v) { return v; }
+
+// X0 = scale * D over one 64 x 64 tile of the padded stored orientation:
+// 16-byte global accesses (8 elements per thread and row pass), zeros in the
+// padding; tall slices go through an LDS tile and are written transposed.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_ns_prep(const PrepItem* __restrict__ items, int n,
+                                                      const float* __restrict__ scale,
+                                                      T* __restrict__ pool) {
+  static_assert(kPrepTile == 64 && kThreads == 256, "prep tile split");
+  __shared__ T tile_s[kPrepTile][kPrepTile + 2];
+  const int64_t tile = blockIdx.x;
+  const int idx = find_segment(items, n, tile);
+  const PrepItem it = items[idx];
+  const float sc = scale[idx];
+  const int64_t lt = tile - it.start;
+  const int r0 = static_cast<int>(lt / it.tiles_c) * kPrepTile;
+  const int c0 = static_cast<int>(lt % it.tiles_c) * kPrepTile;
+  const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
+  float v[2][8];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int row = r0 + lr + 32 * k, col = c0 + lc;
+    if (it.vec && row < it.r && col + 8 <= it.c) {
+      load8(it.in, static_cast<int64_t>(row) * it.ld_in + col, it.in_dt, v[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[k][e] *= sc;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[k][e] = row < it.r && col + e < it.c
+                      ? load_as_f32(it.in, static_cast<int64_t>(row) * it.ld_in + col + e,
+                                    it.in_dt) * sc
+                      : 0.f;
+    }
+  }
+  if (it.sbuf >= 0) {  // uniform over the block
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      st8<T>(pool + it.sbuf + static_cast<int64_t>(r0 + lr + 32 * k) * it.cp + c0 + lc, v[k]);
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile_s[lr + 32 * k][lc + e] = to_elem<T>(v[k][e]);
+  __syncthreads();
+  // output row = stored column c0 + lr + 32 k, 8 output columns = stored rows
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    float w[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = from_elem<T>(tile_s[lc + e][lr + 32 * k]);
+    st8<T>(pool + it.stbuf + static_cast<int64_t>(c0 + lr + 32 * k) * it.rp + r0 + lc, w);
+  }
 }
 
 template <int N>

@@ -161,6 +161,7 @@ mo_status upload_tables(mo_plan* P, char* ws, hipStream_t st) {
     pi.in = m.d;
     pi.ld_in = a.cols;
     pi.in_dt = P->ddt;
+    pi.vec = aligned16(pi.in) && (pi.ld_in * static_cast<int64_t>(esz)) % 16 == 0;
     pi.stat_begin = blk;
     blk += ceil_div(numel, kEltPerBlock);
     pi.stat_end = blk;
