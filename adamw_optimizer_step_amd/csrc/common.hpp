@@ -79,33 +79,55 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, int32_t dt, f
 }
 
 // 8 consecutive elements <-> 8 floats.  Pointers must be 16-byte aligned.
+// NT = non-temporal (streaming) access, for data a launch touches once.
+template <typename V, bool NT>
+__device__ __forceinline__ V ldv(const V* q) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(q);
+  else
+    return *q;
+}
+template <typename V, bool NT>
+__device__ __forceinline__ void stv(V* q, const V& v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(v, q);
+  else
+    *q = v;
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NT = false>
 __device__ __forceinline__ void load8(const void* p, int64_t i, int32_t dt, float* v) {
   if (dt == MO_F32) {
-    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    float4 a = q[0], b = q[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const f32x4_t* q = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i);
+    const f32x4_t a = ldv<f32x4_t, NT>(q), b = ldv<f32x4_t, NT>(q + 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { v[k] = a[k]; v[4 + k] = b[k]; }
   } else {
-    uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
-    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
-    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
-    v[4] = __uint_as_float(u.z << 16); v[5] = __uint_as_float(u.z & 0xffff0000u);
-    v[6] = __uint_as_float(u.w << 16); v[7] = __uint_as_float(u.w & 0xffff0000u);
+    const u32x4_t u =
+        ldv<u32x4_t, NT>(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p) + i));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(u[k] << 16);
+      v[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+    }
   }
 }
 
+template <bool NT = false>
 __device__ __forceinline__ void store8(void* p, int64_t i, int32_t dt, const float* v) {
   if (dt == MO_F32) {
-    float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + i);
-    q[0] = make_float4(v[0], v[1], v[2], v[3]);
-    q[1] = make_float4(v[4], v[5], v[6], v[7]);
+    f32x4_t* q = reinterpret_cast<f32x4_t*>(static_cast<float*>(p) + i);
+    stv<f32x4_t, NT>(q, f32x4_t{v[0], v[1], v[2], v[3]});
+    stv<f32x4_t, NT>(q + 1, f32x4_t{v[4], v[5], v[6], v[7]});
   } else {
-    uint4 u;
-    u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-    u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-    u.z = f32_to_bf16(v[4]) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
-    u.w = f32_to_bf16(v[6]) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = u;
+    u32x4_t u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      u[k] = f32_to_bf16(v[2 * k]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * k + 1])) << 16);
+    stv<u32x4_t, NT>(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p) + i), u);
   }
 }
 

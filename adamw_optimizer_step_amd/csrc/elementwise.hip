@@ -43,8 +43,8 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
     const int cnt = sg.numel - e0 >= 8 ? 8 : static_cast<int>(sg.numel - e0);
     const bool vec = cnt == 8 && sg.vec;
     if (vec) {
-      load8(sg.g, e0, sg.gdt, g);
-      load8(sg.b, e0, MO_F32, b);
+      load8<true>(sg.g, e0, sg.gdt, g);
+      load8<true>(sg.b, e0, MO_F32, b);
     } else {
       for (int k = 0; k < 8; ++k) {
         g[k] = k < cnt ? load_as_f32(sg.g, e0 + k, sg.gdt) : 0.f;
@@ -57,8 +57,8 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
       d[k] = nesterov ? g[k] + mu * b[k] : b[k];
     }
     if (vec) {
-      store8(sg.b, e0, MO_F32, b);
-      if (sg.d) store8(sg.d, e0, sg.ddt, d);
+      store8<true>(sg.b, e0, MO_F32, b);
+      if (sg.d) store8<true>(sg.d, e0, sg.ddt, d);
     } else {
       for (int k = 0; k < cnt; ++k) {
         sg.b[e0 + k] = b[k];
@@ -110,18 +110,22 @@ __global__ __launch_bounds__(kThreads) void k_adam_sumsq(const AdamSeg* __restri
   if (threadIdx.x == 0) partials[blk] = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
 }
 
-__global__ __launch_bounds__(kThreads) void k_adam_norm(const double* __restrict__ partials,
-                                                        int64_t n, float max_norm,
-                                                        double* __restrict__ scal,
-                                                        double* __restrict__ norm_out) {
+constexpr int kNormThreads = 1024;
+__global__ __launch_bounds__(kNormThreads) void k_adam_norm(const double* __restrict__ partials,
+                                                            int64_t n, float max_norm,
+                                                            double* __restrict__ scal,
+                                                            double* __restrict__ norm_out) {
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += kThreads) s += partials[i];
-  __shared__ double s_ss[4];
+#pragma unroll 4
+  for (int64_t i = threadIdx.x; i < n; i += kNormThreads) s += partials[i];
+  __shared__ double s_ss[kNormThreads / 64];
   s = wave_sum(s);
   if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = s;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const double T = sqrt((s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]));
+    double t = 0.0;
+    for (int k = 0; k < kNormThreads / 64; ++k) t += s_ss[k];
+    const double T = sqrt(t);
     const double kappa = (max_norm > 0.f && T > static_cast<double>(max_norm))
                              ? static_cast<double>(max_norm) / T
                              : 1.0;
@@ -154,10 +158,10 @@ __global__ __launch_bounds__(kThreads) void k_adam_apply(const AdamSeg* __restri
     float g[8], w[8], m[8], v[8];
     const int cnt = sg.numel - e0 >= 8 ? 8 : static_cast<int>(sg.numel - e0);
     if (cnt == 8) {
-      load8(sg.g, e0, sg.dt, g);
-      load8(sg.p, e0, sg.dt, w);
-      load8(sg.m, e0, MO_F32, m);
-      load8(sg.v, e0, MO_F32, v);
+      load8<true>(sg.g, e0, sg.dt, g);
+      load8<true>(sg.p, e0, sg.dt, w);
+      load8<true>(sg.m, e0, MO_F32, m);
+      load8<true>(sg.v, e0, MO_F32, v);
     } else {
       for (int k = 0; k < 8; ++k) {
         const bool in = k < cnt;
@@ -176,9 +180,9 @@ __global__ __launch_bounds__(kThreads) void k_adam_apply(const AdamSeg* __restri
       w[k] = w[k] * decay - step * (m[k] / denom);
     }
     if (cnt == 8) {
-      store8(sg.p, e0, sg.dt, w);
-      store8(sg.m, e0, MO_F32, m);
-      store8(sg.v, e0, MO_F32, v);
+      store8<true>(sg.p, e0, sg.dt, w);
+      store8<true>(sg.m, e0, MO_F32, m);
+      store8<true>(sg.v, e0, MO_F32, v);
     } else {
       for (int k = 0; k < cnt; ++k) {
         store_from_f32(sg.p, e0 + k, sg.dt, w[k]);
@@ -255,13 +259,14 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowSeg* __restrict__ se
   const float decay = 1.f - lr * sg.wd;
   const float coef = lr * sg.scale * inv;
   if (vec_o && vec_w) {
+#pragma unroll 2
     for (int c0 = lane * 8; c0 < cols; c0 += 64 * 8) {
       float o[8], w[8];
-      load8(sg.o, obase + c0, sg.o_dt, o);
-      load8(sg.w, wbase + c0, sg.w_dt, w);
+      load8<true>(sg.o, obase + c0, sg.o_dt, o);
+      load8<true>(sg.w, wbase + c0, sg.w_dt, w);
 #pragma unroll
       for (int k = 0; k < 8; ++k) w[k] = w[k] * decay - coef * o[k];
-      store8(sg.w, wbase + c0, sg.w_dt, w);
+      store8<true>(sg.w, wbase + c0, sg.w_dt, w);
     }
   } else {
     for (int c = lane; c < cols; c += 64) {
@@ -301,7 +306,7 @@ mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, doub
 mo_status launch_adam_norm(const double* partials, int64_t nblocks, float max_norm, double* scal,
                            double* norm_out, hipStream_t st) {
   KTimer tm(MO_KC_ADAM_NORM, st);
-  k_adam_norm<<<dim3(1), dim3(kThreads), 0, st>>>(partials, nblocks, max_norm, scal, norm_out);
+  k_adam_norm<<<dim3(1), dim3(kNormThreads), 0, st>>>(partials, nblocks, max_norm, scal, norm_out);
   MO_LAUNCH_CHECK("k_adam_norm");
   return MO_OK;
 }
@@ -340,23 +345,24 @@ mo_status launch_rows(int32_t mode, const RowSeg* segs, int nseg, const RowSeg& 
 }
 
 // ---------------------------------------------------------------------------
-// Plain device copy of a known byte count (16-byte loads and stores, grid
-// stride): the reference point that scales hardware byte counters.
+// Plain device copy of a known byte count (one non-temporal 16-byte load and
+// store per thread): the reference point that scales hardware byte counters,
+// and the practical ceiling of a read + write stream.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_diag_copy(const uint4* __restrict__ src,
-                                                        uint4* __restrict__ dst, int64_t n16) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n16;
-       i += stride)
-    dst[i] = src[i];
+__global__ __launch_bounds__(kThreads) void k_diag_copy(const u32x4_t* __restrict__ src,
+                                                        u32x4_t* __restrict__ dst, int64_t n16) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i < n16) stv<u32x4_t, true>(dst + i, ldv<u32x4_t, true>(src + i));
 }
 
 mo_status launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
   if (bytes <= 0) return MO_OK;
   const int64_t n16 = bytes / 16;
-  const unsigned grid = static_cast<unsigned>(std::min<int64_t>(ceil_div(n16, kThreads), 8192));
-  k_diag_copy<<<grid, kThreads, 0, st>>>(static_cast<const uint4*>(src), static_cast<uint4*>(dst),
-                                          n16);
+  const int64_t grid = ceil_div(n16, kThreads);
+  if (grid > 0x7fffffff) return fail(MO_EINVAL, "copy of %lld bytes is too large",
+                                     static_cast<long long>(bytes));
+  k_diag_copy<<<static_cast<unsigned>(grid), kThreads, 0, st>>>(
+      static_cast<const u32x4_t*>(src), static_cast<u32x4_t*>(dst), n16);
   MO_LAUNCH_CHECK("k_diag_copy");
   return MO_OK;
 }

@@ -30,7 +30,7 @@ class KTimer {
 
 // ----- momentum (elementwise, 8192 elements per block) ----------------------
 constexpr int kEltPerThread = 8;
-constexpr int kEltIters = 4;
+constexpr int kEltIters = 1;
 constexpr int kEltPerBlock = kThreads * kEltPerThread * kEltIters;
 
 struct MomSeg {
