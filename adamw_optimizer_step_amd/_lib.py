@@ -112,7 +112,7 @@ SIGNATURES = [
 ]
 
 KERNEL_CLASSES = ["momentum", "ns_stats", "ns_scale", "ns_prep", "ns_gemm", "ns_final", "rows",
-                  "adam_sumsq", "adam_norm", "adam_apply"]
+                  "adam_sumsq", "adam_norm", "adam_apply", "ns_small"]
 
 #: ctypes mirror of each struct, in the order of mo_abi_struct_size's index.
 ABI_STRUCTS = [MomentumItem, NsItem, AdamwItem, ParamDesc, RouteOut, Param, HParams, StepArgs]

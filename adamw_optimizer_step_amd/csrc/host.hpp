@@ -28,6 +28,8 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
 // for tables with a quintic-type row, A (s x s).  Iteration k reads X[k % 2]
 // and writes X[(k + 1) % 2]; the last iteration of a tall matrix writes its
 // result transposed (stored orientation, l x s) into that buffer instead.
+// bf16 matrices whose padded short side is kSmallS go to the slice-resident
+// kernel instead (same iterate buffers and conventions, P kept in LDS).
 constexpr int kBigTile = 256;
 constexpr int kBigTileMinS = 512;
 
@@ -44,6 +46,7 @@ struct NsLayout {
   int n = 0;
   std::vector<PrepItem> prep;
   std::vector<NsBucket> buckets;
+  std::vector<SmallProb> small;
   int64_t prep_tiles = 0;
   std::vector<int64_t> x_off[2];
   std::vector<int32_t> tall, sp, lp;
@@ -62,7 +65,7 @@ struct NsBucketTables {
   size_t gram_p[2] = {0, 0}, gram_a[2] = {0, 0}, square = 0, upd[2] = {0, 0}, fin[2] = {0, 0};
 };
 struct NsTables {
-  size_t prep = 0, bytes = 0;
+  size_t prep = 0, small = 0, bytes = 0;
   std::vector<NsBucketTables> b;
 };
 NsTables ns_table_offsets(const NsLayout& L);

@@ -151,6 +151,20 @@ mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const flo
                          void* pool, int elem, hipStream_t st);
 // One batched GEMM phase:  out = c0 * E + c1 * (A_op B_op^T), with square
 // workgroup tiles of edge `tile` (128 or 256; the problems' padding).
+// Slice-resident Newton-Schulz (all iterations in one launch) for slices whose
+// padded short side is 128: one workgroup per slice.
+struct SmallProb {
+  int64_t x_off[2];        // pool offsets of the two iterate buffers (128 x lp each)
+  int32_t lp;              // padded long side = row stride of the iterates
+  int32_t tall;            // last iteration writes the result transposed (lp x 128)
+};
+struct NsCoeffTable {
+  float a[MO_NS_MAX_STEPS], b[MO_NS_MAX_STEPS], c[MO_NS_MAX_STEPS];
+};
+constexpr int kSmallS = 128;
+mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const float* coeffs,
+                          int steps, hipStream_t st);
+
 // bk = 1: B is read K-major (K x N row-major) through LDS transpose reads.
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, hipStream_t st);

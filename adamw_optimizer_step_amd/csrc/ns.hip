@@ -14,6 +14,8 @@
 // needed inside the GEMM.
 #include <type_traits>
 
+#include <cstring>
+
 #include "kernels.hpp"
 
 namespace mo {
@@ -172,6 +174,14 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
 // synchronises the workgroup before the data is read.
 __device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t lds_byte, int voff,
                                           int soff) {
+  // every operand but the lane offset must live in scalar registers
+  u32x4 rs;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    rs[k] = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(rsrc[k])));
+  const uint32_t lb =
+      static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(lds_byte)));
+  const int so = __builtin_amdgcn_readfirstlane(soff);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -179,7 +189,7 @@ __device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t lds_byte, 
       "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds_byte), "v"(voff), "s"(rsrc), "s"(soff)
+      : "s"(lb), "v"(voff), "s"(rs), "s"(so)
       : "memory");
 }
 
@@ -723,6 +733,255 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Slice-resident Newton-Schulz for bf16 slices whose padded short side is
+// 128 (head-sized slices).  One workgroup of 8 waves owns one slice for all
+// iterations.  X (128 x lp) streams through LDS in 128 x 128 column blocks;
+// P = b A (+ c A^2), A = X X^T, lives in LDS.  Per block of iteration k:
+//   X'_b = a X_b + P X_b        (B operand and E term read from the staged block)
+//   X'_b -> global, and A' += X'_b X'_b^T for iteration k + 1 (registers)
+// so each iteration reads and writes X once; one extra read of X0 forms the
+// first Gram.  Same iterate buffers and conventions as the GEMM path: the
+// last iteration of a tall slice is written transposed (lp x 128).
+// ---------------------------------------------------------------------------
+constexpr int kSmThreads = 512;                 // 8 waves: 2 (rows) x 4 (cols), 64 x 32 each
+constexpr int kSmTile = kSmallS * kSmallS * 2;  // one 128 x 128 bf16 tile (32 KiB)
+constexpr int kSmStages = 3;                    // X blocks in LDS (2 loads ahead)
+
+// 128 x 128 bf16 tiles in LDS: rows of 256 bytes, 16-byte chunk c of row r at
+// c ^ swz(r), swz XOR-ing (r1, r0, r0 ^ r2, r1 ^ r3) into chunk bits 0..3.
+// Chosen by search: conflict-free for the MFMA operand reads (32 rows x one
+// chunk) under every lane grouping consistent with the gfx950 bank-conflict
+// measurements, and for the transpose reads (4 rows x 64 bytes per 16 lanes).
+__device__ __forceinline__ int sm_swz(int r) {
+  return ((r >> 1) & 1) | ((r & 1) << 1) | (((r ^ (r >> 2)) & 1) << 2) |
+         ((((r >> 1) ^ (r >> 3)) & 1) << 3);
+}
+__device__ __forceinline__ int sm_off(int row, int col) {
+  return row * 256 + ((((col >> 3) ^ sm_swz(row)) & 15) << 4) + (col & 7) * 2;
+}
+
+__global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __restrict__ probs,
+                                                            uint16_t* __restrict__ pool,
+                                                            NsCoeffTable cf, int steps) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmTile * (2 + kSmStages)];
+  char* const Ps = smem;             // P (A operand of the update)
+  char* const Xn = smem + kSmTile;   // the new block X'_b (and A in a quintic step)
+  const SmallProb pr = probs[blockIdx.x];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int fr = lane & 31, fg = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
+  const int NB = pr.lp / kSmallS;
+  const int total = NB * (steps + 1);   // pass 0: first Gram; pass k + 1: iteration k
+  const uint32_t ld_b = static_cast<uint32_t>(pr.lp) * 2;
+  uint16_t* const X0 = pool + pr.x_off[0];
+  uint16_t* const X1 = pool + pr.x_off[1];
+  const u32x4 rs0 = buffer_rsrc(X0, kSmallS * ld_b), rs1 = buffer_rsrc(X1, kSmallS * ld_b);
+
+  // Direct-to-LDS loads of one 128 x 128 block: 32 instructions of 4 rows
+  // (1 KiB), 4 per wave; lane i lands at row + i / 16, physical chunk i % 16
+  // and fetches logical chunk (i % 16) ^ swz(row).
+  int vo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = (wv * 4 + q) * 4 + (lane >> 4);
+    vo[q] = static_cast<int>(row * ld_b) + (((lane & 15) ^ sm_swz(row)) << 4);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
+  auto issue = [&](int e) __attribute__((always_inline)) {
+    const int pass = e / NB, b = e - pass * NB;
+    const bool from1 = pass >= 2 && ((pass - 1) & 1);   // iteration k reads X[k % 2]
+    const uint32_t st = lds0 + (2 + e % kSmStages) * kSmTile;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      lds_dma16(from1 ? rs1 : rs0, st + (wv * 4 + q) * 1024, vo[q], b * 256);
+  };
+
+  // Operand reads.  NT fragment (A of every product, B of the Grams): row
+  // m, logical chunk 2 ks + fg.  K-major fragment (B of the update): two
+  // transpose reads, lane j of 16-lane group g at row 16 ks + 8 (g / 2) + 4 h
+  // + j / 4, columns wn * 32 + 16 (g % 2) + 4 (j % 4).
+  auto nt_frag = [&](const char* t, int m, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4*>(t + m * 256 +
+                                           ((((2 * ks + fg) ^ sm_swz(m)) & 15) << 4));
+  };
+  const int trow = 8 * (g16 >> 1) + (j16 >> 2), tcol = wn * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
+  // rows of an accumulator group: 4 fg + e (lane j of group g at row 4 (g / 2) + j / 4)
+  const int etrow = 4 * (g16 >> 1) + (j16 >> 2);
+  auto kmaj_frag = [&](const char* t, int ks) __attribute__((always_inline)) {
+    const u32x2 lo = lds_read_tr16(t + sm_off(16 * ks + trow, tcol));
+    const u32x2 hi = lds_read_tr16(t + sm_off(16 * ks + trow + 4, tcol));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  // C[m][n] += sum_k A[m][k] B[n][k] over a 128-wide K, both operands NT
+  auto gram_acc = [&](const char* ta, const char* tb, f32x16 (&acc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 b = nt_frag(tb, wn * 32 + fr, ks);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(nt_frag(ta, wm * 64 + mi * 32 + fr, ks), b, acc[mi]);
+    }
+  };
+  auto zero = [](f32x16 (&acc)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mi][v] = 0.f;
+  };
+  // element (row, col) of the wave's accumulator value (mi, v)
+  auto acc_row = [&](int mi, int v) __attribute__((always_inline)) {
+    return wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * fg + (v & 3);
+  };
+  const int acc_col = wn * 32 + fr;
+
+  f32x16 accg[2], accu[2];
+  zero(accg);
+  // Load issue bookkeeping (uniform): element e is issued while processing
+  // element at_e; stores of elements up to at(cur) - 1 are older than the loads
+  // of `cur` and have completed once those are waited for (vector memory
+  // operations complete in order).
+  // at_k: element at which element cur + k was issued (k = 0, 1, 2)
+  int next = 0, at_0 = 0, at_1 = 0, at_2 = 0;
+  auto note_issue = [&](int e, int cur) __attribute__((always_inline)) {
+    if (e == cur) at_0 = cur;
+    else if (e == cur + 1) at_1 = cur;
+    else at_2 = cur;
+  };
+
+#pragma unroll 1
+  for (int cur = 0; cur < total; ++cur) {
+    const int pass = cur / NB, b = cur - pass * NB;
+    int done;   // stores of elements <= done are complete after the wait below
+    if (next == cur) {
+      // not issued ahead (its block was written too recently): drain, then load
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __syncthreads();
+      issue(cur);
+      at_0 = cur;
+      ++next;
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      done = cur - 1;
+    } else {
+      // operations of this wave younger than the loads of `cur`: loads of
+      // later elements (4 each) and the stores (4 each) of update elements
+      // processed since those loads were issued
+      const int a = at_0;
+      const int first_store = a > NB ? a : NB;
+      const int young = 4 * (next - 1 - cur) + 4 * (cur > first_store ? cur - first_store : 0);
+      switch (young >> 2) {
+        case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
+        case 1: __builtin_amdgcn_s_waitcnt(0x0070 | 4); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0070 | 8); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0070 | 12); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0070 | 16); break;
+      }
+      done = a - 1;
+    }
+    __syncthreads();   // B1: block `cur` in LDS; element cur - 1 fully done
+    // Loads ahead: at most 2 elements ahead (their stage was last read by
+    // element cur - 1), and a block written by an earlier pass only once its
+    // stores are known complete.
+    while (next < total && next <= cur + 2 && (next < 2 * NB || next - NB <= done)) {
+      issue(next);
+      note_issue(next, cur);
+      ++next;
+    }
+    const char* stg = smem + (2 + cur % kSmStages) * kSmTile;
+    if (pass == 0) {
+      gram_acc(stg, stg, accg);
+    } else {
+      // update: X'_b = a X_b + P X_b
+      zero(accu);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 bf = kmaj_frag(stg, ks);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          mma<uint16_t>(nt_frag(Ps, wm * 64 + mi * 32 + fr, ks), bf, accu[mi]);
+      }
+      const float ak = cf.a[pass - 1];
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // E: rows 8 q + 4 fg + e of column acc_col, via one transpose read
+          const u32x2 e2 = lds_read_tr16(stg + sm_off(wm * 64 + mi * 32 + 8 * q + etrow, tcol));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t bits = (e & 1) ? (e2[e >> 1] & 0xffff0000u) : (e2[e >> 1] << 16);
+            const float x = ak * __uint_as_float(bits) + accu[mi][4 * q + e];
+            *reinterpret_cast<uint16_t*>(Xn + sm_off(acc_row(mi, 4 * q + e), acc_col)) =
+                f32_to_bf16(x);
+          }
+        }
+      __syncthreads();   // B2: X'_b complete in LDS
+      const bool last = pass == steps;
+      if (last && pr.tall) {
+        // stored orientation: out[b * 128 + n][k] = X'_b[k][n], ld 128
+        uint16_t* out = (steps & 1) ? X1 : X0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int T = q * 32 + wv * 4 + g16;
+          const int n0 = 16 * (T & 7), k0 = 8 * (T >> 3);
+          const u32x2 lo = lds_read_tr16(Xn + sm_off(k0 + (j16 >> 2), n0 + 4 * (j16 & 3)));
+          const u32x2 hi = lds_read_tr16(Xn + sm_off(k0 + 4 + (j16 >> 2), n0 + 4 * (j16 & 3)));
+          *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(b * kSmallS + n0 + j16) * kSmallS +
+                                    k0) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+      } else {
+        uint16_t* out = (pass & 1) ? X1 : X0;   // iteration k writes X[(k + 1) % 2]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int id = q * kSmThreads + tid;
+          const int row = id >> 4, c = id & 15;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(Xn + row * 256 +
+                                                         (((c ^ sm_swz(row)) & 15) << 4));
+          *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row) * pr.lp + b * kSmallS +
+                                    c * 8) = v;
+        }
+      }
+      if (!last) gram_acc(Xn, Xn, accg);
+    }
+    if (b == NB - 1 && pass < steps) {
+      // P for iteration `pass` from A = accg
+      const float bk = cf.b[pass], ck = cf.c[pass];
+      if (ck == 0.f) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            *reinterpret_cast<uint16_t*>(Ps + sm_off(acc_row(mi, v), acc_col)) =
+                f32_to_bf16(bk * accg[mi][v]);
+      } else {
+        __syncthreads();   // X'_b reads of this element are done
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const uint16_t h = f32_to_bf16(accg[mi][v]);
+            accg[mi][v] = bf16_to_f32(h);   // A as stored
+            *reinterpret_cast<uint16_t*>(Xn + sm_off(acc_row(mi, v), acc_col)) = h;
+          }
+        __syncthreads();
+        zero(accu);
+        gram_acc(Xn, Xn, accu);   // A A (A is symmetric, so it is its own transpose)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            *reinterpret_cast<uint16_t*>(Ps + sm_off(acc_row(mi, v), acc_col)) =
+                f32_to_bf16(bk * accg[mi][v] + ck * accu[mi][v]);
+      }
+      zero(accg);
+    }
+    at_0 = at_1;
+    at_1 = at_2;
+  }
+}
+
 }  // namespace
 
 mo_status launch_ns_stats(const PrepItem* items, int n, int64_t ntiles, StatPartial* partials,
@@ -790,6 +1049,24 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);
   }
   MO_LAUNCH_CHECK("k_ns_gemm");
+  return MO_OK;
+}
+
+mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const float* coeffs,
+                          int steps, hipStream_t st) {
+  if (n <= 0) return MO_OK;
+  if (steps < 1 || steps > MO_NS_MAX_STEPS) return fail(MO_EINVAL, "bad step count %d", steps);
+  NsCoeffTable cf;
+  std::memset(&cf, 0, sizeof(cf));
+  for (int k = 0; k < steps; ++k) {
+    cf.a[k] = coeffs[3 * k];
+    cf.b[k] = coeffs[3 * k + 1];
+    cf.c[k] = coeffs[3 * k + 2];
+  }
+  KTimer tm(MO_KC_NS_SMALL, st);
+  k_ns_small<<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
+      probs, static_cast<uint16_t*>(pool), cf, steps);
+  MO_LAUNCH_CHECK("k_ns_small");
   return MO_OK;
 }
 

@@ -57,9 +57,10 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     NsBucket& B = L.buckets[s_ >= kBigTileMinS ? 1 : 0];
     const int tile = B.tile;
     const int32_t sp = pad_to(s_, tile), lp = pad_to(l_, tile);
+    const bool small = elem == 2 && tile == kGemmTile && sp == kSmallS;
     const int64_t x[2] = {take(static_cast<int64_t>(sp) * lp), take(static_cast<int64_t>(sp) * lp)};
-    const int64_t p = take(static_cast<int64_t>(sp) * sp);
-    const int64_t a = need_a ? take(static_cast<int64_t>(sp) * sp) : -1;
+    const int64_t p = small ? -1 : take(static_cast<int64_t>(sp) * sp);
+    const int64_t a = need_a && !small ? take(static_cast<int64_t>(sp) * sp) : -1;
     L.x_off[0].push_back(x[0]);
     L.x_off[1].push_back(x[1]);
     L.tall.push_back(tall);
@@ -80,6 +81,16 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     L.prep_tiles += static_cast<int64_t>(pi.rp / kPrepTile) * pi.tiles_c;
     L.prep.push_back(pi);
 
+    if (small) {
+      SmallProb sm;
+      std::memset(&sm, 0, sizeof(sm));
+      sm.x_off[0] = x[0];
+      sm.x_off[1] = x[1];
+      sm.lp = lp;
+      sm.tall = tall;
+      L.small.push_back(sm);
+      continue;
+    }
     const int32_t ts = sp / tile, tl = lp / tile;
     for (int q = 0; q < 2; ++q) {
       const int64_t xc = x[q], xn = x[q ^ 1];
@@ -110,6 +121,9 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     B.gram_tiles += tiles_of(ts, ts, true);
     B.upd_tiles += tiles_of(ts, tl, false);
   }
+  // slice-resident problems: longest first
+  std::stable_sort(L.small.begin(), L.small.end(),
+                   [](const SmallProb& a, const SmallProb& b) { return a.lp > b.lp; });
   for (NsBucket& B : L.buckets) {
     for (int q = 0; q < 2; ++q) {
       order_by_k(B.gram_p[q]);
@@ -126,6 +140,7 @@ NsTables ns_table_offsets(const NsLayout& L) {
   NsTables T;
   WsCursor c;
   T.prep = c.take(L.prep.size() * sizeof(PrepItem), 64);
+  T.small = c.take(L.small.size() * sizeof(SmallProb), 64);
   for (const NsBucket& B : L.buckets) {
     NsBucketTables b;
     auto take = [&c](const std::vector<GemmProb>& v) { return c.take(v.size() * sizeof(GemmProb), 64); };
@@ -149,6 +164,8 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
   };
   if (!L.prep.empty())
     std::memcpy(buf.data() + T.prep, L.prep.data(), L.prep.size() * sizeof(PrepItem));
+  if (!L.small.empty())
+    std::memcpy(buf.data() + T.small, L.small.data(), L.small.size() * sizeof(SmallProb));
   for (size_t k = 0; k < L.buckets.size(); ++k) {
     const NsBucket& B = L.buckets[k];
     const NsBucketTables& b = T.b[k];
@@ -165,6 +182,11 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* coeffs, int steps, hipStream_t st) {
   auto tab = [dtab](size_t off) { return reinterpret_cast<const GemmProb*>(dtab + off); };
+  if (!L.small.empty()) {
+    mo_status s = launch_ns_small(reinterpret_cast<const SmallProb*>(dtab + T.small),
+                                  static_cast<int>(L.small.size()), pool, coeffs, steps, st);
+    if (s != MO_OK) return s;
+  }
   for (int k = 0; k < steps; ++k) {
     const float a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
     const bool cubic_step = c == 0.f || !L.need_a;

@@ -30,6 +30,7 @@ _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 # sources that define each measured kernel and its launch configuration
 KERNEL_SOURCES = {
     "k_ns_gemm": ("ns.hip", "ns_host.cpp", "kernels.hpp", "common.hpp"),
+    "k_ns_small": ("ns.hip", "ns_host.cpp", "kernels.hpp", "common.hpp"),
     "k_momentum": ("elementwise.hip", "kernels.hpp", "common.hpp"),
     "k_adam_apply": ("elementwise.hip", "kernels.hpp", "common.hpp"),
     "k_rows": ("elementwise.hip", "kernels.hpp", "common.hpp"),

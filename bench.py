@@ -50,25 +50,30 @@ def workload_by_name(name: str):
 
 
 def ns_work(slices, coeffs, elem):
-    """Algorithmic Newton-Schulz work per step, from the per-slice, per-iteration
-    unit figures (s = short side, l = long side of each slice):
-    * dense flops 4 s^2 l (A = X X^T and P X), + 2 s^3 for a quintic-type row;
-    * executed flops with the symmetric Gram: 3 s^2 l (+ s^3);
-    * algorithmic HBM bytes: read X for the Gram, write P, read P and X for the
-      update and write the new X: elem * (3 s l + 2 s^2) (+ 2 s^2 for A).
+    """Algorithmic Newton-Schulz work per step, from the per-slice unit figures
+    (s = short side, l = long side of each slice, N iterations):
+    * dense flops 4 s^2 l per iteration (A = X X^T and P X), + 2 s^3 for a
+      quintic-type row;
+    * executed flops with the symmetric Gram: 3 s^2 l (+ s^3) per iteration;
+    * algorithmic HBM bytes when X does not stay on chip: one read of X0 for
+      the first Gram, then a read of X and a write of X' per iteration:
+      elem * s * l * (2 N + 1).
     Returns (dense_flops, executed_flops, bytes)."""
     dense = exe = byt = 0.0
     for r, c in slices:
         s, l = float(min(r, c)), float(max(r, c))
+        byt += elem * s * l * (2 * len(coeffs) + 1)
         for a, b, cc in coeffs:
             dense += 4.0 * s * s * l
             exe += 3.0 * s * s * l
-            byt += elem * (3.0 * s * l + 2.0 * s * s)
             if cc != 0.0:
                 dense += 2.0 * s ** 3
                 exe += s ** 3
-                byt += elem * 2.0 * s * s
     return dense, exe, byt
+
+
+# slices whose padded short side is 128 run in the slice-resident kernel (bf16)
+SMALL_SIDE = 128
 
 
 def build_plan(w, coeffs, precision, normuon):
@@ -249,13 +254,19 @@ def main() -> int:
     # algorithmic work
     slices = [(r, c) for _, _, r, c in plan.slices()]
     elem = 2 if args.precision == "bf16" else 4
-    dense, exe, nbytes = ns_work(slices, coeffs, elem)
     muon_elems = sum(r * c for r, c in slices)
     adam_elems = sum(p.numel for p, r in zip(w.params, routes) if r[0] == L.MO_ALG_ADAMW)
-    g = kern.get("ns_gemm")
+    small = [sc for sc in slices if args.precision == "bf16" and min(sc) <= SMALL_SIDE]
+    large = [sc for sc in slices if not (args.precision == "bf16" and min(sc) <= SMALL_SIDE)]
     peak = BF16_PEAK_TFLOPS if args.precision == "bf16" else FP32_PEAK_TFLOPS
+    # the dominant Newton-Schulz kernel and the slices it processes
+    cands = [(name, part) for name, part in (("ns_gemm", large), ("ns_small", small))
+             if name in kern and part]
     roofline = None
-    if g:
+    if cands:
+        kname, part = max(cands, key=lambda x: kern[x[0]]["ms_per_step"])
+        g = kern[kname]
+        dense, exe, nbytes = ns_work(part, coeffs, elem)
         n = g["launches_per_step"]
         t = g["avg_launch_ms"] * 1e-3
         # the binding roof is the one with the longer ideal time
@@ -269,13 +280,13 @@ def main() -> int:
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
         roofline.update({
-            "traffic": None, "kernel": "k_ns_gemm", "avg_launch_ms": g["avg_launch_ms"],
-            "launches_per_step": n,
+            "traffic": None, "kernel": "k_" + kname, "avg_launch_ms": g["avg_launch_ms"],
+            "launches_per_step": n, "slices": len(part),
             "dense_flops_per_launch": dense / n, "dense_tflops": round(dense / n / t / 1e12, 2),
             "executed_tflops": round(exe / n / t / 1e12, 2),
             "algorithmic_bytes_per_launch": nbytes / n,
             "algorithmic_gbs": round(nbytes / n / t / 1e9, 1),
-            "symmetry_exploited": True})
+            "symmetry_exploited": kname == "ns_gemm"})
     hbm = {}
     elt = w.params[0].dtype == "bf16" and 2 or 4
     if "momentum" in kern:
@@ -311,7 +322,7 @@ def main() -> int:
         del src, dst
 
     if roofline is not None:
-        roofline["traffic"] = counted_traffic("k_ns_gemm", w.key)
+        roofline["traffic"] = counted_traffic(roofline["kernel"], w.key)
 
     cpu = None
     if args.cpu_budget > 0:

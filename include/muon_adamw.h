@@ -347,7 +347,7 @@ mo_status mo_plan_ns_output(const mo_plan* plan, int32_t slice, const void* ws, 
 typedef enum mo_kernel_class {
   MO_KC_MOMENTUM = 0, MO_KC_NS_STATS = 1, MO_KC_NS_SCALE = 2, MO_KC_NS_PREP = 3,
   MO_KC_NS_GEMM = 4, MO_KC_NS_FINAL = 5, MO_KC_ROWS = 6, MO_KC_ADAM_SUMSQ = 7,
-  MO_KC_ADAM_NORM = 8, MO_KC_ADAM_APPLY = 9, MO_KC_COUNT = 10
+  MO_KC_ADAM_NORM = 8, MO_KC_ADAM_APPLY = 9, MO_KC_NS_SMALL = 10, MO_KC_COUNT = 11
 } mo_kernel_class;
 
 mo_status mo_timing_enable(int32_t on);
