@@ -21,7 +21,8 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
 // buffers per matrix and the GEMM / prep problem tables (pool offsets only;
 // device pointers and statistics ranges are filled by the caller).  Matrices
 // are bucketed by GEMM tile size: short side >= kBigTileMinS -> 256 x 256
-// tiles, otherwise 128 x 128; each bucket has its own tables and launches.
+// tiles (when the batch has at least kBigTileMinWork such Gram tiles),
+// otherwise 128 x 128; each bucket has its own tables and launches.
 //
 // Per matrix (s = short side, l = long side, both padded to the tile): two
 // iterate buffers X0, X1 (s x l, short-side rows) used in turn, P (s x s) and,
@@ -32,6 +33,7 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
 // kernel instead (same iterate buffers and conventions, P kept in LDS).
 constexpr int kBigTile = 256;
 constexpr int kBigTileMinS = 512;
+constexpr int64_t kBigTileMinWork = 512;   // Gram tiles of the 256 bucket: 2 per CU
 
 struct NsBucket {
   int tile = kGemmTile;

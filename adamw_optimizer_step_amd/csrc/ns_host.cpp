@@ -1,6 +1,7 @@
 // Host side of the Newton-Schulz path: pool layout, problem tables and the
 // iteration driver.
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 
 #include "host.hpp"
@@ -20,6 +21,17 @@ GemmProb make_prob(int64_t a, int64_t b, int64_t c, int64_t ct, int64_t e, int32
   p.K = K; p.tiles_m = tm; p.tiles_n = tn; p.sym = sym;
   p.start = static_cast<int32_t>(start);
   return p;
+}
+
+// Threshold on the 256-bucket Gram tile count; the environment variable
+// MO_NS_BIG_TILE_MIN_WORK overrides it (0 = always use 256 x 256 tiles for
+// short sides >= kBigTileMinS), for tuning and for tests of that kernel.
+int64_t big_tile_min_work() {
+  const char* e = std::getenv("MO_NS_BIG_TILE_MIN_WORK");
+  if (!e || !*e) return kBigTileMinWork;
+  char* end = nullptr;
+  const long long v = std::strtoll(e, &end, 10);
+  return (end && *end == '\0' && v >= 0) ? static_cast<int64_t>(v) : kBigTileMinWork;
 }
 
 int64_t tiles_of(int32_t tm, int32_t tn, bool sym) {
@@ -50,11 +62,21 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
   L.buckets[1].tile = kBigTile;
   int64_t pool = 0;
   auto take = [&pool](int64_t elems) { int64_t at = pool; pool += elems; return at; };
+  // 256 x 256 tiles only when they give enough workgroups per launch to fill
+  // the chip; otherwise 128 x 128 tiles (4x as many) finish sooner
+  int64_t big_tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t s_ = std::min(rows[i], cols[i]), l_ = std::max(rows[i], cols[i]);
+    if (s_ < kBigTileMinS) continue;
+    const int64_t ts = ceil_div(s_, kBigTile), tl = ceil_div(l_, kBigTile);
+    big_tiles += std::min(ts * (ts + 1) / 2, ts * tl);
+  }
+  const bool use_big = big_tiles >= big_tile_min_work();
   for (int i = 0; i < n; ++i) {
     const int64_t r = rows[i], c = cols[i];
     const bool tall = r > c;
     const int64_t s_ = tall ? c : r, l_ = tall ? r : c;
-    NsBucket& B = L.buckets[s_ >= kBigTileMinS ? 1 : 0];
+    NsBucket& B = L.buckets[use_big && s_ >= kBigTileMinS ? 1 : 0];
     const int tile = B.tile;
     const int32_t sp = pad_to(s_, tile), lp = pad_to(l_, tile);
     const bool small = elem == 2 && tile == kGemmTile && sp == kSmallS;

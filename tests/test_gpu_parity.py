@@ -87,13 +87,34 @@ def test_ns_parity_ragged_shapes(precision, kind):
         assert_ns_close(f64(o), ref, precision)
 
 
+# bf16 slices whose short side is at most 128 run slice-resident: 1 to 8
+# column blocks of 128, both orientations (a tall slice's last iteration is
+# written transposed), and step counts around the pass structure
+NS_SMALL_SHAPES = [(100, 250), (250, 100), (128, 384), (384, 128), (96, 1000), (33, 600),
+                   (128, 128), (120, 520), (7, 129)]
+
+
+@pytest.mark.parametrize("kind", ["cubic", "quintic"])
+@pytest.mark.parametrize("steps", [1, 2, 7])
+def test_ns_small_slices_steps(kind, steps):
+    mats, dev = _ns_case(NS_SMALL_SHAPES, "bf16", 31)
+    coeffs = wl.coeff_table(kind, steps)
+    outs = api.ns_orthogonalize_batched(dev, coeffs=coeffs, precision="bf16")
+    for m, o in zip(mats, outs):
+        ref = omuon.newton_schulz(wl.from_storage(m, "bf16").astype(np.float64), coeffs)
+        assert_ns_close(f64(o), ref, "bf16")
+
+
 # short side >= 512 goes to the 256 x 256 tile bucket; mixed with small ones
 NS_BIG_SHAPES = [(520, 600), (1100, 530), (512, 512), (768, 2050), (40, 90), (300, 200)]
 
 
 @pytest.mark.parametrize("precision", ["bf16", "fp32"])
 @pytest.mark.parametrize("kind", ["cubic", "quintic"])
-def test_ns_parity_big_tiles(precision, kind):
+def test_ns_parity_big_tiles(precision, kind, monkeypatch):
+    # force the 256 x 256 kernels for these few tiles (by default they are
+    # used only when a launch has enough tiles to fill the chip)
+    monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0")
     dtype = "bf16" if precision == "bf16" else "f32"
     mats, dev = _ns_case(NS_BIG_SHAPES, dtype, 25)
     coeffs = wl.coeff_table(kind)
@@ -101,6 +122,24 @@ def test_ns_parity_big_tiles(precision, kind):
     for m, o in zip(mats, outs):
         ref = omuon.newton_schulz(wl.from_storage(m, dtype).astype(np.float64), coeffs)
         assert_ns_close(f64(o), ref, precision)
+
+
+def test_ns_tile_choice_agrees():
+    """The default tile choice (128 x 128 for so few tiles) and forced
+    256 x 256 tiles both meet the oracle bound."""
+    mats, dev = _ns_case([(600, 700), (520, 1030)], "bf16", 27)
+    coeffs = wl.coeff_table("cubic")
+    a = api.ns_orthogonalize_batched(dev, coeffs=coeffs)
+    import os
+    os.environ["MO_NS_BIG_TILE_MIN_WORK"] = "0"
+    try:
+        b = api.ns_orthogonalize_batched(dev, coeffs=coeffs)
+    finally:
+        del os.environ["MO_NS_BIG_TILE_MIN_WORK"]
+    for m, x, y in zip(mats, a, b):
+        ref = omuon.newton_schulz(wl.from_storage(m, "bf16").astype(np.float64), coeffs)
+        assert_ns_close(f64(x), ref, "bf16")
+        assert_ns_close(f64(y), ref, "bf16")
 
 
 def test_ns_strided_views_and_fp32_output():
