@@ -45,6 +45,10 @@ struct mo_plan {
   int device = -1;
   std::vector<char> htab;
   void* uploaded_ws = nullptr;
+  // AdamW runs on a side stream, forked from and joined back into the
+  // caller's stream, so that it overlaps the Muon path (created on first use)
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool dirty = true;
   int32_t tdelta = 0;
 };
@@ -249,6 +253,9 @@ mo_status mo_plan_create(const mo_param* params, int32_t n, const mo_hparams* hp
 void mo_plan_destroy(mo_plan* plan) {
   if (!plan) return;
   if (plan->dtab) (void)hipFree(plan->dtab);
+  if (plan->ev_fork) (void)hipEventDestroy(plan->ev_fork);
+  if (plan->ev_join) (void)hipEventDestroy(plan->ev_join);
+  if (plan->side) (void)hipStreamDestroy(plan->side);
   delete plan;
 }
 
@@ -343,11 +350,12 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     if ((s = upload_tables(P, base, st)) != MO_OK) return s;
   }
   const int nsl = static_cast<int>(P->active.size());
+  // Muon: momentum and the Newton-Schulz input (HBM-bound) first
+  const char* dns = P->dtab + P->tab_ns;
+  void* pool = base + P->ws_pool;
   if (nsl > 0) {
     StatPartial* stats = reinterpret_cast<StatPartial*>(base + P->ws_stats);
     float* scale = reinterpret_cast<float*>(base + P->ws_scale);
-    void* pool = base + P->ws_pool;
-    const char* dns = P->dtab + P->tab_ns;
     const PrepItem* dprep = reinterpret_cast<const PrepItem*>(dns + P->nst.prep);
     if ((s = launch_momentum(reinterpret_cast<const MomSeg*>(P->dtab + P->tab_mom), nsl,
                              P->mom_blocks, hp.mu, hp.nesterov, stats, st)) != MO_OK)
@@ -355,6 +363,42 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     if ((s = launch_ns_scale(dprep, nsl, stats, scale, st)) != MO_OK) return s;
     if ((s = launch_ns_prep(dprep, nsl, P->ns.prep_tiles, scale, pool, P->ns.elem, st)) != MO_OK)
       return s;
+  }
+  // AdamW (clip norm and update) is independent of the Muon path: with both
+  // present it goes to a side stream forked here, so that it overlaps the
+  // MFMA-bound Newton-Schulz iterations rather than the HBM-bound kernels.
+  hipStream_t ast = st;
+  const bool fork = nsl > 0 && P->n_adam > 0;
+  if (fork) {
+    if (!P->side) {
+      MO_HIP_TRY(hipStreamCreateWithFlags(&P->side, hipStreamNonBlocking));
+      MO_HIP_TRY(hipEventCreateWithFlags(&P->ev_fork, hipEventDisableTiming));
+      MO_HIP_TRY(hipEventCreateWithFlags(&P->ev_join, hipEventDisableTiming));
+    }
+    MO_HIP_TRY(hipEventRecord(P->ev_fork, st));
+    MO_HIP_TRY(hipStreamWaitEvent(P->side, P->ev_fork, 0));
+    ast = P->side;
+  }
+  if (P->n_adam > 0) {
+    const AdamSeg* dad = reinterpret_cast<const AdamSeg*>(P->dtab + P->tab_adam);
+    double* partials = reinterpret_cast<double*>(base + P->ws_adam_partials);
+    double* scal = reinterpret_cast<double*>(base + P->ws_adam_scal);
+    if ((s = launch_adam_sumsq(dad, P->n_adam, P->adam_blocks, partials, ast)) != MO_OK) return s;
+    if ((s = launch_adam_norm(partials, P->adam_blocks, hp.max_norm, scal,
+                              args ? args->norm_out : nullptr, ast)) != MO_OK)
+      return s;
+    if ((s = launch_adam_apply(dad, P->n_adam, P->adam_blocks, scal, adamw_lr, hp.beta1,
+                               hp.beta2, hp.eps, P->tdelta, ast)) != MO_OK)
+      return s;
+  } else if (args && args->norm_out) {
+    // no AdamW gradient: report T = 0 (a kernel write, not a memset node)
+    if ((s = launch_adam_norm(nullptr, 0, hp.max_norm,
+                              reinterpret_cast<double*>(base + P->ws_adam_scal), args->norm_out,
+                              st)) != MO_OK)
+      return s;
+  }
+  if (fork) MO_HIP_TRY(hipEventRecord(P->ev_join, ast));
+  if (nsl > 0) {
     float coeffs[3 * MO_NS_MAX_STEPS];
     for (int k = 0; k < hp.ns_steps; ++k)
       for (int j = 0; j < 3; ++j) coeffs[3 * k + j] = hp.ns_coeffs[k][j];
@@ -367,24 +411,7 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
                          P->total_rows, muon_lr, hp.normuon_beta2, hp.normuon_eps, st)) != MO_OK)
       return s;
   }
-  if (P->n_adam > 0) {
-    const AdamSeg* dad = reinterpret_cast<const AdamSeg*>(P->dtab + P->tab_adam);
-    double* partials = reinterpret_cast<double*>(base + P->ws_adam_partials);
-    double* scal = reinterpret_cast<double*>(base + P->ws_adam_scal);
-    if ((s = launch_adam_sumsq(dad, P->n_adam, P->adam_blocks, partials, st)) != MO_OK) return s;
-    if ((s = launch_adam_norm(partials, P->adam_blocks, hp.max_norm, scal,
-                              args ? args->norm_out : nullptr, st)) != MO_OK)
-      return s;
-    if ((s = launch_adam_apply(dad, P->n_adam, P->adam_blocks, scal, adamw_lr, hp.beta1,
-                               hp.beta2, hp.eps, P->tdelta, st)) != MO_OK)
-      return s;
-  } else if (args && args->norm_out) {
-    // no AdamW gradient: report T = 0 (a kernel write, not a memset node)
-    if ((s = launch_adam_norm(nullptr, 0, hp.max_norm,
-                              reinterpret_cast<double*>(base + P->ws_adam_scal), args->norm_out,
-                              st)) != MO_OK)
-      return s;
-  }
+  if (fork) MO_HIP_TRY(hipStreamWaitEvent(st, P->ev_join, 0));
   for (size_t i = 0; i < P->params.size(); ++i)
     if (P->routes[i].algorithm == MO_ALG_ADAMW && P->params[i].grad) ++P->steps[i];
   ++P->tdelta;
