@@ -159,6 +159,10 @@ __device__ __forceinline__ void decode_tile(int t, int tm, int tn, int sym, int&
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n) (6 bits: [3:0] and [15:14]),
+// lgkmcnt(0), expcnt not waited on.
+constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
+
 // Buffer resource (raw, stride 0) over `bytes` bytes from `base`; accesses
 // past the range read zero instead of faulting.
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
@@ -397,7 +401,7 @@ struct GemmCfg {
   static_assert(kInstB * kWaves * 1024 == kBStageBytes, "B slab split");
   static_assert(!BK || (kBkRowsPerInst >= 1 && kBkRowsPerInst * kBkRowBytes == 1024),
                 "K-major B rows per instruction");
-  static_assert(kInst <= 7, "vector-memory wait counts below assume at most 7 loads per slab");
+  static_assert(kInst <= 31, "vector-memory wait counts below assume at most 31 loads per slab");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
 };
 
@@ -593,13 +597,13 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   // counter, kInst per slab, completing in order) and its LDS reads are done
   // (the stage they read is refilled after the next barrier).
   auto wait_slab = [](int younger) __attribute__((always_inline)) {
-    static_assert(2 * C::kInst <= 15, "vmcnt immediate");
+    static_assert(2 * C::kInst <= 63, "vmcnt immediate");
     if (younger >= 2)
-      __builtin_amdgcn_s_waitcnt(0x0070 | (2 * C::kInst));
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * C::kInst));
     else if (younger == 1)
-      __builtin_amdgcn_s_waitcnt(0x0070 | C::kInst);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(C::kInst));
     else
-      __builtin_amdgcn_s_waitcnt(0x0070);
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
   };
   // Software pipeline over K slabs (kSub = 2 substeps of 16 k), two fragment
   // register sets, kStages = 4 LDS stages with the loads of 3 slabs in flight.
@@ -800,22 +804,15 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       lds_dma16(from1 ? rs1 : rs0, st + (wv * 4 + q) * 1024, vo[q], b * 256);
   };
 
-  // Operand reads.  NT fragment (A of every product, B of the Grams): row
-  // m, logical chunk 2 ks + fg.  K-major fragment (B of the update): two
-  // transpose reads, lane j of 16-lane group g at row 16 ks + 8 (g / 2) + 4 h
-  // + j / 4, columns wn * 32 + 16 (g % 2) + 4 (j % 4).
+  // Operand reads.  NT fragment: row m, logical chunk 2 ks + fg (both
+  // operands of the Grams, P in the update).  K-major fragment (X_b^T in the
+  // update): two transpose reads, lane j of 16-lane group g at row
+  // 16 ks + 8 (g / 2) + 4 h + j / 4, columns c + 16 (g % 2) + 4 (j % 4).
   auto nt_frag = [&](const char* t, int m, int ks) __attribute__((always_inline)) {
     return *reinterpret_cast<const u32x4*>(t + m * 256 +
                                            ((((2 * ks + fg) ^ sm_swz(m)) & 15) << 4));
   };
-  const int trow = 8 * (g16 >> 1) + (j16 >> 2), tcol = wn * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
-  // rows of an accumulator group: 4 fg + e (lane j of group g at row 4 (g / 2) + j / 4)
-  const int etrow = 4 * (g16 >> 1) + (j16 >> 2);
-  auto kmaj_frag = [&](const char* t, int ks) __attribute__((always_inline)) {
-    const u32x2 lo = lds_read_tr16(t + sm_off(16 * ks + trow, tcol));
-    const u32x2 hi = lds_read_tr16(t + sm_off(16 * ks + trow + 4, tcol));
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-  };
+  const int trow = 8 * (g16 >> 1) + (j16 >> 2);
   // C[m][n] += sum_k A[m][k] B[n][k] over a 128-wide K, both operands NT
   auto gram_acc = [&](const char* ta, const char* tb, f32x16 (&acc)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -872,11 +869,11 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       const int first_store = a > NB ? a : NB;
       const int young = 4 * (next - 1 - cur) + 4 * (cur > first_store ? cur - first_store : 0);
       switch (young >> 2) {
-        case 0: __builtin_amdgcn_s_waitcnt(0x0070); break;
-        case 1: __builtin_amdgcn_s_waitcnt(0x0070 | 4); break;
-        case 2: __builtin_amdgcn_s_waitcnt(0x0070 | 8); break;
-        case 3: __builtin_amdgcn_s_waitcnt(0x0070 | 12); break;
-        default: __builtin_amdgcn_s_waitcnt(0x0070 | 16); break;
+        case 0: __builtin_amdgcn_s_waitcnt(vm_wait_imm(0)); break;
+        case 1: __builtin_amdgcn_s_waitcnt(vm_wait_imm(4)); break;
+        case 2: __builtin_amdgcn_s_waitcnt(vm_wait_imm(8)); break;
+        case 3: __builtin_amdgcn_s_waitcnt(vm_wait_imm(12)); break;
+        default: __builtin_amdgcn_s_waitcnt(vm_wait_imm(16)); break;
       }
       done = a - 1;
     }
@@ -893,29 +890,42 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
     if (pass == 0) {
       gram_acc(stg, stg, accg);
     } else {
-      // update: X'_b = a X_b + P X_b
+      // update, computed transposed: (P X_b)^T = X_b^T P (P is symmetric), so
+      // that each lane's accumulator holds 4 consecutive columns of one row of
+      // X'_b.  A operand X_b^T: rows = block columns, read K-major (transpose
+      // reads); B operand P: rows read as stored.
       zero(accu);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 bf = kmaj_frag(stg, ks);
+        const u32x4 bp = nt_frag(Ps, wn * 32 + fr, ks);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
-          mma<uint16_t>(nt_frag(Ps, wm * 64 + mi * 32 + fr, ks), bf, accu[mi]);
+        for (int mi = 0; mi < 2; ++mi) {
+          const int c0 = wm * 64 + mi * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
+          const u32x2 lo = lds_read_tr16(stg + sm_off(16 * ks + trow, c0));
+          const u32x2 hi = lds_read_tr16(stg + sm_off(16 * ks + trow + 4, c0));
+          mma<uint16_t>(u32x4{lo[0], lo[1], hi[0], hi[1]}, bp, accu[mi]);
+        }
       }
+      // accu[mi][4 q + e] = X'_b[i][j0 + e], i = wn * 32 + fr,
+      // j0 = wm * 64 + mi * 32 + 8 q + 4 fg: 8-byte E reads and X'_b writes
       const float ak = cf.a[pass - 1];
+      const int xi = wn * 32 + fr;
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          // E: rows 8 q + 4 fg + e of column acc_col, via one transpose read
-          const u32x2 e2 = lds_read_tr16(stg + sm_off(wm * 64 + mi * 32 + 8 * q + etrow, tcol));
+          const int off = sm_off(xi, wm * 64 + mi * 32 + 8 * q + 4 * fg);
+          const u32x2 e2 = *reinterpret_cast<const u32x2*>(stg + off);
+          float x[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t bits = (e & 1) ? (e2[e >> 1] & 0xffff0000u) : (e2[e >> 1] << 16);
-            const float x = ak * __uint_as_float(bits) + accu[mi][4 * q + e];
-            *reinterpret_cast<uint16_t*>(Xn + sm_off(acc_row(mi, 4 * q + e), acc_col)) =
-                f32_to_bf16(x);
+            x[e] = ak * __uint_as_float(bits) + accu[mi][4 * q + e];
           }
+          u32x2 o;
+          o[0] = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
+          o[1] = f32_to_bf16(x[2]) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+          *reinterpret_cast<u32x2*>(Xn + off) = o;
         }
       __syncthreads();   // B2: X'_b complete in LDS
       const bool last = pass == steps;
