@@ -1,14 +1,55 @@
 // Memory-bound kernels: Muon momentum, AdamW with the global-norm clip, and
 // the row kernels (NorMuon row normalisation, scaled Muon update).
 //
-// All are HBM-bound streaming passes: 8 elements (16-byte bf16 / 2 x 16-byte
-// fp32 vectors) per thread per iteration, 8192 elements per 256-thread block,
+// All are HBM-bound streaming passes over 2048 elements per 256-thread block,
 // one launch over every tensor of a call (segment table + binary search).
+// Momentum and AdamW give each thread two groups of 4 consecutive elements,
+// 1024 apart, so that each access instruction of a wave covers one contiguous
+// span (1 KiB of fp32, 512 bytes of bf16) and whole cache lines of every array.
 #include "kernels.hpp"
 
 namespace mo {
 
 namespace {
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+// 4 consecutive elements <-> 4 floats: one 16-byte fp32 or 8-byte bf16
+// access.  `i` is a multiple of 4 and the base pointer 16-byte aligned.
+template <bool NT>
+__device__ __forceinline__ void load4(const void* p, int64_t i, int32_t dt, float* v) {
+  if (dt == MO_F32) {
+    const f32x4_t a = ldv<f32x4_t, NT>(reinterpret_cast<const f32x4_t*>(static_cast<const float*>(p) + i));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = a[k];
+  } else {
+    const u32x2_t u =
+        ldv<u32x2_t, NT>(reinterpret_cast<const u32x2_t*>(static_cast<const uint16_t*>(p) + i));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      v[2 * k] = __uint_as_float(u[k] << 16);
+      v[2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+    }
+  }
+}
+
+template <bool NT>
+__device__ __forceinline__ void store4(void* p, int64_t i, int32_t dt, const float* v) {
+  if (dt == MO_F32) {
+    stv<f32x4_t, NT>(reinterpret_cast<f32x4_t*>(static_cast<float*>(p) + i),
+                     f32x4_t{v[0], v[1], v[2], v[3]});
+  } else {
+    u32x2_t u;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      u[k] = f32_to_bf16(v[2 * k]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * k + 1])) << 16);
+    stv<u32x2_t, NT>(reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p) + i), u);
+  }
+}
+
+// Groups of 4 per thread in a block, and the distance between a thread's groups.
+constexpr int kGroups = kEltPerBlock / (kThreads * 4);
+constexpr int kGroupStride = kThreads * 4;
 
 // (1 - beta^t) by binary exponentiation in fp64 (t >= 1).
 __device__ double one_minus_pow(double beta, int t) {
@@ -34,31 +75,30 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
   const int64_t base = (blk - sg.start) * kEltPerBlock;
   float amax = 0.f;
   double ss = 0.0;
-#pragma unroll 1
-  for (int it = 0; it < kEltIters; ++it) {
-    const int64_t e0 = base + static_cast<int64_t>(it) * kThreads * kEltPerThread +
-                       threadIdx.x * kEltPerThread;
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const int64_t e0 = base + q * kGroupStride + threadIdx.x * 4;
     if (e0 >= sg.numel) break;
-    float g[8], b[8], d[8];
-    const int cnt = sg.numel - e0 >= 8 ? 8 : static_cast<int>(sg.numel - e0);
-    const bool vec = cnt == 8 && sg.vec;
+    float g[4], b[4], d[4];
+    const int cnt = sg.numel - e0 >= 4 ? 4 : static_cast<int>(sg.numel - e0);
+    const bool vec = cnt == 4 && sg.vec;
     if (vec) {
-      load8<true>(sg.g, e0, sg.gdt, g);
-      load8<true>(sg.b, e0, MO_F32, b);
+      load4<true>(sg.g, e0, sg.gdt, g);
+      load4<true>(sg.b, e0, MO_F32, b);
     } else {
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 4; ++k) {
         g[k] = k < cnt ? load_as_f32(sg.g, e0 + k, sg.gdt) : 0.f;
         b[k] = k < cnt ? sg.b[e0 + k] : 0.f;
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       b[k] = mu * b[k] + g[k];
       d[k] = nesterov ? g[k] + mu * b[k] : b[k];
     }
     if (vec) {
-      store8<true>(sg.b, e0, MO_F32, b);
-      if (sg.d) store8<true>(sg.d, e0, sg.ddt, d);
+      store4<true>(sg.b, e0, MO_F32, b);
+      if (sg.d) store4<true>(sg.d, e0, sg.ddt, d);
     } else {
       for (int k = 0; k < cnt; ++k) {
         sg.b[e0 + k] = b[k];
@@ -67,7 +107,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
     }
     if (kStats) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 4; ++k) {
         // statistics of the value as stored
         const float dv = sg.ddt == MO_BF16 ? bf16_to_f32(f32_to_bf16(d[k])) : d[k];
         const float a = k < cnt ? fabsf(dv) : 0.f;
@@ -88,20 +128,19 @@ __global__ __launch_bounds__(kThreads) void k_adam_sumsq(const AdamSeg* __restri
   const AdamSeg sg = segs[find_segment(segs, nseg, blk)];
   const int64_t base = (blk - sg.start) * kEltPerBlock;
   double ss = 0.0;
-#pragma unroll 1
-  for (int it = 0; it < kEltIters; ++it) {
-    const int64_t e0 = base + static_cast<int64_t>(it) * kThreads * kEltPerThread +
-                       threadIdx.x * kEltPerThread;
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const int64_t e0 = base + q * kGroupStride + threadIdx.x * 4;
     if (e0 >= sg.numel) break;
-    float g[8];
-    const int cnt = sg.numel - e0 >= 8 ? 8 : static_cast<int>(sg.numel - e0);
-    if (cnt == 8) {
-      load8(sg.g, e0, sg.dt, g);
+    float g[4];
+    const int cnt = sg.numel - e0 >= 4 ? 4 : static_cast<int>(sg.numel - e0);
+    if (cnt == 4) {
+      load4<false>(sg.g, e0, sg.dt, g);
     } else {
-      for (int k = 0; k < 8; ++k) g[k] = k < cnt ? load_as_f32(sg.g, e0 + k, sg.dt) : 0.f;
+      for (int k = 0; k < 4; ++k) g[k] = k < cnt ? load_as_f32(sg.g, e0 + k, sg.dt) : 0.f;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ss += static_cast<double>(g[k]) * g[k];
+    for (int k = 0; k < 4; ++k) ss += static_cast<double>(g[k]) * g[k];
   }
   __shared__ double s_ss[4];
   ss = wave_sum(ss);
@@ -150,20 +189,19 @@ __global__ __launch_bounds__(kThreads) void k_adam_apply(const AdamSeg* __restri
   const float ibc2 = static_cast<float>(1.0 / sqrt(bc2));
   const float decay = 1.f - lr * sg.wd;
   const float omb1 = 1.f - beta1, omb2 = 1.f - beta2;
-#pragma unroll 1
-  for (int it = 0; it < kEltIters; ++it) {
-    const int64_t e0 = base + static_cast<int64_t>(it) * kThreads * kEltPerThread +
-                       threadIdx.x * kEltPerThread;
+#pragma unroll
+  for (int q = 0; q < kGroups; ++q) {
+    const int64_t e0 = base + q * kGroupStride + threadIdx.x * 4;
     if (e0 >= sg.numel) break;
-    float g[8], w[8], m[8], v[8];
-    const int cnt = sg.numel - e0 >= 8 ? 8 : static_cast<int>(sg.numel - e0);
-    if (cnt == 8) {
-      load8<true>(sg.g, e0, sg.dt, g);
-      load8<true>(sg.p, e0, sg.dt, w);
-      load8<true>(sg.m, e0, MO_F32, m);
-      load8<true>(sg.v, e0, MO_F32, v);
+    float g[4], w[4], m[4], v[4];
+    const int cnt = sg.numel - e0 >= 4 ? 4 : static_cast<int>(sg.numel - e0);
+    if (cnt == 4) {
+      load4<true>(sg.g, e0, sg.dt, g);
+      load4<true>(sg.p, e0, sg.dt, w);
+      load4<true>(sg.m, e0, MO_F32, m);
+      load4<true>(sg.v, e0, MO_F32, v);
     } else {
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < 4; ++k) {
         const bool in = k < cnt;
         g[k] = in ? load_as_f32(sg.g, e0 + k, sg.dt) : 0.f;
         w[k] = in ? load_as_f32(sg.p, e0 + k, sg.dt) : 0.f;
@@ -172,17 +210,17 @@ __global__ __launch_bounds__(kThreads) void k_adam_apply(const AdamSeg* __restri
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    for (int k = 0; k < 4; ++k) {
       const float gk = kappa * g[k];
       m[k] = beta1 * m[k] + omb1 * gk;
       v[k] = beta2 * v[k] + omb2 * gk * gk;
       const float denom = sqrtf(v[k]) * ibc2 + eps;
       w[k] = w[k] * decay - step * (m[k] / denom);
     }
-    if (cnt == 8) {
-      store8<true>(sg.p, e0, sg.dt, w);
-      store8<true>(sg.m, e0, MO_F32, m);
-      store8<true>(sg.v, e0, MO_F32, v);
+    if (cnt == 4) {
+      store4<true>(sg.p, e0, sg.dt, w);
+      store4<true>(sg.m, e0, MO_F32, m);
+      store4<true>(sg.v, e0, MO_F32, v);
     } else {
       for (int k = 0; k < cnt; ++k) {
         store_from_f32(sg.p, e0 + k, sg.dt, w[k]);

@@ -81,4 +81,7 @@ mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st)
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* coeffs, int steps, hipStream_t st);
 
+// True while kernel timing (mo_timing_enable) is on.
+bool timing_enabled();
+
 }  // namespace mo

@@ -367,8 +367,10 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
   // AdamW (clip norm and update) is independent of the Muon path: with both
   // present it goes to a side stream forked here, so that it overlaps the
   // MFMA-bound Newton-Schulz iterations rather than the HBM-bound kernels.
+  // While kernel timing is enabled everything stays on `st`, in order, so that
+  // each bracketed duration belongs to one kernel running alone.
   hipStream_t ast = st;
-  const bool fork = nsl > 0 && P->n_adam > 0;
+  const bool fork = nsl > 0 && P->n_adam > 0 && !timing_enabled();
   if (fork) {
     if (!P->side) {
       MO_HIP_TRY(hipStreamCreateWithFlags(&P->side, hipStreamNonBlocking));

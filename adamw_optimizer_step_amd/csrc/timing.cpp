@@ -47,6 +47,11 @@ KTimer::~KTimer() {
   g_recs.push_back({cls_, a_, b_});
 }
 
+bool timing_enabled() {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_on;
+}
+
 }  // namespace mo
 
 extern "C" {

@@ -10,7 +10,8 @@ update for every Muon matrix; clip + AdamW for every AdamW parameter) through
 
 Prints one JSON line (rank 0, N=1) with the steps/s, a roofline entry for the
 dominant kernel (the batched Newton-Schulz GEMM, from HIP events on its own
-stream), and the fp64 oracle timed on a bounded sample on the host cores.
+stream, in extra steps that run every kernel alone), and the fp64 oracle
+timed on a bounded sample on the host cores.
 """
 
 from __future__ import annotations
@@ -234,7 +235,9 @@ def main() -> int:
     ms_per_step = 1e3 * elapsed / args.steps
     log(f"{ms_per_step:.3f} ms/step")
 
-    # per-kernel-class durations with HIP events on the launch stream
+    # per-kernel-class durations with HIP events on the launch stream; while
+    # timing is on, the grouped step runs every kernel in order on one stream
+    # (no AdamW overlap), so each duration is one kernel running alone
     lib = L.lib()
     L.check("timing", lib.mo_timing_enable(1))
     for _ in range(args.timing_steps):

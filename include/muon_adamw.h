@@ -342,7 +342,10 @@ mo_status mo_plan_ns_output(const mo_plan* plan, int32_t slice, const void* ws, 
  * library is bracketed by two HIP events recorded on the launch's own
  * stream.  mo_timing_read waits for the recorded events of one kernel class
  * and returns their summed duration (ms) and launch count.  Enabling (on=1)
- * or disabling (on=0) clears earlier records.  Host thread safe.
+ * or disabling (on=0) clears earlier records.  While enabled, the grouped
+ * step also keeps its AdamW kernels on the caller's stream instead of the
+ * overlapping side stream, so that each duration is one kernel's alone.
+ * Host thread safe.
  * ------------------------------------------------------------------------ */
 typedef enum mo_kernel_class {
   MO_KC_MOMENTUM = 0, MO_KC_NS_STATS = 1, MO_KC_NS_SCALE = 2, MO_KC_NS_PREP = 3,

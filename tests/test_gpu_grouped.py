@@ -185,3 +185,21 @@ def bf16_extra(x):
     # two AdamW steps each rounded to bf16: allow one more ulp of drift
     from gpu_common import bf16_ulp
     return bf16_ulp(x)
+
+
+def test_overlapped_step_equals_serial():
+    """AdamW on the side stream (the default) and every kernel in order on one
+    stream (what the step does while kernel timing is on) read and write
+    disjoint buffers in the same kernels: the results are bit-identical."""
+    _, over, _, _ = _run_small(False, False)
+    lib = L.lib()
+    L.check("timing", lib.mo_timing_enable(1))
+    try:
+        _, serial, _, _ = _run_small(False, False)
+        torch.cuda.synchronize()
+    finally:
+        L.check("timing", lib.mo_timing_enable(0))
+    for a, b in zip(over, serial):
+        for k in ("param", "momentum", "exp_avg", "exp_avg_sq"):
+            if k in a:
+                assert torch.equal(a[k], b[k]), (a["desc"].name, k)
