@@ -122,31 +122,46 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
 // ---------------------------------------------------------------------------
 // AdamW (OMN page, recipe paragraph; Qwen3.8 optimizer notes, Adam/AdamW).
 // ---------------------------------------------------------------------------
+// Sum of squares of the gradients: each block covers kSumsqSub blocks of the
+// apply kernel's partition (all loads issued before the reduction) and writes
+// one partial.
+constexpr int kSumsqSub = 4;
+__host__ __device__ constexpr int64_t sumsq_partials(int64_t nblocks) {
+  return (nblocks + kSumsqSub - 1) / kSumsqSub;
+}
+
 __global__ __launch_bounds__(kThreads) void k_adam_sumsq(const AdamSeg* __restrict__ segs, int nseg,
+                                                         int64_t nblocks,
                                                          double* __restrict__ partials) {
-  const int64_t blk = blockIdx.x;
-  const AdamSeg sg = segs[find_segment(segs, nseg, blk)];
-  const int64_t base = (blk - sg.start) * kEltPerBlock;
+  float g[kSumsqSub][kGroups][4];
+#pragma unroll
+  for (int j = 0; j < kSumsqSub; ++j) {
+    const int64_t ab = static_cast<int64_t>(blockIdx.x) * kSumsqSub + j;
+    const AdamSeg* sp = ab < nblocks ? &segs[find_segment(segs, nseg, ab)] : nullptr;
+#pragma unroll
+    for (int q = 0; q < kGroups; ++q) {
+      const int64_t e0 =
+          sp ? (ab - sp->start) * kEltPerBlock + q * kGroupStride + threadIdx.x * 4 : 0;
+      const int64_t left = sp ? sp->numel - e0 : 0;
+      if (left >= 4) {
+        load4<false>(sp->g, e0, sp->dt, g[j][q]);
+      } else {
+        for (int k = 0; k < 4; ++k) g[j][q][k] = k < left ? load_as_f32(sp->g, e0 + k, sp->dt) : 0.f;
+      }
+    }
+  }
   double ss = 0.0;
 #pragma unroll
-  for (int q = 0; q < kGroups; ++q) {
-    const int64_t e0 = base + q * kGroupStride + threadIdx.x * 4;
-    if (e0 >= sg.numel) break;
-    float g[4];
-    const int cnt = sg.numel - e0 >= 4 ? 4 : static_cast<int>(sg.numel - e0);
-    if (cnt == 4) {
-      load4<false>(sg.g, e0, sg.dt, g);
-    } else {
-      for (int k = 0; k < 4; ++k) g[k] = k < cnt ? load_as_f32(sg.g, e0 + k, sg.dt) : 0.f;
-    }
+  for (int j = 0; j < kSumsqSub; ++j)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) ss += static_cast<double>(g[k]) * g[k];
-  }
+    for (int q = 0; q < kGroups; ++q)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ss += static_cast<double>(g[j][q][k]) * g[j][q][k];
   __shared__ double s_ss[4];
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = ss;
   __syncthreads();
-  if (threadIdx.x == 0) partials[blk] = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
+  if (threadIdx.x == 0) partials[blockIdx.x] = (s_ss[0] + s_ss[1]) + (s_ss[2] + s_ss[3]);
 }
 
 constexpr int kNormThreads = 1024;
@@ -335,8 +350,8 @@ mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, doub
                             hipStream_t st) {
   if (nblocks <= 0) return MO_OK;
   KTimer tm(MO_KC_ADAM_SUMSQ, st);
-  k_adam_sumsq<<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(segs, nseg,
-                                                                               partials);
+  k_adam_sumsq<<<dim3(static_cast<unsigned>(sumsq_partials(nblocks))), dim3(kThreads), 0, st>>>(
+      segs, nseg, nblocks, partials);
   MO_LAUNCH_CHECK("k_adam_sumsq");
   return MO_OK;
 }
@@ -344,7 +359,8 @@ mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, doub
 mo_status launch_adam_norm(const double* partials, int64_t nblocks, float max_norm, double* scal,
                            double* norm_out, hipStream_t st) {
   KTimer tm(MO_KC_ADAM_NORM, st);
-  k_adam_norm<<<dim3(1), dim3(kNormThreads), 0, st>>>(partials, nblocks, max_norm, scal, norm_out);
+  k_adam_norm<<<dim3(1), dim3(kNormThreads), 0, st>>>(partials, sumsq_partials(nblocks), max_norm,
+                                                       scal, norm_out);
   MO_LAUNCH_CHECK("k_adam_norm");
   return MO_OK;
 }
