@@ -165,9 +165,12 @@ constexpr int kSmallS = 128;
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const float* coeffs,
                           int steps, hipStream_t st);
 
-// bk = 1: B is read K-major (K x N row-major) through LDS transpose reads.
+// C = c1 A B (+ c0 E) (+ cd I on diagonal tiles).  bk = 1: B is read K-major
+// (K x N row-major) through LDS transpose reads; no E term, and the output
+// goes straight from registers to c (or, transposed, to ct).
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
-                         void* pool, int elem, float c0, float c1, int has_e, hipStream_t st);
+                         void* pool, int elem, float c0, float c1, int has_e, float cd,
+                         hipStream_t st);
 mo_status launch_ns_final(const FinalItem* items, int n, int64_t total_rows, const void* pool,
                           int elem, hipStream_t st);
 

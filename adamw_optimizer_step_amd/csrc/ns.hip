@@ -3,15 +3,20 @@
 // Per independent matrix (slice) the iteration X <- a X + (b A + c A^2) X,
 // A = X X^T, runs on the short side (NorMuon paper section 2.2 eq. (5); OMN
 // "Dual-Manifold Optimization", Muon-path paragraphs).  Every slice lives in a
-// zero-padded pool in two layouts: X (s x l) and X^T (l x s), padded to
-// multiples of 128, so that all three products are "NT" GEMMs with the
-// contraction index contiguous in memory for both operands:
-//   Gram    A[i][j]  = sum_k X[i][k]  X[j][k]        (symmetric: tiles i <= j)
-//   Square  P[i][j]  = b A[i][j] + c sum_k A[i][k] A[j][k]   (A symmetric)
-//   Update  X'[i][n] = a X[i][n] + sum_k P[i][k] Xt[n][k]
-// The update writes X' in place and its transpose into the other X^T buffer.
-// Zero padding stays zero through every product, so no bounds checks are
-// needed inside the GEMM.
+// zero-padded pool as X (s x l, padded to the GEMM tile), with two iterate
+// buffers used in turn.  The batched GEMM path runs per iteration:
+//   Gram    P[i][j] = a [i == j] + b sum_k X[i][k] X[j][k]   (symmetric: tiles
+//           i <= j, the lower triangle written as the mirror)
+//   or      A = X X^T, then P = a I + b A + c A A (A symmetric: its own
+//           transposed operand and its own E term)
+//   Update  X'[i][n] = sum_k P[i][k] X[k][n], X read K-major through LDS
+//           transpose reads; a X is folded into P's diagonal, so the update is
+//           a plain product stored straight from registers.
+// Zero padding stays zero through every product (a zero row of X gives a
+// zero row of X X^T and of P X; a on a padded diagonal entry meets a zero row
+// of X), so no bounds checks are needed inside the GEMM.  Head-sized slices
+// (short side at most 128, bf16) run all iterations in one slice-resident
+// kernel instead.
 #include <type_traits>
 
 #include <cstring>
@@ -237,6 +242,25 @@ __device__ __forceinline__ void ld8<float>(const float* p, float* v) {
   for (int k = 0; k < 4; ++k) { v[k] = a[k]; v[4 + k] = b[k]; }
 }
 
+// 4 values to 4 consecutive elements (8 bytes of bf16, 16 of fp32).
+template <typename T, bool NT = false>
+__device__ __forceinline__ void st4(T* p, float v0, float v1, float v2, float v3) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x2 u{f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16),
+                  f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16)};
+    if constexpr (NT)
+      __builtin_nontemporal_store(u, reinterpret_cast<u32x2*>(p));
+    else
+      *reinterpret_cast<u32x2*>(p) = u;
+  } else {
+    const f32x4 a{v0, v1, v2, v3};
+    if constexpr (NT)
+      __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p));
+    else
+      *reinterpret_cast<f32x4*>(p) = a;
+  }
+}
+
 // 8 values to 8 consecutive elements; NT = non-temporal (streaming) stores,
 // for outputs that the same launch does not read again.
 template <typename T, bool NT = false>
@@ -422,7 +446,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK>
 __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1,
-    int has_e) {
+    int has_e, float cd) {
   using C = GemmCfg<T, BM, BN, WM, WN, BK>;
   constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
@@ -585,12 +609,25 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
       }
     }
   };
-  auto mfma_block = [&](auto setc) __attribute__((always_inline)) {
+  // The update (K-major B) writes C = A B row-major from registers: with the
+  // operands swapped (SW), the MFMA produces C^T tiles, whose lane layout
+  // holds 4 consecutive columns of one row of C.  A problem with a transposed
+  // output (ct_off) keeps the plain order, whose lanes hold 4 consecutive rows
+  // of one column of C, i.e. 4 consecutive elements of a row of C^T.  The
+  // order is a compile-time choice: the main loop exists once per order.
+  auto mfma_block = [&](auto setc, auto swc) __attribute__((always_inline)) {
     constexpr int set = decltype(setc)::value;
+    if constexpr (decltype(swc)::value) {
 #pragma unroll
-    for (int mi = 0; mi < FM; ++mi)
+      for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < FN; ++ni) mma<T>(av[set][mi], bv[set][ni], acc[mi][ni]);
+        for (int ni = 0; ni < FN; ++ni) mma<T>(bv[set][ni], av[set][mi], acc[mi][ni]);
+    } else {
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni) mma<T>(av[set][mi], bv[set][ni], acc[mi][ni]);
+    }
   };
   // Wait until this wave's loads of all but the `younger` most recent slabs
   // have landed (the direct-to-LDS loads are counted by the vector memory
@@ -615,26 +652,104 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   //   read frags ks0 of slab kt+1 | MFMAs ks1
   static_assert(C::kSub == 2, "pipeline below is written for two substeps per slab");
   const int KT = pr.K / C::kSlabK;
-  const int pre = KT < C::kStages - 1 ? KT : C::kStages - 1;
-  for (int k = 0; k < pre; ++k) issue(k, k);
-  wait_slab(pre - 1);
-  __syncthreads();
-  fload(0, 0, Int<0>{});
-  for (int kt = 0; kt < KT; ++kt) {
-    const int stage = kt & (C::kStages - 1);
-    if (kt + C::kStages - 1 < KT) issue(kt + C::kStages - 1, (kt + C::kStages - 1) & (C::kStages - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    fload(stage, 1, Int<1>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_block(Int<0>{});
-    __builtin_amdgcn_sched_barrier(0);
-    const int last = min(KT - 1, kt + C::kStages - 1);
-    wait_slab(last - (kt + 1));
+  auto main_loop = [&](auto swc) __attribute__((always_inline)) {
+    const int pre = KT < C::kStages - 1 ? KT : C::kStages - 1;
+    for (int k = 0; k < pre; ++k) issue(k, k);
+    wait_slab(pre - 1);
     __syncthreads();
-    if (kt + 1 < KT) fload((kt + 1) & (C::kStages - 1), 0, Int<0>{});
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_block(Int<1>{});
-    __builtin_amdgcn_sched_barrier(0);
+    fload(0, 0, Int<0>{});
+    for (int kt = 0; kt < KT; ++kt) {
+      const int stage = kt & (C::kStages - 1);
+      if (kt + C::kStages - 1 < KT)
+        issue(kt + C::kStages - 1, (kt + C::kStages - 1) & (C::kStages - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      fload(stage, 1, Int<1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_block(Int<0>{}, swc);
+      __builtin_amdgcn_sched_barrier(0);
+      const int last = min(KT - 1, kt + C::kStages - 1);
+      wait_slab(last - (kt + 1));
+      __syncthreads();
+      if (kt + 1 < KT) fload((kt + 1) & (C::kStages - 1), 0, Int<0>{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_block(Int<1>{}, swc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  if constexpr (BK) {
+    // Update epilogue.  32x32 MFMA output: lane l holds column l % 32 and rows
+    // 8 (v / 4) + 4 (l / 32) + v % 4 of its tile, which with swapped operands
+    // is a tile of C^T: 4 consecutive columns of one row of C per lane (and,
+    // in plain order, 4 consecutive elements of one row of C^T).  bf16: the
+    // whole output tile (row-major C, or C^T for a transposed output) is
+    // staged once in LDS, rows of BN * 2 bytes with 16-byte chunk c at
+    // c ^ row (8-byte writes of 32 rows and 16-byte reads of a row are both
+    // conflict-free), then every 32 lanes store one contiguous row segment.
+    // fp32: 16-byte stores straight from registers.  The output is read only
+    // by the next launch: streaming stores.
+    const bool to_c = pr.ct_off < 0;
+    if (to_c)
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
+    // tile-local (row, col) of value 4q of acc[mi][ni] in the staged tile
+    auto at = [&](int mi, int ni, int q, int& r, int& c) __attribute__((always_inline)) {
+      const int m = wm * C::kWaveM + mi * 32, n = wn * C::kWaveN + ni * 32;
+      if (to_c) { r = m + fr; c = n + 8 * q + 4 * fg; }
+      else      { r = n + fr; c = m + 8 * q + 4 * fg; }
+    };
+    if constexpr (sizeof(T) == 2) {
+      static_assert(BM == BN, "square output tiles");
+      constexpr int RB = BN * 2, NCH = RB / 16;
+      static_assert(BM * RB <= C::kLdsBytes, "staged output tile fits the stages");
+      __syncthreads();   // every wave is done reading the operand stages
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            int r, c;
+            at(mi, ni, q, r, c);
+            const f32x16& a = acc[mi][ni];
+            const u32x2 u{f32_to_bf16(c1 * a[4 * q]) |
+                              (static_cast<uint32_t>(f32_to_bf16(c1 * a[4 * q + 1])) << 16),
+                          f32_to_bf16(c1 * a[4 * q + 2]) |
+                              (static_cast<uint32_t>(f32_to_bf16(c1 * a[4 * q + 3])) << 16)};
+            *reinterpret_cast<u32x2*>(smem + r * RB + ((((c >> 3) ^ r) & (NCH - 1)) << 4) +
+                                      (c & 7) * 2) = u;
+          }
+      __syncthreads();
+      T* const g = to_c ? pool + pr.c_off + static_cast<size_t>(ti * BM) * pr.ldc + tj * BN
+                        : pool + pr.ct_off + static_cast<size_t>(tj * BN) * pr.ldct + ti * BM;
+      const size_t ld = to_c ? pr.ldc : pr.ldct;
+#pragma unroll
+      for (int p = 0; p < BM * NCH / NT; ++p) {
+        const int idx = p * NT + tid, r = idx / NCH, c = idx % NCH;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(smem + r * RB + (((c ^ r) & (NCH - 1)) << 4));
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(g + r * ld + c * 8));
+      }
+    } else {
+      T* const g = to_c ? pool + pr.c_off + static_cast<size_t>(ti * BM) * pr.ldc + tj * BN
+                        : pool + pr.ct_off + static_cast<size_t>(tj * BN) * pr.ldct + ti * BM;
+      const size_t ld = to_c ? pr.ldc : pr.ldct;
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            int r, c;
+            at(mi, ni, q, r, c);
+            const f32x16& a = acc[mi][ni];
+            st4<T>(g + r * ld + c, c1 * a[4 * q], c1 * a[4 * q + 1], c1 * a[4 * q + 2],
+                   c1 * a[4 * q + 3]);
+          }
+    }
+    return;
+  } else {
+    main_loop(std::false_type{});
   }
   __syncthreads();
 
@@ -710,6 +825,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) v[k] += c0 * e[k];
+      }
+      // + cd I (the update's a X folded into P); diagonal tiles only
+      if (ti == tj) {
+        const int d = band * BR + i - j;
+        if (d >= 0 && d < 8) v[d] += cd;
       }
       // the update's output is read only by the next launch: stream it past
       // L2, which holds this launch's operand panels (the Gram's stores are
@@ -1028,33 +1148,35 @@ mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const flo
 
 template <typename T, int BM, int WM, int WN>
 void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
-                       float c1, int has_e, hipStream_t st) {
+                       float c1, int has_e, float cd, hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
   if (bk)
-    k_ns_gemm<T, BM, BM, WM, WN, 2, true><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e);
+    k_ns_gemm<T, BM, BM, WM, WN, 2, true><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e, cd);
   else
-    k_ns_gemm<T, BM, BM, WM, WN, 2, false><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e);
+    k_ns_gemm<T, BM, BM, WM, WN, 2, false><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e, cd);
 }
 
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
-                         void* pool, int elem, float c0, float c1, int has_e, hipStream_t st) {
+                         void* pool, int elem, float c0, float c1, int has_e, float cd,
+                         hipStream_t st) {
   if (ntiles <= 0) return MO_OK;
+  if (bk && has_e) return fail(MO_EINVAL, "the K-major-B GEMM takes no E term");
   KTimer tm(MO_KC_NS_GEMM, st);
   const dim3 grid(static_cast<unsigned>(ntiles));
   if (tile == 256) {
     if (elem == 2)
       launch_gemm_shape<uint16_t, 256, 2, 4>(probs, n, grid, bk, static_cast<uint16_t*>(pool), c0,
-                                             c1, has_e, st);
+                                             c1, has_e, cd, st);
     else
       launch_gemm_shape<float, 256, 2, 4>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, st);
+                                          has_e, cd, st);
   } else if (tile == 128) {
     if (elem == 2)
       launch_gemm_shape<uint16_t, 128, 2, 2>(probs, n, grid, bk, static_cast<uint16_t*>(pool), c0,
-                                             c1, has_e, st);
+                                             c1, has_e, cd, st);
     else
       launch_gemm_shape<float, 128, 2, 2>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, st);
+                                          has_e, cd, st);
   } else {
     return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);
   }

@@ -123,13 +123,13 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       if (need_a)
         B.gram_a[q].push_back(make_prob(xc, xc, a, a, -1, lp, lp, sp, sp, 0, lp, ts, ts, 1,
                                         B.gram_tiles));
-      // Update X' = a X + P X: A = P (s x s), B = X read K-major (K = s),
-      // E = X; the next buffer receives the result.
-      B.upd[q].push_back(make_prob(p, xc, xn, -1, xc, sp, lp, lp, 0, lp, sp, ts, tl, 0,
+      // Update X' = P X (P = a I + b A + c A^2): A = P (s x s), B = X read
+      // K-major (K = s); the next buffer receives the result.
+      B.upd[q].push_back(make_prob(p, xc, xn, -1, -1, sp, lp, lp, 0, 0, sp, ts, tl, 0,
                                    B.upd_tiles));
       // Last iteration: a tall matrix is written transposed (l x s, stored
       // orientation) instead.
-      B.fin[q].push_back(tall ? make_prob(p, xc, -1, xn, xc, sp, lp, 0, sp, lp, sp, ts, tl, 0,
+      B.fin[q].push_back(tall ? make_prob(p, xc, -1, xn, -1, sp, lp, 0, sp, 0, sp, ts, tl, 0,
                                           B.upd_tiles)
                               : B.upd[q].back());
     }
@@ -213,7 +213,8 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
     const float a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
     const bool cubic_step = c == 0.f || !L.need_a;
     const int q = k & 1;
-    // phase 1: P = b X X^T (cubic-type step), or A = X X^T then P = b A + c A A
+    // phase 1: P = a I + b X X^T (cubic-type step), or A = X X^T then
+    // P = a I + b A + c A A.  The a X term of the update is folded into P.
     for (size_t i = 0; i < L.buckets.size(); ++i) {
       const NsBucket& B = L.buckets[i];
       if (B.gram_p[q].empty()) continue;
@@ -222,24 +223,24 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       mo_status s;
       if (cubic_step) {
         s = launch_ns_gemm(tab(tb.gram_p[q]), n, B.gram_tiles, B.tile, 0, pool, L.elem, 0.f, b, 0,
-                           st);
+                           a, st);
       } else {
         s = launch_ns_gemm(tab(tb.gram_a[q]), n, B.gram_tiles, B.tile, 0, pool, L.elem, 0.f, 1.f,
-                           0, st);
+                           0, 0.f, st);
         if (s == MO_OK)
           s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, B.tile, 0, pool, L.elem, b, c, 1,
-                             st);
+                             a, st);
       }
       if (s != MO_OK) return s;
     }
-    // phase 2: X' = a X + P X
+    // phase 2: X' = P X
     for (size_t i = 0; i < L.buckets.size(); ++i) {
       const NsBucket& B = L.buckets[i];
       if (B.upd[q].empty()) continue;
       const NsBucketTables& tb = T.b[i];
       const size_t off = k + 1 == steps ? tb.fin[q] : tb.upd[q];
       mo_status s = launch_ns_gemm(tab(off), static_cast<int>(B.upd[q].size()), B.upd_tiles,
-                                   B.tile, 1, pool, L.elem, a, 1.f, 1, st);
+                                   B.tile, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, st);
       if (s != MO_OK) return s;
     }
   }
