@@ -749,6 +749,68 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     }
     return;
   } else {
+    if constexpr (sizeof(T) == 2) {
+      if (!has_e) {
+        // Gram epilogue (bf16, no E term): with swapped operands each lane
+        // holds 4 consecutive columns of one row of the tile.  The tile
+        // c1 C + cd I is staged once in LDS as bf16 (layout as in the update
+        // epilogue); C's rows are stored as contiguous row segments, and the
+        // mirror (the transposed tile, for the lower triangle) is read with
+        // transpose reads: per 16-lane group, two reads give lane i 8
+        // consecutive elements of row n0 + i of C^T, and the 4 groups of a
+        // wave cover 32 consecutive columns, 64 contiguous bytes per row.
+        main_loop(std::true_type{});
+        static_assert(BM == BN, "square output tiles");
+        constexpr int RB = BN * 2, NCH = RB / 16;
+        static_assert(BM * RB <= C::kLdsBytes, "staged output tile fits the stages");
+        auto soff = [](int r, int c) __attribute__((always_inline)) {
+          return r * RB + ((((c >> 3) ^ r) & (NCH - 1)) << 4) + (c & 7) * 2;
+        };
+        const bool diag = ti == tj;
+        __syncthreads();   // every wave is done reading the operand stages
+#pragma unroll
+        for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = wm * C::kWaveM + mi * 32 + fr;
+              const int c = wn * C::kWaveN + ni * 32 + 8 * q + 4 * fg;
+              float x[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                x[e] = c1 * acc[mi][ni][4 * q + e] + (diag && r == c + e ? cd : 0.f);
+              const u32x2 u{f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16),
+                            f32_to_bf16(x[2]) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16)};
+              *reinterpret_cast<u32x2*>(smem + soff(r, c)) = u;
+            }
+        __syncthreads();
+        if (pr.c_off >= 0) {
+          T* const g = pool + pr.c_off + static_cast<size_t>(ti * BM) * pr.ldc + tj * BN;
+#pragma unroll
+          for (int p = 0; p < BM * NCH / NT; ++p) {
+            const int idx = p * NT + tid, r = idx / NCH, c = idx % NCH;
+            *reinterpret_cast<u32x4*>(g + static_cast<size_t>(r) * pr.ldc + c * 8) =
+                *reinterpret_cast<const u32x4*>(smem + r * RB + (((c ^ r) & (NCH - 1)) << 4));
+          }
+        }
+        if (pr.ct_off >= 0 && !(pr.sym && diag)) {
+          T* const g = pool + pr.ct_off + static_cast<size_t>(tj * BN) * pr.ldct + ti * BM;
+          constexpr int kUnits = (BN / 16) * (BM / 32);   // 16 rows x 32 columns of C^T
+          static_assert(kUnits % C::kWaves == 0, "mirror units per wave");
+#pragma unroll 4
+          for (int u = wv; u < kUnits; u += C::kWaves) {
+            const int n0 = (u % (BN / 16)) * 16, k0 = (u / (BN / 16)) * 32 + 8 * g16;
+            const int col = n0 + 4 * (j16 & 3);
+            const u32x2 lo = lds_read_tr16(smem + soff(k0 + (j16 >> 2), col));
+            const u32x2 hi = lds_read_tr16(smem + soff(k0 + 4 + (j16 >> 2), col));
+            *reinterpret_cast<u32x4*>(g + static_cast<size_t>(n0 + j16) * pr.ldct + k0) =
+                u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
+        }
+        return;
+      }
+    }
     main_loop(std::false_type{});
   }
   __syncthreads();
