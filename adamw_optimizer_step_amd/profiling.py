@@ -65,7 +65,8 @@ def _match(table: Dict[str, List[float]], kernel: str) -> List[float]:
 
 
 def traffic_summary(kernel: str, workload: str, copy_bytes: int, fetch_csv: str,
-                    write_csv: str) -> Dict[str, float]:
+                    write_csv: str, coeffs: str = "cubic",
+                    precision: str = "bf16") -> Dict[str, float]:
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
     cf, cw = _match(fetch, "k_diag_copy"), _match(write, "k_diag_copy")
@@ -75,7 +76,8 @@ def traffic_summary(kernel: str, workload: str, copy_bytes: int, fetch_csv: str,
     sf = copy_bytes / (sum(cf) / len(cf))
     sw = copy_bytes / (sum(cw) / len(cw))
     return {
-        "kernel": kernel, "workload": workload, "source_digest": source_digest(kernel),
+        "kernel": kernel, "workload": workload, "coeffs": coeffs, "precision": precision,
+        "source_digest": source_digest(kernel),
         "launches": len(kf), "copy_bytes": copy_bytes,
         "copy_fetch_counted": sum(cf) / len(cf), "copy_write_counted": sum(cw) / len(cw),
         "scale_fetch": sf, "scale_write": sw,
@@ -104,13 +106,16 @@ def main(argv=None) -> int:
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
     t.add_argument("--workload", required=True)
+    t.add_argument("--coeffs", default="cubic", choices=["cubic", "quintic"])
+    t.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--command", default="")
     a = ap.parse_args(argv)
-    s = traffic_summary(a.kernel, a.workload, a.copy_bytes, a.fetch, a.write)
-    print(f"# HBM traffic of {a.kernel}, workload {a.workload}")
+    s = traffic_summary(a.kernel, a.workload, a.copy_bytes, a.fetch, a.write, a.coeffs,
+                        a.precision)
+    print(f"# HBM traffic of {a.kernel}, workload {a.workload} ({a.coeffs}, {a.precision})")
     print()
     print("Commands (one MI355X, repository root):")
     print()

@@ -166,15 +166,17 @@ def cpu_baseline(w, coeffs, normuon, budget_s: float):
                        f"{spent:.1f}s of Muon work measured")}
 
 
-def counted_traffic(kernel: str, workload: str):
+def counted_traffic(kernel: str, workload: str, coeffs: str, precision: str):
     """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none for
-    this workload or the kernel's sources have changed since it was taken."""
+    this workload, coefficient set and NS precision, or the kernel's sources
+    have changed since it was taken."""
     from adamw_optimizer_step_amd import profiling
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         f"{kernel}_{workload}_traffic.md")
     s = profiling.read_summary(path)
-    if not s or s.get("workload") != workload:
+    if not s or s.get("workload") != workload or s.get("coeffs") != coeffs or \
+            s.get("precision") != precision:
         return None
     if s.get("source_digest") != profiling.source_digest(kernel):
         log(f"{path}: counters predate the current {kernel} sources; traffic = null")
@@ -325,7 +327,8 @@ def main() -> int:
         del src, dst
 
     if roofline is not None:
-        roofline["traffic"] = counted_traffic(roofline["kernel"], w.key)
+        roofline["traffic"] = counted_traffic(roofline["kernel"], w.key, args.coeffs,
+                                              args.precision)
 
     cpu = None
     if args.cpu_budget > 0:
