@@ -58,12 +58,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest, ties to even; NaN -> quiet NaN.
+// fp32 -> bf16, round to nearest, ties to even; NaN stays NaN.  The casts
+// select gfx950's v_cvt_pk_bf16_f32, whose results equal the integer
+// rounding (add 0x7fff plus the kept lsb, truncate) for every non-NaN input.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two values -> packed bf16, lo | hi << 16 (one conversion instruction).
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float load_as_f32(const void* p, int64_t i, int32_t dt) {
@@ -126,7 +131,7 @@ __device__ __forceinline__ void store8(void* p, int64_t i, int32_t dt, const flo
     u32x4_t u;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      u[k] = f32_to_bf16(v[2 * k]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * k + 1])) << 16);
+      u[k] = pk_bf16(v[2 * k], v[2 * k + 1]);
     stv<u32x4_t, NT>(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p) + i), u);
   }
 }

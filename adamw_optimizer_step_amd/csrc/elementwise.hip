@@ -42,7 +42,7 @@ __device__ __forceinline__ void store4(void* p, int64_t i, int32_t dt, const flo
     u32x2_t u;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-      u[k] = f32_to_bf16(v[2 * k]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * k + 1])) << 16);
+      u[k] = pk_bf16(v[2 * k], v[2 * k + 1]);
     stv<u32x2_t, NT>(reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(p) + i), u);
   }
 }

@@ -246,8 +246,8 @@ __device__ __forceinline__ void ld8<float>(const float* p, float* v) {
 template <typename T, bool NT = false>
 __device__ __forceinline__ void st4(T* p, float v0, float v1, float v2, float v3) {
   if constexpr (sizeof(T) == 2) {
-    const u32x2 u{f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16),
-                  f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16)};
+    const u32x2 u{pk_bf16(v0, v1),
+                  pk_bf16(v2, v3)};
     if constexpr (NT)
       __builtin_nontemporal_store(u, reinterpret_cast<u32x2*>(p));
     else
@@ -269,7 +269,7 @@ __device__ __forceinline__ void st8(T* p, const float* v) {
     u32x4 u;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      u[k] = f32_to_bf16(v[2 * k]) | (static_cast<uint32_t>(f32_to_bf16(v[2 * k + 1])) << 16);
+      u[k] = pk_bf16(v[2 * k], v[2 * k + 1]);
     if constexpr (NT)
       __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(p));
     else
@@ -308,8 +308,8 @@ __device__ __forceinline__ void st4(T* p, const float* v);
 template <>
 __device__ __forceinline__ void st4<uint16_t>(uint16_t* p, const float* v) {
   u32x2 u;
-  u[0] = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-  u[1] = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+  u[0] = pk_bf16(v[0], v[1]);
+  u[1] = pk_bf16(v[2], v[3]);
   *reinterpret_cast<u32x2*>(p) = u;
 }
 template <>
@@ -713,10 +713,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
             int r, c;
             at(mi, ni, q, r, c);
             const f32x16& a = acc[mi][ni];
-            const u32x2 u{f32_to_bf16(c1 * a[4 * q]) |
-                              (static_cast<uint32_t>(f32_to_bf16(c1 * a[4 * q + 1])) << 16),
-                          f32_to_bf16(c1 * a[4 * q + 2]) |
-                              (static_cast<uint32_t>(f32_to_bf16(c1 * a[4 * q + 3])) << 16)};
+            const u32x2 u{pk_bf16(c1 * a[4 * q], c1 * a[4 * q + 1]),
+                          pk_bf16(c1 * a[4 * q + 2], c1 * a[4 * q + 3])};
             *reinterpret_cast<u32x2*>(smem + r * RB + ((((c >> 3) ^ r) & (NCH - 1)) << 4) +
                                       (c & 7) * 2) = u;
           }
@@ -780,8 +778,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
 #pragma unroll
               for (int e = 0; e < 4; ++e)
                 x[e] = c1 * acc[mi][ni][4 * q + e] + (diag && r == c + e ? cd : 0.f);
-              const u32x2 u{f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16),
-                            f32_to_bf16(x[2]) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16)};
+              const u32x2 u{pk_bf16(x[0], x[1]),
+                            pk_bf16(x[2], x[3])};
               *reinterpret_cast<u32x2*>(smem + soff(r, c)) = u;
             }
         __syncthreads();
@@ -1105,8 +1103,8 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
             x[e] = ak * __uint_as_float(bits) + accu[mi][4 * q + e];
           }
           u32x2 o;
-          o[0] = f32_to_bf16(x[0]) | (static_cast<uint32_t>(f32_to_bf16(x[1])) << 16);
-          o[1] = f32_to_bf16(x[2]) | (static_cast<uint32_t>(f32_to_bf16(x[3])) << 16);
+          o[0] = pk_bf16(x[0], x[1]);
+          o[1] = pk_bf16(x[2], x[3]);
           *reinterpret_cast<u32x2*>(Xn + off) = o;
         }
       __syncthreads();   // B2: X'_b complete in LDS

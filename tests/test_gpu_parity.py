@@ -10,6 +10,7 @@ import torch
 import workloads as wl
 from adamw_optimizer_step_amd import api
 from oracle import adamw as oadamw
+from oracle import bf16 as obf16
 from oracle import muon as omuon
 
 from gpu_common import (REL_F32, assert_bf16_close, assert_ns_close, f64, rel_inf,
@@ -68,6 +69,35 @@ def test_momentum_no_nesterov_and_no_dir():
 
 NS_SHAPES = [(4, 8), (16, 8), (6, 8), (300, 200), (130, 700), (256, 256), (1, 64), (64, 1),
              (129, 129), (520, 300)]
+
+
+def test_bf16_rounding_bit_exact():
+    """D = bf16(G) through muon_momentum (mu = 0, no Nesterov, fp32 G): every
+    upper half of an fp32 with lower halves 0, 1, 0x7fff, 0x8000 (ties),
+    0x8001 and 0xffff, plus random patterns; subnormals, overflow to infinity
+    and NaN included.  Bit-exact against round-to-nearest-even of the oracle;
+    NaN stays NaN.  G = -0 is left out: mu B + G is +0 there."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    rng = np.random.default_rng(11)
+    bits = np.concatenate([(hi[:, None] | lows[None, :]).ravel(),
+                           rng.integers(0, 1 << 32, size=1 << 20, dtype=np.uint64)
+                           .astype(np.uint32)])
+    bits = bits[bits != 0x80000000]
+    G = bits.view(np.float32)
+    g = torch.from_numpy(G.copy()).cuda()
+    b = torch.zeros_like(g)
+    d = torch.empty(g.shape, dtype=torch.bfloat16, device="cuda")
+    api.muon_momentum([g], [b], [d], mu=0.0, nesterov=False)
+    got = d.cpu().view(torch.int16).numpy().view(np.uint16)
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = obf16.round_bf16(G.astype(np.float64)).astype(np.float32)
+    ref_bits = (ref.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(G)
+    got_nan = (got & 0x7FFF) > 0x7F80
+    assert np.array_equal(got_nan, nan)
+    bad = np.flatnonzero((got != ref_bits) & ~nan)
+    assert bad.size == 0, [(hex(bits[i]), hex(got[i]), hex(ref_bits[i])) for i in bad[:8]]
 
 
 def _ns_case(shapes, dtype, seed, std=1.0):
