@@ -922,8 +922,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
 // Slice-resident Newton-Schulz for bf16 slices whose padded short side is
 // 128 (head-sized slices).  One workgroup of 8 waves owns one slice for all
 // iterations.  X (128 x lp) streams through LDS in 128 x 128 column blocks;
-// P = b A (+ c A^2), A = X X^T, lives in LDS.  Per block of iteration k:
-//   X'_b = a X_b + P X_b        (B operand and E term read from the staged block)
+// P = a I + b A (+ c A^2), A = X X^T, lives in LDS (a X folded into P's
+// diagonal, as in the GEMM path).  Per block of iteration k:
+//   X'_b = P X_b                (B operand read from the staged block)
 //   X'_b -> global, and A' += X'_b X'_b^T for iteration k + 1 (registers)
 // so each iteration reads and writes X once; one extra read of X0 forms the
 // first Gram.  Same iterate buffers and conventions as the GEMM path: the
@@ -1088,24 +1089,16 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       }
       // accu[mi][4 q + e] = X'_b[i][j0 + e], i = wn * 32 + fr,
       // j0 = wm * 64 + mi * 32 + 8 q + 4 fg: 8-byte E reads and X'_b writes
-      const float ak = cf.a[pass - 1];
+      // (a X_b is on P's diagonal: P = a I + b A + c A^2)
       const int xi = wn * 32 + fr;
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int off = sm_off(xi, wm * 64 + mi * 32 + 8 * q + 4 * fg);
-          const u32x2 e2 = *reinterpret_cast<const u32x2*>(stg + off);
-          float x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t bits = (e & 1) ? (e2[e >> 1] & 0xffff0000u) : (e2[e >> 1] << 16);
-            x[e] = ak * __uint_as_float(bits) + accu[mi][4 * q + e];
-          }
-          u32x2 o;
-          o[0] = pk_bf16(x[0], x[1]);
-          o[1] = pk_bf16(x[2], x[3]);
-          *reinterpret_cast<u32x2*>(Xn + off) = o;
+          const f32x16& x = accu[mi];
+          *reinterpret_cast<u32x2*>(Xn + off) =
+              u32x2{pk_bf16(x[4 * q], x[4 * q + 1]), pk_bf16(x[4 * q + 2], x[4 * q + 3])};
         }
       __syncthreads();   // B2: X'_b complete in LDS
       const bool last = pass == steps;
@@ -1136,15 +1129,15 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       if (!last) gram_acc(Xn, Xn, accg);
     }
     if (b == NB - 1 && pass < steps) {
-      // P for iteration `pass` from A = accg
-      const float bk = cf.b[pass], ck = cf.c[pass];
+      // P = a I + b A (+ c A^2) for iteration `pass`, from A = accg
+      const float ak = cf.a[pass], bk = cf.b[pass], ck = cf.c[pass];
       if (ck == 0.f) {
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             *reinterpret_cast<uint16_t*>(Ps + sm_off(acc_row(mi, v), acc_col)) =
-                f32_to_bf16(bk * accg[mi][v]);
+                f32_to_bf16(bk * accg[mi][v] + (acc_row(mi, v) == acc_col ? ak : 0.f));
       } else {
         __syncthreads();   // X'_b reads of this element are done
 #pragma unroll
@@ -1163,7 +1156,8 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
 #pragma unroll
           for (int v = 0; v < 16; ++v)
             *reinterpret_cast<uint16_t*>(Ps + sm_off(acc_row(mi, v), acc_col)) =
-                f32_to_bf16(bk * accg[mi][v] + ck * accu[mi][v]);
+                f32_to_bf16(bk * accg[mi][v] + ck * accu[mi][v] +
+                            (acc_row(mi, v) == acc_col ? ak : 0.f));
       }
       zero(accg);
     }
