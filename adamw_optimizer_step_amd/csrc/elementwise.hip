@@ -123,8 +123,9 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
 // AdamW (OMN page, recipe paragraph; Qwen3.8 optimizer notes, Adam/AdamW).
 // ---------------------------------------------------------------------------
 // Sum of squares of the gradients: each block covers kSumsqSub blocks of the
-// apply kernel's partition (all loads issued before the reduction) and writes
-// one partial.
+// apply kernel's partition, one 16-byte load of 8 elements per thread and
+// block, all issued before the reduction (four independent fp64 sums), and
+// writes one partial.
 constexpr int kSumsqSub = 4;
 __host__ __device__ constexpr int64_t sumsq_partials(int64_t nblocks) {
   return (nblocks + kSumsqSub - 1) / kSumsqSub;
@@ -133,30 +134,25 @@ __host__ __device__ constexpr int64_t sumsq_partials(int64_t nblocks) {
 __global__ __launch_bounds__(kThreads) void k_adam_sumsq(const AdamSeg* __restrict__ segs, int nseg,
                                                          int64_t nblocks,
                                                          double* __restrict__ partials) {
-  float g[kSumsqSub][kGroups][4];
+  float g[kSumsqSub][8];
 #pragma unroll
   for (int j = 0; j < kSumsqSub; ++j) {
     const int64_t ab = static_cast<int64_t>(blockIdx.x) * kSumsqSub + j;
     const AdamSeg* sp = ab < nblocks ? &segs[find_segment(segs, nseg, ab)] : nullptr;
-#pragma unroll
-    for (int q = 0; q < kGroups; ++q) {
-      const int64_t e0 =
-          sp ? (ab - sp->start) * kEltPerBlock + q * kGroupStride + threadIdx.x * 4 : 0;
-      const int64_t left = sp ? sp->numel - e0 : 0;
-      if (left >= 4) {
-        load4<false>(sp->g, e0, sp->dt, g[j][q]);
-      } else {
-        for (int k = 0; k < 4; ++k) g[j][q][k] = k < left ? load_as_f32(sp->g, e0 + k, sp->dt) : 0.f;
-      }
+    const int64_t e0 = sp ? (ab - sp->start) * kEltPerBlock + threadIdx.x * 8 : 0;
+    const int64_t left = sp ? sp->numel - e0 : 0;
+    if (left >= 8) {
+      load8(sp->g, e0, sp->dt, g[j]);
+    } else {
+      for (int k = 0; k < 8; ++k) g[j][k] = k < left ? load_as_f32(sp->g, e0 + k, sp->dt) : 0.f;
     }
   }
-  double ss = 0.0;
+  double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int j = 0; j < kSumsqSub; ++j)
 #pragma unroll
-    for (int q = 0; q < kGroups; ++q)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) ss += static_cast<double>(g[j][q][k]) * g[j][q][k];
+    for (int k = 0; k < 8; ++k) s4[k & 3] += static_cast<double>(g[j][k]) * g[j][k];
+  double ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   __shared__ double s_ss[4];
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) s_ss[threadIdx.x >> 6] = ss;

@@ -808,7 +808,6 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
           T* const g = pool + pr.ct_off + static_cast<size_t>(tj * BN) * pr.ldct + ti * BM;
           constexpr int kUnits = (BN / 16) * (BM / 32);   // 16 rows x 32 columns of C^T
           static_assert(kUnits % C::kWaves == 0, "mirror units per wave");
-#pragma unroll 4
           for (int u = wv; u < kUnits; u += C::kWaves) {
             const int n0 = (u % (BN / 16)) * 16, k0 = (u / (BN / 16)) * 32 + 8 * g16;
             const int col = n0 + 4 * (j16 & 3);
