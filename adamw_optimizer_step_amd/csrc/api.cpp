@@ -69,8 +69,17 @@ mo_status validate_ns_items(const mo_ns_item* items, int32_t n, int32_t precisio
 void ns_layout_from_items(const mo_ns_item* items, int32_t n, int32_t precision, bool need_a,
                           NsLayout& L) {
   std::vector<int64_t> r(n), c(n);
-  for (int32_t i = 0; i < n; ++i) { r[i] = items[i].rows; c[i] = items[i].cols; }
-  build_ns_layout(L, r.data(), c.data(), n, precision == MO_NS_F32 ? 4 : 2, need_a);
+  std::vector<uint8_t> direct(n);
+  for (int32_t i = 0; i < n; ++i) {
+    r[i] = items[i].rows;
+    c[i] = items[i].cols;
+    // an input the slice-resident kernel can read in place (it must be the
+    // pool's element type, unpadded rows, 16-byte aligned)
+    direct[i] = precision == MO_NS_BF16 && items[i].in_dtype == MO_BF16 &&
+                items[i].ld_in == items[i].cols && aligned16(items[i].in);
+  }
+  build_ns_layout(L, r.data(), c.data(), n, precision == MO_NS_F32 ? 4 : 2, need_a,
+                  direct.data(), true);
 }
 
 // ----- AdamW -----------------------------------------------------------------
@@ -191,7 +200,8 @@ mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const flo
   if ((s = launch_ns_stats(dprep, n, L.prep_tiles, partials, st)) != MO_OK) return s;
   if ((s = launch_ns_scale(dprep, n, partials, scale, st)) != MO_OK) return s;
   if ((s = launch_ns_prep(dprep, n, L.prep_tiles, scale, pool, L.elem, st)) != MO_OK) return s;
-  if ((s = ns_run_iterations(L, base + W.tab, W.tabs, pool, coeffs, steps, st)) != MO_OK) return s;
+  if ((s = ns_run_iterations(L, base + W.tab, W.tabs, pool, scale, coeffs, steps, st)) != MO_OK)
+    return s;
   return launch_ns_final(reinterpret_cast<const FinalItem*>(base + W.fin), n, rows, pool, L.elem,
                          st);
 }

@@ -59,8 +59,13 @@ struct NsLayout {
   int32_t final_ld(int i) const { return tall[i] ? sp[i] : lp[i]; }
 };
 
+// direct_ok[i] (nullable: none) says that slice i's input can be read in
+// place by the slice-resident kernel: bf16, row stride equal to cols,
+// 16-byte aligned.  Such a slice with 128 rows and a multiple of 128 columns
+// skips the prep copy: its prep item writes nothing, and has no tiles at all
+// unless the statistics are taken over the prep tiles (stats_from_prep).
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
-                     bool need_a);
+                     bool need_a, const uint8_t* direct_ok, bool stats_from_prep);
 
 // Byte offsets of the device tables inside one contiguous table block.
 struct NsBucketTables {
@@ -78,8 +83,9 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
 mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st);
 
 // Enqueue the Newton-Schulz iterations on the prepared pool.
+// `scale` holds the per-slice normalisation scales (the prep kernel's).
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
-                            const float* coeffs, int steps, hipStream_t st);
+                            const float* scale, const float* coeffs, int steps, hipStream_t st);
 
 // True while kernel timing (mo_timing_enable) is on.
 bool timing_enabled();

@@ -157,13 +157,17 @@ struct SmallProb {
   int64_t x_off[2];        // pool offsets of the two iterate buffers (128 x lp each)
   int32_t lp;              // padded long side = row stride of the iterates
   int32_t tall;            // last iteration writes the result transposed (lp x 128)
+  int32_t item;            // index of the slice's prep item and normalisation scale
+  int32_t direct;          // the first two passes read the item's input D (bf16,
+                           // 128 x lp, row stride lp) and fold the scale into P,
+                           // instead of reading the prepared X0
 };
 struct NsCoeffTable {
   float a[MO_NS_MAX_STEPS], b[MO_NS_MAX_STEPS], c[MO_NS_MAX_STEPS];
 };
 constexpr int kSmallS = 128;
-mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const float* coeffs,
-                          int steps, hipStream_t st);
+mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
+                          const float* scale, const float* coeffs, int steps, hipStream_t st);
 
 // C = c1 A B (+ c0 E) (+ cd I on diagonal tiles).  bk = 1: B is read K-major
 // (K x N row-major) through LDS transpose reads; no E term, and the output

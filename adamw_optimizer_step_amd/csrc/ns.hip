@@ -348,6 +348,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_prep(const PrepItem* __restrict
   const int64_t tile = blockIdx.x;
   const int idx = find_segment(items, n, tile);
   const PrepItem it = items[idx];
+  if (it.sbuf < 0 && it.stbuf < 0) return;   // read in place by the slice-resident kernel
   const float sc = scale[idx];
   const int64_t lt = tile - it.start;
   const int r0 = static_cast<int>(lt / it.tiles_c) * kPrepTile;
@@ -960,6 +961,8 @@ __device__ __forceinline__ int sm_off(int row, int col) {
 
 __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __restrict__ probs,
                                                             uint16_t* __restrict__ pool,
+                                                            const PrepItem* __restrict__ items,
+                                                            const float* __restrict__ scale,
                                                             NsCoeffTable cf, int steps) {
   __shared__ __attribute__((aligned(16))) char smem[kSmTile * (2 + kSmStages)];
   char* const Ps = smem;             // P (A operand of the update)
@@ -974,7 +977,13 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   const uint32_t ld_b = static_cast<uint32_t>(pr.lp) * 2;
   uint16_t* const X0 = pool + pr.x_off[0];
   uint16_t* const X1 = pool + pr.x_off[1];
+  // In-place input: passes 0 and 1 read D itself (128 x lp bf16, row stride
+  // lp, the layout of X0) and form X0 = bf16(s D) in LDS, with the same fp32
+  // product and rounding as the prep kernel.
+  const bool direct = pr.direct != 0;
   const u32x4 rs0 = buffer_rsrc(X0, kSmallS * ld_b), rs1 = buffer_rsrc(X1, kSmallS * ld_b);
+  const u32x4 rsin = direct ? buffer_rsrc(items[pr.item].in, kSmallS * ld_b) : rs0;
+  const float dscale = direct ? scale[pr.item] : 1.f;
 
   // Direct-to-LDS loads of one 128 x 128 block: 32 instructions of 4 rows
   // (1 KiB), 4 per wave; lane i lands at row + i / 16, physical chunk i % 16
@@ -991,11 +1000,17 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
   auto issue = [&](int e) __attribute__((always_inline)) {
     const int pass = e / NB, b = e - pass * NB;
-    const bool from1 = pass >= 2 && ((pass - 1) & 1);   // iteration k reads X[k % 2]
+    // iteration k reads X[k % 2]; passes 0 and 1 read X0 (or D in place).
+    // Selected per 32-bit word: a select between whole descriptors made the
+    // compiler keep them in scratch memory.
+    const bool from1 = pass >= 2 && ((pass - 1) & 1);
+    u32x4 rs;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) rs[k] = pass < 2 ? rsin[k] : from1 ? rs1[k] : rs0[k];
     const uint32_t st = lds0 + (2 + e % kSmStages) * kSmTile;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      lds_dma16<true>(from1 ? rs1 : rs0, st + (wv * 4 + q) * 1024, vo[q], b * 256);
+      lds_dma16<true>(rs, st + (wv * 4 + q) * 1024, vo[q], b * 256);
   };
 
   // Operand reads.  NT fragment: row m, logical chunk 2 ks + fg (both
@@ -1072,6 +1087,22 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       done = a - 1;
     }
     __syncthreads();   // B1: block `cur` in LDS; element cur - 1 fully done
+    if (direct && cur < 2 * NB) {
+      // D block -> X0 block in place (16 bytes = 8 elements per access; the
+      // chunk swizzle does not matter for an elementwise pass)
+      char* const blk = smem + (2 + cur % kSmStages) * kSmTile;
+#pragma unroll
+      for (int q = 0; q < kSmTile / (16 * kSmThreads); ++q) {
+        u32x4* const p = reinterpret_cast<u32x4*>(blk + (q * kSmThreads + tid) * 16);
+        u32x4 v = *p;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          v[k] = pk_bf16(dscale * __uint_as_float(v[k] << 16),
+                         dscale * __uint_as_float(v[k] & 0xffff0000u));
+        *p = v;
+      }
+      __syncthreads();
+    }
     // Loads ahead: at most 2 elements ahead (their stage was last read by
     // element cur - 1), and a block written by an earlier pass only once its
     // stores are known complete.
@@ -1251,8 +1282,8 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
   return MO_OK;
 }
 
-mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const float* coeffs,
-                          int steps, hipStream_t st) {
+mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
+                          const float* scale, const float* coeffs, int steps, hipStream_t st) {
   if (n <= 0) return MO_OK;
   if (steps < 1 || steps > MO_NS_MAX_STEPS) return fail(MO_EINVAL, "bad step count %d", steps);
   NsCoeffTable cf;
@@ -1264,7 +1295,7 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const float
   }
   KTimer tm(MO_KC_NS_SMALL, st);
   k_ns_small<<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
-      probs, static_cast<uint16_t*>(pool), cf, steps);
+      probs, static_cast<uint16_t*>(pool), items, scale, cf, steps);
   MO_LAUNCH_CHECK("k_ns_small");
   return MO_OK;
 }

@@ -52,7 +52,7 @@ void order_by_k(std::vector<GemmProb>& v) {
 }  // namespace
 
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
-                     bool need_a) {
+                     bool need_a, const uint8_t* direct_ok, bool stats_from_prep) {
   L = NsLayout();
   L.elem = elem;
   L.need_a = need_a;
@@ -110,6 +110,14 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       sm.x_off[1] = x[1];
       sm.lp = lp;
       sm.tall = tall;
+      sm.item = i;
+      sm.direct = direct_ok && direct_ok[i] && !tall && s_ == kSmallS && lp == l_;
+      if (sm.direct) {
+        // no X0 copy; the prep tiles stay only where they feed the statistics
+        L.prep.back().sbuf = -1;
+        L.prep.back().stbuf = -1;
+        if (!stats_from_prep) L.prep_tiles = L.prep.back().start;
+      }
       L.small.push_back(sm);
       continue;
     }
@@ -202,11 +210,13 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
 }
 
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
-                            const float* coeffs, int steps, hipStream_t st) {
+                            const float* scale, const float* coeffs, int steps, hipStream_t st) {
   auto tab = [dtab](size_t off) { return reinterpret_cast<const GemmProb*>(dtab + off); };
   if (!L.small.empty()) {
     mo_status s = launch_ns_small(reinterpret_cast<const SmallProb*>(dtab + T.small),
-                                  static_cast<int>(L.small.size()), pool, coeffs, steps, st);
+                                  static_cast<int>(L.small.size()), pool,
+                                  reinterpret_cast<const PrepItem*>(dtab + T.prep), scale, coeffs,
+                                  steps, st);
     if (s != MO_OK) return s;
   }
   for (int k = 0; k < steps; ++k) {

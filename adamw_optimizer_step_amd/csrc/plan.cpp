@@ -108,8 +108,11 @@ mo_status build_plan(mo_plan* P) {
   for (const auto& a : P->active) P->mom_blocks += ceil_div(a.rows * a.cols, kEltPerBlock);
   std::vector<int64_t> rr, cc;
   for (const auto& a : P->active) { rr.push_back(a.rows); cc.push_back(a.cols); P->total_rows += a.rows; }
+  // D lives in the (256-byte aligned) workspace in the pool's element type,
+  // rows of cols elements: readable in place whenever the path is bf16
+  const std::vector<uint8_t> direct(rr.size(), P->ddt == MO_BF16 ? 1 : 0);
   build_ns_layout(P->ns, rr.data(), cc.data(), static_cast<int>(rr.size()),
-                  P->ddt == MO_F32 ? 4 : 2, P->need_a);
+                  P->ddt == MO_F32 ? 4 : 2, P->need_a, direct.data(), false);
   P->ws_stats = ws.take(sizeof(StatPartial) * P->mom_blocks);
   P->ws_scale = ws.take(sizeof(float) * P->active.size());
   P->ws_adam_partials = ws.take(sizeof(double) * P->adam_blocks);
@@ -404,7 +407,9 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     float coeffs[3 * MO_NS_MAX_STEPS];
     for (int k = 0; k < hp.ns_steps; ++k)
       for (int j = 0; j < 3; ++j) coeffs[3 * k + j] = hp.ns_coeffs[k][j];
-    if ((s = ns_run_iterations(P->ns, dns, P->nst, pool, coeffs, hp.ns_steps, st)) != MO_OK)
+    if ((s = ns_run_iterations(P->ns, dns, P->nst, pool,
+                               reinterpret_cast<const float*>(base + P->ws_scale), coeffs,
+                               hp.ns_steps, st)) != MO_OK)
       return s;
     RowSeg none;
     std::memset(&none, 0, sizeof(none));
