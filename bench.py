@@ -166,22 +166,14 @@ def cpu_baseline(w, coeffs, normuon, budget_s: float):
                        f"{spent:.1f}s of Muon work measured")}
 
 
-def counted_traffic(kernel: str, workload: str, coeffs: str, precision: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when there is none for
-    this workload, coefficient set and NS precision, or the kernel's sources
-    have changed since it was taken."""
+def counted(kernel: str, workload: str, coeffs: str, precision: str):
+    """The kernel's counter figures (calibrated HBM bytes per launch, mean
+    MfmaUtil) from the committed summary for this workload, coefficient set
+    and NS precision, or None when there is none or the kernel's sources have
+    changed since the counters were taken."""
     from adamw_optimizer_step_amd import profiling
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        f"{kernel}_{workload}_traffic.md")
-    s = profiling.read_summary(path)
-    if not s or s.get("workload") != workload or s.get("coeffs") != coeffs or \
-            s.get("precision") != precision:
-        return None
-    if s.get("source_digest") != profiling.source_digest(kernel):
-        log(f"{path}: counters predate the current {kernel} sources; traffic = null")
-        return None
-    return float(s["fetch_bytes_per_launch"]) + float(s["write_bytes_per_launch"])
+    path = os.path.join(ROOT, "profiles", profiling.summary_name(workload, coeffs, precision))
+    return profiling.kernel_figures(path, kernel, workload, coeffs, precision)
 
 
 def main() -> int:
@@ -326,9 +318,27 @@ def main() -> int:
         hbm["copy"] = copy_gbs
         del src, dst
 
+    # counter-based figures (committed rocprofv3 summaries; null when stale)
+    cnt = {k: counted(k, w.key, args.coeffs, args.precision)
+           for k in ("k_ns_gemm", "k_ns_small", "k_momentum", "k_rows", "k_adam_sumsq",
+                     "k_adam_apply")}
     if roofline is not None:
-        roofline["traffic"] = counted_traffic(roofline["kernel"], w.key, args.coeffs,
-                                              args.precision)
+        c = cnt.get(roofline["kernel"])
+        roofline["traffic"] = (c["fetch_bytes_per_launch"] + c["write_bytes_per_launch"]
+                               if c else None)
+        roofline["mfma_util_pct"] = round(c["mfma_util_pct"], 2) \
+            if c and "mfma_util_pct" in c else None
+    hbm_counted = {}
+    for name, ks in (("momentum", ("k_momentum",)), ("update", ("k_rows",)),
+                     ("adamw", ("k_adam_sumsq", "k_adam_apply"))):
+        cs = [cnt.get(k) for k in ks]
+        t = sum(kern[n]["ms_per_step"] for n in kern
+                if "k_" + n in ks or (name == "adamw" and n == "adam_norm"))
+        if all(cs) and t > 0:
+            b = sum((c["fetch_bytes_per_launch"] + c["write_bytes_per_launch"]) for c in cs)
+            hbm_counted[name] = round(b / (t * 1e-3) / 1e9, 1)
+        else:
+            hbm_counted[name] = None
 
     cpu = None
     if args.cpu_budget > 0:
@@ -350,6 +360,7 @@ def main() -> int:
                                         if roofline else None),
         "adamw_hbm_gbs": hbm.get("adamw"),
         "hbm_gbs": hbm,
+        "hbm_gbs_counted": hbm_counted,
         "kernels": kern,
         "cpu_baseline": cpu,
     }
