@@ -19,6 +19,7 @@
 // kernel instead.
 #include <type_traits>
 
+#include <cstdlib>
 #include <cstring>
 
 #include "kernels.hpp"
@@ -404,15 +405,18 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <typename T, int BM, int BN, int WM, int WN, bool BK>
+template <typename T, int BM, int BN, int WM, int WN, bool BK, int ST = 4, int SRB = 64>
 struct GemmCfg {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kWaves = WM * WN;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int FM = kWaveM / 32, FN = kWaveN / 32;
-  // K slab: 64-byte rows (32 bf16 / 16 fp32 of k), 4 LDS stages, 3 in flight
-  static constexpr int kRowB = 64;
-  static constexpr int kStages = 4;
+  // K slab: SRB-byte rows (64: 32 bf16 / 16 fp32 of k; 128: twice that); ST
+  // LDS stages (a power of two), ST - 1 slabs in flight
+  static constexpr int kRowB = SRB;
+  static_assert(SRB == 64 || SRB == 128, "slab rows of 64 or 128 bytes");
+  static constexpr int kStages = ST;
+  static_assert(ST >= 2 && (ST & (ST - 1)) == 0, "stage count is a power of two");
   static constexpr int kSub = kRowB / 32;                   // 16-k substeps per slab
   static constexpr int kChunks = kRowB / 16;                // 16-byte chunks per row
   static constexpr int kSh = kRowB == 64 ? 2 : 1;           // swizzle shift
@@ -456,11 +460,11 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK>
+template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK, int ST, int SRB>
 __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1,
     int has_e, float cd) {
-  using C = GemmCfg<T, BM, BN, WM, WN, BK>;
+  using C = GemmCfg<T, BM, BN, WM, WN, BK, ST, SRB>;
   constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
   // XCD-aware order: consecutive workgroup ids go round-robin over the 8
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int fr = lane & 31, fg = lane >> 5;
-  static_assert(FM % 2 == 0 && FN % 2 == 0, "wave tiles span an even number of 32-row blocks");
+  static_assert(FM % 2 == 0, "wave tiles span an even number of 32-row blocks");
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave index as a scalar
 
   // Global -> LDS through buffer resources (hardware range-checked).  A (and
@@ -647,23 +651,24 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   // counter, kInst per slab, completing in order) and its LDS reads are done
   // (the stage they read is refilled after the next barrier).
   auto wait_slab = [](int younger) __attribute__((always_inline)) {
-    static_assert(2 * C::kInst <= 63, "vmcnt immediate");
-    if (younger >= 2)
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(2 * C::kInst));
-    else if (younger == 1)
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(C::kInst));
-    else
-      __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+    constexpr int kMaxYoung = C::kStages - 2;
+    static_assert(kMaxYoung * C::kInst <= 63, "vmcnt immediate");
+    const int y = younger < kMaxYoung ? younger : kMaxYoung;
+    static_for<0, kMaxYoung + 1>([&](auto yc) {
+      constexpr int k = decltype(yc)::value;
+      if (y == k) __builtin_amdgcn_s_waitcnt(vm_wait_imm(k * C::kInst));
+    });
   };
-  // Software pipeline over K slabs (kSub = 2 substeps of 16 k), two fragment
-  // register sets, kStages = 4 LDS stages with the loads of 3 slabs in flight.
+  // Software pipeline over K slabs (kSub = 2 or 4 substeps of 16 k), two
+  // fragment register sets used in turn, kStages LDS stages with the loads of
+  // kStages - 1 slabs in flight (below: 4 and 3).
   // Per slab kt:
   //   loads of slab kt+3 into stage (kt+3) % 4 (last read in slab kt-1,
   //   which ended with a barrier)
   //   read frags ks1              | MFMAs ks0
   //   wait for slab kt+1; barrier
   //   read frags ks0 of slab kt+1 | MFMAs ks1
-  static_assert(C::kSub == 2, "pipeline below is written for two substeps per slab");
+  static_assert(C::kSub % 2 == 0, "an even number of substeps per slab");
   const int KT = pr.K / C::kSlabK;
   auto main_loop = [&](auto swc) __attribute__((always_inline)) {
     const int pre = KT < C::kStages - 1 ? KT : C::kStages - 1;
@@ -676,17 +681,23 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
       if (kt + C::kStages - 1 < KT)
         issue(kt + C::kStages - 1, (kt + C::kStages - 1) & (C::kStages - 1));
       __builtin_amdgcn_sched_barrier(0);
-      fload(stage, 1, Int<1>{});
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_block(Int<0>{}, swc);
-      __builtin_amdgcn_sched_barrier(0);
-      const int last = min(KT - 1, kt + C::kStages - 1);
-      wait_slab(last - (kt + 1));
-      __syncthreads();
-      if (kt + 1 < KT) fload((kt + 1) & (C::kStages - 1), 0, Int<0>{});
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_block(Int<1>{}, swc);
-      __builtin_amdgcn_sched_barrier(0);
+      // substep ks multiplies set ks & 1 while the next substep's fragments
+      // load into the other set; before the last substep, wait for slab
+      // kt + 1 and load its first substep
+      static_for<0, C::kSub>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        if constexpr (ks + 1 < C::kSub) {
+          fload(stage, ks + 1, Int<(ks + 1) & 1>{});
+        } else {
+          const int last = min(KT - 1, kt + C::kStages - 1);
+          wait_slab(last - (kt + 1));
+          __syncthreads();
+          if (kt + 1 < KT) fload((kt + 1) & (C::kStages - 1), 0, Int<0>{});
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_block(Int<ks & 1>{}, swc);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
   };
 
@@ -1244,14 +1255,28 @@ mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const flo
   return MO_OK;
 }
 
-template <typename T, int BM, int WM, int WN>
+// Below this many tiles a 128-tile launch uses 8 waves per tile; the
+// environment variable MO_NS_FEW_TILES overrides it (0 = always 4 waves), for
+// tuning and for tests of both kernels.
+constexpr int64_t kFewTiles = 512;
+int64_t few_tiles() {
+  const char* e = std::getenv("MO_NS_FEW_TILES");
+  if (!e || !*e) return kFewTiles;
+  char* end = nullptr;
+  const long long v = std::strtoll(e, &end, 10);
+  return (end && *end == '\0' && v >= 0) ? static_cast<int64_t>(v) : kFewTiles;
+}
+
+template <typename T, int BM, int WM, int WN, int ST = 4, int SRB = 64>
 void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
                        float c1, int has_e, float cd, hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
   if (bk)
-    k_ns_gemm<T, BM, BM, WM, WN, 2, true><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e, cd);
+    k_ns_gemm<T, BM, BM, WM, WN, 2, true, ST, SRB><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1,
+                                                                       has_e, cd);
   else
-    k_ns_gemm<T, BM, BM, WM, WN, 2, false><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e, cd);
+    k_ns_gemm<T, BM, BM, WM, WN, 2, false, ST, SRB><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1,
+                                                                        has_e, cd);
 }
 
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
@@ -1269,7 +1294,17 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
       launch_gemm_shape<float, 256, 2, 4>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
                                           has_e, cd, st);
   } else if (tile == 128) {
-    if (elem == 2)
+    // A launch with few tiles leaves most CUs idle and lasts as long as one
+    // tile's K loop, whose length is set by the fixed cost of each K slab
+    // (wait, barrier, fragment reads): split each tile over 8 waves of
+    // 64 x 32 instead of 4 of 64 x 64, and take 64-deep slabs (128-byte
+    // rows; 4 stages, 128 KiB) instead of 32-deep ones.  15-20% faster on the
+    // single-matrix sweeps; 8 stages of 32-deep slabs were slower.
+    if (elem == 2 && ntiles < few_tiles())
+      launch_gemm_shape<uint16_t, 128, 2, 4, 4, 128>(probs, n, grid, bk,
+                                                     static_cast<uint16_t*>(pool), c0, c1, has_e,
+                                                     cd, st);
+    else if (elem == 2)
       launch_gemm_shape<uint16_t, 128, 2, 2>(probs, n, grid, bk, static_cast<uint16_t*>(pool), c0,
                                              c1, has_e, cd, st);
     else

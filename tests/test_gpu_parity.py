@@ -105,9 +105,14 @@ def _ns_case(shapes, dtype, seed, std=1.0):
     return mats, [to_dev(m, dtype) for m in mats]
 
 
+@pytest.mark.parametrize("few_tiles", ["default", "0"])
 @pytest.mark.parametrize("precision", ["bf16", "fp32"])
 @pytest.mark.parametrize("kind", ["cubic", "quintic"])
-def test_ns_parity_ragged_shapes(precision, kind):
+def test_ns_parity_ragged_shapes(precision, kind, few_tiles, monkeypatch):
+    # these launches have few tiles, so bf16 uses the 8-wave 128 x 128
+    # kernels; MO_NS_FEW_TILES=0 forces the 4-wave ones
+    if few_tiles != "default":
+        monkeypatch.setenv("MO_NS_FEW_TILES", few_tiles)
     dtype = "bf16" if precision == "bf16" else "f32"
     mats, dev = _ns_case(NS_SHAPES, dtype, 21)
     coeffs = wl.coeff_table(kind)
