@@ -169,6 +169,22 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 // lgkmcnt(0), expcnt not waited on.
 constexpr int vm_wait_imm(int n) { return (n & 15) | (((n >> 4) & 3) << 14) | (7 << 4); }
 
+// Wait until at most min(younger, K) groups of INST vector-memory
+// instructions are outstanding: an if / else chain tested from the largest
+// count down, so the common case (younger >= K) takes one compare.
+template <int K, int INST>
+__device__ __forceinline__ void wait_vm_groups(int younger) {
+  static_assert(K * INST <= 63, "vmcnt immediate");
+  if constexpr (K == 0) {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+  } else {
+    if (younger >= K)
+      __builtin_amdgcn_s_waitcnt(vm_wait_imm(K * INST));
+    else
+      wait_vm_groups<K - 1, INST>(younger);
+  }
+}
+
 // Buffer resource (raw, stride 0) over `bytes` bytes from `base`; accesses
 // past the range read zero instead of faulting.
 __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
@@ -651,13 +667,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   // counter, kInst per slab, completing in order) and its LDS reads are done
   // (the stage they read is refilled after the next barrier).
   auto wait_slab = [](int younger) __attribute__((always_inline)) {
-    constexpr int kMaxYoung = C::kStages - 2;
-    static_assert(kMaxYoung * C::kInst <= 63, "vmcnt immediate");
-    const int y = younger < kMaxYoung ? younger : kMaxYoung;
-    static_for<0, kMaxYoung + 1>([&](auto yc) {
-      constexpr int k = decltype(yc)::value;
-      if (y == k) __builtin_amdgcn_s_waitcnt(vm_wait_imm(k * C::kInst));
-    });
+    wait_vm_groups<C::kStages - 2, C::kInst>(younger);
   };
   // Software pipeline over K slabs (kSub = 2 or 4 substeps of 16 k), two
   // fragment register sets used in turn, kStages LDS stages with the loads of

@@ -37,15 +37,15 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def workload_by_name(name: str):
+def workload_by_name(name: str, coeffs: str = "cubic"):
     import workloads as wl
     table = {
         "dense_decoder_1p2b": lambda: wl.dense_decoder(),
         "dense_decoder_1p2b_fused_normuon": lambda: wl.dense_decoder(fused_gate_up=True,
                                                                      normuon=True),
         "head_batched_mla_kda": lambda: wl.head_batched(),
-        "ns_sweep_1024x1024": lambda: wl.ns_sweep(1024, 1024, "cubic"),
-        "ns_sweep_4096x1024": lambda: wl.ns_sweep(4096, 1024, "cubic"),
+        "ns_sweep_1024x1024": lambda: wl.ns_sweep(1024, 1024, coeffs),
+        "ns_sweep_4096x1024": lambda: wl.ns_sweep(4096, 1024, coeffs),
     }
     return table[name]()
 
@@ -193,10 +193,10 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this library runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
-        log("multi-GPU runs are not part of this build: the sharding design is documented "
-            "but only the one-GPU path is implemented")
+        log("multi-GPU runs are not implemented: the sharding design is documented "
+            "but only the one-GPU path exists")
         return 2
 
     import torch
@@ -208,7 +208,7 @@ def main() -> int:
         log("no HIP device visible")
         return 1
     torch.cuda.set_device(0)
-    w = workload_by_name(args.workload)
+    w = workload_by_name(args.workload, args.coeffs)
     coeffs = wl.coeff_table(args.coeffs, w.ns_steps)
     log(f"building {w.key} on {torch.cuda.get_device_name(0)}")
     plan, ents, routes = build_plan(w, coeffs, args.precision, w.normuon)
