@@ -106,6 +106,8 @@ SIGNATURES = [
     ("mo_grouped_step", i32, [vp, C.POINTER(StepArgs), vp, C.c_size_t, vp]),
     ("mo_diag_copy", i32, [vp, vp, i64, vp]),
     ("mo_plan_ns_output", i32, [vp, i32, vp, C.POINTER(vp), C.POINTER(i64), C.POINTER(i32)]),
+    ("mo_plan_keep_ns_output", i32, [vp, i32]),
+    ("mo_plan_fuses_update", i32, [vp]),
     ("mo_abi_struct_size", C.c_size_t, [i32]),
     ("mo_timing_enable", i32, [i32]),
     ("mo_timing_read", i32, [i32, C.POINTER(C.c_double), C.POINTER(i64)]),

@@ -338,6 +338,17 @@ class Plan:
         arr = (C.c_int32 * max(self.n, 1))(*[int(s) for s in steps])
         L.check("mo_plan_set_steps", L.lib().mo_plan_set_steps(self._h, arr, self.n))
 
+    def keep_ns_output(self, keep: bool = True) -> None:
+        """Keep each step's Newton-Schulz output O in the workspace (for
+        ns_output) instead of applying the update inside the last Newton-Schulz
+        launch; the weights are the same bits either way."""
+        L.check("mo_plan_keep_ns_output", L.lib().mo_plan_keep_ns_output(self._h, int(bool(keep))))
+
+    def fuses_update(self) -> bool:
+        """True if the next step applies the update inside the last
+        Newton-Schulz launch."""
+        return bool(L.lib().mo_plan_fuses_update(self._h))
+
     def ns_output(self, slice_index: int, workspace: Optional[torch.Tensor] = None
                   ) -> torch.Tensor:
         """View into the workspace of one slice's Newton-Schulz output O after

@@ -200,7 +200,8 @@ mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const flo
   if ((s = launch_ns_stats(dprep, n, L.prep_tiles, partials, st)) != MO_OK) return s;
   if ((s = launch_ns_scale(dprep, n, partials, scale, st)) != MO_OK) return s;
   if ((s = launch_ns_prep(dprep, n, L.prep_tiles, scale, pool, L.elem, st)) != MO_OK) return s;
-  if ((s = ns_run_iterations(L, base + W.tab, W.tabs, pool, scale, coeffs, steps, st)) != MO_OK)
+  if ((s = ns_run_iterations(L, base + W.tab, W.tabs, pool, scale, coeffs, steps, nullptr, 0.f,
+                             st)) != MO_OK)
     return s;
   return launch_ns_final(reinterpret_cast<const FinalItem*>(base + W.fin), n, rows, pool, L.elem,
                          st);

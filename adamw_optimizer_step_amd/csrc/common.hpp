@@ -138,6 +138,59 @@ __device__ __forceinline__ void store8(void* p, int64_t i, int32_t dt, const flo
 
 __device__ __forceinline__ float4 ld_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
+// Muon weight update of one element, W (1 - lr wd) - lr scale O: one rounded
+// product W * decay, then one fused multiply-add.  Every kernel that applies
+// the update uses this exact sequence, so the separate pass and the update
+// fused into the last Newton-Schulz launch give identical bits.
+__device__ __forceinline__ float muon_apply(float w, float o, float decay, float coef) {
+  return __builtin_fmaf(-coef, o, w * decay);
+}
+
+// 8 consecutive weights (dtype dt, 16-byte aligned) as raw bits: one
+// streaming 16-byte load for bf16, two for fp32.  Loaded ahead of the
+// updates below so that a thread's loads are all in flight at once.
+struct W8 {
+  u32x4_t a, b;
+};
+__device__ __forceinline__ W8 load_w8(const void* w, int64_t i, int32_t dt) {
+  W8 r;
+  if (dt == MO_F32) {
+    const u32x4_t* q = reinterpret_cast<const u32x4_t*>(static_cast<const float*>(w) + i);
+    r.a = ldv<u32x4_t, true>(q);
+    r.b = ldv<u32x4_t, true>(q + 1);
+  } else {
+    r.a = ldv<u32x4_t, true>(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(w) + i));
+    r.b = u32x4_t{0u, 0u, 0u, 0u};
+  }
+  return r;
+}
+
+// The update on those 8 weights from 8 bf16 values of O packed in `o`, low
+// half first; the result is stored (streaming) in the weights' dtype.
+__device__ __forceinline__ void apply_w8(void* w, int64_t i, int32_t dt, const W8& raw,
+                                         const u32x4_t& o, float decay, float coef) {
+  float wf[8];
+  if (dt == MO_F32) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      wf[k] = __uint_as_float(raw.a[k]);
+      wf[4 + k] = __uint_as_float(raw.b[k]);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      wf[2 * k] = __uint_as_float(raw.a[k] << 16);
+      wf[2 * k + 1] = __uint_as_float(raw.a[k] & 0xffff0000u);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    wf[2 * k] = muon_apply(wf[2 * k], __uint_as_float(o[k] << 16), decay, coef);
+    wf[2 * k + 1] = muon_apply(wf[2 * k + 1], __uint_as_float(o[k] & 0xffff0000u), decay, coef);
+  }
+  store8<true>(w, i, dt, wf);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

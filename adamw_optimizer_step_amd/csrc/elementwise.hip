@@ -314,14 +314,14 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowSeg* __restrict__ se
       load8<true>(sg.o, obase + c0, sg.o_dt, o);
       load8<true>(sg.w, wbase + c0, sg.w_dt, w);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) w[k] = w[k] * decay - coef * o[k];
+      for (int k = 0; k < 8; ++k) w[k] = muon_apply(w[k], o[k], decay, coef);
       store8<true>(sg.w, wbase + c0, sg.w_dt, w);
     }
   } else {
     for (int c = lane; c < cols; c += 64) {
       const float o = load_as_f32(sg.o, obase + c, sg.o_dt);
       const float w = load_as_f32(sg.w, wbase + c, sg.w_dt);
-      store_from_f32(sg.w, wbase + c, sg.w_dt, w * decay - coef * o);
+      store_from_f32(sg.w, wbase + c, sg.w_dt, muon_apply(w, o, decay, coef));
     }
   }
 }

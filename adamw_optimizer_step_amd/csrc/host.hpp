@@ -84,8 +84,12 @@ mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st)
 
 // Enqueue the Newton-Schulz iterations on the prepared pool.
 // `scale` holds the per-slice normalisation scales (the prep kernel's).
+// wt (nullable): per-slice weight rows; the last iteration then applies the
+// Muon update with learning rate lr to them instead of writing O (bf16 pool,
+// every slice eligible; see fused_apply_ok).
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
-                            const float* scale, const float* coeffs, int steps, hipStream_t st);
+                            const float* scale, const float* coeffs, int steps, const RowSeg* wt,
+                            float lr, hipStream_t st);
 
 // True while kernel timing (mo_timing_enable) is on.
 bool timing_enabled();

@@ -128,6 +128,10 @@ struct GemmProb {
   int32_t tiles_m, tiles_n;
   int32_t sym;             // only tiles (i <= j); mirror written through ct
   int32_t start;           // first tile of this problem
+  int32_t item;            // slice index (the last update of a slice), else -1: with a
+                           // weight table, the launch applies the Muon update to that
+                           // slice's weights instead of writing its output
+  int32_t pad;
 };
 
 struct FinalItem {         // NS output copy (stored orientation)
@@ -166,15 +170,22 @@ struct NsCoeffTable {
   float a[MO_NS_MAX_STEPS], b[MO_NS_MAX_STEPS], c[MO_NS_MAX_STEPS];
 };
 constexpr int kSmallS = 128;
+// wt (nullable): per-slice weight rows (the RowSeg of the slice index); the
+// last iteration then applies W <- W (1 - lr wd) - lr scale O to them instead
+// of writing O.  Requires bf16 O, cols % 8 == 0 and 16-byte aligned rows.
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
-                          const float* scale, const float* coeffs, int steps, hipStream_t st);
+                          const float* scale, const float* coeffs, int steps, const RowSeg* wt,
+                          float lr, hipStream_t st);
 
 // C = c1 A B (+ c0 E) (+ cd I on diagonal tiles).  bk = 1: B is read K-major
 // (K x N row-major) through LDS transpose reads; no E term, and the output
 // goes straight from registers to c (or, transposed, to ct).
+// wt (nullable, bf16 with bk = 1 only): problems with item >= 0 apply the Muon
+// update to the weights of slice `item` (as launch_ns_small) instead of
+// writing their output.
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
-                         hipStream_t st);
+                         const RowSeg* wt, float lr, hipStream_t st);
 mo_status launch_ns_final(const FinalItem* items, int n, int64_t total_rows, const void* pool,
                           int elem, hipStream_t st);
 

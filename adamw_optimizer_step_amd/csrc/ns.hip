@@ -469,7 +469,9 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 // (i & 3) of the 4-element words addressed by lanes 4e + (i >> 2), e = 0..3.
 // With lane j pointing at row k0 + (j >> 2), columns n0 + 4 (j & 3) .. + 3 of
 // a K x N row-major array, lane i therefore gets column n0 + i, rows
-// k0 .. k0 + 3: an MFMA B fragment piece read from K-major data.
+// k0 .. k0 + 3: an MFMA B fragment piece read from K-major data.  A lane's
+// result depends on the addresses of other lanes, so all 16 lanes of a group
+// must execute it (never under a lane-dependent branch).
 __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
       (lds_bf16x4*)((__attribute__((address_space(3))) char*)(p)));
@@ -479,7 +481,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK, int ST, int SRB>
 __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1,
-    int has_e, float cd) {
+    int has_e, float cd, const RowSeg* __restrict__ wt, float lr) {
   using C = GemmCfg<T, BM, BN, WM, WN, BK, ST, SRB>;
   constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
@@ -752,6 +754,36 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
                                       (c & 7) * 2) = u;
           }
       __syncthreads();
+      if (wt != nullptr && pr.item >= 0) {
+        // last update of a slice: apply the Muon step to its weights from the
+        // staged (bf16-rounded) output tile, rows and columns in the weight's
+        // stored orientation, clipped to the slice's real extent
+        // (every weight load of the thread is issued before the first update)
+        const RowSeg w = wt[pr.item];
+        const int orow0 = to_c ? ti * BM : tj * BN, ocol0 = to_c ? tj * BN : ti * BM;
+        const float decay = 1.f - lr * w.wd, coef = lr * w.scale;
+        constexpr int NP = BM * NCH / NT;
+        W8 wr[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int idx = p * NT + tid, r = idx / NCH, c = idx % NCH;
+          const int orow = orow0 + r, ocol = ocol0 + c * 8;
+          if (orow < w.rows && ocol < w.cols)
+            wr[p] = load_w8(w.w, static_cast<int64_t>(orow) * w.ld_w + ocol, w.w_dt);
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int idx = p * NT + tid, r = idx / NCH, c = idx % NCH;
+          const int orow = orow0 + r, ocol = ocol0 + c * 8;
+          if (orow < w.rows && ocol < w.cols) {
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(smem + r * RB + (((c ^ r) & (NCH - 1)) << 4));
+            apply_w8(w.w, static_cast<int64_t>(orow) * w.ld_w + ocol, w.w_dt, wr[p], v, decay,
+                     coef);
+          }
+        }
+        return;
+      }
       T* const g = to_c ? pool + pr.c_off + static_cast<size_t>(ti * BM) * pr.ldc + tj * BN
                         : pool + pr.ct_off + static_cast<size_t>(tj * BN) * pr.ldct + ti * BM;
       const size_t ld = to_c ? pr.ldc : pr.ldct;
@@ -983,7 +1015,9 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
                                                             uint16_t* __restrict__ pool,
                                                             const PrepItem* __restrict__ items,
                                                             const float* __restrict__ scale,
-                                                            NsCoeffTable cf, int steps) {
+                                                            NsCoeffTable cf, int steps,
+                                                            const RowSeg* __restrict__ wt,
+                                                            float lr) {
   __shared__ __attribute__((aligned(16))) char smem[kSmTile * (2 + kSmStages)];
   char* const Ps = smem;             // P (A operand of the update)
   char* const Xn = smem + kSmTile;   // the new block X'_b (and A in a quintic step)
@@ -1166,7 +1200,66 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
         }
       __syncthreads();   // B2: X'_b complete in LDS
       const bool last = pass == steps;
-      if (last && pr.tall) {
+      if (last && wt != nullptr) {
+        // apply the Muon step to the slice's weights (stored orientation,
+        // clipped to the real extent) instead of writing O
+        const RowSeg w = wt[pr.item];
+        const float decay = 1.f - lr * w.wd, coef = lr * w.scale;
+        // (one chunk at a time: holding all four weight chunks of a thread
+        // in registers would spill in this kernel)
+        if (pr.tall) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int T = q * 32 + wv * 4 + g16;
+            const int n0 = 16 * (T & 7), k0 = 8 * (T >> 3);
+            // transpose reads exchange data between the lanes of a 16-lane
+            // group: every lane takes part, whatever its row
+            const u32x2 lo = lds_read_tr16(Xn + sm_off(k0 + (j16 >> 2), n0 + 4 * (j16 & 3)));
+            const u32x2 hi = lds_read_tr16(Xn + sm_off(k0 + 4 + (j16 >> 2), n0 + 4 * (j16 & 3)));
+            const int orow = b * kSmallS + n0 + j16;
+            if (orow < w.rows && k0 < w.cols) {
+              const int64_t at = static_cast<int64_t>(orow) * w.ld_w + k0;
+              apply_w8(w.w, at, w.w_dt, load_w8(w.w, at, w.w_dt),
+                       u32x4{lo[0], lo[1], hi[0], hi[1]}, decay, coef);
+            }
+          }
+        } else if (w.w_dt == MO_BF16) {
+          W8 wr[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int id = q * kSmThreads + tid;
+            const int row = id >> 4, c = id & 15;
+            const int ocol = b * kSmallS + c * 8;
+            if (row < w.rows && ocol < w.cols)
+              wr[q] = load_w8(w.w, static_cast<int64_t>(row) * w.ld_w + ocol, MO_BF16);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int id = q * kSmThreads + tid;
+            const int row = id >> 4, c = id & 15;
+            const int ocol = b * kSmallS + c * 8;
+            if (row < w.rows && ocol < w.cols)
+              apply_w8(w.w, static_cast<int64_t>(row) * w.ld_w + ocol, MO_BF16, wr[q],
+                       *reinterpret_cast<const u32x4*>(Xn + row * 256 +
+                                                       (((c ^ sm_swz(row)) & 15) << 4)),
+                       decay, coef);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int id = q * kSmThreads + tid;
+            const int row = id >> 4, c = id & 15;
+            const int ocol = b * kSmallS + c * 8;
+            if (row < w.rows && ocol < w.cols) {
+              const int64_t at = static_cast<int64_t>(row) * w.ld_w + ocol;
+              apply_w8(w.w, at, w.w_dt, load_w8(w.w, at, w.w_dt),
+                       *reinterpret_cast<const u32x4*>(Xn + row * 256 +
+                                                       (((c ^ sm_swz(row)) & 15) << 4)),
+                       decay, coef);
+            }
+          }
+        }
+      } else if (last && pr.tall) {
         // stored orientation: out[b * 128 + n][k] = X'_b[k][n], ld 128
         uint16_t* out = (steps & 1) ? X1 : X0;
 #pragma unroll
@@ -1278,21 +1371,24 @@ int64_t few_tiles() {
 
 template <typename T, int BM, int WM, int WN, int ST = 4, int SRB = 64>
 void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
-                       float c1, int has_e, float cd, hipStream_t st) {
+                       float c1, int has_e, float cd, const RowSeg* wt, float lr,
+                       hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
   if (bk)
     k_ns_gemm<T, BM, BM, WM, WN, 2, true, ST, SRB><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1,
-                                                                       has_e, cd);
+                                                                       has_e, cd, wt, lr);
   else
     k_ns_gemm<T, BM, BM, WM, WN, 2, false, ST, SRB><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1,
-                                                                        has_e, cd);
+                                                                        has_e, cd, wt, lr);
 }
 
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
-                         hipStream_t st) {
+                         const RowSeg* wt, float lr, hipStream_t st) {
   if (ntiles <= 0) return MO_OK;
   if (bk && has_e) return fail(MO_EINVAL, "the K-major-B GEMM takes no E term");
+  if (wt && (!bk || elem != 2))
+    return fail(MO_EINVAL, "the fused weight update needs the bf16 K-major-B GEMM");
   KTimer tm(MO_KC_NS_GEMM, st);
   const dim3 grid(static_cast<unsigned>(ntiles));
   if (tile == 256) {
@@ -1303,10 +1399,10 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     if (elem == 2)
       launch_gemm_shape<uint16_t, 256, 2, 4, 2, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, st);
+                                                     cd, wt, lr, st);
     else
       launch_gemm_shape<float, 256, 2, 4>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, cd, st);
+                                          has_e, cd, wt, lr, st);
   } else if (tile == 128) {
     // A launch with few tiles leaves most CUs idle and lasts as long as one
     // tile's K loop, whose length is set by the fixed cost of each K slab
@@ -1317,14 +1413,14 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     if (elem == 2 && ntiles < few_tiles())
       launch_gemm_shape<uint16_t, 128, 2, 4, 4, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, st);
+                                                     cd, wt, lr, st);
     else if (elem == 2)  // 2 stages of 64-deep slabs, as for 256 x 256 tiles (64 KiB)
       launch_gemm_shape<uint16_t, 128, 2, 2, 2, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, st);
+                                                     cd, wt, lr, st);
     else
       launch_gemm_shape<float, 128, 2, 2>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, cd, st);
+                                          has_e, cd, wt, lr, st);
   } else {
     return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);
   }
@@ -1333,7 +1429,8 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
 }
 
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
-                          const float* scale, const float* coeffs, int steps, hipStream_t st) {
+                          const float* scale, const float* coeffs, int steps, const RowSeg* wt,
+                          float lr, hipStream_t st) {
   if (n <= 0) return MO_OK;
   if (steps < 1 || steps > MO_NS_MAX_STEPS) return fail(MO_EINVAL, "bad step count %d", steps);
   NsCoeffTable cf;
@@ -1345,7 +1442,7 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
   }
   KTimer tm(MO_KC_NS_SMALL, st);
   k_ns_small<<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
-      probs, static_cast<uint16_t*>(pool), items, scale, cf, steps);
+      probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr);
   MO_LAUNCH_CHECK("k_ns_small");
   return MO_OK;
 }

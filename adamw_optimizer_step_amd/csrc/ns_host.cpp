@@ -20,6 +20,7 @@ GemmProb make_prob(int64_t a, int64_t b, int64_t c, int64_t ct, int64_t e, int32
   p.lda = lda; p.ldb = ldb; p.ldc = ldc; p.ldct = ldct; p.lde = lde;
   p.K = K; p.tiles_m = tm; p.tiles_n = tn; p.sym = sym;
   p.start = static_cast<int32_t>(start);
+  p.item = -1;
   return p;
 }
 
@@ -140,6 +141,7 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       B.fin[q].push_back(tall ? make_prob(p, xc, -1, xn, -1, sp, lp, 0, sp, 0, sp, ts, tl, 0,
                                           B.upd_tiles)
                               : B.upd[q].back());
+      B.fin[q].back().item = i;
     }
     if (need_a) {
       // P = b A + c A A; A is exactly symmetric, so it is its own transposed
@@ -210,13 +212,14 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
 }
 
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
-                            const float* scale, const float* coeffs, int steps, hipStream_t st) {
+                            const float* scale, const float* coeffs, int steps, const RowSeg* wt,
+                            float lr, hipStream_t st) {
   auto tab = [dtab](size_t off) { return reinterpret_cast<const GemmProb*>(dtab + off); };
   if (!L.small.empty()) {
     mo_status s = launch_ns_small(reinterpret_cast<const SmallProb*>(dtab + T.small),
                                   static_cast<int>(L.small.size()), pool,
                                   reinterpret_cast<const PrepItem*>(dtab + T.prep), scale, coeffs,
-                                  steps, st);
+                                  steps, wt, lr, st);
     if (s != MO_OK) return s;
   }
   for (int k = 0; k < steps; ++k) {
@@ -233,13 +236,13 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       mo_status s;
       if (cubic_step) {
         s = launch_ns_gemm(tab(tb.gram_p[q]), n, B.gram_tiles, B.tile, 0, pool, L.elem, 0.f, b, 0,
-                           a, st);
+                           a, nullptr, 0.f, st);
       } else {
         s = launch_ns_gemm(tab(tb.gram_a[q]), n, B.gram_tiles, B.tile, 0, pool, L.elem, 0.f, 1.f,
-                           0, 0.f, st);
+                           0, 0.f, nullptr, 0.f, st);
         if (s == MO_OK)
           s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, B.tile, 0, pool, L.elem, b, c, 1,
-                             a, st);
+                             a, nullptr, 0.f, st);
       }
       if (s != MO_OK) return s;
     }
@@ -248,9 +251,10 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const NsBucket& B = L.buckets[i];
       if (B.upd[q].empty()) continue;
       const NsBucketTables& tb = T.b[i];
-      const size_t off = k + 1 == steps ? tb.fin[q] : tb.upd[q];
-      mo_status s = launch_ns_gemm(tab(off), static_cast<int>(B.upd[q].size()), B.upd_tiles,
-                                   B.tile, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, st);
+      const bool fin = k + 1 == steps;
+      mo_status s = launch_ns_gemm(tab(fin ? tb.fin[q] : tb.upd[q]),
+                                   static_cast<int>(B.upd[q].size()), B.upd_tiles, B.tile, 1, pool,
+                                   L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr, lr, st);
       if (s != MO_OK) return s;
     }
   }

@@ -51,6 +51,12 @@ struct mo_plan {
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
   bool dirty = true;
   int32_t tdelta = 0;
+  // Muon update fused into the last Newton-Schulz launch (no O in the
+  // workspace, no separate row pass): possible for every active slice
+  // (fuse_ok), unless the caller keeps O for mo_plan_ns_output
+  bool fuse_ok = false;
+  bool keep_ns_output = false;
+  bool last_fused = false;
 };
 
 namespace {
@@ -103,6 +109,15 @@ mo_status build_plan(mo_plan* P) {
         ++P->n_adam;
       }
     }
+  }
+  // The fused update needs the bf16 pool, no NorMuon (whose row statistics
+  // span whole rows) and 16-byte weight chunks: cols % 8 == 0 and aligned rows.
+  P->fuse_ok = P->ddt == MO_BF16 && !hp.normuon;
+  for (const auto& a : P->active) {
+    const mo_param& p = P->params[a.param];
+    const int64_t es = static_cast<int64_t>(dtype_size(p.dtype));
+    const char* w = static_cast<const char*>(p.param) + a.off * a.cols * es;
+    if (a.cols % 8 != 0 || (a.cols * es) % 16 != 0 || !aligned16(w)) P->fuse_ok = false;
   }
   // momentum blocks per active slice (one statistics partial per block)
   for (const auto& a : P->active) P->mom_blocks += ceil_div(a.rows * a.cols, kEltPerBlock);
@@ -308,6 +323,17 @@ mo_status mo_plan_set_steps(mo_plan* plan, const int32_t* steps, int32_t n) {
   return MO_OK;
 }
 
+mo_status mo_plan_keep_ns_output(mo_plan* plan, int32_t keep) {
+  clear_error();
+  if (!plan) return fail(MO_EINVAL, "NULL plan");
+  plan->keep_ns_output = keep != 0;
+  return MO_OK;
+}
+
+int32_t mo_plan_fuses_update(const mo_plan* plan) {
+  return plan && plan->fuse_ok && !plan->keep_ns_output ? 1 : 0;
+}
+
 mo_status mo_plan_ns_output(const mo_plan* P, int32_t slice, const void* ws, void** o,
                             int64_t* ld, int32_t* dtype) {
   clear_error();
@@ -316,6 +342,10 @@ mo_status mo_plan_ns_output(const mo_plan* P, int32_t slice, const void* ws, voi
     return fail(MO_EINVAL, "slice %d out of range", slice);
   if (P->uploaded_ws != ws || P->tdelta == 0)
     return fail(MO_EINVAL, "no grouped step has run on this workspace");
+  if (P->last_fused)
+    return fail(MO_EINVAL,
+                "the last grouped step applied the update inside the Newton-Schulz launch and "
+                "kept no output: call mo_plan_keep_ns_output(plan, 1) before stepping");
   const int32_t param = P->slices[slice].param;
   if (!P->params[param].grad) return fail(MO_EINVAL, "slice %d: param has no gradient", slice);
   // active slices are the slices of params with a gradient, in the same order
@@ -407,16 +437,23 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     float coeffs[3 * MO_NS_MAX_STEPS];
     for (int k = 0; k < hp.ns_steps; ++k)
       for (int j = 0; j < 3; ++j) coeffs[3 * k + j] = hp.ns_coeffs[k][j];
+    // the row table is the weight target of the fused update and the input
+    // of the separate row pass
+    const RowSeg* drows = reinterpret_cast<const RowSeg*>(P->dtab + P->tab_rows);
+    const bool fuse = P->fuse_ok && !P->keep_ns_output;
     if ((s = ns_run_iterations(P->ns, dns, P->nst, pool,
                                reinterpret_cast<const float*>(base + P->ws_scale), coeffs,
-                               hp.ns_steps, st)) != MO_OK)
+                               hp.ns_steps, fuse ? drows : nullptr, muon_lr, st)) != MO_OK)
       return s;
-    RowSeg none;
-    std::memset(&none, 0, sizeof(none));
-    if ((s = launch_rows(hp.normuon ? kRowNormUpdate : kRowUpdate,
-                         reinterpret_cast<const RowSeg*>(P->dtab + P->tab_rows), nsl, none,
-                         P->total_rows, muon_lr, hp.normuon_beta2, hp.normuon_eps, st)) != MO_OK)
-      return s;
+    if (!fuse) {
+      RowSeg none;
+      std::memset(&none, 0, sizeof(none));
+      if ((s = launch_rows(hp.normuon ? kRowNormUpdate : kRowUpdate, drows, nsl, none,
+                           P->total_rows, muon_lr, hp.normuon_beta2, hp.normuon_eps,
+                           st)) != MO_OK)
+        return s;
+    }
+    P->last_fused = fuse;
   }
   if (fork) MO_HIP_TRY(hipStreamWaitEvent(st, P->ev_join, 0));
   for (size_t i = 0; i < P->params.size(); ++i)

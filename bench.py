@@ -50,7 +50,7 @@ def workload_by_name(name: str, coeffs: str = "cubic"):
     return table[name]()
 
 
-def ns_work(slices, coeffs, elem):
+def ns_work(slices, coeffs, elem, w_elem=None):
     """Algorithmic Newton-Schulz work per step, from the per-slice unit figures
     (s = short side, l = long side of each slice, N iterations):
     * dense flops 4 s^2 l per iteration (A = X X^T and P X), + 2 s^3 for a
@@ -58,12 +58,16 @@ def ns_work(slices, coeffs, elem):
     * executed flops with the symmetric Gram: 3 s^2 l (+ s^3) per iteration;
     * algorithmic HBM bytes when X does not stay on chip: one read of X0 for
       the first Gram, then a read of X and a write of X' per iteration:
-      elem * s * l * (2 N + 1).
+      elem * s * l * (2 N + 1); with the Muon update fused into the last
+      launch (w_elem = weight element size) the last write of O is replaced
+      by a read and a write of W: + (2 w_elem - elem) * s * l.
     Returns (dense_flops, executed_flops, bytes)."""
     dense = exe = byt = 0.0
     for r, c in slices:
         s, l = float(min(r, c)), float(max(r, c))
         byt += elem * s * l * (2 * len(coeffs) + 1)
+        if w_elem is not None:
+            byt += (2 * w_elem - elem) * s * l
         for a, b, cc in coeffs:
             dense += 4.0 * s * s * l
             exe += 3.0 * s * s * l
@@ -185,6 +189,9 @@ def main() -> int:
     ap.add_argument("--coeffs", default="cubic", choices=["cubic", "quintic"])
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--timing-steps", type=int, default=3)
+    ap.add_argument("--separate-update", action="store_true",
+                    help="keep O and apply the Muon update in its own row pass instead of "
+                         "inside the last Newton-Schulz launch")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=1024, metavar="MIB",
@@ -212,6 +219,8 @@ def main() -> int:
     coeffs = wl.coeff_table(args.coeffs, w.ns_steps)
     log(f"building {w.key} on {torch.cuda.get_device_name(0)}")
     plan, ents, routes = build_plan(w, coeffs, args.precision, w.normuon)
+    if args.separate_update:
+        plan.keep_ns_output(True)
     ws = plan.workspace(torch.device("cuda"))
     torch.cuda.synchronize()
     log(f"plan ready: {plan.workspace_bytes / 2**30:.2f} GiB workspace, "
@@ -249,6 +258,8 @@ def main() -> int:
     L.check("timing", lib.mo_timing_enable(0))
 
     # algorithmic work
+    fused = plan.fuses_update()
+    welt = w.params[0].dtype == "bf16" and 2 or 4
     slices = [(r, c) for _, _, r, c in plan.slices()]
     elem = 2 if args.precision == "bf16" else 4
     muon_elems = sum(r * c for r, c in slices)
@@ -263,7 +274,7 @@ def main() -> int:
     if cands:
         kname, part = max(cands, key=lambda x: kern[x[0]]["ms_per_step"])
         g = kern[kname]
-        dense, exe, nbytes = ns_work(part, coeffs, elem)
+        dense, exe, nbytes = ns_work(part, coeffs, elem, welt if fused else None)
         n = g["launches_per_step"]
         t = g["avg_launch_ms"] * 1e-3
         # the binding roof is the one with the longer ideal time
@@ -354,6 +365,7 @@ def main() -> int:
         "config": {"workload": w.key, "muon_params": muon_elems, "adamw_params": adam_elems,
                    "muon_slices": len(slices), "ns_steps": len(coeffs), "coeffs": args.coeffs,
                    "ns_precision": args.precision, "normuon": bool(w.normuon),
+                   "fused_update": fused,
                    "param_dtype": w.params[0].dtype, "state_dtype": "f32"},
         "roofline": roofline,
         "ns_dense_tflops_pct_of_peak": (round(100 * roofline["dense_tflops"] / peak, 2)

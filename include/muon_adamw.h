@@ -336,6 +336,20 @@ mo_status mo_grouped_step(mo_plan* plan, const mo_step_args* args, void* ws, siz
  * gradient, or a plan that has not run a step on `ws`. */
 mo_status mo_plan_ns_output(const mo_plan* plan, int32_t slice, const void* ws, void** o,
                             int64_t* ld, int32_t* dtype);
+/* Whether grouped steps keep O in the workspace.  By default (keep = 0) a
+ * plan whose every active slice allows it applies the Muon update
+ * W <- W (1 - lr wd) - lr scale O (the Muon post on OMN, update paragraph)
+ * inside the last Newton-Schulz launch, from the same bf16-rounded O and
+ * with the same arithmetic as the separate row pass, so the weights are
+ * bit-identical either way; O is then not stored and mo_plan_ns_output
+ * fails (MO_EINVAL) for that step.  Allowed when the NS precision is bf16,
+ * NorMuon is off, and every slice has cols % 8 == 0 with 16-byte aligned
+ * weight rows.  keep = 1 always runs the separate pass and keeps O.
+ * Host only; takes effect from the next step.  MO_EINVAL for a NULL plan. */
+mo_status mo_plan_keep_ns_output(mo_plan* plan, int32_t keep);
+/* 1 if the next grouped step will apply the update inside the last
+ * Newton-Schulz launch (see mo_plan_keep_ns_output), else 0 (also for NULL). */
+int32_t mo_plan_fuses_update(const mo_plan* plan);
 
 /* ------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel launch of this

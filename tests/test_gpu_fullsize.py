@@ -41,11 +41,15 @@ def _gpu():
 
 def _run(w, coeffs_kind, precision, sample_params):
     """Build the benchmark's plan for `w`, keep host copies of what the checks
-    need, run one step.  Returns (plan, entries, routes, before, T_gpu)."""
+    need, run one step with O kept in the workspace.  Returns (plan, entries,
+    routes, before, T_gpu); before["muon_w0"] holds device copies of every
+    Muon weight as it was before the step."""
     coeffs = wl.coeff_table(coeffs_kind, w.ns_steps)
     plan, ents, routes = bench.build_plan(w, coeffs, precision, w.normuon)
+    plan.keep_ns_output(True)      # the checks read O from the workspace
     ws = plan.workspace(torch.device("cuda"))
-    before = {}
+    before = {"muon_w0": {i: e["param"].clone() for i, (e, r) in enumerate(zip(ents, routes))
+                          if r[0] == L.MO_ALG_MUON}}
     for i in sample_params:
         before[i] = {"W": f64(ents[i]["param"]), "G": f64(ents[i]["grad"])}
     norm = torch.zeros(1, dtype=torch.float64, device="cuda")
@@ -54,6 +58,25 @@ def _run(w, coeffs_kind, precision, sample_params):
     plan.step(workspace=ws, norm_out=norm)
     torch.cuda.synchronize()
     return plan, ents, routes, before, float(norm.item()), coeffs
+
+
+def _fused_equals_kept(plan, ents, before):
+    """Repeat the step from the same Muon weights and zero momentum, now in
+    the benchmark's default mode (the update inside the last Newton-Schulz
+    launch): every Muon weight equals the kept-O step's bit for bit."""
+    kept = {}
+    for i, w0 in before["muon_w0"].items():
+        kept[i] = ents[i]["param"].clone()
+        ents[i]["param"].copy_(w0)
+        ents[i]["momentum"].zero_()
+    plan.keep_ns_output(False)
+    assert plan.fuses_update()
+    torch.cuda.synchronize()
+    print("[fullsize] fused step", flush=True)
+    plan.step()
+    torch.cuda.synchronize()
+    for i, k in kept.items():
+        assert torch.equal(ents[i]["param"], k), i
 
 
 def _slice_index(plan, param, off):
@@ -155,6 +178,7 @@ def test_ns_sweep_full(rows, cols, coeffs):
     w = wl.ns_sweep(rows, cols, coeffs)
     plan, ents, routes, before, _, cf = _run(w, coeffs, "bf16", [0])
     _check_muon_param(w, plan, ents, 0, before, cf, "bf16")
+    _fused_equals_kept(plan, ents, before)
 
 
 def test_ns_sweep_fp32_path():
@@ -185,6 +209,7 @@ def test_dense_decoder_full():
             _check_muon_param(w, plan, ents, i, before, cf, "bf16")
     _check_adamw(w, ents, routes, before, T_gpu, sample, np.random.default_rng(3))
     _all_slices_bounded(plan, "bf16")
+    _fused_equals_kept(plan, ents, before)
 
 
 def test_dense_decoder_fused_normuon_full():
@@ -196,6 +221,9 @@ def test_dense_decoder_fused_normuon_full():
         if routes[i][0] == L.MO_ALG_MUON:
             _check_muon_param(w, plan, ents, i, before, cf, "bf16")
     _check_adamw(w, ents, routes, before, T_gpu, sample, np.random.default_rng(4))
+    # NorMuon's row statistics span whole rows: the separate row pass stays
+    plan.keep_ns_output(False)
+    assert not plan.fuses_update()
 
 
 def test_head_batched_full():
@@ -210,3 +238,4 @@ def test_head_batched_full():
         i = w.index(n)
         _check_muon_param(w, plan, ents, i, before, cf, "bf16", slices_to_check=ks)
     _all_slices_bounded(plan, "bf16")
+    _fused_equals_kept(plan, ents, before)

@@ -203,3 +203,63 @@ def test_overlapped_step_equals_serial():
         for k in ("param", "momentum", "exp_avg", "exp_avg_sq"):
             if k in a:
                 assert torch.equal(a[k], b[k]), (a["desc"].name, k)
+
+
+def _mixed_shapes():
+    """Slices for every kernel that can finish a step: slice-resident (wide,
+    tall, split view), 128 x 128 GEMM tiles (wide, tall), 256 x 256 tiles
+    (with MO_NS_BIG_TILE_MIN_WORK=0), fp32 weights, and AdamW params."""
+    ps = [wl.ParamSpec("embed", (256, 64), "bf16", wl.ROLE_EMBEDDING, no_decay=True),
+          wl.ParamSpec("norm", (64,), "bf16", wl.ROLE_NORM, no_decay=True),
+          wl.ParamSpec("small_wide", (96, 256), "bf16"),
+          wl.ParamSpec("small_tall", (392, 120), "bf16"),
+          wl.ParamSpec("kv", (80, 64), "bf16", view=(2, 40, 64), split=(16, 24)),
+          wl.ParamSpec("gemm_wide", (200, 336), "bf16"),
+          wl.ParamSpec("gemm_tall", (344, 192), "bf16"),
+          wl.ParamSpec("big", (520, 776), "bf16"),
+          wl.ParamSpec("f32_tall", (136, 48), "f32")]
+    return wl.Workload("mixed_shapes", 11, tuple(ps), grad_std=1e-3)
+
+
+@pytest.mark.parametrize("big_tiles", [False, True])
+def test_fused_update_bit_identical(big_tiles, monkeypatch):
+    """The Muon update applied inside the last Newton-Schulz launch (the
+    default) gives the same bits as the separate row pass over the stored O,
+    for every kernel that can end a step, over two steps."""
+    if big_tiles:
+        monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0")
+    w = _mixed_shapes()
+    runs = []
+    for keep in (True, False):
+        ents = build_entries(w, normuon=False)
+        plan = api.Plan(ents, api.make_hparams(muon_wd=0.1))
+        plan.keep_ns_output(keep)
+        assert plan.fuses_update() == (not keep)
+        for t in (1, 2):
+            for i, (e, p) in enumerate(zip(ents, w.params)):
+                e["grad"].copy_(to_dev(wl.grad(w, i, t), p.dtype))
+            plan.step()
+        torch.cuda.synchronize()
+        runs.append(ents)
+    for a, b, p in zip(runs[0], runs[1], w.params):
+        for k in ("param", "momentum", "exp_avg", "exp_avg_sq"):
+            if k in a:
+                assert torch.equal(a[k], b[k]), (p.name, k)
+    # the weights did move
+    assert not torch.equal(runs[1][5]["param"], to_dev(wl.init_weight(w, 5), "bf16"))
+
+
+def test_ns_output_refused_after_fused_step():
+    w = _mixed_shapes()
+    ents = build_entries(w, normuon=False)
+    plan = api.Plan(ents, api.make_hparams())
+    for i, (e, p) in enumerate(zip(ents, w.params)):
+        e["grad"].copy_(to_dev(wl.grad(w, i, 1), p.dtype))
+    plan.step()
+    torch.cuda.synchronize()
+    with pytest.raises(L.LibraryError):
+        plan.ns_output(0)
+    plan.keep_ns_output(True)
+    plan.step()
+    torch.cuda.synchronize()
+    assert plan.ns_output(0).shape == (96, 256)

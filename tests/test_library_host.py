@@ -222,3 +222,37 @@ def test_entry_point_validation_before_enqueue():
     assert lib.muon_update(_fake_ptr(1), 3, _fake_ptr(2), 0, 4, 4, 4, 4, 0.1, 0.0, 1.0, None) == \
         L.MO_EDTYPE
     assert lib.mo_last_error()  # message recorded
+
+
+def _fuses(specs, normuon=False, precision="bf16", keep=False, offset=0):
+    arr = _fake_entries(specs, normuon=normuon)
+    if offset:   # Muon weights only (AdamW pointers must be aligned)
+        for i, sp in enumerate(specs):
+            if len(sp.shape) == 2:
+                arr[i].param = _fake_ptr(8 * i) + offset
+    h = C.c_void_p()
+    hp = api.make_hparams(ns_precision=precision, normuon=normuon)
+    L.check("plan", L.lib().mo_plan_create(arr, len(specs), C.byref(hp), C.byref(h)))
+    try:
+        if keep:
+            L.check("keep", L.lib().mo_plan_keep_ns_output(h, 1))
+        return L.lib().mo_plan_fuses_update(h)
+    finally:
+        L.lib().mo_plan_destroy(h)
+
+
+def test_fused_update_eligibility():
+    """The Muon update runs inside the last Newton-Schulz launch only for the
+    bf16 path without NorMuon, with 16-byte weight chunks, unless O is kept."""
+    ok = [wl.ParamSpec("w", (64, 48), "bf16"), wl.ParamSpec("t", (96, 16), "f32"),
+          wl.ParamSpec("g", (16,), "bf16", role=wl.ROLE_NORM)]
+    assert _fuses(ok) == 1
+    assert _fuses(ok, normuon=True) == 0
+    assert _fuses(ok, precision="fp32") == 0
+    assert _fuses(ok, keep=True) == 0
+    # 12 columns: rows are not 16-byte chunks
+    assert _fuses(ok + [wl.ParamSpec("odd", (24, 12), "bf16")]) == 0
+    # a weight whose rows start off 16-byte alignment
+    assert _fuses(ok, offset=8) == 0
+    assert L.lib().mo_plan_fuses_update(None) == 0
+    assert L.lib().mo_plan_keep_ns_output(None, 1) == L.MO_EINVAL
