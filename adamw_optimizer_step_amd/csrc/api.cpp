@@ -198,10 +198,10 @@ mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const flo
   float* scale = reinterpret_cast<float*>(base + W.scale);
   void* pool = base + W.pool;
   if ((s = launch_ns_stats(dprep, n, L.prep_tiles, partials, st)) != MO_OK) return s;
-  if ((s = launch_ns_scale(dprep, n, partials, scale, st)) != MO_OK) return s;
+  if ((s = launch_ns_scale(dprep, n, partials, scale, nullptr, st)) != MO_OK) return s;
   if ((s = launch_ns_prep(dprep, n, L.prep_tiles, scale, pool, L.elem, st)) != MO_OK) return s;
   if ((s = ns_run_iterations(L, base + W.tab, W.tabs, pool, scale, coeffs, steps, nullptr, 0.f,
-                             st)) != MO_OK)
+                             nullptr, st)) != MO_OK)
     return s;
   return launch_ns_final(reinterpret_cast<const FinalItem*>(base + W.fin), n, rows, pool, L.elem,
                          st);

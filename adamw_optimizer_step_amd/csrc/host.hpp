@@ -37,8 +37,11 @@ constexpr int64_t kBigTileMinWork = 512;   // Gram tiles of the 256 bucket: 2 pe
 
 struct NsBucket {
   int tile = kGemmTile;
-  // [parity of the iteration]; fin = the update of the last iteration
+  // [parity of the iteration]; fin = the update of the last iteration.
+  // gram_p0 / gram_a0 / upd0 / fin0: iteration 0, which reads the input D in
+  // place (with the scale folded into the products) for slices that allow it
   std::vector<GemmProb> gram_p[2], gram_a[2], square, upd[2], fin[2];
+  std::vector<GemmProb> gram_p0, gram_a0, upd0, fin0;
   int64_t gram_tiles = 0, square_tiles = 0, upd_tiles = 0;
 };
 
@@ -47,6 +50,9 @@ struct NsLayout {
   bool need_a = false;
   int n = 0;
   std::vector<PrepItem> prep;
+  // prep items (X0 into the pool) of the slices whose iteration 0 reads D in
+  // place, run only for those whose range flag is set (slice index in .slice)
+  std::vector<PrepItem> prep_fb;
   std::vector<NsBucket> buckets;
   std::vector<SmallProb> small;
   int64_t prep_tiles = 0;
@@ -60,19 +66,25 @@ struct NsLayout {
 };
 
 // direct_ok[i] (nullable: none) says that slice i's input can be read in
-// place by the slice-resident kernel: bf16, row stride equal to cols,
-// 16-byte aligned.  Such a slice with 128 rows and a multiple of 128 columns
-// skips the prep copy: its prep item writes nothing, and has no tiles at all
-// unless the statistics are taken over the prep tiles (stats_from_prep).
+// place: bf16, row stride equal to cols, 16-byte aligned.  Such a slice
+// skips the prep copy (its prep item writes nothing, and has no tiles at all
+// unless the statistics are taken over the prep tiles, stats_from_prep) when
+//  * it goes to the slice-resident kernel with 128 rows and a multiple of 128
+//    columns, or
+//  * in_off (nullable) gives its input's element offset from the pool base,
+//    it is not tall and both sides are multiples of its GEMM tile: iteration
+//    0 then reads D itself, the scale folded into the products.
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
-                     bool need_a, const uint8_t* direct_ok, bool stats_from_prep);
+                     bool need_a, const uint8_t* direct_ok, bool stats_from_prep,
+                     const int64_t* in_off = nullptr);
 
 // Byte offsets of the device tables inside one contiguous table block.
 struct NsBucketTables {
   size_t gram_p[2] = {0, 0}, gram_a[2] = {0, 0}, square = 0, upd[2] = {0, 0}, fin[2] = {0, 0};
+  size_t gram_p0 = 0, gram_a0 = 0, upd0 = 0, fin0 = 0;
 };
 struct NsTables {
-  size_t prep = 0, small = 0, bytes = 0;
+  size_t prep = 0, prep_fb = 0, small = 0, bytes = 0;
   std::vector<NsBucketTables> b;
 };
 NsTables ns_table_offsets(const NsLayout& L);
@@ -87,9 +99,11 @@ mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st)
 // wt (nullable): per-slice weight rows; the last iteration then applies the
 // Muon update with learning rate lr to them instead of writing O (bf16 pool,
 // every slice eligible; see fused_apply_ok).
+// range_fb (nullable): the per-slice range flags of launch_ns_scale, which
+// send a slice's in-place iteration 0 back to the prepared X0.
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                            float lr, hipStream_t st);
+                            float lr, const int32_t* range_fb, hipStream_t st);
 
 // True while kernel timing (mo_timing_enable) is on.
 bool timing_enabled();

@@ -113,7 +113,7 @@ struct PrepItem {
   int32_t tiles_c;         // cp / kPrepTile
   int32_t in_dt;
   int32_t vec;             // rows of `in` allow 16-byte loads of 8 elements
-  int32_t pad;
+  int32_t slice;           // fallback table only: the slice's index (scale and flag)
 };
 
 struct GemmProb {
@@ -131,7 +131,11 @@ struct GemmProb {
   int32_t item;            // slice index (the last update of a slice), else -1: with a
                            // weight table, the launch applies the Muon update to that
                            // slice's weights instead of writing its output
-  int32_t pad;
+  int32_t sitem;           // slice index whose normalisation scale s multiplies the
+                           // product (iteration 0 reading the unscaled D in place:
+                           // s^2 for the Gram, s for the update), else -1
+  int64_t alt_off;         // with sitem >= 0: the pool's X0, read instead of D (and
+                           // no scaling) when the slice's range flag is set
 };
 
 struct FinalItem {         // NS output copy (stored orientation)
@@ -148,11 +152,19 @@ struct FinalItem {         // NS output copy (stored orientation)
 mo_status launch_ns_stats(const PrepItem* items, int n, int64_t ntiles, StatPartial* partials,
                           hipStream_t st);
 // Per-item scale = 1 / (alpha (||D||/alpha + 1e-7)), alpha = max(amax, 1e-7).
+// range_fb (nullable): per item, 1 when max|D| lies outside [2^-50, 2^40],
+// where products of the unscaled D could leave fp32's normal range (the
+// in-place first iteration then falls back to the prepared X0), else 0.
 mo_status launch_ns_scale(const PrepItem* items, int n, const StatPartial* partials,
-                          float* scale, hipStream_t st);
+                          float* scale, int32_t* range_fb, hipStream_t st);
 // X0 (scaled, padded, both orientations) into the pool.  elem = 2 (bf16) or 4.
 mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const float* scale,
                          void* pool, int elem, hipStream_t st);
+// The prep copy for the items (bf16, slice index in .slice) whose range flag is
+// set: a fixed grid that skips unflagged items, so the common case (no flag)
+// costs one pass over the item table.
+mo_status launch_ns_prep_fallback(const PrepItem* items, int n, const float* scale,
+                                  const int32_t* range_fb, void* pool, hipStream_t st);
 // One batched GEMM phase:  out = c0 * E + c1 * (A_op B_op^T), with square
 // workgroup tiles of edge `tile` (128 or 256; the problems' padding).
 // Slice-resident Newton-Schulz (all iterations in one launch) for slices whose
@@ -182,10 +194,13 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
 // goes straight from registers to c (or, transposed, to ct).
 // wt (nullable, bf16 with bk = 1 only): problems with item >= 0 apply the Muon
 // update to the weights of slice `item` (as launch_ns_small) instead of
-// writing their output.
+// writing their output.  pscale (nullable): problems with sitem >= 0 scale
+// c1 by pscale[sitem]^2 (bk = 0) or pscale[sitem] (bk = 1), unless
+// pfb[sitem] is set: they then read alt_off for the X operand(s), unscaled.
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
-                         const RowSeg* wt, float lr, hipStream_t st);
+                         const RowSeg* wt, float lr, const float* pscale, const int32_t* pfb,
+                         hipStream_t st);
 mo_status launch_ns_final(const FinalItem* items, int n, int64_t total_rows, const void* pool,
                           int elem, hipStream_t st);
 

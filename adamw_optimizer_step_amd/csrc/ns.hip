@@ -59,7 +59,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_stats(const PrepItem* __restric
 
 __global__ __launch_bounds__(kThreads) void k_ns_scale(const PrepItem* __restrict__ items,
                                                        const StatPartial* __restrict__ partials,
-                                                       float* __restrict__ scale) {
+                                                       float* __restrict__ scale,
+                                                       int32_t* __restrict__ range_fb) {
   const PrepItem it = items[blockIdx.x];
   float amax = 0.f;
   double ss = 0.0;
@@ -74,6 +75,10 @@ __global__ __launch_bounds__(kThreads) void k_ns_scale(const PrepItem* __restric
     // X = D / alpha, X <- X / (||X||_F + 1e-7)  ==  D / (||D||_F + 1e-7 alpha)
     const double alpha = fmax(static_cast<double>(red.amax), 1e-7);
     scale[blockIdx.x] = static_cast<float>(1.0 / (sqrt(red.sumsq) + 1e-7 * alpha));
+    // unscaled products D D^T (K <= 2^16 terms) stay normal fp32 numbers, and
+    // s^2 too, while max|D| is in [2^-50, 2^40]
+    if (range_fb)
+      range_fb[blockIdx.x] = !(red.amax >= 0x1p-50f && red.amax <= 0x1p40f);
   }
 }
 
@@ -356,18 +361,11 @@ __device__ __forceinline__ float from_elem<float>(float v) { return v; }
 // X0 = scale * D over one 64 x 64 tile of the padded stored orientation:
 // 16-byte global accesses (8 elements per thread and row pass), zeros in the
 // padding; tall slices go through an LDS tile and are written transposed.
+// One 64 x 64 tile (number lt of item `it`) of X0 = s D into the pool, in
+// the stored orientation (sbuf) or transposed through LDS (stbuf).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_ns_prep(const PrepItem* __restrict__ items, int n,
-                                                      const float* __restrict__ scale,
-                                                      T* __restrict__ pool) {
-  static_assert(kPrepTile == 64 && kThreads == 256, "prep tile split");
-  __shared__ T tile_s[kPrepTile][kPrepTile + 2];
-  const int64_t tile = blockIdx.x;
-  const int idx = find_segment(items, n, tile);
-  const PrepItem it = items[idx];
-  if (it.sbuf < 0 && it.stbuf < 0) return;   // read in place by the slice-resident kernel
-  const float sc = scale[idx];
-  const int64_t lt = tile - it.start;
+__device__ __forceinline__ void prep_tile(const PrepItem& it, float sc, int64_t lt, T* pool,
+                                          T (*tile_s)[kPrepTile + 2]) {
   const int r0 = static_cast<int>(lt / it.tiles_c) * kPrepTile;
   const int c0 = static_cast<int>(lt % it.tiles_c) * kPrepTile;
   const int lr = threadIdx.x >> 3, lc = (threadIdx.x & 7) * 8;
@@ -406,6 +404,44 @@ __global__ __launch_bounds__(kThreads) void k_ns_prep(const PrepItem* __restrict
 #pragma unroll
     for (int e = 0; e < 8; ++e) w[e] = from_elem<T>(tile_s[lc + e][lr + 32 * k]);
     st8<T>(pool + it.stbuf + static_cast<int64_t>(c0 + lr + 32 * k) * it.rp + r0 + lc, w);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_ns_prep(const PrepItem* __restrict__ items, int n,
+                                                      const float* __restrict__ scale,
+                                                      T* __restrict__ pool) {
+  static_assert(kPrepTile == 64 && kThreads == 256, "prep tile split");
+  __shared__ T tile_s[kPrepTile][kPrepTile + 2];
+  const int64_t tile = blockIdx.x;
+  const int idx = find_segment(items, n, tile);
+  const PrepItem it = items[idx];
+  if (it.sbuf < 0 && it.stbuf < 0) return;   // read in place
+  prep_tile<T>(it, scale[idx], tile - it.start, pool, tile_s);
+}
+
+// The prep copy of the items whose range flag is set (see k_ns_scale): every
+// workgroup checks the flags of kThreads items at a time, one per thread, and
+// takes every gridDim.x-th tile of the flagged ones (none, normally).
+__global__ __launch_bounds__(kThreads) void k_ns_prep_fb(const PrepItem* __restrict__ items,
+                                                         int n, const float* __restrict__ scale,
+                                                         const int32_t* __restrict__ range_fb,
+                                                         uint16_t* __restrict__ pool) {
+  __shared__ uint16_t tile_s[kPrepTile][kPrepTile + 2];
+  for (int k0 = 0; k0 < n; k0 += kThreads) {
+    const int mine = k0 + static_cast<int>(threadIdx.x);
+    const int flagged = mine < n && range_fb[items[mine].slice] != 0;
+    if (!__syncthreads_or(flagged)) continue;
+    for (int k = k0; k < min(n, k0 + kThreads); ++k) {
+      const PrepItem it = items[k];
+      if (range_fb[it.slice] == 0) continue;   // uniform over the block
+      const int64_t nt = static_cast<int64_t>(it.rp / kPrepTile) * it.tiles_c;
+      const float sc = scale[it.slice];
+      for (int64_t lt = blockIdx.x; lt < nt; lt += gridDim.x) {
+        prep_tile<uint16_t>(it, sc, lt, pool, tile_s);
+        __syncthreads();   // before the next tile reuses tile_s
+      }
+    }
   }
 }
 
@@ -480,8 +516,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 
 template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK, int ST, int SRB>
 __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
-    const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1,
-    int has_e, float cd, const RowSeg* __restrict__ wt, float lr) {
+    const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1_arg,
+    int has_e, float cd, const RowSeg* __restrict__ wt, float lr,
+    const float* __restrict__ pscale, const int32_t* __restrict__ pfb) {
   using C = GemmCfg<T, BM, BN, WM, WN, BK, ST, SRB>;
   constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
@@ -504,6 +541,20 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   const GemmProb pr = probs[find_segment(probs, nprob, tile)];
   int ti, tj;
   decode_tile(tile - pr.start, pr.tiles_m, pr.tiles_n, pr.sym, ti, tj);
+  // iteration 0 on the unscaled input D: (s D)(s D)^T = s^2 D D^T for the
+  // Gram, P (s D) = s P D for the update; a slice whose range flag is set
+  // reads the prepared X0 (alt_off) as later iterations do
+  float c1 = c1_arg;
+  int64_t a_off = pr.a_off, b_off = pr.b_off;
+  if (pscale != nullptr && pr.sitem >= 0) {
+    if (pfb != nullptr && pfb[pr.sitem] != 0) {
+      if (!BK) a_off = pr.alt_off;
+      b_off = pr.alt_off;
+    } else {
+      const float sc = pscale[pr.sitem];
+      c1 = BK ? c1_arg * sc : c1_arg * (sc * sc);
+    }
+  }
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -518,11 +569,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   // kSlabK rows; its resource moves with the slab so offsets stay small.
   const uint32_t lda_b = static_cast<uint32_t>(pr.lda) * sizeof(T);
   const uint32_t ldb_b = static_cast<uint32_t>(pr.ldb) * sizeof(T);
-  const char* abase = reinterpret_cast<const char*>(pool + pr.a_off) +
+  const char* abase = reinterpret_cast<const char*>(pool + a_off) +
                       static_cast<size_t>(ti) * BM * lda_b;
   const u32x4 rsa = buffer_rsrc(abase, BM * lda_b);
-  const char* bbase = BK ? reinterpret_cast<const char*>(pool + pr.b_off + tj * BN)
-                         : reinterpret_cast<const char*>(pool + pr.b_off) +
+  const char* bbase = BK ? reinterpret_cast<const char*>(pool + b_off + tj * BN)
+                         : reinterpret_cast<const char*>(pool + b_off) +
                                static_cast<size_t>(tj) * BN * ldb_b;
   auto rsb_at = [&](int kt) __attribute__((always_inline)) {
     if constexpr (BK)
@@ -1335,10 +1386,10 @@ mo_status launch_ns_stats(const PrepItem* items, int n, int64_t ntiles, StatPart
 }
 
 mo_status launch_ns_scale(const PrepItem* items, int n, const StatPartial* partials,
-                          float* scale, hipStream_t st) {
+                          float* scale, int32_t* range_fb, hipStream_t st) {
   if (n <= 0) return MO_OK;
   KTimer tm(MO_KC_NS_SCALE, st);
-  k_ns_scale<<<dim3(n), kThreads, 0, st>>>(items, partials, scale);
+  k_ns_scale<<<dim3(n), kThreads, 0, st>>>(items, partials, scale, range_fb);
   MO_LAUNCH_CHECK("k_ns_scale");
   return MO_OK;
 }
@@ -1357,6 +1408,16 @@ mo_status launch_ns_prep(const PrepItem* items, int n, int64_t ntiles, const flo
   return MO_OK;
 }
 
+mo_status launch_ns_prep_fallback(const PrepItem* items, int n, const float* scale,
+                                  const int32_t* range_fb, void* pool, hipStream_t st) {
+  if (n <= 0) return MO_OK;
+  KTimer tm(MO_KC_NS_PREP, st);
+  k_ns_prep_fb<<<dim3(1024), kThreads, 0, st>>>(items, n, scale, range_fb,
+                                                static_cast<uint16_t*>(pool));
+  MO_LAUNCH_CHECK("k_ns_prep_fb");
+  return MO_OK;
+}
+
 // Below this many tiles a 128-tile launch uses 8 waves per tile; the
 // environment variable MO_NS_FEW_TILES overrides it (0 = always 4 waves), for
 // tuning and for tests of both kernels.
@@ -1372,19 +1433,20 @@ int64_t few_tiles() {
 template <typename T, int BM, int WM, int WN, int ST = 4, int SRB = 64>
 void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
                        float c1, int has_e, float cd, const RowSeg* wt, float lr,
-                       hipStream_t st) {
+                       const float* pscale, const int32_t* pfb, hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
   if (bk)
     k_ns_gemm<T, BM, BM, WM, WN, 2, true, ST, SRB><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1,
-                                                                       has_e, cd, wt, lr);
+                                                                       has_e, cd, wt, lr, pscale, pfb);
   else
     k_ns_gemm<T, BM, BM, WM, WN, 2, false, ST, SRB><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1,
-                                                                        has_e, cd, wt, lr);
+                                                                        has_e, cd, wt, lr, pscale, pfb);
 }
 
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
-                         const RowSeg* wt, float lr, hipStream_t st) {
+                         const RowSeg* wt, float lr, const float* pscale, const int32_t* pfb,
+                         hipStream_t st) {
   if (ntiles <= 0) return MO_OK;
   if (bk && has_e) return fail(MO_EINVAL, "the K-major-B GEMM takes no E term");
   if (wt && (!bk || elem != 2))
@@ -1399,10 +1461,10 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     if (elem == 2)
       launch_gemm_shape<uint16_t, 256, 2, 4, 2, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, st);
+                                                     cd, wt, lr, pscale, pfb, st);
     else
       launch_gemm_shape<float, 256, 2, 4>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, cd, wt, lr, st);
+                                          has_e, cd, wt, lr, pscale, pfb, st);
   } else if (tile == 128) {
     // A launch with few tiles leaves most CUs idle and lasts as long as one
     // tile's K loop, whose length is set by the fixed cost of each K slab
@@ -1413,14 +1475,14 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     if (elem == 2 && ntiles < few_tiles())
       launch_gemm_shape<uint16_t, 128, 2, 4, 4, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, st);
+                                                     cd, wt, lr, pscale, pfb, st);
     else if (elem == 2)  // 2 stages of 64-deep slabs, as for 256 x 256 tiles (64 KiB)
       launch_gemm_shape<uint16_t, 128, 2, 2, 2, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, st);
+                                                     cd, wt, lr, pscale, pfb, st);
     else
       launch_gemm_shape<float, 128, 2, 2>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, cd, wt, lr, st);
+                                          has_e, cd, wt, lr, pscale, pfb, st);
   } else {
     return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);
   }

@@ -21,6 +21,8 @@ GemmProb make_prob(int64_t a, int64_t b, int64_t c, int64_t ct, int64_t e, int32
   p.K = K; p.tiles_m = tm; p.tiles_n = tn; p.sym = sym;
   p.start = static_cast<int32_t>(start);
   p.item = -1;
+  p.sitem = -1;
+  p.alt_off = -1;
   return p;
 }
 
@@ -53,7 +55,8 @@ void order_by_k(std::vector<GemmProb>& v) {
 }  // namespace
 
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
-                     bool need_a, const uint8_t* direct_ok, bool stats_from_prep) {
+                     bool need_a, const uint8_t* direct_ok, bool stats_from_prep,
+                     const int64_t* in_off) {
   L = NsLayout();
   L.elem = elem;
   L.need_a = need_a;
@@ -123,6 +126,38 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       continue;
     }
     const int32_t ts = sp / tile, tl = lp / tile;
+    // iteration 0 reads D in place when it already has X0's layout (not
+    // tall, no padding): no prep copy, the scale folded into the products
+    const bool gdirect = in_off && direct_ok && direct_ok[i] && !tall && sp == s_ && lp == l_;
+    if (gdirect) {
+      // the prep copy stays available for slices whose range flag is set
+      PrepItem fb = L.prep.back();
+      fb.slice = i;
+      L.prep_fb.push_back(fb);
+      L.prep.back().sbuf = -1;
+      L.prep.back().stbuf = -1;
+      if (!stats_from_prep) L.prep_tiles = L.prep.back().start;
+    }
+    const int64_t x0 = gdirect ? in_off[i] : x[0];
+    const int32_t si = gdirect ? i : -1;
+    auto first = [&](GemmProb g) {
+      g.sitem = si;
+      g.alt_off = gdirect ? x[0] : -1;
+      return g;
+    };
+    B.gram_p0.push_back(
+        first(make_prob(x0, x0, p, p, -1, lp, lp, sp, sp, 0, lp, ts, ts, 1, B.gram_tiles)));
+    if (need_a)
+      B.gram_a0.push_back(
+          first(make_prob(x0, x0, a, a, -1, lp, lp, sp, sp, 0, lp, ts, ts, 1, B.gram_tiles)));
+    const GemmProb u0 =
+        first(make_prob(p, x0, x[1], -1, -1, sp, lp, lp, 0, 0, sp, ts, tl, 0, B.upd_tiles));
+    B.upd0.push_back(u0);
+    GemmProb f0 = tall ? first(make_prob(p, x0, -1, x[1], -1, sp, lp, 0, sp, 0, sp, ts, tl, 0,
+                                         B.upd_tiles))
+                       : u0;
+    f0.item = i;
+    B.fin0.push_back(f0);
     for (int q = 0; q < 2; ++q) {
       const int64_t xc = x[q], xn = x[q ^ 1];
       // Gram X X^T (K = l), B = X read N x K: into P (scaled by b) or into A;
@@ -164,6 +199,10 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       order_by_k(B.fin[q]);
     }
     order_by_k(B.square);
+    order_by_k(B.gram_p0);
+    order_by_k(B.gram_a0);
+    order_by_k(B.upd0);
+    order_by_k(B.fin0);
   }
   L.pool_elems = pool;
 }
@@ -172,6 +211,7 @@ NsTables ns_table_offsets(const NsLayout& L) {
   NsTables T;
   WsCursor c;
   T.prep = c.take(L.prep.size() * sizeof(PrepItem), 64);
+  T.prep_fb = c.take(L.prep_fb.size() * sizeof(PrepItem), 64);
   T.small = c.take(L.small.size() * sizeof(SmallProb), 64);
   for (const NsBucket& B : L.buckets) {
     NsBucketTables b;
@@ -183,6 +223,10 @@ NsTables ns_table_offsets(const NsLayout& L) {
       b.fin[q] = take(B.fin[q]);
     }
     b.square = take(B.square);
+    b.gram_p0 = take(B.gram_p0);
+    b.gram_a0 = take(B.gram_a0);
+    b.upd0 = take(B.upd0);
+    b.fin0 = take(B.fin0);
     T.b.push_back(b);
   }
   T.bytes = align_up(c.off, 256);
@@ -196,6 +240,8 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
   };
   if (!L.prep.empty())
     std::memcpy(buf.data() + T.prep, L.prep.data(), L.prep.size() * sizeof(PrepItem));
+  if (!L.prep_fb.empty())
+    std::memcpy(buf.data() + T.prep_fb, L.prep_fb.data(), L.prep_fb.size() * sizeof(PrepItem));
   if (!L.small.empty())
     std::memcpy(buf.data() + T.small, L.small.data(), L.small.size() * sizeof(SmallProb));
   for (size_t k = 0; k < L.buckets.size(); ++k) {
@@ -208,12 +254,16 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
       put(b.fin[q], B.fin[q]);
     }
     put(b.square, B.square);
+    put(b.gram_p0, B.gram_p0);
+    put(b.gram_a0, B.gram_a0);
+    put(b.upd0, B.upd0);
+    put(b.fin0, B.fin0);
   }
 }
 
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                            float lr, hipStream_t st) {
+                            float lr, const int32_t* range_fb, hipStream_t st) {
   auto tab = [dtab](size_t off) { return reinterpret_cast<const GemmProb*>(dtab + off); };
   if (!L.small.empty()) {
     mo_status s = launch_ns_small(reinterpret_cast<const SmallProb*>(dtab + T.small),
@@ -226,6 +276,11 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
     const float a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
     const bool cubic_step = c == 0.f || !L.need_a;
     const int q = k & 1;
+    // iteration 0 has tables of its own (inputs read in place, scaled by the
+    // per-slice scale); later iterations alternate between two parities
+    const bool first = k == 0;
+    const float* ps = first ? scale : nullptr;
+    const int32_t* pfb = first ? range_fb : nullptr;
     // phase 1: P = a I + b X X^T (cubic-type step), or A = X X^T then
     // P = a I + b A + c A A.  The a X term of the update is folded into P.
     for (size_t i = 0; i < L.buckets.size(); ++i) {
@@ -235,14 +290,14 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const int n = static_cast<int>(B.gram_p[q].size());
       mo_status s;
       if (cubic_step) {
-        s = launch_ns_gemm(tab(tb.gram_p[q]), n, B.gram_tiles, B.tile, 0, pool, L.elem, 0.f, b, 0,
-                           a, nullptr, 0.f, st);
+        s = launch_ns_gemm(tab(first ? tb.gram_p0 : tb.gram_p[q]), n, B.gram_tiles, B.tile, 0,
+                           pool, L.elem, 0.f, b, 0, a, nullptr, 0.f, ps, pfb, st);
       } else {
-        s = launch_ns_gemm(tab(tb.gram_a[q]), n, B.gram_tiles, B.tile, 0, pool, L.elem, 0.f, 1.f,
-                           0, 0.f, nullptr, 0.f, st);
+        s = launch_ns_gemm(tab(first ? tb.gram_a0 : tb.gram_a[q]), n, B.gram_tiles, B.tile, 0,
+                           pool, L.elem, 0.f, 1.f, 0, 0.f, nullptr, 0.f, ps, pfb, st);
         if (s == MO_OK)
           s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, B.tile, 0, pool, L.elem, b, c, 1,
-                             a, nullptr, 0.f, st);
+                             a, nullptr, 0.f, nullptr, nullptr, st);
       }
       if (s != MO_OK) return s;
     }
@@ -252,9 +307,10 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       if (B.upd[q].empty()) continue;
       const NsBucketTables& tb = T.b[i];
       const bool fin = k + 1 == steps;
-      mo_status s = launch_ns_gemm(tab(fin ? tb.fin[q] : tb.upd[q]),
-                                   static_cast<int>(B.upd[q].size()), B.upd_tiles, B.tile, 1, pool,
-                                   L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr, lr, st);
+      const size_t off = fin ? (first ? tb.fin0 : tb.fin[q]) : (first ? tb.upd0 : tb.upd[q]);
+      mo_status s = launch_ns_gemm(tab(off), static_cast<int>(B.upd[q].size()), B.upd_tiles,
+                                   B.tile, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr,
+                                   lr, ps, pfb, st);
       if (s != MO_OK) return s;
     }
   }

@@ -33,7 +33,8 @@ struct mo_plan {
   NsLayout ns;
   // workspace layout (byte offsets)
   std::vector<size_t> d_off;        // per param: direction buffer (Muon with grad)
-  size_t ws_stats = 0, ws_scale = 0, ws_adam_partials = 0, ws_adam_scal = 0, ws_pool = 0;
+  size_t ws_stats = 0, ws_scale = 0, ws_fb = 0, ws_adam_partials = 0, ws_adam_scal = 0;
+  size_t ws_pool = 0;
   size_t ws_total = 0;
   int64_t mom_blocks = 0, adam_blocks = 0, total_rows = 0;
   int n_adam = 0;
@@ -123,16 +124,28 @@ mo_status build_plan(mo_plan* P) {
   for (const auto& a : P->active) P->mom_blocks += ceil_div(a.rows * a.cols, kEltPerBlock);
   std::vector<int64_t> rr, cc;
   for (const auto& a : P->active) { rr.push_back(a.rows); cc.push_back(a.cols); P->total_rows += a.rows; }
-  // D lives in the (256-byte aligned) workspace in the pool's element type,
-  // rows of cols elements: readable in place whenever the path is bf16
-  const std::vector<uint8_t> direct(rr.size(), P->ddt == MO_BF16 ? 1 : 0);
-  build_ns_layout(P->ns, rr.data(), cc.data(), static_cast<int>(rr.size()),
-                  P->ddt == MO_F32 ? 4 : 2, P->need_a, direct.data(), false);
   P->ws_stats = ws.take(sizeof(StatPartial) * P->mom_blocks);
   P->ws_scale = ws.take(sizeof(float) * P->active.size());
+  P->ws_fb = ws.take(sizeof(int32_t) * P->active.size());
   P->ws_adam_partials = ws.take(sizeof(double) * P->adam_blocks);
   P->ws_adam_scal = ws.take(2 * sizeof(double));
+  // D lives in the (256-byte aligned) workspace in the pool's element type,
+  // rows of cols elements: readable in place whenever the path is bf16.  The
+  // pool comes last; its base is known before its size, so each D can be
+  // addressed by its element offset from the pool.
+  const size_t esz_ns = dtype_size(P->ddt);
+  const size_t pool_base = align_up(ws.off, 256);
+  std::vector<int64_t> in_off;
+  for (const auto& a : P->active)
+    in_off.push_back((static_cast<int64_t>(P->d_off[a.param]) +
+                      a.off * a.cols * static_cast<int64_t>(esz_ns) -
+                      static_cast<int64_t>(pool_base)) / static_cast<int64_t>(esz_ns));
+  const std::vector<uint8_t> direct(rr.size(), P->ddt == MO_BF16 ? 1 : 0);
+  build_ns_layout(P->ns, rr.data(), cc.data(), static_cast<int>(rr.size()),
+                  static_cast<int>(esz_ns), P->need_a, direct.data(), false,
+                  P->ddt == MO_BF16 ? in_off.data() : nullptr);
   P->ws_pool = ws.take(static_cast<size_t>(P->ns.pool_elems) * P->ns.elem);
+  if (P->ws_pool != pool_base) return fail(MO_EINVAL, "internal: pool base moved");
   P->ws_total = align_up(ws.off, 256);
 
   P->nst = ns_table_offsets(P->ns);
@@ -202,6 +215,14 @@ mo_status upload_tables(mo_plan* P, char* ws, hipStream_t st) {
     r.scale = static_cast<float>(std::sqrt(std::max(1.0, static_cast<double>(a.rows) / a.cols)));
     r.wd = P->routes[a.param].decay ? hp.muon_wd : 0.f;
     row += a.rows;
+  }
+  // fallback prep items: the same input as the slice's prep item
+  for (PrepItem& fb : P->ns.prep_fb) {
+    const PrepItem& pi = P->ns.prep[fb.slice];
+    fb.in = pi.in;
+    fb.ld_in = pi.ld_in;
+    fb.in_dt = pi.in_dt;
+    fb.vec = pi.vec;
   }
   std::vector<char> nsbuf;
   ns_pack_tables(P->ns, P->nst, nsbuf);
@@ -393,8 +414,13 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     if ((s = launch_momentum(reinterpret_cast<const MomSeg*>(P->dtab + P->tab_mom), nsl,
                              P->mom_blocks, hp.mu, hp.nesterov, stats, st)) != MO_OK)
       return s;
-    if ((s = launch_ns_scale(dprep, nsl, stats, scale, st)) != MO_OK) return s;
+    int32_t* fb = reinterpret_cast<int32_t*>(base + P->ws_fb);
+    if ((s = launch_ns_scale(dprep, nsl, stats, scale, fb, st)) != MO_OK) return s;
     if ((s = launch_ns_prep(dprep, nsl, P->ns.prep_tiles, scale, pool, P->ns.elem, st)) != MO_OK)
+      return s;
+    if ((s = launch_ns_prep_fallback(reinterpret_cast<const PrepItem*>(dns + P->nst.prep_fb),
+                                     static_cast<int>(P->ns.prep_fb.size()), scale, fb, pool,
+                                     st)) != MO_OK)
       return s;
   }
   // AdamW (clip norm and update) is independent of the Muon path: with both
@@ -443,7 +469,8 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     const bool fuse = P->fuse_ok && !P->keep_ns_output;
     if ((s = ns_run_iterations(P->ns, dns, P->nst, pool,
                                reinterpret_cast<const float*>(base + P->ws_scale), coeffs,
-                               hp.ns_steps, fuse ? drows : nullptr, muon_lr, st)) != MO_OK)
+                               hp.ns_steps, fuse ? drows : nullptr, muon_lr,
+                               reinterpret_cast<const int32_t*>(base + P->ws_fb), st)) != MO_OK)
       return s;
     if (!fuse) {
       RowSeg none;

@@ -16,7 +16,7 @@ from oracle.routing import descs_from_specs
 from oracle.views import expand
 
 from gpu_common import (NS_BF16_MAXABS, NS_BF16_RELFRO, NS_F32_MAXABS, REL_F32,
-                        assert_bf16_close, f64, rel_inf, require_gpu, to_dev)
+                        assert_bf16_close, assert_ns_close, f64, rel_inf, require_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -263,3 +263,41 @@ def test_ns_output_refused_after_fused_step():
     plan.step()
     torch.cuda.synchronize()
     assert plan.ns_output(0).shape == (96, 256)
+
+
+def _aligned_shapes():
+    """Slices whose iteration 0 reads D in place (wide or square, sides
+    multiples of the tile) beside ones that keep the prep copy (tall, padded)."""
+    ps = [wl.ParamSpec("norm", (64,), "bf16", wl.ROLE_NORM, no_decay=True),
+          wl.ParamSpec("square", (256, 256), "bf16"),
+          wl.ParamSpec("wide", (256, 640), "bf16"),
+          wl.ParamSpec("big", (512, 768), "bf16"),
+          wl.ParamSpec("tall", (512, 256), "bf16"),
+          wl.ParamSpec("padded", (200, 336), "bf16")]
+    return wl.Workload("aligned_shapes", 13, tuple(ps), grad_std=1e-3)
+
+
+@pytest.mark.parametrize("coeffs", ["cubic", "quintic"])
+@pytest.mark.parametrize("exp2", [0, -35, 35, -60, 55])
+def test_first_iteration_in_place_and_range_fallback(exp2, coeffs, monkeypatch):
+    """Iteration 0 reads the unscaled D in place, the normalisation scale
+    folded into the products; a slice whose max|D| leaves [2^-50, 2^40] (here
+    gradients scaled by 2^-60 or 2^55) falls back to the prepared X0.  The
+    Newton-Schulz output meets the oracle's bound at every scale; the quintic
+    cases put the 512-row slice on 256 x 256 tiles."""
+    monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0" if coeffs == "quintic" else "512")
+    w = _aligned_shapes()
+    cf = wl.coeff_table(coeffs)
+    ents = build_entries(w, normuon=False)
+    plan = api.Plan(ents, api.make_hparams(coeffs=cf))
+    plan.keep_ns_output(True)
+    for i, (e, p) in enumerate(zip(ents, w.params)):
+        e["grad"].copy_(to_dev(wl.grad(w, i, 1), p.dtype))
+        e["grad"].mul_(2.0 ** exp2)     # a power of two: exact in bf16
+    G = [f64(e["grad"]) for e in ents]
+    plan.step()
+    torch.cuda.synchronize()
+    for k, (param, off, r, c) in enumerate(plan.slices()):
+        _, D = omuon.momentum(np.zeros_like(G[param]), G[param], wl.MUON_MU)
+        O_ref = omuon.newton_schulz(D[off:off + r], cf)
+        assert_ns_close(f64(plan.ns_output(k)), O_ref, "bf16")
