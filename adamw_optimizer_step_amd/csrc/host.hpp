@@ -43,6 +43,17 @@ struct NsBucket {
   std::vector<GemmProb> gram_p[2], gram_a[2], square, upd[2], fin[2];
   std::vector<GemmProb> gram_p0, gram_a0, upd0, fin0;
   int64_t gram_tiles = 0, square_tiles = 0, upd_tiles = 0;
+  // Gram-space mode: one problem table per launch, in order (see NsLayout)
+  std::vector<std::vector<GemmProb>> gs;
+  std::vector<int32_t> gs_kind, gs_k;   // GsKind; coefficient row of the launch
+  std::vector<int64_t> gs_tiles;
+};
+
+// Launch kinds of the Gram-space sequence.
+enum GsKind : int32_t {
+  kGsGram = 0,   // A0 = X0 X0^T, and Q1 = a0 I + b0 A0 as a second output
+  kGsProd = 1,   // C = a E + b (U V^T) over s x s operands (symmetric result)
+  kGsFinal = 2,  // X_N = Q_N X0 (K-major B), the last update
 };
 
 struct NsLayout {
@@ -58,10 +69,11 @@ struct NsLayout {
   int64_t prep_tiles = 0;
   std::vector<int64_t> x_off[2];
   std::vector<int32_t> tall, sp, lp;
+  std::vector<uint8_t> gspace;   // slice runs the Gram-space sequence
   int64_t pool_elems = 0;
 
   // buffer of the final iterate (stored orientation) and its row stride
-  int64_t final_off(int i, int steps) const { return x_off[steps & 1][i]; }
+  int64_t final_off(int i, int steps) const { return x_off[gspace[i] ? 1 : steps & 1][i]; }
   int32_t final_ld(int i) const { return tall[i] ? sp[i] : lp[i]; }
 };
 
@@ -74,14 +86,22 @@ struct NsLayout {
 //  * in_off (nullable) gives its input's element offset from the pool base,
 //    it is not tall and both sides are multiples of its GEMM tile: iteration
 //    0 then reads D itself, the scale folded into the products.
+//
+// steps > 0 with a bf16 pool and cubic-type rows only (!need_a) selects the
+// Gram-space sequence for the GEMM slices: every iterate is P_k ... P_0 X0
+// with P_k = a_k I + b_k A_k, A_{k+1} = P_k A_k P_k, so the iterations run on
+// s x s matrices (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q with
+// P kept implicit through the E term) and X0 is multiplied once, by Q_N, at
+// the end.  MO_NS_GRAM_SPACE=0 in the environment turns it off.
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
                      bool need_a, const uint8_t* direct_ok, bool stats_from_prep,
-                     const int64_t* in_off = nullptr);
+                     const int64_t* in_off = nullptr, int steps = 0);
 
 // Byte offsets of the device tables inside one contiguous table block.
 struct NsBucketTables {
   size_t gram_p[2] = {0, 0}, gram_a[2] = {0, 0}, square = 0, upd[2] = {0, 0}, fin[2] = {0, 0};
   size_t gram_p0 = 0, gram_a0 = 0, upd0 = 0, fin0 = 0;
+  std::vector<size_t> gs;
 };
 struct NsTables {
   size_t prep = 0, prep_fb = 0, small = 0, bytes = 0;

@@ -136,6 +136,8 @@ struct GemmProb {
                            // s^2 for the Gram, s for the update), else -1
   int64_t alt_off;         // with sitem >= 0: the pool's X0, read instead of D (and
                            // no scaling) when the slice's range flag is set
+  int64_t c2_off;          // bf16 product without E only: a second output
+                           // c1b C + cdb I (layout and mirror as c), -1 = none
 };
 
 struct FinalItem {         // NS output copy (stored orientation)
@@ -197,10 +199,11 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
 // writing their output.  pscale (nullable): problems with sitem >= 0 scale
 // c1 by pscale[sitem]^2 (bk = 0) or pscale[sitem] (bk = 1), unless
 // pfb[sitem] is set: they then read alt_off for the X operand(s), unscaled.
+// c1b, cdb: the constants of the second outputs (c2_off).
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
                          const RowSeg* wt, float lr, const float* pscale, const int32_t* pfb,
-                         hipStream_t st);
+                         hipStream_t st, float c1b = 0.f, float cdb = 0.f);
 mo_status launch_ns_final(const FinalItem* items, int n, int64_t total_rows, const void* pool,
                           int elem, hipStream_t st);
 

@@ -518,7 +518,8 @@ template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK, int ST,
 __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1_arg,
     int has_e, float cd, const RowSeg* __restrict__ wt, float lr,
-    const float* __restrict__ pscale, const int32_t* __restrict__ pfb) {
+    const float* __restrict__ pscale, const int32_t* __restrict__ pfb, float c1b_arg,
+    float cdb) {
   using C = GemmCfg<T, BM, BN, WM, WN, BK, ST, SRB>;
   constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
@@ -544,7 +545,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   // iteration 0 on the unscaled input D: (s D)(s D)^T = s^2 D D^T for the
   // Gram, P (s D) = s P D for the update; a slice whose range flag is set
   // reads the prepared X0 (alt_off) as later iterations do
-  float c1 = c1_arg;
+  float c1 = c1_arg, c1b = c1b_arg;
   int64_t a_off = pr.a_off, b_off = pr.b_off;
   if (pscale != nullptr && pr.sitem >= 0) {
     if (pfb != nullptr && pfb[pr.sitem] != 0) {
@@ -553,6 +554,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     } else {
       const float sc = pscale[pr.sitem];
       c1 = BK ? c1_arg * sc : c1_arg * (sc * sc);
+      c1b = c1b_arg * (sc * sc);
     }
   }
 
@@ -881,45 +883,57 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
           return r * RB + ((((c >> 3) ^ r) & (NCH - 1)) << 4) + (c & 7) * 2;
         };
         const bool diag = ti == tj;
-        __syncthreads();   // every wave is done reading the operand stages
+        // stage cc1 C + ccd I and store it to `off_c` (rows) and, for the
+        // lower triangle, to `off_ct` (mirror)
+        auto emit = [&](float cc1, float ccd, int64_t off_c, int64_t off_ct)
+            __attribute__((always_inline)) {
 #pragma unroll
-        for (int mi = 0; mi < FM; ++mi)
+          for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-          for (int ni = 0; ni < FN; ++ni)
+            for (int ni = 0; ni < FN; ++ni)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int r = wm * C::kWaveM + mi * 32 + fr;
-              const int c = wn * C::kWaveN + ni * 32 + 8 * q + 4 * fg;
-              float x[4];
+              for (int q = 0; q < 4; ++q) {
+                const int r = wm * C::kWaveM + mi * 32 + fr;
+                const int c = wn * C::kWaveN + ni * 32 + 8 * q + 4 * fg;
+                float x[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                x[e] = c1 * acc[mi][ni][4 * q + e] + (diag && r == c + e ? cd : 0.f);
-              const u32x2 u{pk_bf16(x[0], x[1]),
-                            pk_bf16(x[2], x[3])};
-              *reinterpret_cast<u32x2*>(smem + soff(r, c)) = u;
+                for (int e = 0; e < 4; ++e)
+                  x[e] = cc1 * acc[mi][ni][4 * q + e] + (diag && r == c + e ? ccd : 0.f);
+                const u32x2 u{pk_bf16(x[0], x[1]),
+                              pk_bf16(x[2], x[3])};
+                *reinterpret_cast<u32x2*>(smem + soff(r, c)) = u;
+              }
+          __syncthreads();
+          if (off_c >= 0) {
+            T* const g = pool + off_c + static_cast<size_t>(ti * BM) * pr.ldc + tj * BN;
+#pragma unroll
+            for (int p = 0; p < BM * NCH / NT; ++p) {
+              const int idx = p * NT + tid, r = idx / NCH, c = idx % NCH;
+              *reinterpret_cast<u32x4*>(g + static_cast<size_t>(r) * pr.ldc + c * 8) =
+                  *reinterpret_cast<const u32x4*>(smem + r * RB + (((c ^ r) & (NCH - 1)) << 4));
             }
-        __syncthreads();
-        if (pr.c_off >= 0) {
-          T* const g = pool + pr.c_off + static_cast<size_t>(ti * BM) * pr.ldc + tj * BN;
-#pragma unroll
-          for (int p = 0; p < BM * NCH / NT; ++p) {
-            const int idx = p * NT + tid, r = idx / NCH, c = idx % NCH;
-            *reinterpret_cast<u32x4*>(g + static_cast<size_t>(r) * pr.ldc + c * 8) =
-                *reinterpret_cast<const u32x4*>(smem + r * RB + (((c ^ r) & (NCH - 1)) << 4));
           }
-        }
-        if (pr.ct_off >= 0 && !(pr.sym && diag)) {
-          T* const g = pool + pr.ct_off + static_cast<size_t>(tj * BN) * pr.ldct + ti * BM;
-          constexpr int kUnits = (BN / 16) * (BM / 32);   // 16 rows x 32 columns of C^T
-          static_assert(kUnits % C::kWaves == 0, "mirror units per wave");
-          for (int u = wv; u < kUnits; u += C::kWaves) {
-            const int n0 = (u % (BN / 16)) * 16, k0 = (u / (BN / 16)) * 32 + 8 * g16;
-            const int col = n0 + 4 * (j16 & 3);
-            const u32x2 lo = lds_read_tr16(smem + soff(k0 + (j16 >> 2), col));
-            const u32x2 hi = lds_read_tr16(smem + soff(k0 + 4 + (j16 >> 2), col));
-            *reinterpret_cast<u32x4*>(g + static_cast<size_t>(n0 + j16) * pr.ldct + k0) =
-                u32x4{lo[0], lo[1], hi[0], hi[1]};
+          if (off_ct >= 0 && !(pr.sym && diag)) {
+            T* const g = pool + off_ct + static_cast<size_t>(tj * BN) * pr.ldct + ti * BM;
+            constexpr int kUnits = (BN / 16) * (BM / 32);   // 16 rows x 32 columns of C^T
+            static_assert(kUnits % C::kWaves == 0, "mirror units per wave");
+            for (int u = wv; u < kUnits; u += C::kWaves) {
+              const int n0 = (u % (BN / 16)) * 16, k0 = (u / (BN / 16)) * 32 + 8 * g16;
+              const int col = n0 + 4 * (j16 & 3);
+              const u32x2 lo = lds_read_tr16(smem + soff(k0 + (j16 >> 2), col));
+              const u32x2 hi = lds_read_tr16(smem + soff(k0 + 4 + (j16 >> 2), col));
+              *reinterpret_cast<u32x4*>(g + static_cast<size_t>(n0 + j16) * pr.ldct + k0) =
+                  u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
           }
+        };
+        __syncthreads();   // every wave is done reading the operand stages
+        emit(c1, cd, pr.c_off, pr.ct_off);
+        if (pr.c2_off >= 0) {
+          // second output of the same product (same layout and mirror):
+          // c1b C + cdb I, e.g. A = X X^T and P = a I + b A together
+          __syncthreads();   // the staged tile has been read
+          emit(c1b, cdb, pr.c2_off, pr.c2_off);
         }
         return;
       }
@@ -1433,20 +1447,21 @@ int64_t few_tiles() {
 template <typename T, int BM, int WM, int WN, int ST = 4, int SRB = 64>
 void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
                        float c1, int has_e, float cd, const RowSeg* wt, float lr,
-                       const float* pscale, const int32_t* pfb, hipStream_t st) {
+                       const float* pscale, const int32_t* pfb, float c1b, float cdb,
+                       hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
   if (bk)
-    k_ns_gemm<T, BM, BM, WM, WN, 2, true, ST, SRB><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1,
-                                                                       has_e, cd, wt, lr, pscale, pfb);
+    k_ns_gemm<T, BM, BM, WM, WN, 2, true, ST, SRB><<<grid, NT, 0, st>>>(
+        probs, n, pool, c0, c1, has_e, cd, wt, lr, pscale, pfb, c1b, cdb);
   else
-    k_ns_gemm<T, BM, BM, WM, WN, 2, false, ST, SRB><<<grid, NT, 0, st>>>(probs, n, pool, c0, c1,
-                                                                        has_e, cd, wt, lr, pscale, pfb);
+    k_ns_gemm<T, BM, BM, WM, WN, 2, false, ST, SRB><<<grid, NT, 0, st>>>(
+        probs, n, pool, c0, c1, has_e, cd, wt, lr, pscale, pfb, c1b, cdb);
 }
 
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
                          const RowSeg* wt, float lr, const float* pscale, const int32_t* pfb,
-                         hipStream_t st) {
+                         hipStream_t st, float c1b, float cdb) {
   if (ntiles <= 0) return MO_OK;
   if (bk && has_e) return fail(MO_EINVAL, "the K-major-B GEMM takes no E term");
   if (wt && (!bk || elem != 2))
@@ -1461,10 +1476,10 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     if (elem == 2)
       launch_gemm_shape<uint16_t, 256, 2, 4, 2, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, pscale, pfb, st);
+                                                     cd, wt, lr, pscale, pfb, c1b, cdb, st);
     else
       launch_gemm_shape<float, 256, 2, 4>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, cd, wt, lr, pscale, pfb, st);
+                                          has_e, cd, wt, lr, pscale, pfb, c1b, cdb, st);
   } else if (tile == 128) {
     // A launch with few tiles leaves most CUs idle and lasts as long as one
     // tile's K loop, whose length is set by the fixed cost of each K slab
@@ -1475,14 +1490,14 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     if (elem == 2 && ntiles < few_tiles())
       launch_gemm_shape<uint16_t, 128, 2, 4, 4, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, pscale, pfb, st);
+                                                     cd, wt, lr, pscale, pfb, c1b, cdb, st);
     else if (elem == 2)  // 2 stages of 64-deep slabs, as for 256 x 256 tiles (64 KiB)
       launch_gemm_shape<uint16_t, 128, 2, 2, 2, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, pscale, pfb, st);
+                                                     cd, wt, lr, pscale, pfb, c1b, cdb, st);
     else
       launch_gemm_shape<float, 128, 2, 2>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, cd, wt, lr, pscale, pfb, st);
+                                          has_e, cd, wt, lr, pscale, pfb, c1b, cdb, st);
   } else {
     return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);
   }

@@ -23,6 +23,7 @@ GemmProb make_prob(int64_t a, int64_t b, int64_t c, int64_t ct, int64_t e, int32
   p.item = -1;
   p.sitem = -1;
   p.alt_off = -1;
+  p.c2_off = -1;
   return p;
 }
 
@@ -35,6 +36,11 @@ int64_t big_tile_min_work() {
   char* end = nullptr;
   const long long v = std::strtoll(e, &end, 10);
   return (end && *end == '\0' && v >= 0) ? static_cast<int64_t>(v) : kBigTileMinWork;
+}
+
+bool gram_space_enabled() {
+  const char* e = std::getenv("MO_NS_GRAM_SPACE");
+  return !(e && e[0] == '0' && e[1] == '\0');
 }
 
 int64_t tiles_of(int32_t tm, int32_t tn, bool sym) {
@@ -56,8 +62,9 @@ void order_by_k(std::vector<GemmProb>& v) {
 
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
                      bool need_a, const uint8_t* direct_ok, bool stats_from_prep,
-                     const int64_t* in_off) {
+                     const int64_t* in_off, int steps) {
   L = NsLayout();
+  const bool gspace_mode = elem == 2 && !need_a && steps > 0 && gram_space_enabled();
   L.elem = elem;
   L.need_a = need_a;
   L.n = n;
@@ -84,9 +91,11 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     const int tile = B.tile;
     const int32_t sp = pad_to(s_, tile), lp = pad_to(l_, tile);
     const bool small = elem == 2 && tile == kGemmTile && sp == kSmallS;
+    const bool gs = gspace_mode && !small;
     const int64_t x[2] = {take(static_cast<int64_t>(sp) * lp), take(static_cast<int64_t>(sp) * lp)};
-    const int64_t p = small ? -1 : take(static_cast<int64_t>(sp) * sp);
+    const int64_t p = small || gs ? -1 : take(static_cast<int64_t>(sp) * sp);
     const int64_t a = need_a && !small ? take(static_cast<int64_t>(sp) * sp) : -1;
+    L.gspace.push_back(gs);
     L.x_off[0].push_back(x[0]);
     L.x_off[1].push_back(x[1]);
     L.tall.push_back(tall);
@@ -145,6 +154,56 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       g.alt_off = gdirect ? x[0] : -1;
       return g;
     };
+    if (gs) {
+      // s x s buffers: A / T rotate through S[3] (A_k in S[2k % 3], T_k in
+      // S[(2k + 1) % 3], A_{k+1} in S[(2k + 2) % 3]); Q_k in Qb[(k - 1) % 2]
+      int64_t S[3], Qb[2];
+      for (auto& v : S) v = take(static_cast<int64_t>(sp) * sp);
+      for (auto& v : Qb) v = take(static_cast<int64_t>(sp) * sp);
+      size_t stage = 0;
+      auto add = [&](int32_t kind, int32_t k, const GemmProb& g) {
+        if (B.gs.size() <= stage) {
+          B.gs.resize(stage + 1);
+          B.gs_kind.resize(stage + 1);
+          B.gs_k.resize(stage + 1);
+          B.gs_tiles.resize(stage + 1);
+        }
+        B.gs[stage].push_back(g);
+        B.gs_kind[stage] = kind;
+        B.gs_k[stage] = k;
+        B.gs_tiles[stage] += tiles_of(g.tiles_m, g.tiles_n, g.sym != 0);
+      };
+      // C = a E + b (U V^T) over s x s symmetric operands; the result is
+      // symmetric too (all factors are polynomials in A_0)
+      auto prod = [&](int64_t u, int64_t v, int64_t e, int64_t out) {
+        return make_prob(u, v, out, out, e, sp, sp, sp, sp, sp, sp, ts, ts, 1, 0);
+      };
+      GemmProb g = first(make_prob(x0, x0, S[0], S[0], -1, lp, lp, sp, sp, 0, lp, ts, ts, 1, 0));
+      g.c2_off = Qb[0];
+      add(kGsGram, 0, g);
+      ++stage;
+      for (int k = 0; k + 1 < steps; ++k) {
+        const int64_t Ak = S[(2 * k) % 3], Tk = S[(2 * k + 1) % 3], An = S[(2 * k + 2) % 3];
+        add(kGsProd, k, prod(Ak, Ak, Ak, Tk));
+        if (k >= 1) add(kGsProd, k, prod(Ak, Qb[(k - 1) % 2], Qb[(k - 1) % 2], Qb[k % 2]));
+        ++stage;
+        add(kGsProd, k, prod(Tk, Ak, Tk, An));
+        ++stage;
+      }
+      if (steps >= 2) {
+        const int k = steps - 1;
+        add(kGsProd, k, prod(S[(2 * k) % 3], Qb[(k - 1) % 2], Qb[(k - 1) % 2], Qb[k % 2]));
+        ++stage;
+      }
+      // X_N = Q_N X0 into the second iterate buffer (transposed when tall)
+      const int64_t qn = Qb[(steps - 1) % 2];
+      GemmProb f = first(tall ? make_prob(qn, x0, -1, x[1], -1, sp, lp, 0, sp, 0, sp, ts, tl, 0, 0)
+                              : make_prob(qn, x0, x[1], -1, -1, sp, lp, lp, 0, 0, sp, ts, tl, 0,
+                                          0));
+      f.item = i;
+      add(kGsFinal, steps - 1, f);
+      continue;
+    }
     B.gram_p0.push_back(
         first(make_prob(x0, x0, p, p, -1, lp, lp, sp, sp, 0, lp, ts, ts, 1, B.gram_tiles)));
     if (need_a)
@@ -199,6 +258,7 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       order_by_k(B.fin[q]);
     }
     order_by_k(B.square);
+    for (auto& v : B.gs) order_by_k(v);
     order_by_k(B.gram_p0);
     order_by_k(B.gram_a0);
     order_by_k(B.upd0);
@@ -227,6 +287,7 @@ NsTables ns_table_offsets(const NsLayout& L) {
     b.gram_a0 = take(B.gram_a0);
     b.upd0 = take(B.upd0);
     b.fin0 = take(B.fin0);
+    for (const auto& v : B.gs) b.gs.push_back(take(v));
     T.b.push_back(b);
   }
   T.bytes = align_up(c.off, 256);
@@ -258,6 +319,7 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
     put(b.gram_a0, B.gram_a0);
     put(b.upd0, B.upd0);
     put(b.fin0, B.fin0);
+    for (size_t j = 0; j < B.gs.size(); ++j) put(b.gs[j], B.gs[j]);
   }
 }
 
@@ -271,6 +333,30 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
                                   reinterpret_cast<const PrepItem*>(dtab + T.prep), scale, coeffs,
                                   steps, wt, lr, st);
     if (s != MO_OK) return s;
+  }
+  // Gram-space sequence (every GEMM slice of the layout, or none)
+  size_t nstage = 0;
+  for (const NsBucket& B : L.buckets) nstage = std::max(nstage, B.gs.size());
+  for (size_t j = 0; j < nstage; ++j) {
+    for (size_t i = 0; i < L.buckets.size(); ++i) {
+      const NsBucket& B = L.buckets[i];
+      if (j >= B.gs.size()) continue;
+      const int k = B.gs_k[j];
+      const float a = coeffs[3 * k], b = coeffs[3 * k + 1];
+      const GemmProb* t = tab(T.b[i].gs[j]);
+      const int n = static_cast<int>(B.gs[j].size());
+      mo_status s;
+      if (B.gs_kind[j] == kGsGram)
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, 0, pool, L.elem, 0.f, 1.f, 0, 0.f,
+                           nullptr, 0.f, scale, range_fb, st, b, a);
+      else if (B.gs_kind[j] == kGsProd)
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, 0, pool, L.elem, a, b, 1, 0.f, nullptr,
+                           0.f, nullptr, nullptr, st);
+      else
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, wt,
+                           lr, scale, range_fb, st);
+      if (s != MO_OK) return s;
+    }
   }
   for (int k = 0; k < steps; ++k) {
     const float a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];

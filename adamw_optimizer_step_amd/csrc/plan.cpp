@@ -143,7 +143,7 @@ mo_status build_plan(mo_plan* P) {
   const std::vector<uint8_t> direct(rr.size(), P->ddt == MO_BF16 ? 1 : 0);
   build_ns_layout(P->ns, rr.data(), cc.data(), static_cast<int>(rr.size()),
                   static_cast<int>(esz_ns), P->need_a, direct.data(), false,
-                  P->ddt == MO_BF16 ? in_off.data() : nullptr);
+                  P->ddt == MO_BF16 ? in_off.data() : nullptr, hp.ns_steps);
   P->ws_pool = ws.take(static_cast<size_t>(P->ns.pool_elems) * P->ns.elem);
   if (P->ws_pool != pool_base) return fail(MO_EINVAL, "internal: pool base moved");
   P->ws_total = align_up(ws.off, 256);
