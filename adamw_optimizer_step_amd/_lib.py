@@ -108,6 +108,7 @@ SIGNATURES = [
     ("mo_plan_ns_output", i32, [vp, i32, vp, C.POINTER(vp), C.POINTER(i64), C.POINTER(i32)]),
     ("mo_plan_keep_ns_output", i32, [vp, i32]),
     ("mo_plan_fuses_update", i32, [vp]),
+    ("mo_plan_gram_space", i32, [vp]),
     ("mo_abi_struct_size", C.c_size_t, [i32]),
     ("mo_timing_enable", i32, [i32]),
     ("mo_timing_read", i32, [i32, C.POINTER(C.c_double), C.POINTER(i64)]),

@@ -349,6 +349,10 @@ class Plan:
         Newton-Schulz launch."""
         return bool(L.lib().mo_plan_fuses_update(self._h))
 
+    def gram_space(self) -> bool:
+        """True if the GEMM-path slices run the Gram-space sequence."""
+        return bool(L.lib().mo_plan_gram_space(self._h))
+
     def ns_output(self, slice_index: int, workspace: Optional[torch.Tensor] = None
                   ) -> torch.Tensor:
         """View into the workspace of one slice's Newton-Schulz output O after

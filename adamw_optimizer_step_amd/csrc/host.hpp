@@ -34,6 +34,7 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
 constexpr int kBigTile = 256;
 constexpr int kBigTileMinS = 512;
 constexpr int64_t kBigTileMinWork = 512;   // Gram tiles of the 256 bucket: 2 per CU
+constexpr int64_t kGramSpaceMinS = 64;
 
 struct NsBucket {
   int tile = kGemmTile;
@@ -70,6 +71,7 @@ struct NsLayout {
   std::vector<int64_t> x_off[2];
   std::vector<int32_t> tall, sp, lp;
   std::vector<uint8_t> gspace;   // slice runs the Gram-space sequence
+  std::vector<SmallProb> small_gs;   // slice-resident slices run in Gram space
   int64_t pool_elems = 0;
 
   // buffer of the final iterate (stored orientation) and its row stride
@@ -92,7 +94,11 @@ struct NsLayout {
 // with P_k = a_k I + b_k A_k, A_{k+1} = P_k A_k P_k, so the iterations run on
 // s x s matrices (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q with
 // P kept implicit through the E term) and X0 is multiplied once, by Q_N, at
-// the end.  MO_NS_GRAM_SPACE=0 in the environment turns it off.
+// the end.  The slice-resident kernel does the same with its 128 x 128
+// matrices in LDS, for slices with a short side of at least kGramSpaceMinS:
+// on smaller ones the bf16 products of Gram space lose more than the plain
+// iteration (O(1) entries).  MO_NS_GRAM_SPACE=0 in the environment turns it
+// off.
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
                      bool need_a, const uint8_t* direct_ok, bool stats_from_prep,
                      const int64_t* in_off = nullptr, int steps = 0);
@@ -104,7 +110,7 @@ struct NsBucketTables {
   std::vector<size_t> gs;
 };
 struct NsTables {
-  size_t prep = 0, prep_fb = 0, small = 0, bytes = 0;
+  size_t prep = 0, prep_fb = 0, small = 0, small_gs = 0, bytes = 0;
   std::vector<NsBucketTables> b;
 };
 NsTables ns_table_offsets(const NsLayout& L);

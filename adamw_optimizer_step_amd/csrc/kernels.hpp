@@ -187,9 +187,11 @@ constexpr int kSmallS = 128;
 // wt (nullable): per-slice weight rows (the RowSeg of the slice index); the
 // last iteration then applies W <- W (1 - lr wd) - lr scale O to them instead
 // of writing O.  Requires bf16 O, cols % 8 == 0 and 16-byte aligned rows.
+// gspace: run the iterations in Gram space (two passes over X; see
+// build_ns_layout), the result in the second iterate buffer.
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
                           const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                          float lr, hipStream_t st);
+                          float lr, hipStream_t st, int gspace = 0);
 
 // C = c1 A B (+ c0 E) (+ cd I on diagonal tiles).  bk = 1: B is read K-major
 // (K x N row-major) through LDS transpose reads; no E term, and the output

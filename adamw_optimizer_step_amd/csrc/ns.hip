@@ -1076,6 +1076,105 @@ __device__ __forceinline__ int sm_off(int row, int col) {
   return row * 256 + ((((col >> 3) ^ sm_swz(row)) & 15) << 4) + (col & 7) * 2;
 }
 
+// The Newton-Schulz iterations in Gram space for one 128 x 128 slice Gram,
+// by the 8 waves of the slice-resident kernel (2 x 4 waves of 64 x 32
+// outputs).  With P_k = a_k I + R_k, R_k = b_k A_k + c_k A_k^2:
+// Q_1 = P_0, Q_{k+1} = P_k Q_k, T_k = P_k A_k, A_{k+1} = T_k P_k.  All
+// factors are polynomials in A_0, so every product is symmetric and each
+// operand is read as its own transpose.  In: A_0 (bf16) in xa.  Out: Q_N
+// (bf16) in qs.  xa and yb are scratch tiles (A, the quintic T; the cubic T
+// or the quintic R).  E terms are read one value at a time, so that the
+// phase needs no registers beyond one accumulator block.
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+__device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_char* yb,
+                                           const NsCoeffTable* cfp, int steps) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3, fr = lane & 31, fg = lane >> 5;
+  auto frag = [&](const lds_char* t, int m, int ks) __attribute__((always_inline)) {
+    return *reinterpret_cast<const lds_u32x4*>(t + m * 256 +
+                                               ((((2 * ks + fg) ^ sm_swz(m)) & 15) << 4));
+  };
+  // x = U V^T over the wave's 64 x 32 block
+  auto prod = [&](const lds_char* u, const lds_char* v, f32x16 (&x)[2])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[mi][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const u32x4 bf = frag(v, wn * 32 + fr, ks);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(frag(u, wm * 64 + mi * 32 + fr, ks), bf, x[mi]);
+    }
+  };
+  auto row = [&](int mi, int e) { return wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * fg + (e & 3); };
+  const int col = wn * 32 + fr;
+  auto put = [&](lds_char* dst, const f32x16 (&x)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        *reinterpret_cast<lds_u16*>(dst + sm_off(row(mi, e), col)) = f32_to_bf16(x[mi][e]);
+  };
+  auto at = [&](const lds_char* src, int mi, int e) __attribute__((always_inline)) {
+    return bf16_to_f32(*reinterpret_cast<const lds_u16*>(src + sm_off(row(mi, e), col)));
+  };
+  // x = alpha E + beta x, E from the tile `src` (read before any write)
+  auto axpy = [&](f32x16 (&x)[2], float alpha, const lds_char* src, float beta)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[mi][e] = alpha * at(src, mi, e) + beta * x[mi][e];
+  };
+  f32x16 x[2];
+  for (int k = 0; k < steps; ++k) {
+    const float ak = cfp->a[k], bk = cfp->b[k], ck = cfp->c[k];
+    const bool quint = ck != 0.f;
+    if (quint) {        // R = b A + c A A into yb
+      prod(xa, xa, x);
+      axpy(x, bk, xa, ck);
+      put(yb, x);
+      __syncthreads();
+    }
+    // the left factor: R (quintic), or A scaled by b (cubic)
+    const lds_char* const rt = quint ? yb : xa;
+    const float rs = quint ? 1.f : bk;
+    if (k == 0) {       // Q_1 = a_0 I + R_0
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          x[mi][e] = rs * at(rt, mi, e) + (row(mi, e) == col ? ak : 0.f);
+      put(qs, x);
+    } else {            // Q' = a Q + rs (R Q)
+      prod(rt, qs, x);
+      axpy(x, ak, qs, rs);
+      __syncthreads();
+      put(qs, x);
+    }
+    __syncthreads();
+    if (k + 1 == steps) break;
+    // T = a A + rs (R A): into yb (cubic) or over A (quintic)
+    prod(rt, xa, x);
+    axpy(x, ak, xa, rs);
+    if (quint) __syncthreads();
+    lds_char* const tt = quint ? xa : yb;
+    put(tt, x);
+    __syncthreads();
+    // A' = a T + rs (T R), over A
+    prod(tt, rt, x);
+    axpy(x, ak, tt, rs);
+    __syncthreads();
+    put(xa, x);
+    __syncthreads();
+  }
+}
+
+template <bool GS>
 __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __restrict__ probs,
                                                             uint16_t* __restrict__ pool,
                                                             const PrepItem* __restrict__ items,
@@ -1092,7 +1191,11 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   const int wm = wave >> 2, wn = wave & 3;
   const int fr = lane & 31, fg = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
   const int NB = pr.lp / kSmallS;
-  const int total = NB * (steps + 1);   // pass 0: first Gram; pass k + 1: iteration k
+  // passes over X: pass 0 forms the first Gram; pass k + 1 runs iteration k.
+  // Gram space: pass 0, then all iterations on 128 x 128 matrices in LDS,
+  // then one pass for X_N = Q_N X0.
+  const int npass = GS ? 1 : steps;
+  const int total = NB * (npass + 1);
   const uint32_t ld_b = static_cast<uint32_t>(pr.lp) * 2;
   uint16_t* const X0 = pool + pr.x_off[0];
   uint16_t* const X1 = pool + pr.x_off[1];
@@ -1264,7 +1367,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
               u32x2{pk_bf16(x[4 * q], x[4 * q + 1]), pk_bf16(x[4 * q + 2], x[4 * q + 3])};
         }
       __syncthreads();   // B2: X'_b complete in LDS
-      const bool last = pass == steps;
+      const bool last = GS || pass == npass;
       if (last && wt != nullptr) {
         // apply the Muon step to the slice's weights (stored orientation,
         // clipped to the real extent) instead of writing O
@@ -1326,7 +1429,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
         }
       } else if (last && pr.tall) {
         // stored orientation: out[b * 128 + n][k] = X'_b[k][n], ld 128
-        uint16_t* out = (steps & 1) ? X1 : X0;
+        uint16_t* out = (npass & 1) ? X1 : X0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int T = q * 32 + wv * 4 + g16;
@@ -1350,7 +1453,23 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       }
       if (!last) gram_acc(Xn, Xn, accg);
     }
-    if (b == NB - 1 && pass < steps) {
+    if (GS && b == NB - 1 && pass == 0) {
+      // Gram space: A_0 (as stored, bf16) into Xn, then every iteration on
+      // 128 x 128 matrices in LDS; Q_N lands in Ps for the final pass.  The
+      // stage this element's block has just left is free for the phase.
+      __syncthreads();   // every wave is done with this element's staged block
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          *reinterpret_cast<uint16_t*>(Xn + sm_off(acc_row(mi, v), acc_col)) =
+              f32_to_bf16(accg[mi][v]);
+      __syncthreads();
+      // (C-style casts: generic pointers to LDS, into the LDS address space)
+      sm_gram_space((lds_char*)(Ps), (lds_char*)(Xn),
+                    (lds_char*)(smem + (2 + cur % kSmStages) * kSmTile), &cf, steps);
+      zero(accg);
+    } else if (!GS && b == NB - 1 && pass < steps) {
       // P = a I + b A (+ c A^2) for iteration `pass`, from A = accg
       const float ak = cf.a[pass], bk = cf.b[pass], ck = cf.c[pass];
       if (ck == 0.f) {
@@ -1507,7 +1626,7 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
 
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
                           const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                          float lr, hipStream_t st) {
+                          float lr, hipStream_t st, int gspace) {
   if (n <= 0) return MO_OK;
   if (steps < 1 || steps > MO_NS_MAX_STEPS) return fail(MO_EINVAL, "bad step count %d", steps);
   NsCoeffTable cf;
@@ -1518,8 +1637,12 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
     cf.c[k] = coeffs[3 * k + 2];
   }
   KTimer tm(MO_KC_NS_SMALL, st);
-  k_ns_small<<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
-      probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr);
+  if (gspace)
+    k_ns_small<true><<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
+        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr);
+  else
+    k_ns_small<false><<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
+        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr);
   MO_LAUNCH_CHECK("k_ns_small");
   return MO_OK;
 }

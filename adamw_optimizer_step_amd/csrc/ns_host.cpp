@@ -92,10 +92,11 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     const int32_t sp = pad_to(s_, tile), lp = pad_to(l_, tile);
     const bool small = elem == 2 && tile == kGemmTile && sp == kSmallS;
     const bool gs = gspace_mode && !small;
+    const bool sgs = gspace_mode && small && s_ >= kGramSpaceMinS;
     const int64_t x[2] = {take(static_cast<int64_t>(sp) * lp), take(static_cast<int64_t>(sp) * lp)};
     const int64_t p = small || gs ? -1 : take(static_cast<int64_t>(sp) * sp);
     const int64_t a = need_a && !small ? take(static_cast<int64_t>(sp) * sp) : -1;
-    L.gspace.push_back(gs);
+    L.gspace.push_back(gs || sgs);
     L.x_off[0].push_back(x[0]);
     L.x_off[1].push_back(x[1]);
     L.tall.push_back(tall);
@@ -131,7 +132,7 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
         L.prep.back().stbuf = -1;
         if (!stats_from_prep) L.prep_tiles = L.prep.back().start;
       }
-      L.small.push_back(sm);
+      (sgs ? L.small_gs : L.small).push_back(sm);
       continue;
     }
     const int32_t ts = sp / tile, tl = lp / tile;
@@ -248,8 +249,9 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     B.upd_tiles += tiles_of(ts, tl, false);
   }
   // slice-resident problems: longest first
-  std::stable_sort(L.small.begin(), L.small.end(),
-                   [](const SmallProb& a, const SmallProb& b) { return a.lp > b.lp; });
+  for (auto* v : {&L.small, &L.small_gs})
+    std::stable_sort(v->begin(), v->end(),
+                     [](const SmallProb& a, const SmallProb& b) { return a.lp > b.lp; });
   for (NsBucket& B : L.buckets) {
     for (int q = 0; q < 2; ++q) {
       order_by_k(B.gram_p[q]);
@@ -273,6 +275,7 @@ NsTables ns_table_offsets(const NsLayout& L) {
   T.prep = c.take(L.prep.size() * sizeof(PrepItem), 64);
   T.prep_fb = c.take(L.prep_fb.size() * sizeof(PrepItem), 64);
   T.small = c.take(L.small.size() * sizeof(SmallProb), 64);
+  T.small_gs = c.take(L.small_gs.size() * sizeof(SmallProb), 64);
   for (const NsBucket& B : L.buckets) {
     NsBucketTables b;
     auto take = [&c](const std::vector<GemmProb>& v) { return c.take(v.size() * sizeof(GemmProb), 64); };
@@ -305,6 +308,9 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
     std::memcpy(buf.data() + T.prep_fb, L.prep_fb.data(), L.prep_fb.size() * sizeof(PrepItem));
   if (!L.small.empty())
     std::memcpy(buf.data() + T.small, L.small.data(), L.small.size() * sizeof(SmallProb));
+  if (!L.small_gs.empty())
+    std::memcpy(buf.data() + T.small_gs, L.small_gs.data(),
+                L.small_gs.size() * sizeof(SmallProb));
   for (size_t k = 0; k < L.buckets.size(); ++k) {
     const NsBucket& B = L.buckets[k];
     const NsBucketTables& b = T.b[k];
@@ -327,11 +333,13 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
                             const float* scale, const float* coeffs, int steps, const RowSeg* wt,
                             float lr, const int32_t* range_fb, hipStream_t st) {
   auto tab = [dtab](size_t off) { return reinterpret_cast<const GemmProb*>(dtab + off); };
-  if (!L.small.empty()) {
-    mo_status s = launch_ns_small(reinterpret_cast<const SmallProb*>(dtab + T.small),
-                                  static_cast<int>(L.small.size()), pool,
-                                  reinterpret_cast<const PrepItem*>(dtab + T.prep), scale, coeffs,
-                                  steps, wt, lr, st);
+  for (int gsm = 0; gsm < 2; ++gsm) {
+    const std::vector<SmallProb>& v = gsm ? L.small_gs : L.small;
+    if (v.empty()) continue;
+    mo_status s = launch_ns_small(
+        reinterpret_cast<const SmallProb*>(dtab + (gsm ? T.small_gs : T.small)),
+        static_cast<int>(v.size()), pool, reinterpret_cast<const PrepItem*>(dtab + T.prep),
+        scale, coeffs, steps, wt, lr, st, gsm);
     if (s != MO_OK) return s;
   }
   // Gram-space sequence (every GEMM slice of the layout, or none)

@@ -355,6 +355,13 @@ int32_t mo_plan_fuses_update(const mo_plan* plan) {
   return plan && plan->fuse_ok && !plan->keep_ns_output ? 1 : 0;
 }
 
+int32_t mo_plan_gram_space(const mo_plan* plan) {
+  if (!plan) return 0;
+  for (uint8_t g : plan->ns.gspace)
+    if (g) return 1;
+  return 0;
+}
+
 mo_status mo_plan_ns_output(const mo_plan* P, int32_t slice, const void* ws, void** o,
                             int64_t* ld, int32_t* dtype) {
   clear_error();

@@ -50,30 +50,43 @@ def workload_by_name(name: str, coeffs: str = "cubic"):
     return table[name]()
 
 
-def ns_work(slices, coeffs, elem, w_elem=None):
-    """Algorithmic Newton-Schulz work per step, from the per-slice unit figures
-    (s = short side, l = long side of each slice, N iterations):
-    * dense flops 4 s^2 l per iteration (A = X X^T and P X), + 2 s^3 for a
-      quintic-type row;
-    * executed flops with the symmetric Gram: 3 s^2 l (+ s^3) per iteration;
-    * algorithmic HBM bytes when X does not stay on chip: one read of X0 for
-      the first Gram, then a read of X and a write of X' per iteration:
-      elem * s * l * (2 N + 1); with the Muon update fused into the last
-      launch (w_elem = weight element size) the last write of O is replaced
-      by a read and a write of W: + (2 w_elem - elem) * s * l.
+def ns_work(slices, coeffs, elem, w_elem=None, gram_space=False, sxs_on_chip=False):
+    """Newton-Schulz work per step, from the per-slice unit figures (s = short
+    side, l = long side of each slice, N iterations):
+    * dense flops, the method's count: 4 s^2 l per iteration (A = X X^T and
+      P X), + 2 s^3 for a quintic-type row;
+    * executed flops, plain iteration with the symmetric Gram: 3 s^2 l
+      (+ s^3) per iteration; Gram-space sequence (cubic rows): s^2 l for
+      A0 = X0 X0^T, 3 N - 3 symmetric s x s products of s^3 each, and
+      2 s^2 l for X_N = Q_N X0;
+    * HBM bytes when X does not stay on chip: plain, one read of X0 for the
+      first Gram, then a read of X and a write of X' per iteration:
+      elem * s * l * (2 N + 1); Gram space, two reads of X0 and one write of
+      X_N, elem * s * l * 3, plus per s x s product two operands, the E term
+      and the result, 4 elem s^2, and A0 and Q1, 2 elem s^2 (none when the
+      s x s matrices stay in LDS, sxs_on_chip).  With the Muon
+      update fused into the last launch (w_elem = weight element size) the
+      last write is replaced by a read and a write of W: + (2 w_elem - elem) s l.
     Returns (dense_flops, executed_flops, bytes)."""
     dense = exe = byt = 0.0
+    n = len(coeffs)
     for r, c in slices:
         s, l = float(min(r, c)), float(max(r, c))
-        byt += elem * s * l * (2 * len(coeffs) + 1)
-        if w_elem is not None:
-            byt += (2 * w_elem - elem) * s * l
         for a, b, cc in coeffs:
             dense += 4.0 * s * s * l
-            exe += 3.0 * s * s * l
             if cc != 0.0:
                 dense += 2.0 * s ** 3
-                exe += s ** 3
+        if gram_space:
+            exe += 3.0 * s * s * l + (3 * n - 3) * s ** 3
+            byt += elem * s * l * 3
+            if not sxs_on_chip:
+                byt += (4 * (3 * n - 3) + 2) * elem * s * s
+        else:
+            for a, b, cc in coeffs:
+                exe += 3.0 * s * s * l + (s ** 3 if cc != 0.0 else 0.0)
+            byt += elem * s * l * (2 * n + 1)
+        if w_elem is not None:
+            byt += (2 * w_elem - elem) * s * l
     return dense, exe, byt
 
 
@@ -259,6 +272,7 @@ def main() -> int:
 
     # algorithmic work
     fused = plan.fuses_update()
+    gspace = plan.gram_space()
     welt = w.params[0].dtype == "bf16" and 2 or 4
     slices = [(r, c) for _, _, r, c in plan.slices()]
     elem = 2 if args.precision == "bf16" else 4
@@ -274,7 +288,8 @@ def main() -> int:
     if cands:
         kname, part = max(cands, key=lambda x: kern[x[0]]["ms_per_step"])
         g = kern[kname]
-        dense, exe, nbytes = ns_work(part, coeffs, elem, welt if fused else None)
+        dense, exe, nbytes = ns_work(part, coeffs, elem, welt if fused else None,
+                                     gram_space=gspace, sxs_on_chip=kname == "ns_small")
         n = g["launches_per_step"]
         t = g["avg_launch_ms"] * 1e-3
         # the binding roof is the one with the longer ideal time
@@ -294,7 +309,9 @@ def main() -> int:
             "executed_tflops": round(exe / n / t / 1e12, 2),
             "algorithmic_bytes_per_launch": nbytes / n,
             "algorithmic_gbs": round(nbytes / n / t / 1e9, 1),
-            "symmetry_exploited": kname == "ns_gemm"})
+            "executed_frac": round(exe / n / t / 1e12 / peak, 4),
+            "symmetry_exploited": kname == "ns_gemm",
+            "algorithm": "gram_space" if gspace else "plain"})
     hbm = {}
     elt = w.params[0].dtype == "bf16" and 2 or 4
     if "momentum" in kern:
@@ -365,7 +382,7 @@ def main() -> int:
         "config": {"workload": w.key, "muon_params": muon_elems, "adamw_params": adam_elems,
                    "muon_slices": len(slices), "ns_steps": len(coeffs), "coeffs": args.coeffs,
                    "ns_precision": args.precision, "normuon": bool(w.normuon),
-                   "fused_update": fused,
+                   "fused_update": fused, "gram_space": gspace,
                    "param_dtype": w.params[0].dtype, "state_dtype": "f32"},
         "roofline": roofline,
         "ns_dense_tflops_pct_of_peak": (round(100 * roofline["dense_tflops"] / peak, 2)

@@ -350,6 +350,19 @@ mo_status mo_plan_keep_ns_output(mo_plan* plan, int32_t keep);
 /* 1 if the next grouped step will apply the update inside the last
  * Newton-Schulz launch (see mo_plan_keep_ns_output), else 0 (also for NULL). */
 int32_t mo_plan_fuses_update(const mo_plan* plan);
+/* 1 if the plan runs its GEMM-path slices in Gram space, else 0 (also for
+ * NULL).  The Newton-Schulz iteration of the NorMuon paper section 2.2,
+ * eq. (5), X <- a X + b A X with A = X X^T, keeps every iterate of the form
+ * Q X0 with Q a polynomial in A0 = X0 X0^T; the plan then forms A0 once,
+ * runs the iterations on s x s matrices (A_{k+1} = P_k A_k P_k,
+ * Q_{k+1} = P_k Q_k) and multiplies X0 once, by Q_N.  Chosen at plan
+ * creation for the bf16 path when every coefficient row has c = 0 and the
+ * environment does not set MO_NS_GRAM_SPACE=0; equal to the plain iteration
+ * up to rounding.  The slice-resident kernel (padded short side 128) runs
+ * the same sequence with its 128 x 128 matrices in LDS, two passes over X
+ * instead of N + 1, for slices with a short side of at least 64; smaller
+ * ones keep the plain iteration, where it is the more accurate in bf16. */
+int32_t mo_plan_gram_space(const mo_plan* plan);
 
 /* ------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel launch of this

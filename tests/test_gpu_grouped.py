@@ -221,13 +221,17 @@ def _mixed_shapes():
     return wl.Workload("mixed_shapes", 11, tuple(ps), grad_std=1e-3)
 
 
+@pytest.mark.parametrize("mode", ["gram_space", "plain"])
 @pytest.mark.parametrize("big_tiles", [False, True])
-def test_fused_update_bit_identical(big_tiles, monkeypatch):
+def test_fused_update_bit_identical(big_tiles, mode, monkeypatch):
     """The Muon update applied inside the last Newton-Schulz launch (the
     default) gives the same bits as the separate row pass over the stored O,
-    for every kernel that can end a step, over two steps."""
+    for every kernel that can end a step, over two steps, in the Gram-space
+    sequence and in the plain iteration."""
     if big_tiles:
         monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0")
+    if mode == "plain":
+        monkeypatch.setenv("MO_NS_GRAM_SPACE", "0")
     w = _mixed_shapes()
     runs = []
     for keep in (True, False):
@@ -301,3 +305,28 @@ def test_first_iteration_in_place_and_range_fallback(exp2, coeffs, monkeypatch):
         _, D = omuon.momentum(np.zeros_like(G[param]), G[param], wl.MUON_MU)
         O_ref = omuon.newton_schulz(D[off:off + r], cf)
         assert_ns_close(f64(plan.ns_output(k)), O_ref, "bf16")
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 7])
+@pytest.mark.parametrize("mode", ["gram_space", "plain"])
+def test_iteration_count_and_mode(steps, mode, monkeypatch):
+    """The grouped step's Newton-Schulz output for 1, 2, 3 and 7 cubic
+    iterations, in the Gram-space sequence (the default for the bf16 GEMM
+    path) and in the plain iteration (MO_NS_GRAM_SPACE=0), against the
+    oracle; both tile sizes (the 512-row slice on 256 x 256 tiles)."""
+    if mode == "plain":
+        monkeypatch.setenv("MO_NS_GRAM_SPACE", "0")
+    monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0")
+    w = _aligned_shapes()
+    cf = [(1.5, -0.5, 0.0)] * steps
+    ents = build_entries(w, normuon=False)
+    plan = api.Plan(ents, api.make_hparams(coeffs=cf))
+    plan.keep_ns_output(True)
+    for i, (e, p) in enumerate(zip(ents, w.params)):
+        e["grad"].copy_(to_dev(wl.grad(w, i, 1), p.dtype))
+    G = [f64(e["grad"]) for e in ents]
+    plan.step()
+    torch.cuda.synchronize()
+    for k, (param, off, r, c) in enumerate(plan.slices()):
+        _, D = omuon.momentum(np.zeros_like(G[param]), G[param], wl.MUON_MU)
+        assert_ns_close(f64(plan.ns_output(k)), omuon.newton_schulz(D[off:off + r], cf), "bf16")
