@@ -95,7 +95,9 @@ struct NsLayout {
 // s x s matrices (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q with
 // P kept implicit through the E term) and X0 is multiplied once, by Q_N, at
 // the end.  The slice-resident kernel does the same with its 128 x 128
-// matrices in LDS, for slices with a short side of at least kGramSpaceMinS:
+// matrices in LDS (quintic-type rows included, P_k = a_k I + R_k with
+// R_k = b_k A_k + c_k A_k^2), for slices with a short side of at least
+// kGramSpaceMinS:
 // on smaller ones the bf16 products of Gram space lose more than the plain
 // iteration (O(1) entries).  MO_NS_GRAM_SPACE=0 in the environment turns it
 // off.

@@ -1080,8 +1080,9 @@ __device__ __forceinline__ int sm_off(int row, int col) {
 // by the 8 waves of the slice-resident kernel (2 x 4 waves of 64 x 32
 // outputs).  With P_k = a_k I + R_k, R_k = b_k A_k + c_k A_k^2:
 // Q_1 = P_0, Q_{k+1} = P_k Q_k, T_k = P_k A_k, A_{k+1} = T_k P_k.  All
-// factors are polynomials in A_0, so every product is symmetric and each
-// operand is read as its own transpose.  In: A_0 (bf16) in xa.  Out: Q_N
+// factors are polynomials in A_0; the products are nonetheless formed
+// exactly as U V (the right factor read by columns), since after rounding
+// the factors no longer commute exactly.  In: A_0 (bf16) in xa.  Out: Q_N
 // (bf16) in qs.  xa and yb are scratch tiles (A, the quintic T; the cubic T
 // or the quintic R).  E terms are read one value at a time, so that the
 // phase needs no registers beyond one accumulator block.
@@ -1096,7 +1097,12 @@ __device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_ch
     return *reinterpret_cast<const lds_u32x4*>(t + m * 256 +
                                                ((((2 * ks + fg) ^ sm_swz(m)) & 15) << 4));
   };
-  // x = U V^T over the wave's 64 x 32 block
+  // x = U V over the wave's 64 x 32 block: U by rows, V by columns
+  // (transpose reads of its 16-row slabs), so the product is exact whether
+  // or not the rounded factors are still exactly symmetric
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int trow = 8 * (g16 >> 1) + (j16 >> 2);
+  const int tcol = wn * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
   auto prod = [&](const lds_char* u, const lds_char* v, f32x16 (&x)[2])
       __attribute__((always_inline)) {
 #pragma unroll
@@ -1105,7 +1111,9 @@ __device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_ch
       for (int e = 0; e < 16; ++e) x[mi][e] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 bf = frag(v, wn * 32 + fr, ks);
+      const u32x2 lo = lds_read_tr16((const char*)(v + sm_off(16 * ks + trow, tcol)));
+      const u32x2 hi = lds_read_tr16((const char*)(v + sm_off(16 * ks + trow + 4, tcol)));
+      const u32x4 bf{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(frag(u, wm * 64 + mi * 32 + fr, ks), bf, x[mi]);
     }

@@ -92,7 +92,9 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     const int32_t sp = pad_to(s_, tile), lp = pad_to(l_, tile);
     const bool small = elem == 2 && tile == kGemmTile && sp == kSmallS;
     const bool gs = gspace_mode && !small;
-    const bool sgs = gspace_mode && small && s_ >= kGramSpaceMinS;
+    // (the slice-resident kernel's Gram space also takes quintic-type rows)
+    const bool sgs = elem == 2 && steps > 0 && gram_space_enabled() && small &&
+                     s_ >= kGramSpaceMinS;
     const int64_t x[2] = {take(static_cast<int64_t>(sp) * lp), take(static_cast<int64_t>(sp) * lp)};
     const int64_t p = small || gs ? -1 : take(static_cast<int64_t>(sp) * sp);
     const int64_t a = need_a && !small ? take(static_cast<int64_t>(sp) * sp) : -1;

@@ -360,8 +360,9 @@ int32_t mo_plan_fuses_update(const mo_plan* plan);
  * environment does not set MO_NS_GRAM_SPACE=0; equal to the plain iteration
  * up to rounding.  The slice-resident kernel (padded short side 128) runs
  * the same sequence with its 128 x 128 matrices in LDS, two passes over X
- * instead of N + 1, for slices with a short side of at least 64; smaller
- * ones keep the plain iteration, where it is the more accurate in bf16. */
+ * instead of N + 1, for bf16 slices with a short side of at least 64 and
+ * any coefficient rows (P_k = a_k I + b_k A_k + c_k A_k^2); smaller ones
+ * keep the plain iteration, where it is the more accurate in bf16. */
 int32_t mo_plan_gram_space(const mo_plan* plan);
 
 /* ------------------------------------------------------------------------

@@ -309,16 +309,23 @@ def test_first_iteration_in_place_and_range_fallback(exp2, coeffs, monkeypatch):
 
 @pytest.mark.parametrize("steps", [1, 2, 3, 7])
 @pytest.mark.parametrize("mode", ["gram_space", "plain"])
-def test_iteration_count_and_mode(steps, mode, monkeypatch):
-    """The grouped step's Newton-Schulz output for 1, 2, 3 and 7 cubic
-    iterations, in the Gram-space sequence (the default for the bf16 GEMM
-    path) and in the plain iteration (MO_NS_GRAM_SPACE=0), against the
-    oracle; both tile sizes (the 512-row slice on 256 x 256 tiles)."""
+@pytest.mark.parametrize("row", ["cubic", "quintic"])
+def test_iteration_count_and_mode(steps, mode, row, monkeypatch):
+    """The grouped step's Newton-Schulz output for 1, 2, 3 and 7 iterations,
+    in Gram space (the default for the bf16 path: cubic rows on the GEMM
+    path, any rows in the slice-resident kernel for short sides >= 64) and in
+    the plain iteration (MO_NS_GRAM_SPACE=0), against the oracle, over GEMM
+    slices on both tile sizes and slice-resident slices on both sides of the
+    64-row threshold."""
     if mode == "plain":
         monkeypatch.setenv("MO_NS_GRAM_SPACE", "0")
     monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0")
-    w = _aligned_shapes()
-    cf = [(1.5, -0.5, 0.0)] * steps
+    base = _aligned_shapes()
+    extra = [wl.ParamSpec("small_wide", (96, 256), "bf16"),
+             wl.ParamSpec("small_tall", (392, 120), "bf16"),
+             wl.ParamSpec("kv", (80, 64), "bf16", view=(2, 40, 64), split=(16, 24))]
+    w = wl.Workload("iteration_shapes", 17, base.params + tuple(extra), grad_std=1e-3)
+    cf = [(1.5, -0.5, 0.0) if row == "cubic" else (15 / 8, -5 / 4, 3 / 8)] * steps
     ents = build_entries(w, normuon=False)
     plan = api.Plan(ents, api.make_hparams(coeffs=cf))
     plan.keep_ns_output(True)
