@@ -1287,9 +1287,12 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
     else at_2 = cur;
   };
 
-#pragma unroll 1
-  for (int cur = 0; cur < total; ++cur) {
-    const int pass = cur / NB, b = cur - pass * NB;
+  // One element of the pipeline: block b of pass `pass`.  PC >= 0 fixes the
+  // pass at compile time (the Gram-space kernel runs its two passes as two
+  // loops, so that each loop only holds the registers its pass needs).
+  auto element = [&](int cur, int pass_rt, auto pc) __attribute__((always_inline)) {
+    constexpr int PC = decltype(pc)::value;
+    const int pass = PC >= 0 ? PC : pass_rt, b = cur - pass * NB;
     int done;   // stores of elements <= done are complete after the wait below
     if (next == cur) {
       // not issued ahead (its block was written too recently): drain, then load
@@ -1512,6 +1515,17 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
     }
     at_0 = at_1;
     at_1 = at_2;
+  };
+  if constexpr (GS) {
+#pragma unroll 1
+    for (int cur = 0; cur < NB; ++cur) element(cur, 0, Int<0>{});
+#pragma unroll 1
+    for (int cur = NB; cur < total; ++cur) element(cur, 1, Int<1>{});
+  } else {
+#pragma unroll 1
+    for (int pass = 0; pass <= npass; ++pass)
+#pragma unroll 1
+      for (int cur = pass * NB; cur < (pass + 1) * NB; ++cur) element(cur, pass, Int<-1>{});
   }
 }
 
