@@ -91,7 +91,9 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     const int tile = B.tile;
     const int32_t sp = pad_to(s_, tile), lp = pad_to(l_, tile);
     const bool small = elem == 2 && tile == kGemmTile && sp == kSmallS;
-    const bool gs = gspace_mode && !small;
+    // GEMM path: rectangular slices only; on a square one Gram space executes
+    // the same flops as the plain iteration in one more launch
+    const bool gs = gspace_mode && !small && 4 * l_ >= 5 * s_;
     // (the slice-resident kernel's Gram space also takes quintic-type rows)
     const bool sgs = elem == 2 && steps > 0 && gram_space_enabled() && small &&
                      s_ >= kGramSpaceMinS;

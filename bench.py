@@ -292,8 +292,12 @@ def main() -> int:
                                      gram_space=gspace, sxs_on_chip=kname == "ns_small")
         n = g["launches_per_step"]
         t = g["avg_launch_ms"] * 1e-3
-        # the binding roof is the one with the longer ideal time
-        mfma_bound = dense / (peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9)
+        # the binding roof is the one with the longer ideal time: for the
+        # GEMM launches on the method's dense count, for the slice-resident
+        # kernel on the flops it executes (in Gram space its s x s work is
+        # small next to its passes over X)
+        flops = dense if kname == "ns_gemm" else exe
+        mfma_bound = flops / (peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9)
         if mfma_bound:
             achieved = dense / n / t / 1e12
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
