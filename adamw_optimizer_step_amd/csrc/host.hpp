@@ -90,7 +90,9 @@ struct NsLayout {
 //    0 then reads D itself, the scale folded into the products.
 //
 // steps > 0 with a bf16 pool and cubic-type rows only (!need_a) selects the
-// Gram-space sequence for the GEMM slices: every iterate is P_k ... P_0 X0
+// Gram-space sequence for the rectangular GEMM slices (l >= 1.25 s; on a
+// square slice it executes the same flops in one more launch): every
+// iterate is P_k ... P_0 X0
 // with P_k = a_k I + b_k A_k, A_{k+1} = P_k A_k P_k, so the iterations run on
 // s x s matrices (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q with
 // P kept implicit through the E term) and X0 is multiplied once, by Q_N, at

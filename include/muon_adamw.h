@@ -356,9 +356,10 @@ int32_t mo_plan_fuses_update(const mo_plan* plan);
  * Q X0 with Q a polynomial in A0 = X0 X0^T; the plan then forms A0 once,
  * runs the iterations on s x s matrices (A_{k+1} = P_k A_k P_k,
  * Q_{k+1} = P_k Q_k) and multiplies X0 once, by Q_N.  Chosen at plan
- * creation for the bf16 path when every coefficient row has c = 0 and the
- * environment does not set MO_NS_GRAM_SPACE=0; equal to the plain iteration
- * up to rounding.  The slice-resident kernel (padded short side 128) runs
+ * creation for the bf16 path, for rectangular GEMM-path slices (long side at
+ * least 1.25 times the short side: on square ones it saves no work) when
+ * every coefficient row has c = 0 and the environment does not set
+ * MO_NS_GRAM_SPACE=0; equal to the plain iteration up to rounding.  The slice-resident kernel (padded short side 128) runs
  * the same sequence with its 128 x 128 matrices in LDS, two passes over X
  * instead of N + 1, for bf16 slices with a short side of at least 64 and
  * any coefficient rows (P_k = a_k I + b_k A_k + c_k A_k^2); smaller ones
