@@ -51,7 +51,7 @@ class ParamDesc(C.Structure):
     _fields_ = [("name", C.c_char_p), ("ident", i64), ("ndim", i32), ("role", i32),
                 ("shape", i64 * MO_MAX_NDIM), ("no_decay", i32), ("requires_grad", i32),
                 ("view_ndim", i32), ("nsplit", i32), ("view", i64 * MO_MAX_NDIM),
-                ("split", i64 * MO_MAX_SPLIT)]
+                ("split", i64 * MO_MAX_SPLIT), ("exclude_mask", C.c_uint32), ("reserved", i32)]
 
 
 class RouteOut(C.Structure):

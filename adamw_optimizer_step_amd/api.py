@@ -199,7 +199,9 @@ def adamw_clip_step(params: Sequence[torch.Tensor], grads: Sequence[Optional[tor
 def make_desc(name: str, shape: Sequence[int], role: str = "matrix", no_decay: bool = False,
               requires_grad: bool = True, ident: Optional[int] = None,
               view: Optional[Sequence[int]] = None,
-              split: Optional[Sequence[int]] = None) -> L.ParamDesc:
+              split: Optional[Sequence[int]] = None,
+              exclude: Optional[Sequence[int]] = None) -> L.ParamDesc:
+    """``exclude``: split positions whose pieces AdamW steps instead of Muon."""
     d = L.ParamDesc()
     d.name = name.encode()
     d.ident = ident if ident is not None else (hash(name) & 0x7FFFFFFFFFFFFFFF)
@@ -223,6 +225,10 @@ def make_desc(name: str, shape: Sequence[int], role: str = "matrix", no_decay: b
         d.nsplit = len(split)
         for i, s in enumerate(split):
             d.split[i] = int(s)
+    for j in exclude or ():
+        if not 0 <= int(j) < 32:
+            raise ValueError("excluded piece out of range")
+        d.exclude_mask |= 1 << int(j)
     return d
 
 
@@ -279,7 +285,8 @@ class Plan:
     ``entries``: dicts with ``desc`` (a ParamDesc from ``make_desc``), ``param``,
     ``grad`` (or None) and the states the routing needs: ``momentum`` (and
     ``normuon_v`` with NorMuon) for Muon params, ``exp_avg`` / ``exp_avg_sq``
-    for AdamW params.  The tensors must stay alive and in place.
+    for AdamW params and for Muon params with excluded pieces (all of the
+    param's size).  The tensors must stay alive and in place.
     """
 
     def __init__(self, entries: Sequence[dict], hparams: L.HParams):

@@ -87,8 +87,10 @@ struct GroupKey {
   int32_t decay;
   std::vector<int64_t> view;
   std::vector<int64_t> split;
+  uint32_t exclude = 0;
   bool operator<(const GroupKey& o) const {
-    return std::tie(alg, decay, view, split) < std::tie(o.alg, o.decay, o.view, o.split);
+    return std::tie(alg, decay, view, split, exclude) <
+           std::tie(o.alg, o.decay, o.view, o.split, o.exclude);
   }
 };
 }  // namespace
@@ -98,7 +100,14 @@ struct GroupKey {
 // OMN "Dual-Manifold Optimization": routing paragraph).
 mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* ngroups) {
   if (n < 0 || (n > 0 && (!d || !out))) return fail(MO_EINVAL, "bad routing arguments");
-  std::map<int64_t, std::pair<std::vector<int64_t>, std::vector<int64_t>>> views;
+  struct ViewRec {
+    std::vector<int64_t> view, split;
+    uint32_t exclude;
+    bool operator!=(const ViewRec& o) const {
+      return view != o.view || split != o.split || exclude != o.exclude;
+    }
+  };
+  std::map<int64_t, ViewRec> views;
   std::set<int64_t> seen;
   std::map<GroupKey, int32_t> groups;
   std::vector<Slice> sl;
@@ -112,11 +121,16 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
       mo_status s = expand_view(p.shape[0], p.shape[1], p.view_ndim, p.view, p.nsplit, p.split,
                                 sl);
       if (s != MO_OK) return s;
-      std::vector<int64_t> v(p.view, p.view + p.view_ndim), sp(p.split, p.split + p.nsplit);
+      if (!exclude_ok(p.nsplit, p.exclude_mask))
+        return fail(MO_ESHAPE, "param %d: bad exclude_mask for %d split pieces", i, p.nsplit);
+      ViewRec rec{std::vector<int64_t>(p.view, p.view + p.view_ndim),
+                  std::vector<int64_t>(p.split, p.split + p.nsplit), p.exclude_mask};
       auto it = views.find(p.ident);
-      if (it != views.end() && (it->second.first != v || it->second.second != sp))
+      if (it != views.end() && it->second != rec)
         return fail(MO_ECONFLICT, "param %d: conflicting views for one parameter", i);
-      views[p.ident] = {v, sp};
+      views[p.ident] = rec;
+    } else if (p.exclude_mask != 0) {
+      return fail(MO_ESHAPE, "param %d: exclude_mask needs a view with split sizes", i);
     }
   }
   int32_t ng = 0;
@@ -131,7 +145,11 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
     } else if (p.ndim == 2 && p.role != MO_ROLE_EMBEDDING && p.role != MO_ROLE_HEAD) {
       auto it = views.find(p.ident);
       k = {MO_ALG_MUON, 1, {}, {}};
-      if (it != views.end()) { k.view = it->second.first; k.split = it->second.second; }
+      if (it != views.end()) {
+        k.view = it->second.view;
+        k.split = it->second.split;
+        k.exclude = it->second.exclude;
+      }
     } else {
       k = {MO_ALG_ADAMW, 1, {}, {}};
     }
@@ -142,7 +160,8 @@ mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* n
     if (k.alg == MO_ALG_MUON) {
       expand_view(p.shape[0], p.shape[1], static_cast<int32_t>(k.view.size()), k.view.data(),
                   static_cast<int32_t>(k.split.size()), k.split.data(), sl);
-      nsl = static_cast<int32_t>(sl.size());
+      for (size_t j = 0; j < sl.size(); ++j)
+        nsl += piece_excluded(k.exclude, static_cast<int32_t>(k.split.size()), j) ? 0 : 1;
     }
     out[i] = {k.alg, k.decay, gi, nsl};
   }

@@ -17,6 +17,21 @@ mo_status expand_view(int64_t rows, int64_t cols, int32_t view_ndim, const int64
                       int32_t nsplit, const int64_t* split, std::vector<Slice>& out);
 mo_status route(const mo_param_desc* d, int32_t n, mo_route_out* out, int32_t* ngroups);
 
+// Excluded split pieces (Qwen3.8 optimizer notes, section 4: sub-blocks of a
+// fused weight that AdamW steps).  A mask is valid with split sizes, bits
+// below nsplit only, and at least one piece left to Muon.  expand_view lists
+// slices view matrix by view matrix, split piece by split piece, so slice j
+// is piece j % nsplit.
+inline bool exclude_ok(int32_t nsplit, uint32_t mask) {
+  if (mask == 0) return true;
+  if (nsplit <= 0 || nsplit > 31) return false;
+  const uint32_t all = (1u << nsplit) - 1u;
+  return (mask & ~all) == 0 && mask != all;
+}
+inline bool piece_excluded(uint32_t mask, int32_t nsplit, size_t j) {
+  return mask != 0 && nsplit > 0 && ((mask >> (j % static_cast<size_t>(nsplit))) & 1u) != 0;
+}
+
 // Newton-Schulz layout of a batch of independent matrices: padded pool
 // buffers per matrix and the GEMM / prep problem tables (pool offsets only;
 // device pointers and statistics ranges are filled by the caller).  Matrices

@@ -26,6 +26,8 @@ struct mo_plan {
   std::vector<mo_route_out> routes;
   std::vector<SliceRec> slices;     // all Muon slices, in param order
   std::vector<SliceRec> active;     // slices of Muon params with a gradient
+  std::vector<SliceRec> excluded;   // excluded pieces of Muon params with a gradient (AdamW)
+  std::vector<uint8_t> adam_owner;  // per param: AdamW steps it (whole or excluded pieces)
   std::vector<int32_t> steps;       // AdamW step counters (per param)
   int32_t ddt = MO_BF16;            // direction / pool dtype
   bool need_a = false;
@@ -75,6 +77,7 @@ mo_status build_plan(mo_plan* P) {
   P->need_a = false;
   for (int k = 0; k < hp.ns_steps; ++k) P->need_a |= hp.ns_coeffs[k][2] != 0.f;
   P->steps.assign(n, 0);
+  P->adam_owner.assign(n, 0);
 
   WsCursor ws;
   std::vector<Slice> sl;
@@ -95,7 +98,26 @@ mo_status build_plan(mo_plan* P) {
       // The routing key's view (the parameter's registered view) defines the slices.
       s = expand_view(R, C, p.desc.view_ndim, p.desc.view, p.desc.nsplit, p.desc.split, sl);
       if (s != MO_OK) return s;
-      for (const Slice& x : sl) {
+      const uint32_t mask = p.desc.exclude_mask;
+      if (mask && (!p.exp_avg || !p.exp_avg_sq))
+        return fail(MO_EINVAL, "param %d: excluded pieces need exp_avg and exp_avg_sq", i);
+      for (size_t j = 0; j < sl.size(); ++j) {
+        const Slice& x = sl[j];
+        if (piece_excluded(mask, p.desc.nsplit, j)) {
+          if (!p.grad) continue;
+          // AdamW over the piece's elements of W, G, m and v
+          const int64_t e0 = x.off * x.cols, es = dtype_size(p.dtype);
+          if (!aligned16(static_cast<const char*>(p.param) + e0 * es) ||
+              !aligned16(static_cast<const char*>(p.grad) + e0 * es) ||
+              !aligned16(p.exp_avg + e0) || !aligned16(p.exp_avg_sq + e0))
+            return fail(MO_EALIGN, "param %d: excluded piece at row %lld is not 16-byte aligned",
+                        i, static_cast<long long>(x.off));
+          P->excluded.push_back({i, x.off, x.rows, x.cols});
+          P->adam_blocks += ceil_div(x.rows * x.cols, kEltPerBlock);
+          ++P->n_adam;
+          P->adam_owner[i] = 1;
+          continue;
+        }
         P->slices.push_back({i, x.off, x.rows, x.cols});
         if (p.grad) P->active.push_back({i, x.off, x.rows, x.cols});
       }
@@ -108,6 +130,7 @@ mo_status build_plan(mo_plan* P) {
           return fail(MO_EALIGN, "param %d: AdamW pointers must be 16-byte aligned", i);
         P->adam_blocks += ceil_div(numel, kEltPerBlock);
         ++P->n_adam;
+        P->adam_owner[i] = 1;
       }
     }
   }
@@ -230,19 +253,37 @@ mo_status upload_tables(mo_plan* P, char* ws, hipStream_t st) {
   AdamSeg* ad = reinterpret_cast<AdamSeg*>(h + P->tab_adam);
   int64_t ablk = 0;
   int j = 0;
-  for (size_t i = 0; i < P->params.size(); ++i) {
+  auto add_seg = [&](size_t i, int64_t e0, int64_t numel) {
     const mo_param& p = P->params[i];
-    if (P->routes[i].algorithm != MO_ALG_ADAMW || !p.grad) continue;
-    int64_t numel = 1;
-    for (int k = 0; k < p.desc.ndim; ++k) numel *= p.desc.shape[k];
-    if (numel == 0) continue;
+    const int64_t es = static_cast<int64_t>(dtype_size(p.dtype));
     AdamSeg& s = ad[j++];
-    s.p = p.param; s.g = p.grad; s.m = p.exp_avg; s.v = p.exp_avg_sq; s.numel = numel;
+    s.p = static_cast<char*>(p.param) + e0 * es;
+    s.g = static_cast<const char*>(p.grad) + e0 * es;
+    s.m = p.exp_avg + e0;
+    s.v = p.exp_avg_sq + e0;
+    s.numel = numel;
     s.start = ablk; s.dt = p.dtype; s.t0 = P->steps[i] + 1;
     s.wd = P->routes[i].decay ? hp.adamw_wd : 0.f;
     s.pad = 0.f;
     ablk += ceil_div(numel, kEltPerBlock);
+  };
+  size_t ex = 0;
+  for (size_t i = 0; i < P->params.size(); ++i) {
+    const mo_param& p = P->params[i];
+    if (P->routes[i].algorithm == MO_ALG_MUON) {
+      for (; ex < P->excluded.size() && P->excluded[ex].param == static_cast<int32_t>(i); ++ex) {
+        const auto& x = P->excluded[ex];
+        add_seg(i, x.off * x.cols, x.rows * x.cols);
+      }
+      continue;
+    }
+    if (P->routes[i].algorithm != MO_ALG_ADAMW || !p.grad) continue;
+    int64_t numel = 1;
+    for (int k = 0; k < p.desc.ndim; ++k) numel *= p.desc.shape[k];
+    if (numel == 0) continue;
+    add_seg(i, 0, numel);
   }
+  if (j != P->n_adam) return fail(MO_EINVAL, "internal: AdamW segment count");
   if (P->tab_bytes) {
     mo_status s = stage_upload(P->dtab, h, P->tab_bytes, st);
     if (s != MO_OK) return s;
@@ -491,7 +532,7 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
   }
   if (fork) MO_HIP_TRY(hipStreamWaitEvent(st, P->ev_join, 0));
   for (size_t i = 0; i < P->params.size(); ++i)
-    if (P->routes[i].algorithm == MO_ALG_ADAMW && P->params[i].grad) ++P->steps[i];
+    if (P->adam_owner[i]) ++P->steps[i];
   ++P->tdelta;
   return MO_OK;
 }

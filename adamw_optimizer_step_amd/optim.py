@@ -23,14 +23,16 @@ class MuonAdamW:
     def __init__(self, named_params: Iterable, **hparams):
         """``named_params``: iterable of dicts with ``name``, ``param`` and optional
         ``role`` ('matrix' | 'embedding' | 'head' | 'norm'), ``no_decay``,
-        ``view``, ``split``, ``ident`` (tied parameters share one)."""
+        ``view``, ``split``, ``exclude`` (split positions stepped by AdamW),
+        ``ident`` (tied parameters share one)."""
         self.entries: List[dict] = []
         self.hp = make_hparams(**hparams)
         for k, e in enumerate(named_params):
             p: torch.Tensor = e["param"]
             desc = make_desc(e["name"], tuple(p.shape), e.get("role", "matrix"),
                              e.get("no_decay", False), p.requires_grad,
-                             e.get("ident", id(p)), e.get("view"), e.get("split"))
+                             e.get("ident", id(p)), e.get("view"), e.get("split"),
+                             e.get("exclude"))
             self.entries.append({"desc": desc, "param": p, "name": e["name"]})
         from .api import route
         routes, _ = route([e["desc"] for e in self.entries])
@@ -42,7 +44,7 @@ class MuonAdamW:
                 if self.hp.normuon:
                     e["normuon_v"] = torch.zeros(p.shape[0], dtype=torch.float32,
                                                  device=p.device)
-            elif alg == L.MO_ALG_ADAMW:
+            if alg == L.MO_ALG_ADAMW or (alg == L.MO_ALG_MUON and e["desc"].exclude_mask):
                 e["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device=p.device)
                 e["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32, device=p.device)
         self._plan: Optional[Plan] = None

@@ -212,11 +212,19 @@ mo_status adamw_clip_step(const mo_adamw_item* items, int32_t n, float lr, float
  *   ndim < 2 or no_decay                               -> AdamW, decay 0
  *   ndim == 2 and role not embedding/head              -> Muon (view, split), decay 1
  *   otherwise                                          -> AdamW, decay 1
- * Groups are keyed by (algorithm, view, split, decay) in order of first
- * appearance; out[i].group is the group index (-1 when skipped).  Views are
- * validated ("Recording independent matrix geometry"): MO_ESHAPE for a bad
- * view or split, MO_ECONFLICT for two views on one identity, MO_EEMPTY when
- * nothing is trainable.
+ * Groups are keyed by (algorithm, view, split, exclude_mask, decay) in order
+ * of first appearance; out[i].group is the group index (-1 when skipped).
+ * Views are validated ("Recording independent matrix geometry"): MO_ESHAPE
+ * for a bad view or split, MO_ECONFLICT for two views on one identity,
+ * MO_EEMPTY when nothing is trainable.
+ *
+ * exclude_mask follows the Qwen3.8 optimizer notes (section 4, fused
+ * matrices): the gate/vector sub-blocks of a fused weight that do not suit
+ * Muon are stepped by AdamW.  Bit j names split piece j, in every view matrix
+ * alike (this library's encoding; the notes give none).  It needs split
+ * sizes, bits below nsplit and at least one piece left to Muon, else
+ * MO_ESHAPE; it is ignored when the weight does not route to Muon.
+ * out[i].nslices counts the Muon slices only.
  * ------------------------------------------------------------------------ */
 typedef struct mo_param_desc {
   const char* name;       /* informational, may be NULL */
@@ -230,6 +238,8 @@ typedef struct mo_param_desc {
   int32_t nsplit;         /* 0 = no split */
   int64_t view[MO_MAX_NDIM];
   int64_t split[MO_MAX_SPLIT];
+  uint32_t exclude_mask;  /* bit j: split piece j of every view matrix goes to AdamW */
+  int32_t reserved;
 } mo_param_desc;
 
 typedef struct mo_route_out {
@@ -267,6 +277,13 @@ mo_status mo_expand_view(int64_t rows, int64_t cols, int32_t view_ndim, const in
  *   AdamW params with a grad: adamw_clip_step over all of them jointly
  *     (decay only for decaying groups); the per-parameter step counter t is
  *     kept by the plan and incremented after each call.
+ *   Excluded pieces of a Muon param (exclude_mask) are AdamW parameters of
+ *     their own: they join the clip norm and take the AdamW update with the
+ *     param's step counter, reading and writing exp_avg / exp_avg_sq at the
+ *     same element offsets as the param; Muon leaves their rows alone
+ *     (momentum, direction and weight).  Such a param needs momentum,
+ *     exp_avg and exp_avg_sq buffers of numel elements, and each excluded
+ *     piece must start on a 16-byte boundary in all four (MO_EALIGN).
  * Sources: as for the individual entry points above; the ordering of NorMuon
  * before the shape scale is this library's reading (the pages do not order
  * them).

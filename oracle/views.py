@@ -7,7 +7,10 @@ axes gives back the stored (R, C) shape, and nothing new is allocated.  The
 optional split sizes cut each view matrix's row axis again (MLA's K versus V
 rows within a head, "The layout declarations are literal").  The Qwen3.8 notes
 (section 4, fused matrices) state the same rule: each true sub-matrix is
-orthogonalised on its own.
+orthogonalised on its own.  The same section sends the gate/vector sub-blocks
+that do not suit Muon to AdamW instead; ``exclude`` names those pieces by
+their position in the split list, the same in every view matrix (this
+library's reading: the notes give no encoding).
 """
 
 from typing import List, Optional, Sequence, Tuple
@@ -44,6 +47,19 @@ def validate_view(stored: Sequence[int], view: Optional[Sequence[int]],
             raise ViewError(f"split {tuple(split)} does not sum to {r}")
 
 
+def validate_exclude(split: Optional[Sequence[int]], exclude) -> None:
+    """Excluded pieces are split positions; at least one piece stays Muon."""
+    if not exclude:
+        return
+    if split is None:
+        raise ViewError("excluded pieces need split sizes")
+    for j in exclude:
+        if not isinstance(j, int) or isinstance(j, bool) or not 0 <= j < len(split):
+            raise ViewError(f"excluded piece {j!r} is not a split position")
+    if len(set(exclude)) >= len(split):
+        raise ViewError("every piece excluded: route the weight to AdamW instead")
+
+
 def expand(stored: Sequence[int], view: Optional[Sequence[int]] = None,
            split: Optional[Sequence[int]] = None) -> List[Tuple[int, int, int]]:
     """Independent sub-matrices of a stored (R, C) weight as row slabs.
@@ -67,3 +83,16 @@ def expand(stored: Sequence[int], view: Optional[Sequence[int]] = None,
             out.append((off, q, C))
             off += q
     return out
+
+
+def expand_pieces(stored: Sequence[int], view: Optional[Sequence[int]] = None,
+                  split: Optional[Sequence[int]] = None, exclude=None):
+    """``expand`` cut in two: (Muon slices, excluded slices).  A slice is
+    excluded when its split position is listed in ``exclude``."""
+    validate_exclude(split, exclude)
+    muon, rest = [], []
+    ex = set(exclude or ())
+    npiece = len(split) if split is not None else 1
+    for k, sl in enumerate(expand(stored, view, split)):
+        (rest if k % npiece in ex else muon).append(sl)
+    return muon, rest

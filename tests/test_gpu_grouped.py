@@ -13,10 +13,11 @@ from adamw_optimizer_step_amd import api
 from oracle import muon as omuon
 from oracle.hybrid import HybridState, HyperParams, hybrid_step
 from oracle.routing import descs_from_specs
-from oracle.views import expand
+from oracle.views import expand, expand_pieces
 
 from gpu_common import (NS_BF16_MAXABS, NS_BF16_RELFRO, NS_F32_MAXABS, REL_F32,
-                        assert_bf16_close, assert_ns_close, f64, rel_inf, require_gpu, to_dev)
+                        assert_bf16_close, assert_ns_close, bf16_ulp, f64, rel_inf, require_gpu,
+                        to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,12 +35,13 @@ def build_entries(w: wl.Workload, normuon: bool, init=None):
     """Device tensors for a workload: W from the seeded init, zero states."""
     entries = []
     routes, _ = api.route([api.make_desc(p.name, p.shape, p.role, p.no_decay,
-                                         p.requires_grad, i, p.view, p.split)
+                                         p.requires_grad, i, p.view, p.split,
+                                         p.exclude)
                            for i, p in enumerate(w.params)])
     for i, (p, r) in enumerate(zip(w.params, routes)):
         W0 = wl.init_weight(w, i) if init is None else init[i]
         e = {"desc": api.make_desc(p.name, p.shape, p.role, p.no_decay, p.requires_grad, i,
-                                   p.view, p.split),
+                                   p.view, p.split, p.exclude),
              "param": to_dev(W0, p.dtype),
              "grad": torch.zeros(p.shape, dtype=TORCH_DT[p.dtype], device="cuda"),
              "route": r}
@@ -47,7 +49,7 @@ def build_entries(w: wl.Workload, normuon: bool, init=None):
             e["momentum"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
             if normuon:
                 e["normuon_v"] = torch.zeros(p.shape[0], dtype=torch.float32, device="cuda")
-        elif r[0] == L.MO_ALG_ADAMW:
+        if r[0] == L.MO_ALG_ADAMW or (r[0] == L.MO_ALG_MUON and p.exclude):
             e["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
             e["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
         entries.append(e)
@@ -337,3 +339,81 @@ def test_iteration_count_and_mode(steps, mode, row, monkeypatch):
     for k, (param, off, r, c) in enumerate(plan.slices()):
         _, D = omuon.momentum(np.zeros_like(G[param]), G[param], wl.MUON_MU)
         assert_ns_close(f64(plan.ns_output(k)), omuon.newton_schulz(D[off:off + r], cf), "bf16")
+
+
+@pytest.mark.parametrize("normuon", [False, True], ids=["plain", "normuon"])
+def test_grouped_excluded_pieces(normuon):
+    """Fused weights with excluded pieces (Qwen3.8 optimizer notes, section 4):
+    the excluded rows take the AdamW step (joint clip, the weight's step
+    counter) and Muon leaves their momentum and weight rows alone; the other
+    pieces take the Muon step."""
+    w = wl.fused_exclude()
+    ents = build_entries(w, normuon=normuon)
+    coeffs = wl.coeff_table("cubic")
+    plan = api.Plan(ents, api.make_hparams(coeffs=coeffs, normuon=normuon))
+    descs = _oracle_setup(w)
+    st = HybridState()
+    hp = HyperParams(coeffs=coeffs, normuon=normuon)
+    Wref = {p.name: f64(e["param"]) for p, e in zip(w.params, ents)}
+    norm = torch.zeros(1, dtype=torch.float64, device="cuda")
+    for step in (1, 2, 3):
+        G = {}
+        for i, (p, e) in enumerate(zip(w.params, ents)):
+            g = wl.grad(w, i, step)
+            e["grad"].copy_(to_dev(g, p.dtype))
+            G[p.name] = wl.from_storage(g, p.dtype).astype(np.float64)
+        Wold = {p.name: f64(e["param"]) for p, e in zip(w.params, ents)}
+        vold = {p.name: f64(e["normuon_v"]) for p, e in zip(w.params, ents) if "normuon_v" in e}
+        plan.step(norm_out=norm)
+        torch.cuda.synchronize()
+        print(f"[excluded pieces] normuon={normuon} step {step}", flush=True)
+        out = hybrid_step(descs, Wref, G, st, hp, keep_outputs=True)
+        assert abs(f64(norm)[0] - out["T"]) <= 1e-12 * out["T"]
+        for p, e in zip(w.params, ents):
+            got = f64(e["param"])
+            if p.name in out["muon"]:
+                res = out["muon"][p.name]
+                mine, excl = expand_pieces(p.shape, p.view, p.split, p.exclude)
+                mom = f64(e["momentum"])
+                dgot, dref = got - Wold[p.name], -0.01 * res["U"]
+                pi = w.index(p.name)
+                for off, r, c in mine:
+                    rows = slice(off, off + r)
+                    assert rel_inf(mom[rows], res["B"][rows]) <= REL_F32
+                    sc = math.sqrt(max(1.0, r / c))
+                    if normuon:
+                        # the row step amplifies the Newton-Schulz rounding, so
+                        # it is checked on the GPU's own O (which is checked
+                        # against the oracle's)
+                        k = plan.slices().index((pi, off, r, c))
+                        O = f64(plan.ns_output(k))
+                        assert_ns_close(O, res["O"][rows], "bf16")
+                        On, v_exp = omuon.normuon_rownorm(O, vold[p.name][rows],
+                                                          hp.normuon_beta2, hp.normuon_eps)
+                        assert rel_inf(f64(e["normuon_v"])[rows], v_exp) <= 1e-5
+                        assert_bf16_close(got[rows],
+                                          omuon.apply_update(Wold[p.name][rows], sc * On, 0.01),
+                                          extra=2e-6 * 0.01 * sc * np.abs(On))
+                        continue
+                    err = np.abs(dgot[rows] - dref[rows]).max()
+                    ulp = bf16_ulp(Wold[p.name][rows]).max()
+                    assert err <= 0.01 * sc * NS_BF16_MAXABS + ulp, (p.name, off, err)
+                for off, r, c in excl:
+                    rows = slice(off, off + r)
+                    assert not mom[rows].any(), (p.name, off)
+                    want = out["W"][p.name][rows]
+                    assert np.all(np.abs(got[rows] - want) <= bf16_ulp(want)), (p.name, off)
+                    assert rel_inf(f64(e["exp_avg"])[rows], st.m[p.name][rows]) <= REL_F32
+                    assert rel_inf(f64(e["exp_avg_sq"])[rows], st.v[p.name][rows]) <= REL_F32
+                if excl:
+                    kept = np.ones(p.shape[0], bool)
+                    for off, r, _ in excl:
+                        kept[off:off + r] = False
+                    assert not f64(e["exp_avg"])[kept].any()
+            else:
+                want = out["W"][p.name]
+                assert np.all(np.abs(got - want) <= bf16_ulp(want)), p.name
+                assert rel_inf(f64(e["exp_avg"]), st.m[p.name]) <= REL_F32
+                assert rel_inf(f64(e["exp_avg_sq"]), st.v[p.name]) <= REL_F32
+            Wref[p.name] = got.copy()
+    assert plan.get_steps() == [3, 3, 0, 3]

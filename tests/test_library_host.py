@@ -49,7 +49,7 @@ def test_struct_layouts_match():
 
 def _descs_for(specs):
     return [api.make_desc(p.name, p.shape, p.role, p.no_decay, p.requires_grad, i, p.view,
-                          p.split) for i, p in enumerate(specs)]
+                          p.split, p.exclude) for i, p in enumerate(specs)]
 
 
 def _oracle_routes(specs):
@@ -61,15 +61,18 @@ def _oracle_routes(specs):
     for gi, g in enumerate(groups):
         for idx in g["indices"]:
             alg = L.MO_ALG_MUON if g["algorithm"] == "muon" else L.MO_ALG_ADAMW
-            nsl = len(oviews.expand(specs[idx].shape, g["view"], g["split"])) if alg == 1 else 0
+            nsl = len(oviews.expand_pieces(specs[idx].shape, g["view"], g["split"],
+                                           g["exclude"])[0]) if alg == 1 else 0
             want[idx] = (alg, int(g["decay"]), gi, nsl)
     return want, len(groups)
 
 
 @pytest.mark.parametrize("specs", [wl.tiny_routing().params, wl.dense_decoder().params,
                                    wl.dense_decoder(fused_gate_up=True, normuon=True).params,
-                                   wl.head_batched().params, wl.omn1_shapes()],
-                         ids=["tiny", "dense", "dense_fused", "head_batched", "omn1"])
+                                   wl.head_batched().params, wl.omn1_shapes(),
+                                   wl.fused_exclude().params],
+                         ids=["tiny", "dense", "dense_fused", "head_batched", "omn1",
+                              "fused_exclude"])
 def test_route_bit_exact_with_oracle(specs):
     got, ng = api.route(_descs_for(specs))
     want, wng = _oracle_routes(specs)
@@ -118,7 +121,7 @@ def _fake_entries(specs, normuon=False):
     ents = []
     for i, (p, r) in enumerate(zip(specs, routes)):
         e = {"desc": api.make_desc(p.name, p.shape, p.role, p.no_decay, p.requires_grad, i,
-                                   p.view, p.split)}
+                                   p.view, p.split, p.exclude)}
         ents.append(e)
     arr = (L.Param * len(specs))()
     for i, (e, r) in enumerate(zip(ents, routes)):
@@ -133,8 +136,9 @@ def _fake_entries(specs, normuon=False):
     return arr
 
 
-@pytest.mark.parametrize("w", [wl.tiny_routing(), wl.head_batched(layers=2)],
-                         ids=["tiny", "head_batched_2l"])
+@pytest.mark.parametrize("w", [wl.tiny_routing(), wl.head_batched(layers=2),
+                               wl.fused_exclude()],
+                         ids=["tiny", "head_batched_2l", "fused_exclude"])
 def test_plan_slice_table_host_only(w):
     arr = _fake_entries(w.params)
     h = C.c_void_p()
@@ -148,7 +152,8 @@ def test_plan_slice_table_host_only(w):
         want = []
         for i, p in enumerate(w.params):
             if len(p.shape) == 2 and p.role == "matrix":
-                want += [(i, o, r, c) for o, r, c in oviews.expand(p.shape, p.view, p.split)]
+                want += [(i, o, r, c) for o, r, c in
+                         oviews.expand_pieces(p.shape, p.view, p.split, p.exclude)[0]]
         assert got == want
         assert L.lib().mo_plan_workspace_bytes(h) > 0
         steps = (C.c_int32 * len(w.params))()
@@ -256,3 +261,42 @@ def test_fused_update_eligibility():
     assert _fuses(ok, offset=8) == 0
     assert L.lib().mo_plan_fuses_update(None) == 0
     assert L.lib().mo_plan_keep_ns_output(None, 1) == L.MO_EINVAL
+
+
+def test_exclude_mask_validation():
+    ok = dict(view=(2, 12, 8), split=(4, 8))
+    for split, excl, want in (((4, 8), (1,), L.MO_OK), ((4, 8), (0, 1), L.MO_ESHAPE),
+                              ((4, 8), (2,), L.MO_ESHAPE), (None, (0,), L.MO_ESHAPE)):
+        kw = dict(ok, split=split)
+        d = [api.make_desc("f", (24, 8), ident=1, exclude=excl, **kw)]
+        arr = (L.ParamDesc * 1)(*d)
+        out = (L.RouteOut * 1)()
+        ng = C.c_int32()
+        assert L.lib().mo_route(arr, 1, out, C.byref(ng)) == want, (split, excl)
+        if want == L.MO_OK:
+            assert (out[0].algorithm, out[0].nslices) == (L.MO_ALG_MUON, 2)
+    # one identity, two registrations that disagree on the excluded pieces
+    d = [api.make_desc("f", (24, 8), ident=1, exclude=(1,), **ok),
+         api.make_desc("f2", (24, 8), ident=1, exclude=(0,), **ok)]
+    arr = (L.ParamDesc * 2)(*d)
+    out = (L.RouteOut * 2)()
+    assert L.lib().mo_route(arr, 2, out, C.byref(C.c_int32())) == L.MO_ECONFLICT
+
+
+def test_excluded_piece_alignment_and_buffers():
+    """An excluded piece is an AdamW segment at the param's element offset:
+    it needs exp_avg / exp_avg_sq and 16-byte aligned starts."""
+    ok = wl.ParamSpec("f", (24, 8), "bf16", view=(2, 12, 8), split=(4, 8), exclude=(1,))
+    h = C.c_void_p()
+    hp = api.make_hparams()
+    arr = _fake_entries([ok])
+    L.check("plan", L.lib().mo_plan_create(arr, 1, C.byref(hp), C.byref(h)))
+    assert L.lib().mo_plan_num_slices(h) == 2
+    L.lib().mo_plan_destroy(h)
+    arr = _fake_entries([ok])
+    arr[0].exp_avg = None
+    assert L.lib().mo_plan_create(arr, 1, C.byref(hp), C.byref(h)) == L.MO_EINVAL
+    # rows of 6 bf16 columns: the excluded piece at row 3 starts 36 bytes in
+    bad = wl.ParamSpec("f", (12, 6), "bf16", view=(2, 6, 6), split=(3, 3), exclude=(1,))
+    arr = _fake_entries([bad])
+    assert L.lib().mo_plan_create(arr, 1, C.byref(hp), C.byref(h)) == L.MO_EALIGN

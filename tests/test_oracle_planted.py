@@ -141,3 +141,22 @@ def test_view_mutant_is_caught(monkeypatch):
     cases = TV._load("view_examples.json")["cases"]
     assert _some_pin_fails([lambda: [TV.test_view_expansion_matches_bruteforce_reshape(c)
                                      for c in cases]])
+
+
+@pytest.mark.parametrize("kind", ["wrong_piece_index", "excluded_dropped"])
+def test_exclude_mutants_are_caught(monkeypatch, kind):
+    import test_oracle_hybrid as TH
+    from oracle import hybrid
+
+    def pieces(stored, view=None, split=None, exclude=None):
+        ex = set(exclude or ())
+        n = len(split) if split is not None else 1
+        sl = views.expand(stored, view, split)
+        if kind == "wrong_piece_index":     # piece of slice k taken as k // n
+            return ([x for k, x in enumerate(sl) if k // n not in ex],
+                    [x for k, x in enumerate(sl) if k // n in ex])
+        return [x for k, x in enumerate(sl) if k % n not in ex], []   # never sent to AdamW
+
+    monkeypatch.setattr(hybrid, "expand_pieces", pieces)
+    with pytest.raises(AssertionError):
+        TH.test_excluded_pieces_equal_separate_weights()

@@ -122,6 +122,7 @@ class ParamSpec:
     split: Optional[Tuple[int, ...]] = None
     requires_grad: bool = True
     no_decay: bool = False          # explicit no-decay membership
+    exclude: Optional[Tuple[int, ...]] = None   # split positions stepped by AdamW
 
     @property
     def numel(self) -> int:
@@ -179,6 +180,23 @@ def tiny_routing() -> Workload:
     )
     return Workload("tiny_routing_fp32", 1, params, steps=3, grad_std=1.0,
                     description="tiny routing check, fp32, 3 steps")
+
+
+def fused_exclude(dtype: str = "bf16", heads: int = 4) -> Workload:
+    """Mixed routing inside fused weights (Qwen3.8 optimizer notes, section 4):
+    a gated-delta-net input projection fused per head as q, k, v and two
+    one-row gate vectors, with the gate pieces excluded to AdamW; a fused
+    gate/up projection split in halves; an embedding and a norm gain."""
+    dk, dv, c = 64, 128, 256
+    params = (
+        ParamSpec("embed_tokens.weight", (512, c), dtype, ROLE_EMBEDDING, no_decay=True),
+        ParamSpec("gdn.in_proj.weight", (heads * (2 * dk + dv + 2), c), dtype,
+                  view=(heads, 2 * dk + dv + 2, c), split=(dk, dk, dv, 1, 1), exclude=(3, 4)),
+        ParamSpec("mlp.gate_up_proj.weight", (1024, c), dtype, view=(2, 512, c)),
+        _norm("norm.weight", c, dtype),
+    )
+    return Workload(f"fused_exclude_{dtype}", 6, params, steps=3, grad_std=1e-2,
+                    description="fused weights with excluded gate pieces, 3 steps")
 
 
 def ns_sweep(rows: int, cols: int, coeffs: str) -> Workload:
