@@ -77,6 +77,12 @@ class StepArgs(C.Structure):
     _fields_ = [("muon_lr", f32), ("adamw_lr", f32), ("norm_out", vp)]
 
 
+class LrSchedule(C.Structure):
+    _fields_ = [("peak", C.c_double), ("warmup_tokens", C.c_double),
+                ("stable_end_tokens", C.c_double), ("end_tokens", C.c_double),
+                ("floor", C.c_double)]
+
+
 #: (name, restype, argtypes) of every function the header declares.
 SIGNATURES = [
     ("mo_status_str", C.c_char_p, [i32]),
@@ -110,6 +116,7 @@ SIGNATURES = [
     ("mo_plan_fuses_update", i32, [vp]),
     ("mo_plan_gram_space", i32, [vp]),
     ("mo_abi_struct_size", C.c_size_t, [i32]),
+    ("mo_lr_at", i32, [C.POINTER(LrSchedule), C.c_double, C.POINTER(C.c_double)]),
     ("mo_timing_enable", i32, [i32]),
     ("mo_timing_read", i32, [i32, C.POINTER(C.c_double), C.POINTER(i64)]),
 ]
@@ -118,7 +125,8 @@ KERNEL_CLASSES = ["momentum", "ns_stats", "ns_scale", "ns_prep", "ns_gemm", "ns_
                   "adam_sumsq", "adam_norm", "adam_apply", "ns_small"]
 
 #: ctypes mirror of each struct, in the order of mo_abi_struct_size's index.
-ABI_STRUCTS = [MomentumItem, NsItem, AdamwItem, ParamDesc, RouteOut, Param, HParams, StepArgs]
+ABI_STRUCTS = [MomentumItem, NsItem, AdamwItem, ParamDesc, RouteOut, Param, HParams, StepArgs,
+               LrSchedule]
 
 
 class LibraryError(RuntimeError):

@@ -260,6 +260,35 @@ def expand_view(rows: int, cols: int, view: Optional[Sequence[int]] = None,
 # ---------------------------------------------------------------------------
 # Plan + grouped step
 # ---------------------------------------------------------------------------
+# ---------------------------------------------------------------------------
+# Host-only: token-clock learning-rate schedule
+# ---------------------------------------------------------------------------
+def lr_at(tokens: float, peak: float, warmup: float = 2e9, stable_end: float = 164e9,
+          end: float = 193e9, floor: float = 1e-5) -> float:
+    """Learning rate after ``tokens`` tokens: linear warmup, the peak, then a
+    square-root cooldown to ``floor`` (mo_lr_at)."""
+    sch = L.LrSchedule(peak, warmup, stable_end, end, floor)
+    out = C.c_double()
+    L.check("mo_lr_at", L.lib().mo_lr_at(C.byref(sch), float(tokens), C.byref(out)))
+    return out.value
+
+
+class TokenClock:
+    """One token clock for both optimizers, each at its own peak: ``advance``
+    counts an accepted accumulation window and returns (muon_lr, adamw_lr)."""
+
+    def __init__(self, muon_peak: float = 0.01, adamw_peak: float = 3e-4, **phases):
+        self.tokens = 0.0
+        self.muon_peak, self.adamw_peak, self.phases = muon_peak, adamw_peak, phases
+
+    def advance(self, window_tokens: float) -> Tuple[float, float]:
+        if window_tokens < 0:
+            raise ValueError("negative window")
+        self.tokens += window_tokens
+        return (lr_at(self.tokens, self.muon_peak, **self.phases),
+                lr_at(self.tokens, self.adamw_peak, **self.phases))
+
+
 def make_hparams(muon_lr=0.01, muon_wd=0.0, mu=0.95, nesterov=True, coeffs=((1.5, -0.5, 0.0),) * 5,
                  ns_precision="bf16", normuon=False, normuon_beta2=0.95, normuon_eps=1e-8,
                  adamw_lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, adamw_wd=0.0,

@@ -1,5 +1,6 @@
 // Host-only parts of the library: error strings, the routing predicate and
 // view expansion.  Nothing here touches the GPU.
+#include <cmath>
 #include <cstring>
 #include <map>
 #include <set>
@@ -203,6 +204,7 @@ size_t mo_abi_struct_size(int32_t which) {
     case 5: return sizeof(mo_param);
     case 6: return sizeof(mo_hparams);
     case 7: return sizeof(mo_step_args);
+    case 8: return sizeof(mo_lr_schedule);
   }
   return 0;
 }
@@ -210,6 +212,29 @@ size_t mo_abi_struct_size(int32_t which) {
 mo_status mo_route(const mo_param_desc* descs, int32_t n, mo_route_out* out, int32_t* ngroups) {
   mo::clear_error();
   return mo::route(descs, n, out, ngroups);
+}
+
+// Token-clock schedule (OMN "Dual-Manifold Optimization" page: warmup,
+// stable phase, square-root cooldown to an absolute floor).
+mo_status mo_lr_at(const mo_lr_schedule* s, double tokens, double* lr) {
+  mo::clear_error();
+  if (!s || !lr) return mo::fail(MO_EINVAL, "NULL schedule or output");
+  const double W = s->warmup_tokens, S = s->stable_end_tokens, E = s->end_tokens;
+  if (!(tokens >= 0.0) || !(W >= 0.0 && W <= S && S <= E) ||
+      !(s->floor >= 0.0 && s->floor <= s->peak))
+    return mo::fail(MO_EINVAL, "bad schedule (need 0 <= W <= S <= E, 0 <= floor <= peak, "
+                               "tokens >= 0)");
+  if (tokens < W) {
+    *lr = s->peak * tokens / W;
+  } else if (tokens < S) {
+    *lr = s->peak;
+  } else if (tokens < E) {
+    const double x = (tokens - S) / (E - S);
+    *lr = s->floor + (s->peak - s->floor) * (1.0 - std::sqrt(x));
+  } else {
+    *lr = s->floor;
+  }
+  return MO_OK;
 }
 
 mo_status mo_expand_view(int64_t rows, int64_t cols, int32_t view_ndim, const int64_t* view,

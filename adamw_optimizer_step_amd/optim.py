@@ -20,11 +20,12 @@ from .api import Plan, make_desc, make_hparams
 
 
 class MuonAdamW:
-    def __init__(self, named_params: Iterable, **hparams):
+    def __init__(self, named_params: Iterable, clock=None, **hparams):
         """``named_params``: iterable of dicts with ``name``, ``param`` and optional
         ``role`` ('matrix' | 'embedding' | 'head' | 'norm'), ``no_decay``,
         ``view``, ``split``, ``exclude`` (split positions stepped by AdamW),
-        ``ident`` (tied parameters share one)."""
+        ``ident`` (tied parameters share one).  ``clock``: an optional
+        ``api.TokenClock`` that ``step(window_tokens=...)`` advances."""
         self.entries: List[dict] = []
         self.hp = make_hparams(**hparams)
         for k, e in enumerate(named_params):
@@ -49,6 +50,7 @@ class MuonAdamW:
                 e["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32, device=p.device)
         self._plan: Optional[Plan] = None
         self._grad_ptrs = None
+        self.clock = clock
 
     def _current_grads(self):
         return [None if e["param"].grad is None else e["param"].grad.data_ptr()
@@ -65,7 +67,14 @@ class MuonAdamW:
 
     @torch.no_grad()
     def step(self, muon_lr: Optional[float] = None, adamw_lr: Optional[float] = None,
-             norm_out: Optional[torch.Tensor] = None) -> None:
+             norm_out: Optional[torch.Tensor] = None,
+             window_tokens: Optional[float] = None) -> None:
+        """With ``window_tokens`` and a ``clock`` (an ``api.TokenClock``), the
+        clock counts the window and sets both rates for this step."""
+        if window_tokens is not None:
+            if self.clock is None:
+                raise ValueError("window_tokens needs a token clock")
+            muon_lr, adamw_lr = self.clock.advance(window_tokens)
         if self._plan is None or self._current_grads() != self._grad_ptrs:
             self._build()
         self._plan.step(muon_lr=muon_lr, adamw_lr=adamw_lr, norm_out=norm_out)

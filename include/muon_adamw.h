@@ -64,7 +64,7 @@ const char* mo_last_error(void);
 const char* mo_version(void);
 /* sizeof() of the ABI structs, for binding self-checks: 0 mo_momentum_item,
  * 1 mo_ns_item, 2 mo_adamw_item, 3 mo_param_desc, 4 mo_route_out, 5 mo_param,
- * 6 mo_hparams, 7 mo_step_args; 0 for any other index. */
+ * 6 mo_hparams, 7 mo_step_args, 8 mo_lr_schedule; 0 for any other index. */
 size_t mo_abi_struct_size(int32_t which);
 
 /* ------------------------------------------------------------------------
@@ -260,6 +260,32 @@ mo_status mo_route(const mo_param_desc* descs, int32_t n, mo_route_out* out, int
 mo_status mo_expand_view(int64_t rows, int64_t cols, int32_t view_ndim, const int64_t* view,
                          int32_t nsplit, const int64_t* split, int64_t* out_slices,
                          int32_t max_slices, int32_t* nslices);
+
+/* ------------------------------------------------------------------------
+ * Host-only: token-clock learning-rate schedule.
+ *
+ * OMN "Dual-Manifold Optimization" page (opening summary; recipe paragraph on
+ * separate peaks): warmup over the first 2B tokens, the peak held to 164B,
+ * then a square-root cooldown to an absolute floor of 1e-5 at about 193B;
+ * Muon and AdamW follow the same phases from their own peaks (0.01, 3e-4) on
+ * one token clock.  The page prints no formula; this library's reading, with
+ * tau the clock after the current accumulation window is counted:
+ *   tau < W:           lr = peak * tau / W
+ *   W <= tau < S:      lr = peak
+ *   S <= tau < E:      lr = floor + (peak - floor) * (1 - sqrt((tau - S) / (E - S)))
+ *   tau >= E:          lr = floor
+ * mo_lr_at writes lr (fp64) for one peak.  MO_EINVAL for a NULL pointer,
+ * tau < 0 or a NaN, unless 0 <= W <= S <= E and 0 <= floor <= peak.
+ * ------------------------------------------------------------------------ */
+typedef struct mo_lr_schedule {
+  double peak;
+  double warmup_tokens;      /* W, the page's value 2e9 */
+  double stable_end_tokens;  /* S, 164e9 */
+  double end_tokens;         /* E, about 193e9 */
+  double floor;              /* 1e-5 */
+} mo_lr_schedule;
+
+mo_status mo_lr_at(const mo_lr_schedule* s, double tokens, double* lr);
 
 /* ------------------------------------------------------------------------
  * Plan + grouped hybrid step over a parameter-group table.

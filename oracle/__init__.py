@@ -22,7 +22,10 @@ Everything is float64 numpy, written step by step from the pages:
 * ``adamw``   - global-norm clip over the AdamW parameters and the AdamW
                 update (OMN page, recipe paragraph; Qwen3.8 optimizer notes,
                 "Adam/AdamW" background).
-* ``hybrid``  - one full hybrid step over a parameter table.
+* ``hybrid``  - one full hybrid step over a parameter table, with excluded
+                pieces of fused weights (Qwen3.8 optimizer notes, section 4).
+* ``schedule``- the token-clock learning-rate schedule (OMN page, opening
+                summary and the recipe paragraph on separate peaks).
 * ``bf16``    - exact widening of bf16 storage and fp64 -> bf16 rounding.
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test
@@ -33,4 +36,4 @@ the prescribed-SVD closed form (exact for every input built that way); no page
 prints such values.
 """
 
-from . import adamw, bf16, hybrid, muon, routing, views  # noqa: F401
+from . import adamw, bf16, hybrid, muon, routing, schedule, views  # noqa: F401

@@ -300,3 +300,29 @@ def test_excluded_piece_alignment_and_buffers():
     bad = wl.ParamSpec("f", (12, 6), "bf16", view=(2, 6, 6), split=(3, 3), exclude=(1,))
     arr = _fake_entries([bad])
     assert L.lib().mo_plan_create(arr, 1, C.byref(hp), C.byref(h)) == L.MO_EALIGN
+
+
+def test_lr_schedule_matches_oracle():
+    """mo_lr_at against the oracle's token-clock schedule over every phase,
+    both peaks, and a shortened schedule; bad arguments are MO_EINVAL."""
+    from oracle import schedule as osched
+    taus = [0.0, 1.0, 1e6, 0.7e9, 1.999e9, 2e9, 50e9, 163.9e9, 164e9, 164e9 + 1,
+            170e9, 185e9, 192.99e9, 193e9, 1e12]
+    for peak in (0.01, 3e-4):
+        for t in taus:
+            assert api.lr_at(t, peak) == pytest.approx(osched.lr_at(t, peak), rel=1e-14, abs=0)
+    short = dict(warmup=10.0, stable_end=40.0, end=100.0, floor=1e-4)
+    for t in np.linspace(0, 120, 241):
+        assert api.lr_at(t, 0.02, **short) == pytest.approx(osched.lr_at(t, 0.02, **short),
+                                                            rel=1e-14, abs=0)
+    c, oc = api.TokenClock(), osched.TokenClock()
+    for w in [0.5e9] * 4 + [80e9, 82e9, 14.5e9, 14.5e9]:
+        got, want = c.advance(w), oc.advance(w)
+        assert got == pytest.approx(want, rel=1e-14)
+    out = C.c_double()
+    for bad in (L.LrSchedule(0.01, 5e9, 4e9, 193e9, 1e-5), L.LrSchedule(0.01, 2e9, 164e9, 193e9, 1.0)):
+        assert L.lib().mo_lr_at(C.byref(bad), 1.0, C.byref(out)) == L.MO_EINVAL
+    ok = L.LrSchedule(0.01, 2e9, 164e9, 193e9, 1e-5)
+    assert L.lib().mo_lr_at(C.byref(ok), -1.0, C.byref(out)) == L.MO_EINVAL
+    assert L.lib().mo_lr_at(C.byref(ok), float("nan"), C.byref(out)) == L.MO_EINVAL
+    assert L.lib().mo_lr_at(None, 1.0, C.byref(out)) == L.MO_EINVAL

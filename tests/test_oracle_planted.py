@@ -160,3 +160,28 @@ def test_exclude_mutants_are_caught(monkeypatch, kind):
     monkeypatch.setattr(hybrid, "expand_pieces", pieces)
     with pytest.raises(AssertionError):
         TH.test_excluded_pieces_equal_separate_weights()
+
+
+@pytest.mark.parametrize("kind", ["linear_cooldown", "floor_relative"])
+def test_schedule_mutants_are_caught(monkeypatch, kind):
+    import test_oracle_schedule as TS
+    from oracle import schedule
+
+    def lr(tokens, peak, warmup=2e9, stable_end=164e9, end=193e9, floor=1e-5):
+        if tokens < warmup:
+            return peak * tokens / warmup
+        if tokens < stable_end:
+            return peak
+        if tokens < end:
+            x = (tokens - stable_end) / (end - stable_end)
+            if kind == "linear_cooldown":
+                return floor + (peak - floor) * (1.0 - x)
+            return peak * (floor + (1 - floor) * (1.0 - math.sqrt(x)))
+        return floor if kind == "linear_cooldown" else peak * floor
+
+    monkeypatch.setattr(schedule, "lr_at", lr)
+    monkeypatch.setattr(TS, "lr_at", lr)      # the pins bound the name at import
+    with pytest.raises(AssertionError):
+        for peak in (0.01, 3e-4):
+            TS.test_phase_boundaries_from_the_page(peak)
+            TS.test_square_root_cooldown_shape(peak)
