@@ -50,6 +50,10 @@ def workload_by_name(name: str, coeffs: str = "cubic"):
     return table[name]()
 
 
+# Gram space: shortest short side in the slice-resident kernel
+GS_MIN_SHORT = 64
+
+
 def ns_work(slices, coeffs, elem, w_elem=None, gram_space=False, sxs_on_chip=False):
     """Newton-Schulz work per step, from the per-slice unit figures (s = short
     side, l = long side of each slice, N iterations):
@@ -58,7 +62,10 @@ def ns_work(slices, coeffs, elem, w_elem=None, gram_space=False, sxs_on_chip=Fal
     * executed flops, plain iteration with the symmetric Gram: 3 s^2 l
       (+ s^3) per iteration; Gram-space sequence (cubic rows): s^2 l for
       A0 = X0 X0^T, 3 N - 3 symmetric s x s products of s^3 each, and
-      2 s^2 l for X_N = Q_N X0;
+      2 s^2 l for X_N = Q_N X0.  With ``gram_space`` set, a slice runs in
+      Gram space under the library's rule: in the slice-resident kernel
+      (sxs_on_chip) when s >= 64, in the GEMM path when 4 l >= 5 s (a square
+      slice executes the same flops either way and stays plain);
     * HBM bytes when X does not stay on chip: plain, one read of X0 for the
       first Gram, then a read of X and a write of X' per iteration:
       elem * s * l * (2 N + 1); Gram space, two reads of X0 and one write of
@@ -76,7 +83,8 @@ def ns_work(slices, coeffs, elem, w_elem=None, gram_space=False, sxs_on_chip=Fal
             dense += 4.0 * s * s * l
             if cc != 0.0:
                 dense += 2.0 * s ** 3
-        if gram_space:
+        gs = gram_space and (s >= GS_MIN_SHORT if sxs_on_chip else 4 * l >= 5 * s)
+        if gs:
             exe += 3.0 * s * s * l + (3 * n - 3) * s ** 3
             byt += elem * s * l * 3
             if not sxs_on_chip:
