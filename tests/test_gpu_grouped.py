@@ -341,8 +341,9 @@ def test_iteration_count_and_mode(steps, mode, row, monkeypatch):
         assert_ns_close(f64(plan.ns_output(k)), omuon.newton_schulz(D[off:off + r], cf), "bf16")
 
 
-@pytest.mark.parametrize("normuon", [False, True], ids=["plain", "normuon"])
-def test_grouped_excluded_pieces(normuon):
+@pytest.mark.parametrize("normuon,precision", [(False, "bf16"), (True, "bf16"), (False, "fp32")],
+                         ids=["plain", "normuon", "plain_fp32ns"])
+def test_grouped_excluded_pieces(normuon, precision):
     """Fused weights with excluded pieces (Qwen3.8 optimizer notes, section 4):
     the excluded rows take the AdamW step (joint clip, the weight's step
     counter) and Muon leaves their momentum and weight rows alone; the other
@@ -350,7 +351,9 @@ def test_grouped_excluded_pieces(normuon):
     w = wl.fused_exclude()
     ents = build_entries(w, normuon=normuon)
     coeffs = wl.coeff_table("cubic")
-    plan = api.Plan(ents, api.make_hparams(coeffs=coeffs, normuon=normuon))
+    plan = api.Plan(ents, api.make_hparams(coeffs=coeffs, normuon=normuon,
+                                           ns_precision=precision))
+    tol_ns = NS_F32_MAXABS if precision == "fp32" else NS_BF16_MAXABS
     descs = _oracle_setup(w)
     st = HybridState()
     hp = HyperParams(coeffs=coeffs, normuon=normuon)
@@ -366,7 +369,7 @@ def test_grouped_excluded_pieces(normuon):
         vold = {p.name: f64(e["normuon_v"]) for p, e in zip(w.params, ents) if "normuon_v" in e}
         plan.step(norm_out=norm)
         torch.cuda.synchronize()
-        print(f"[excluded pieces] normuon={normuon} step {step}", flush=True)
+        print(f"[excluded pieces] normuon={normuon} ns={precision} step {step}", flush=True)
         out = hybrid_step(descs, Wref, G, st, hp, keep_outputs=True)
         assert abs(f64(norm)[0] - out["T"]) <= 1e-12 * out["T"]
         for p, e in zip(w.params, ents):
@@ -397,7 +400,7 @@ def test_grouped_excluded_pieces(normuon):
                         continue
                     err = np.abs(dgot[rows] - dref[rows]).max()
                     ulp = bf16_ulp(Wold[p.name][rows]).max()
-                    assert err <= 0.01 * sc * NS_BF16_MAXABS + ulp, (p.name, off, err)
+                    assert err <= 0.01 * sc * tol_ns + ulp, (p.name, off, err)
                 for off, r, c in excl:
                     rows = slice(off, off + r)
                     assert not mom[rows].any(), (p.name, off)
