@@ -73,6 +73,15 @@ class HParams(C.Structure):
                 ("max_norm", f32)]
 
 
+class NsOptions(C.Structure):
+    _fields_ = [("gram_space", i32), ("big_tile_min_work", i32), ("few_tile_max", i32),
+                ("reserved", i32)]
+
+
+class PlanOptions(C.Structure):
+    _fields_ = [("ns", NsOptions), ("keep_ns_output", i32), ("reserved", i32)]
+
+
 class StepArgs(C.Structure):
     _fields_ = [("muon_lr", f32), ("adamw_lr", f32), ("norm_out", vp)]
 
@@ -90,9 +99,11 @@ SIGNATURES = [
     ("mo_version", C.c_char_p, []),
     ("muon_momentum_workspace_bytes", C.c_size_t, [i32]),
     ("muon_momentum", i32, [C.POINTER(MomentumItem), i32, f32, i32, vp, C.c_size_t, vp]),
-    ("ns_workspace_bytes", C.c_size_t, [C.POINTER(NsItem), i32, i32]),
-    ("ns_orthogonalize_batched", i32, [C.POINTER(NsItem), i32, C.POINTER(f32), i32, i32, vp,
-                                       C.c_size_t, vp]),
+    ("mo_ns_options_default", None, [C.POINTER(NsOptions)]),
+    ("ns_workspace_bytes", C.c_size_t, [C.POINTER(NsItem), i32, C.POINTER(f32), i32, i32,
+                                        C.POINTER(NsOptions)]),
+    ("ns_orthogonalize_batched", i32, [C.POINTER(NsItem), i32, C.POINTER(f32), i32, i32,
+                                       C.POINTER(NsOptions), vp, C.c_size_t, vp]),
     ("normuon_rownorm", i32, [vp, i32, i64, i64, i64, vp, f32, f32, vp]),
     ("muon_update", i32, [vp, i32, vp, i32, i64, i64, i64, i64, f32, f32, f32, vp]),
     ("adamw_workspace_bytes", C.c_size_t, [C.POINTER(AdamwItem), i32]),
@@ -101,7 +112,9 @@ SIGNATURES = [
     ("mo_route", i32, [C.POINTER(ParamDesc), i32, C.POINTER(RouteOut), C.POINTER(i32)]),
     ("mo_expand_view", i32, [i64, i64, i32, C.POINTER(i64), i32, C.POINTER(i64),
                              C.POINTER(i64), i32, C.POINTER(i32)]),
-    ("mo_plan_create", i32, [C.POINTER(Param), i32, C.POINTER(HParams), C.POINTER(vp)]),
+    ("mo_plan_options_default", None, [C.POINTER(PlanOptions)]),
+    ("mo_plan_create", i32, [C.POINTER(Param), i32, C.POINTER(HParams), C.POINTER(PlanOptions),
+                             C.POINTER(vp)]),
     ("mo_plan_destroy", None, [vp]),
     ("mo_plan_workspace_bytes", C.c_size_t, [vp]),
     ("mo_plan_route", i32, [vp, C.POINTER(RouteOut), i32]),
@@ -115,6 +128,7 @@ SIGNATURES = [
     ("mo_plan_keep_ns_output", i32, [vp, i32]),
     ("mo_plan_fuses_update", i32, [vp]),
     ("mo_plan_gram_space", i32, [vp]),
+    ("mo_plan_slice_algorithms", i32, [vp, C.POINTER(i32), i32]),
     ("mo_abi_struct_size", C.c_size_t, [i32]),
     ("mo_lr_at", i32, [C.POINTER(LrSchedule), C.c_double, C.POINTER(C.c_double)]),
     ("mo_timing_enable", i32, [i32]),
@@ -126,7 +140,7 @@ KERNEL_CLASSES = ["momentum", "ns_stats", "ns_scale", "ns_prep", "ns_gemm", "ns_
 
 #: ctypes mirror of each struct, in the order of mo_abi_struct_size's index.
 ABI_STRUCTS = [MomentumItem, NsItem, AdamwItem, ParamDesc, RouteOut, Param, HParams, StepArgs,
-               LrSchedule]
+               LrSchedule, NsOptions, PlanOptions]
 
 
 class LibraryError(RuntimeError):

@@ -107,19 +107,46 @@ def ns_items(inputs: Sequence[torch.Tensor], outputs: Sequence[torch.Tensor]):
     return items
 
 
-def ns_workspace_bytes(inputs: Sequence[torch.Tensor], precision: str = "bf16") -> int:
+def ns_options(gram_space: bool = True, big_tile_min_work: Optional[int] = None,
+               few_tile_max: Optional[int] = None) -> L.NsOptions:
+    """Newton-Schulz options (mo_ns_options); None keeps the library default."""
+    o = L.NsOptions()
+    L.lib().mo_ns_options_default(C.byref(o))
+    o.gram_space = int(bool(gram_space))
+    if big_tile_min_work is not None:
+        o.big_tile_min_work = int(big_tile_min_work)
+    if few_tile_max is not None:
+        o.few_tile_max = int(few_tile_max)
+    return o
+
+
+def _ns_opts(options) -> Optional[L.NsOptions]:
+    if options is None or isinstance(options, L.NsOptions):
+        return options
+    return ns_options(**options)
+
+
+def ns_workspace_bytes(inputs: Sequence[torch.Tensor], precision: str = "bf16", coeffs=None,
+                       options=None) -> int:
+    """Workspace of ns_orthogonalize_batched; without ``coeffs`` the most any
+    coefficient table can need."""
     items = ns_items(inputs, inputs)
-    return int(L.lib().ns_workspace_bytes(items, len(inputs), PRECISIONS[precision]))
+    opts = _ns_opts(options)
+    flat, steps = _coeff_array(coeffs) if coeffs is not None else (None, 0)
+    return int(L.lib().ns_workspace_bytes(items, len(inputs), flat, steps, PRECISIONS[precision],
+                                          None if opts is None else C.byref(opts)))
 
 
 def ns_orthogonalize_batched(inputs: Sequence[torch.Tensor],
                              outputs: Optional[Sequence[torch.Tensor]] = None,
                              coeffs=((1.5, -0.5, 0.0),) * 5, precision: str = "bf16",
-                             stream=None, workspace: Optional[torch.Tensor] = None):
+                             stream=None, workspace: Optional[torch.Tensor] = None,
+                             options=None):
     """Newton-Schulz orthogonalisation of independent 2-D matrices.
 
     Returns ``outputs`` (new tensors shaped and typed like the inputs when
-    not given).  ``coeffs`` is a sequence of per-iteration (a, b, c).
+    not given).  ``coeffs`` is a sequence of per-iteration (a, b, c);
+    ``options`` an ``ns_options(...)`` result or a dict of its arguments.
     """
     if outputs is None:
         outputs = [torch.empty_like(x) for x in inputs]
@@ -127,11 +154,13 @@ def ns_orthogonalize_batched(inputs: Sequence[torch.Tensor],
     items = ns_items(inputs, outputs)
     flat, steps = _coeff_array(coeffs)
     prec = PRECISIONS[precision]
-    need = int(L.lib().ns_workspace_bytes(items, n, prec))
+    opts = _ns_opts(options)
+    popts = None if opts is None else C.byref(opts)
+    need = int(L.lib().ns_workspace_bytes(items, n, flat, steps, prec, popts))
     if workspace is None or workspace.numel() < need:
         workspace = _workspace(need, inputs[0].device)
     L.check("ns_orthogonalize_batched",
-            L.lib().ns_orthogonalize_batched(items, n, flat, steps, prec,
+            L.lib().ns_orthogonalize_batched(items, n, flat, steps, prec, popts,
                                              C.c_void_p(workspace.data_ptr()),
                                              workspace.numel(), _stream(stream)))
     return outputs
@@ -308,6 +337,54 @@ def make_hparams(muon_lr=0.01, muon_wd=0.0, mu=0.95, nesterov=True, coeffs=((1.5
     return h
 
 
+def plan_options(keep_ns_output: bool = False, **ns) -> L.PlanOptions:
+    """Plan options (mo_plan_options): ``keep_ns_output`` and the
+    Newton-Schulz options of ``ns_options`` as keyword arguments."""
+    o = L.PlanOptions()
+    L.lib().mo_plan_options_default(C.byref(o))
+    o.ns = ns_options(**ns)
+    o.keep_ns_output = int(bool(keep_ns_output))
+    return o
+
+
+def _numel(shape) -> int:
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
+def _check_entry(i: int, e: dict) -> None:
+    """Shape, dtype, layout and device of one plan entry's tensors, checked
+    before the library records their addresses (it reads G with W's dtype
+    and every buffer with W's element count)."""
+    d = e["desc"]
+    shape = tuple(d.shape[k] for k in range(d.ndim))
+    numel = _numel(shape)
+    p = e.get("param")
+    if p is None:
+        return
+    if p.numel() != numel:
+        raise ValueError(f"entry {i}: param has {p.numel()} elements, descriptor {shape}")
+    dev = p.device
+    want = {"param": (p.dtype, numel), "grad": (p.dtype, numel),
+            "momentum": (torch.float32, numel), "exp_avg": (torch.float32, numel),
+            "exp_avg_sq": (torch.float32, numel),
+            "normuon_v": (torch.float32, shape[0] if shape else 0)}
+    for k, (dt, n) in want.items():
+        t = e.get(k)
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError(f"entry {i}: {k} on {t.device}, param on {dev}")
+        if t.dtype != dt:
+            raise TypeError(f"entry {i}: {k} is {t.dtype}, expected {dt}")
+        if not t.is_contiguous():
+            raise ValueError(f"entry {i}: {k} must be contiguous")
+        if t.numel() != n:
+            raise ValueError(f"entry {i}: {k} has {t.numel()} elements, expected {n}")
+
+
 class Plan:
     """Owns a C plan over a parameter table; ``step()`` runs one hybrid step.
 
@@ -315,27 +392,34 @@ class Plan:
     ``grad`` (or None) and the states the routing needs: ``momentum`` (and
     ``normuon_v`` with NorMuon) for Muon params, ``exp_avg`` / ``exp_avg_sq``
     for AdamW params and for Muon params with excluded pieces (all of the
-    param's size).  The tensors must stay alive and in place.
+    param's size).  The tensors must stay alive and in place.  ``options``:
+    a ``plan_options(...)`` result or a dict of its arguments.
     """
 
-    def __init__(self, entries: Sequence[dict], hparams: L.HParams):
+    def __init__(self, entries: Sequence[dict], hparams: L.HParams, options=None):
         n = len(entries)
         self._keep = list(entries)
         arr = (L.Param * max(n, 1))()
         for i, e in enumerate(entries):
+            _check_entry(i, e)
             arr[i].desc = e["desc"]
             arr[i].param = _ptr(e.get("param"))
             arr[i].grad = _ptr(e.get("grad"))
             if e.get("param") is not None:
                 arr[i].dtype = _dt(e["param"])
             for k in ("momentum", "normuon_v", "exp_avg", "exp_avg_sq"):
-                t = e.get(k)
-                if t is not None and t.dtype != torch.float32:
-                    raise TypeError(f"{k} must be fp32")
-                setattr(arr[i], k, _ptr(t))
+                setattr(arr[i], k, _ptr(e.get(k)))
         self._hp = hparams
+        if options is not None and not isinstance(options, L.PlanOptions):
+            options = plan_options(**options)
+        self._opts = options
         h = C.c_void_p()
-        L.check("mo_plan_create", L.lib().mo_plan_create(arr, n, C.byref(hparams), C.byref(h)))
+        # kept on the instance: __del__ may run after module globals are gone
+        self._destroy = L.lib().mo_plan_destroy
+        L.check("mo_plan_create",
+                L.lib().mo_plan_create(arr, n, C.byref(hparams),
+                                       None if options is None else C.byref(options),
+                                       C.byref(h)))
         self._h = h
         self.n = n
         self._ws: Optional[torch.Tensor] = None
@@ -343,8 +427,12 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            L.lib().mo_plan_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            try:
+                destroy(h)
+            except Exception:  # interpreter teardown
+                pass
             self._h = None
 
     @property
@@ -388,6 +476,15 @@ class Plan:
     def gram_space(self) -> bool:
         """True if the GEMM-path slices run the Gram-space sequence."""
         return bool(L.lib().mo_plan_gram_space(self._h))
+
+    def slice_algorithms(self) -> List[Tuple[bool, str]]:
+        """Per slice of ``slices()``: (Gram space, kernel) with kernel one of
+        'gemm128', 'gemm256', 'resident'; None for a slice without gradient."""
+        k = len(self.slices())
+        out = (C.c_int32 * max(k, 1))()
+        L.check("mo_plan_slice_algorithms", L.lib().mo_plan_slice_algorithms(self._h, out, k))
+        names = ("gemm128", "gemm256", "resident")
+        return [None if v < 0 else (bool(v & 1), names[v >> 1]) for v in out[:k]]
 
     def ns_output(self, slice_index: int, workspace: Optional[torch.Tensor] = None
                   ) -> torch.Tensor:

@@ -1,6 +1,7 @@
 // C entry points of the individual optimizer stages.  Each validates all of
 // its arguments before enqueueing anything, copies its descriptor table into
 // the caller's workspace and launches one kernel per stage on `stream`.
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -66,8 +67,8 @@ mo_status validate_ns_items(const mo_ns_item* items, int32_t n, int32_t precisio
   return MO_OK;
 }
 
-void ns_layout_from_items(const mo_ns_item* items, int32_t n, int32_t precision, bool need_a,
-                          NsLayout& L) {
+void ns_layout_from_items(const mo_ns_item* items, int32_t n, int32_t precision,
+                          const float* coeffs, int32_t steps, const NsOpts& opt, NsLayout& L) {
   std::vector<int64_t> r(n), c(n);
   std::vector<uint8_t> direct(n);
   for (int32_t i = 0; i < n; ++i) {
@@ -78,8 +79,16 @@ void ns_layout_from_items(const mo_ns_item* items, int32_t n, int32_t precision,
     direct[i] = precision == MO_NS_BF16 && items[i].in_dtype == MO_BF16 &&
                 items[i].ld_in == items[i].cols && aligned16(items[i].in);
   }
-  build_ns_layout(L, r.data(), c.data(), n, precision == MO_NS_F32 ? 4 : 2, need_a,
+  build_ns_layout(L, r.data(), c.data(), n, precision == MO_NS_F32 ? 4 : 2, coeffs, steps, opt,
                   direct.data(), true);
+}
+
+mo_status check_coeffs(const float* coeffs, int32_t steps) {
+  if (steps < 1 || steps > MO_NS_MAX_STEPS || !coeffs)
+    return fail(MO_EINVAL, "steps must be in [1, %d] with a coefficient table", MO_NS_MAX_STEPS);
+  for (int k = 0; k < 3 * steps; ++k)
+    if (!std::isfinite(coeffs[k])) return fail(MO_EINVAL, "non-finite coefficient");
+  return MO_OK;
 }
 
 // ----- AdamW -----------------------------------------------------------------
@@ -141,29 +150,46 @@ mo_status muon_momentum(const mo_momentum_item* items, int32_t n, float mu, int3
                          mu, nesterov, nullptr, st);
 }
 
-size_t ns_workspace_bytes(const mo_ns_item* items, int32_t n, int32_t precision) {
+void mo_ns_options_default(mo_ns_options* o) {
+  if (!o) return;
+  o->gram_space = 1;
+  o->big_tile_min_work = -1;
+  o->few_tile_max = -1;
+  o->reserved = 0;
+}
+
+size_t ns_workspace_bytes(const mo_ns_item* items, int32_t n, const float* coeffs, int32_t steps,
+                          int32_t precision, const mo_ns_options* opts) {
   if (validate_ns_items(items, n, precision) != MO_OK) return 0;
-  NsLayout L;
-  ns_layout_from_items(items, n, precision, true, L);
-  return ns_ws_layout(L).total;
+  NsOpts opt;
+  if (resolve_ns_options(opts, opt) != MO_OK) return 0;
+  if (coeffs) {
+    if (check_coeffs(coeffs, steps) != MO_OK) return 0;
+    NsLayout L;
+    ns_layout_from_items(items, n, precision, coeffs, steps, opt, L);
+    return ns_ws_layout(L).total;
+  }
+  // any table: the larger of the quintic-capable plain layout and the
+  // Gram-space layout (whose GEMM slices keep five s x s buffers)
+  const float quintic[3] = {1.875f, -1.25f, 0.375f}, cubic[3] = {1.5f, -0.5f, 0.f};
+  NsLayout La, Lb;
+  ns_layout_from_items(items, n, precision, quintic, 1, opt, La);
+  ns_layout_from_items(items, n, precision, cubic, 1, opt, Lb);
+  return std::max(ns_ws_layout(La).total, ns_ws_layout(Lb).total);
 }
 
 mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const float* coeffs,
-                                   int32_t steps, int32_t precision, void* ws, size_t ws_bytes,
-                                   void* stream) {
+                                   int32_t steps, int32_t precision, const mo_ns_options* opts,
+                                   void* ws, size_t ws_bytes, void* stream) {
   clear_error();
   mo_status s = validate_ns_items(items, n, precision);
   if (s != MO_OK) return s;
-  if (steps < 1 || steps > MO_NS_MAX_STEPS || !coeffs)
-    return fail(MO_EINVAL, "steps must be in [1, %d] with a coefficient table", MO_NS_MAX_STEPS);
-  bool need_a = false;
-  for (int k = 0; k < 3 * steps; ++k)
-    if (!std::isfinite(coeffs[k])) return fail(MO_EINVAL, "non-finite coefficient");
-  for (int k = 0; k < steps; ++k) need_a |= coeffs[3 * k + 2] != 0.f;
+  if ((s = check_coeffs(coeffs, steps)) != MO_OK) return s;
+  NsOpts opt;
+  if ((s = resolve_ns_options(opts, opt)) != MO_OK) return s;
   NsLayout L;
-  ns_layout_from_items(items, n, precision, need_a, L);
+  ns_layout_from_items(items, n, precision, coeffs, steps, opt, L);
   const NsWs W = ns_ws_layout(L);
-  // The size query assumes the quintic-capable layout, which is never smaller.
   if ((s = check_ws(ws, ws_bytes, W.total)) != MO_OK) return s;
 
   char* base = static_cast<char*>(ws);

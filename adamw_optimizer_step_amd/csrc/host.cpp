@@ -205,6 +205,8 @@ size_t mo_abi_struct_size(int32_t which) {
     case 6: return sizeof(mo_hparams);
     case 7: return sizeof(mo_step_args);
     case 8: return sizeof(mo_lr_schedule);
+    case 9: return sizeof(mo_ns_options);
+    case 10: return sizeof(mo_plan_options);
   }
   return 0;
 }

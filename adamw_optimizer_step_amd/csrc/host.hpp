@@ -48,8 +48,27 @@ inline bool piece_excluded(uint32_t mask, int32_t nsplit, size_t j) {
 // kernel instead (same iterate buffers and conventions, P kept in LDS).
 constexpr int kBigTile = 256;
 constexpr int kBigTileMinS = 512;
-constexpr int64_t kBigTileMinWork = 512;   // Gram tiles of the 256 bucket: 2 per CU
 constexpr int64_t kGramSpaceMinS = 64;
+// Gram space carries A_k = X_k X_k^T, whose small eigenvalues are the squares
+// of X's small singular values, so its bf16 rounding noise in those
+// directions is amplified by the table's gain prod_k a_k^2 (p'(0) = a_k per
+// iteration, squared), where the plain iteration's grows with prod_k a_k.
+// Emulated bf16 rounding over spiked and prescribed-spectrum inputs stays
+// within the bf16 tolerance up to a gain of about 650 and leaves it past
+// about 1900; the threshold admits the cubic set for up to 8 iterations and
+// the quintic for up to 5.
+constexpr double kGramSpaceMaxGain = 1024.0;
+
+// Resolved Newton-Schulz options (mo_ns_options with the defaults applied).
+struct NsOpts {
+  bool gram_space = true;
+  int64_t big_tile_min_work = 512;   // 256-bucket Gram tiles: 2 per CU
+  int64_t few_tile_max = 512;        // 8-wave 128 x 128 launches below this
+};
+// NULL = defaults; MO_EINVAL for out-of-range fields.
+mo_status resolve_ns_options(const mo_ns_options* o, NsOpts& out);
+// prod_k a_k^2 <= kGramSpaceMaxGain over the table's rows.
+bool gram_gain_ok(const float* coeffs, int steps);
 
 struct NsBucket {
   int tile = kGemmTile;
@@ -86,14 +105,20 @@ struct NsLayout {
   std::vector<int64_t> x_off[2];
   std::vector<int32_t> tall, sp, lp;
   std::vector<uint8_t> gspace;   // slice runs the Gram-space sequence
+  std::vector<uint8_t> kind;     // 0: GEMM, 128 x 128 tiles; 1: GEMM, 256 x 256; 2: slice-resident
   std::vector<SmallProb> small_gs;   // slice-resident slices run in Gram space
   int64_t pool_elems = 0;
+  int64_t few_tile_max = 512;        // 8-wave 128 x 128 launches below this many tiles
 
   // buffer of the final iterate (stored orientation) and its row stride
   int64_t final_off(int i, int steps) const { return x_off[gspace[i] ? 1 : steps & 1][i]; }
   int32_t final_ld(int i) const { return tall[i] ? sp[i] : lp[i]; }
 };
 
+// coeffs: the [steps][3] table (a, b, c) per iteration; its rows decide
+// whether A is kept (a row with c != 0) and, with `opt`, which slices run in
+// Gram space (see mo_ns_options).
+//
 // direct_ok[i] (nullable: none) says that slice i's input can be read in
 // place: bf16, row stride equal to cols, 16-byte aligned.  Such a slice
 // skips the prep copy (its prep item writes nothing, and has no tiles at all
@@ -104,23 +129,21 @@ struct NsLayout {
 //    it is not tall and both sides are multiples of its GEMM tile: iteration
 //    0 then reads D itself, the scale folded into the products.
 //
-// steps > 0 with a bf16 pool and cubic-type rows only (!need_a) selects the
-// Gram-space sequence for the rectangular GEMM slices (l >= 1.25 s; on a
-// square slice it executes the same flops in one more launch): every
-// iterate is P_k ... P_0 X0
-// with P_k = a_k I + b_k A_k, A_{k+1} = P_k A_k P_k, so the iterations run on
-// s x s matrices (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q with
-// P kept implicit through the E term) and X0 is multiplied once, by Q_N, at
-// the end.  The slice-resident kernel does the same with its 128 x 128
-// matrices in LDS (quintic-type rows included, P_k = a_k I + R_k with
-// R_k = b_k A_k + c_k A_k^2), for slices with a short side of at least
-// kGramSpaceMinS:
-// on smaller ones the bf16 products of Gram space lose more than the plain
-// iteration (O(1) entries).  MO_NS_GRAM_SPACE=0 in the environment turns it
-// off.
+// Gram space on the GEMM path (rectangular slices, l >= 1.25 s; on a square
+// slice it executes the same flops as the plain iteration in one more
+// launch; cubic-type rows only): every iterate is P_k ... P_0 X0 with
+// P_k = a_k I + b_k A_k, A_{k+1} = P_k A_k P_k, so the iterations run on
+// s x s matrices (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q with P kept
+// implicit through the E term) and X0 is multiplied once, by Q_N, at the end.
+// The slice-resident kernel does the same with its 128 x 128 matrices in LDS
+// (quintic-type rows included, P_k = a_k I + R_k with R_k = b_k A_k +
+// c_k A_k^2), for slices with a short side of at least kGramSpaceMinS: on
+// smaller ones the bf16 products of Gram space lose more than the plain
+// iteration (O(1) entries).
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
-                     bool need_a, const uint8_t* direct_ok, bool stats_from_prep,
-                     const int64_t* in_off = nullptr, int steps = 0);
+                     const float* coeffs, int steps, const NsOpts& opt,
+                     const uint8_t* direct_ok, bool stats_from_prep,
+                     const int64_t* in_off = nullptr);
 
 // Byte offsets of the device tables inside one contiguous table block.
 struct NsBucketTables {

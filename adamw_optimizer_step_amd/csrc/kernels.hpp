@@ -202,7 +202,10 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
 // c1 by pscale[sitem]^2 (bk = 0) or pscale[sitem] (bk = 1), unless
 // pfb[sitem] is set: they then read alt_off for the X operand(s), unscaled.
 // c1b, cdb: the constants of the second outputs (c2_off).
-mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
+// few_max: bf16 launches of fewer 128 x 128 tiles than this use the 8-wave
+// variant.
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
+                         int64_t few_max, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
                          const RowSeg* wt, float lr, const float* pscale, const int32_t* pfb,
                          hipStream_t st, float c1b = 0.f, float cdb = 0.f);

@@ -1573,18 +1573,6 @@ mo_status launch_ns_prep_fallback(const PrepItem* items, int n, const float* sca
   return MO_OK;
 }
 
-// Below this many tiles a 128-tile launch uses 8 waves per tile; the
-// environment variable MO_NS_FEW_TILES overrides it (0 = always 4 waves), for
-// tuning and for tests of both kernels.
-constexpr int64_t kFewTiles = 512;
-int64_t few_tiles() {
-  const char* e = std::getenv("MO_NS_FEW_TILES");
-  if (!e || !*e) return kFewTiles;
-  char* end = nullptr;
-  const long long v = std::strtoll(e, &end, 10);
-  return (end && *end == '\0' && v >= 0) ? static_cast<int64_t>(v) : kFewTiles;
-}
-
 template <typename T, int BM, int WM, int WN, int ST = 4, int SRB = 64>
 void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
                        float c1, int has_e, float cd, const RowSeg* wt, float lr,
@@ -1599,7 +1587,8 @@ void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T
         probs, n, pool, c0, c1, has_e, cd, wt, lr, pscale, pfb, c1b, cdb);
 }
 
-mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile, int bk,
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
+                         int64_t few_max, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
                          const RowSeg* wt, float lr, const float* pscale, const int32_t* pfb,
                          hipStream_t st, float c1b, float cdb) {
@@ -1628,7 +1617,7 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     // 64 x 32 instead of 4 of 64 x 64, and take 64-deep slabs (128-byte
     // rows; 4 stages, 128 KiB) instead of 32-deep ones.  15-20% faster on the
     // single-matrix sweeps; 8 stages of 32-deep slabs were slower.
-    if (elem == 2 && ntiles < few_tiles())
+    if (elem == 2 && ntiles < few_max)
       launch_gemm_shape<uint16_t, 128, 2, 4, 4, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
                                                      cd, wt, lr, pscale, pfb, c1b, cdb, st);

@@ -1,7 +1,6 @@
 // Host side of the Newton-Schulz path: pool layout, problem tables and the
 // iteration driver.
 #include <algorithm>
-#include <cstdlib>
 #include <cstring>
 
 #include "host.hpp"
@@ -27,22 +26,6 @@ GemmProb make_prob(int64_t a, int64_t b, int64_t c, int64_t ct, int64_t e, int32
   return p;
 }
 
-// Threshold on the 256-bucket Gram tile count; the environment variable
-// MO_NS_BIG_TILE_MIN_WORK overrides it (0 = always use 256 x 256 tiles for
-// short sides >= kBigTileMinS), for tuning and for tests of that kernel.
-int64_t big_tile_min_work() {
-  const char* e = std::getenv("MO_NS_BIG_TILE_MIN_WORK");
-  if (!e || !*e) return kBigTileMinWork;
-  char* end = nullptr;
-  const long long v = std::strtoll(e, &end, 10);
-  return (end && *end == '\0' && v >= 0) ? static_cast<int64_t>(v) : kBigTileMinWork;
-}
-
-bool gram_space_enabled() {
-  const char* e = std::getenv("MO_NS_GRAM_SPACE");
-  return !(e && e[0] == '0' && e[1] == '\0');
-}
-
 int64_t tiles_of(int32_t tm, int32_t tn, bool sym) {
   return sym ? static_cast<int64_t>(tm) * (tm + 1) / 2 : static_cast<int64_t>(tm) * tn;
 }
@@ -60,11 +43,39 @@ void order_by_k(std::vector<GemmProb>& v) {
 }
 }  // namespace
 
+mo_status resolve_ns_options(const mo_ns_options* o, NsOpts& out) {
+  out = NsOpts();
+  if (!o) return MO_OK;
+  if (o->gram_space != 0 && o->gram_space != 1)
+    return fail(MO_EINVAL, "ns options: gram_space must be 0 or 1");
+  if (o->big_tile_min_work < -1 || o->few_tile_max < -1)
+    return fail(MO_EINVAL, "ns options: thresholds must be >= -1 (-1 = default)");
+  out.gram_space = o->gram_space != 0;
+  if (o->big_tile_min_work >= 0) out.big_tile_min_work = o->big_tile_min_work;
+  if (o->few_tile_max >= 0) out.few_tile_max = o->few_tile_max;
+  return MO_OK;
+}
+
+bool gram_gain_ok(const float* coeffs, int steps) {
+  if (!coeffs || steps <= 0) return false;
+  double gain = 1.0;
+  for (int k = 0; k < steps; ++k) gain *= static_cast<double>(coeffs[3 * k]) * coeffs[3 * k];
+  return gain <= kGramSpaceMaxGain;
+}
+
 void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int n, int elem,
-                     bool need_a, const uint8_t* direct_ok, bool stats_from_prep,
-                     const int64_t* in_off, int steps) {
+                     const float* coeffs, int steps, const NsOpts& opt,
+                     const uint8_t* direct_ok, bool stats_from_prep, const int64_t* in_off) {
   L = NsLayout();
-  const bool gspace_mode = elem == 2 && !need_a && steps > 0 && gram_space_enabled();
+  bool need_a = false, cubic_rows = true;
+  for (int k = 0; k < steps; ++k)
+    if (coeffs[3 * k + 2] != 0.f) need_a = true;
+  cubic_rows = !need_a;
+  // Gram space (bf16): the table's small-singular-value gain bounded, see
+  // kGramSpaceMaxGain; the GEMM path also needs cubic-type rows
+  const bool gram_ok = elem == 2 && opt.gram_space && gram_gain_ok(coeffs, steps);
+  const bool gspace_mode = gram_ok && cubic_rows;
+  L.few_tile_max = opt.few_tile_max;
   L.elem = elem;
   L.need_a = need_a;
   L.n = n;
@@ -82,7 +93,7 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     const int64_t ts = ceil_div(s_, kBigTile), tl = ceil_div(l_, kBigTile);
     big_tiles += std::min(ts * (ts + 1) / 2, ts * tl);
   }
-  const bool use_big = big_tiles >= big_tile_min_work();
+  const bool use_big = big_tiles >= opt.big_tile_min_work;
   for (int i = 0; i < n; ++i) {
     const int64_t r = rows[i], c = cols[i];
     const bool tall = r > c;
@@ -95,12 +106,12 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     // the same flops as the plain iteration in one more launch
     const bool gs = gspace_mode && !small && 4 * l_ >= 5 * s_;
     // (the slice-resident kernel's Gram space also takes quintic-type rows)
-    const bool sgs = elem == 2 && steps > 0 && gram_space_enabled() && small &&
-                     s_ >= kGramSpaceMinS;
+    const bool sgs = gram_ok && small && s_ >= kGramSpaceMinS;
     const int64_t x[2] = {take(static_cast<int64_t>(sp) * lp), take(static_cast<int64_t>(sp) * lp)};
     const int64_t p = small || gs ? -1 : take(static_cast<int64_t>(sp) * sp);
     const int64_t a = need_a && !small ? take(static_cast<int64_t>(sp) * sp) : -1;
     L.gspace.push_back(gs || sgs);
+    L.kind.push_back(small ? 2 : tile == kBigTile ? 1 : 0);
     L.x_off[0].push_back(x[0]);
     L.x_off[1].push_back(x[1]);
     L.tall.push_back(tall);
@@ -359,13 +370,13 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const int n = static_cast<int>(B.gs[j].size());
       mo_status s;
       if (B.gs_kind[j] == kGsGram)
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, 0, pool, L.elem, 0.f, 1.f, 0, 0.f,
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, 0.f, 1.f, 0, 0.f,
                            nullptr, 0.f, scale, range_fb, st, b, a);
       else if (B.gs_kind[j] == kGsProd)
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, 0, pool, L.elem, a, b, 1, 0.f, nullptr,
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, a, b, 1, 0.f, nullptr,
                            0.f, nullptr, nullptr, st);
       else
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, wt,
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, wt,
                            lr, scale, range_fb, st);
       if (s != MO_OK) return s;
     }
@@ -388,13 +399,13 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const int n = static_cast<int>(B.gram_p[q].size());
       mo_status s;
       if (cubic_step) {
-        s = launch_ns_gemm(tab(first ? tb.gram_p0 : tb.gram_p[q]), n, B.gram_tiles, B.tile, 0,
+        s = launch_ns_gemm(tab(first ? tb.gram_p0 : tb.gram_p[q]), n, B.gram_tiles, B.tile, L.few_tile_max, 0,
                            pool, L.elem, 0.f, b, 0, a, nullptr, 0.f, ps, pfb, st);
       } else {
-        s = launch_ns_gemm(tab(first ? tb.gram_a0 : tb.gram_a[q]), n, B.gram_tiles, B.tile, 0,
+        s = launch_ns_gemm(tab(first ? tb.gram_a0 : tb.gram_a[q]), n, B.gram_tiles, B.tile, L.few_tile_max, 0,
                            pool, L.elem, 0.f, 1.f, 0, 0.f, nullptr, 0.f, ps, pfb, st);
         if (s == MO_OK)
-          s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, B.tile, 0, pool, L.elem, b, c, 1,
+          s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, B.tile, L.few_tile_max, 0, pool, L.elem, b, c, 1,
                              a, nullptr, 0.f, nullptr, nullptr, st);
       }
       if (s != MO_OK) return s;
@@ -407,7 +418,7 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const bool fin = k + 1 == steps;
       const size_t off = fin ? (first ? tb.fin0 : tb.fin[q]) : (first ? tb.upd0 : tb.upd[q]);
       mo_status s = launch_ns_gemm(tab(off), static_cast<int>(B.upd[q].size()), B.upd_tiles,
-                                   B.tile, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr,
+                                   B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr,
                                    lr, ps, pfb, st);
       if (s != MO_OK) return s;
     }

@@ -30,7 +30,7 @@ struct mo_plan {
   std::vector<uint8_t> adam_owner;  // per param: AdamW steps it (whole or excluded pieces)
   std::vector<int32_t> steps;       // AdamW step counters (per param)
   int32_t ddt = MO_BF16;            // direction / pool dtype
-  bool need_a = false;
+  NsOpts nsopt;
 
   NsLayout ns;
   // workspace layout (byte offsets)
@@ -74,8 +74,6 @@ mo_status build_plan(mo_plan* P) {
   if (s != MO_OK) return s;
   const mo_hparams& hp = P->hp;
   P->ddt = hp.ns_precision == MO_NS_F32 ? MO_F32 : MO_BF16;
-  P->need_a = false;
-  for (int k = 0; k < hp.ns_steps; ++k) P->need_a |= hp.ns_coeffs[k][2] != 0.f;
   P->steps.assign(n, 0);
   P->adam_owner.assign(n, 0);
 
@@ -165,8 +163,8 @@ mo_status build_plan(mo_plan* P) {
                       static_cast<int64_t>(pool_base)) / static_cast<int64_t>(esz_ns));
   const std::vector<uint8_t> direct(rr.size(), P->ddt == MO_BF16 ? 1 : 0);
   build_ns_layout(P->ns, rr.data(), cc.data(), static_cast<int>(rr.size()),
-                  static_cast<int>(esz_ns), P->need_a, direct.data(), false,
-                  P->ddt == MO_BF16 ? in_off.data() : nullptr, hp.ns_steps);
+                  static_cast<int>(esz_ns), &hp.ns_coeffs[0][0], hp.ns_steps, P->nsopt,
+                  direct.data(), false, P->ddt == MO_BF16 ? in_off.data() : nullptr);
   P->ws_pool = ws.take(static_cast<size_t>(P->ns.pool_elems) * P->ns.elem);
   if (P->ws_pool != pool_base) return fail(MO_EINVAL, "internal: pool base moved");
   P->ws_total = align_up(ws.off, 256);
@@ -298,8 +296,15 @@ mo_status upload_tables(mo_plan* P, char* ws, hipStream_t st) {
 
 extern "C" {
 
+void mo_plan_options_default(mo_plan_options* o) {
+  if (!o) return;
+  mo_ns_options_default(&o->ns);
+  o->keep_ns_output = 0;
+  o->reserved = 0;
+}
+
 mo_status mo_plan_create(const mo_param* params, int32_t n, const mo_hparams* hp,
-                         mo_plan** out) {
+                         const mo_plan_options* opts, mo_plan** out) {
   clear_error();
   if (!out || !hp || n < 0 || (n > 0 && !params)) return fail(MO_EINVAL, "bad arguments");
   *out = nullptr;
@@ -321,7 +326,13 @@ mo_status mo_plan_create(const mo_param* params, int32_t n, const mo_hparams* hp
   if (!P) return fail(MO_EINVAL, "out of host memory");
   P->params.assign(params, params + n);
   P->hp = *hp;
-  mo_status s = build_plan(P);
+  mo_status s = resolve_ns_options(opts ? &opts->ns : nullptr, P->nsopt);
+  if (s == MO_OK && opts && opts->keep_ns_output != 0 && opts->keep_ns_output != 1)
+    s = fail(MO_EINVAL, "keep_ns_output must be 0 or 1");
+  if (s == MO_OK) {
+    P->keep_ns_output = opts && opts->keep_ns_output;
+    s = build_plan(P);
+  }
   if (s != MO_OK) {
     delete P;
     return s;
@@ -401,6 +412,22 @@ int32_t mo_plan_gram_space(const mo_plan* plan) {
   for (uint8_t g : plan->ns.gspace)
     if (g) return 1;
   return 0;
+}
+
+mo_status mo_plan_slice_algorithms(const mo_plan* P, int32_t* out, int32_t n) {
+  clear_error();
+  if (!P || !out || n < static_cast<int32_t>(P->slices.size()))
+    return fail(MO_EINVAL, "bad arguments");
+  int k = 0;
+  for (size_t i = 0; i < P->slices.size(); ++i) {
+    if (!P->params[P->slices[i].param].grad) {
+      out[i] = -1;
+      continue;
+    }
+    out[i] = (P->ns.gspace[k] ? 1 : 0) | (P->ns.kind[k] << 1);
+    ++k;
+  }
+  return MO_OK;
 }
 
 mo_status mo_plan_ns_output(const mo_plan* P, int32_t slice, const void* ws, void** o,
@@ -488,49 +515,66 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     MO_HIP_TRY(hipStreamWaitEvent(P->side, P->ev_fork, 0));
     ast = P->side;
   }
-  if (P->n_adam > 0) {
-    const AdamSeg* dad = reinterpret_cast<const AdamSeg*>(P->dtab + P->tab_adam);
-    double* partials = reinterpret_cast<double*>(base + P->ws_adam_partials);
-    double* scal = reinterpret_cast<double*>(base + P->ws_adam_scal);
-    if ((s = launch_adam_sumsq(dad, P->n_adam, P->adam_blocks, partials, ast)) != MO_OK) return s;
-    if ((s = launch_adam_norm(partials, P->adam_blocks, hp.max_norm, scal,
-                              args ? args->norm_out : nullptr, ast)) != MO_OK)
-      return s;
-    if ((s = launch_adam_apply(dad, P->n_adam, P->adam_blocks, scal, adamw_lr, hp.beta1,
-                               hp.beta2, hp.eps, P->tdelta, ast)) != MO_OK)
-      return s;
-  } else if (args && args->norm_out) {
-    // no AdamW gradient: report T = 0 (a kernel write, not a memset node)
-    if ((s = launch_adam_norm(nullptr, 0, hp.max_norm,
-                              reinterpret_cast<double*>(base + P->ws_adam_scal), args->norm_out,
-                              st)) != MO_OK)
-      return s;
-  }
-  if (fork) MO_HIP_TRY(hipEventRecord(P->ev_join, ast));
-  if (nsl > 0) {
-    float coeffs[3 * MO_NS_MAX_STEPS];
-    for (int k = 0; k < hp.ns_steps; ++k)
-      for (int j = 0; j < 3; ++j) coeffs[3 * k + j] = hp.ns_coeffs[k][j];
-    // the row table is the weight target of the fused update and the input
-    // of the separate row pass
-    const RowSeg* drows = reinterpret_cast<const RowSeg*>(P->dtab + P->tab_rows);
-    const bool fuse = P->fuse_ok && !P->keep_ns_output;
-    if ((s = ns_run_iterations(P->ns, dns, P->nst, pool,
-                               reinterpret_cast<const float*>(base + P->ws_scale), coeffs,
-                               hp.ns_steps, fuse ? drows : nullptr, muon_lr,
-                               reinterpret_cast<const int32_t*>(base + P->ws_fb), st)) != MO_OK)
-      return s;
-    if (!fuse) {
-      RowSeg none;
-      std::memset(&none, 0, sizeof(none));
-      if ((s = launch_rows(hp.normuon ? kRowNormUpdate : kRowUpdate, drows, nsl, none,
-                           P->total_rows, muon_lr, hp.normuon_beta2, hp.normuon_eps,
-                           st)) != MO_OK)
-        return s;
+  // Everything after the fork runs in one function so that the side stream
+  // is joined back into `st` on every path, errors included: the caller may
+  // reuse the workspace and the tensors once `st` has drained.
+  auto forked_work = [&]() -> mo_status {
+    mo_status r;
+    if (P->n_adam > 0) {
+      const AdamSeg* dad = reinterpret_cast<const AdamSeg*>(P->dtab + P->tab_adam);
+      double* partials = reinterpret_cast<double*>(base + P->ws_adam_partials);
+      double* scal = reinterpret_cast<double*>(base + P->ws_adam_scal);
+      if ((r = launch_adam_sumsq(dad, P->n_adam, P->adam_blocks, partials, ast)) != MO_OK)
+        return r;
+      if ((r = launch_adam_norm(partials, P->adam_blocks, hp.max_norm, scal,
+                                args ? args->norm_out : nullptr, ast)) != MO_OK)
+        return r;
+      if ((r = launch_adam_apply(dad, P->n_adam, P->adam_blocks, scal, adamw_lr, hp.beta1,
+                                 hp.beta2, hp.eps, P->tdelta, ast)) != MO_OK)
+        return r;
+    } else if (args && args->norm_out) {
+      // no AdamW gradient: report T = 0 (a kernel write, not a memset node)
+      if ((r = launch_adam_norm(nullptr, 0, hp.max_norm,
+                                reinterpret_cast<double*>(base + P->ws_adam_scal), args->norm_out,
+                                st)) != MO_OK)
+        return r;
     }
-    P->last_fused = fuse;
+    if (nsl > 0) {
+      float coeffs[3 * MO_NS_MAX_STEPS];
+      for (int k = 0; k < hp.ns_steps; ++k)
+        for (int j = 0; j < 3; ++j) coeffs[3 * k + j] = hp.ns_coeffs[k][j];
+      // the row table is the weight target of the fused update and the input
+      // of the separate row pass
+      const RowSeg* drows = reinterpret_cast<const RowSeg*>(P->dtab + P->tab_rows);
+      const bool fuse = P->fuse_ok && !P->keep_ns_output;
+      if ((r = ns_run_iterations(P->ns, dns, P->nst, pool,
+                                 reinterpret_cast<const float*>(base + P->ws_scale), coeffs,
+                                 hp.ns_steps, fuse ? drows : nullptr, muon_lr,
+                                 reinterpret_cast<const int32_t*>(base + P->ws_fb), st)) != MO_OK)
+        return r;
+      if (!fuse) {
+        RowSeg none;
+        std::memset(&none, 0, sizeof(none));
+        if ((r = launch_rows(hp.normuon ? kRowNormUpdate : kRowUpdate, drows, nsl, none,
+                             P->total_rows, muon_lr, hp.normuon_beta2, hp.normuon_eps,
+                             st)) != MO_OK)
+          return r;
+      }
+      P->last_fused = fuse;
+    }
+    return MO_OK;
+  };
+  s = forked_work();
+  if (fork) {
+    // join even after an error (the first failure's message is kept)
+    const hipError_t e1 = hipEventRecord(P->ev_join, ast);
+    const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(st, P->ev_join, 0) : e1;
+    if (s == MO_OK && e2 != hipSuccess)
+      return fail(MO_EHIP, "joining the AdamW stream failed: %s", hipGetErrorString(e2));
+    if (s == MO_OK && e1 != hipSuccess)
+      return fail(MO_EHIP, "joining the AdamW stream failed: %s", hipGetErrorString(e1));
   }
-  if (fork) MO_HIP_TRY(hipStreamWaitEvent(st, P->ev_join, 0));
+  if (s != MO_OK) return s;
   for (size_t i = 0; i < P->params.size(); ++i)
     if (P->adam_owner[i]) ++P->steps[i];
   ++P->tdelta;

@@ -50,56 +50,50 @@ def workload_by_name(name: str, coeffs: str = "cubic"):
     return table[name]()
 
 
-# Gram space: shortest short side in the slice-resident kernel
-GS_MIN_SHORT = 64
+def ns_work(slices, coeffs, elem, w_elem=None):
+    """Newton-Schulz work per step from the per-slice unit figures.
 
-
-def ns_work(slices, coeffs, elem, w_elem=None, gram_space=False, sxs_on_chip=False):
-    """Newton-Schulz work per step, from the per-slice unit figures (s = short
-    side, l = long side of each slice, N iterations):
-    * dense flops, the method's count: 4 s^2 l per iteration (A = X X^T and
-      P X), + 2 s^3 for a quintic-type row;
-    * executed flops, plain iteration with the symmetric Gram: 3 s^2 l
-      (+ s^3) per iteration; Gram-space sequence (cubic rows): s^2 l for
-      A0 = X0 X0^T, 3 N - 3 symmetric s x s products of s^3 each, and
-      2 s^2 l for X_N = Q_N X0.  With ``gram_space`` set, a slice runs in
-      Gram space under the library's rule: in the slice-resident kernel
-      (sxs_on_chip) when s >= 64, in the GEMM path when 4 l >= 5 s (a square
-      slice executes the same flops either way and stays plain);
-    * HBM bytes when X does not stay on chip: plain, one read of X0 for the
-      first Gram, then a read of X and a write of X' per iteration:
-      elem * s * l * (2 N + 1); Gram space, two reads of X0 and one write of
-      X_N, elem * s * l * 3, plus per s x s product two operands, the E term
-      and the result, 4 elem s^2, and A0 and Q1, 2 elem s^2 (none when the
-      s x s matrices stay in LDS, sxs_on_chip).  With the Muon
-      update fused into the last launch (w_elem = weight element size) the
-      last write is replaced by a read and a write of W: + (2 w_elem - elem) s l.
-    Returns (dense_flops, executed_flops, bytes)."""
-    dense = exe = byt = 0.0
+    ``slices``: (rows, cols, gram_space, kernel) per slice, kernel one of
+    'gemm128', 'gemm256', 'resident' (the library's own choice, from
+    mo_plan_slice_algorithms).  With s the short side, l the long side and N
+    the table's rows:
+    * method flops, the method's own work with the symmetric Gram (SURVEY
+      8(d)): 3 s^2 l per iteration (s^2 l for A = X X^T, 2 s^2 l for P X),
+      + s^3 for a quintic-type row (A^2);
+    * dense flops, the same without symmetry: 4 s^2 l (+ 2 s^3);
+    * executed flops, what the kernels run: the plain iteration executes the
+      method flops; the Gram-space sequence executes s^2 l for A0 = X0 X0^T,
+      3 N - 3 symmetric s x s products of s^3 each (+ one more per
+      quintic-type row, in the slice-resident kernel) and 2 s^2 l for
+      X_N = Q_N X0;
+    * HBM bytes of the iterate traffic: plain, one read of X0 for the first
+      Gram, then a read of X and a write of X' per iteration,
+      elem s l (2 N + 1); Gram space, two reads of X0 and one write of X_N,
+      3 elem s l, plus for the GEMM kernels per s x s product two operands,
+      the E term and the result (4 elem s^2) and A0 and Q1 (2 elem s^2).  With
+      the Muon update fused into the last launch (w_elem = weight element
+      size) the last write becomes a read and a write of W:
+      + (2 w_elem - elem) s l.
+    Returns a dict of totals."""
+    t = {"method": 0.0, "dense": 0.0, "executed": 0.0, "bytes": 0.0}
     n = len(coeffs)
-    for r, c in slices:
+    nq = sum(1 for _, _, cc in coeffs if cc != 0.0)
+    for r, c, gram, kernel in slices:
         s, l = float(min(r, c)), float(max(r, c))
-        for a, b, cc in coeffs:
-            dense += 4.0 * s * s * l
-            if cc != 0.0:
-                dense += 2.0 * s ** 3
-        gs = gram_space and (s >= GS_MIN_SHORT if sxs_on_chip else 4 * l >= 5 * s)
-        if gs:
-            exe += 3.0 * s * s * l + (3 * n - 3) * s ** 3
-            byt += elem * s * l * 3
-            if not sxs_on_chip:
-                byt += (4 * (3 * n - 3) + 2) * elem * s * s
+        t["method"] += n * 3.0 * s * s * l + nq * s ** 3
+        t["dense"] += n * 4.0 * s * s * l + nq * 2.0 * s ** 3
+        if gram:
+            prods = 3 * n - 3 + (nq if kernel == "resident" else 0)
+            t["executed"] += 3.0 * s * s * l + prods * s ** 3
+            t["bytes"] += elem * s * l * 3
+            if kernel != "resident":
+                t["bytes"] += (4 * (3 * n - 3) + 2) * elem * s * s
         else:
-            for a, b, cc in coeffs:
-                exe += 3.0 * s * s * l + (s ** 3 if cc != 0.0 else 0.0)
-            byt += elem * s * l * (2 * n + 1)
+            t["executed"] += n * 3.0 * s * s * l + nq * s ** 3
+            t["bytes"] += elem * s * l * (2 * n + 1)
         if w_elem is not None:
-            byt += (2 * w_elem - elem) * s * l
-    return dense, exe, byt
-
-
-# slices whose padded short side is 128 run in the slice-resident kernel (bf16)
-SMALL_SIDE = 128
+            t["bytes"] += (2 * w_elem - elem) * s * l
+    return t
 
 
 def build_plan(w, coeffs, precision, normuon):
@@ -134,8 +128,10 @@ def build_plan(w, coeffs, precision, normuon):
 
 def cpu_baseline(w, coeffs, normuon, budget_s: float):
     """The fp64 oracle on a bounded sample of the same workload, extrapolated
-    to one full step: one Muon matrix of each distinct shape and a contiguous
-    slab of the AdamW elements."""
+    to one full step: one Muon matrix of each distinct slice shape (every
+    shape is measured; the sample is bounded by the number of shapes) and a
+    contiguous slab of the AdamW elements.  ``budget_s`` is reported against
+    the time spent."""
     import numpy as np
 
     import workloads as wl
@@ -170,8 +166,6 @@ def cpu_baseline(w, coeffs, normuon, budget_s: float):
         spent += dt
         t_total += dt * count
         parts.append(f"{count}x{p.shape}")
-        if spent > budget_s:
-            break
     n_adam = 0
     if adam_elems:
         n = min(adam_elems, 1 << 22)
@@ -204,8 +198,8 @@ def counted(kernel: str, workload: str, coeffs: str, precision: str):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dense_decoder_1p2b")
     ap.add_argument("--coeffs", default="cubic", choices=["cubic", "quintic"])
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp32"])
@@ -251,13 +245,21 @@ def main() -> int:
         plan.step(workspace=ws)
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done; timing {args.steps} steps")
+    # each step bracketed by events on the launch stream (the step joins its
+    # side stream back into it); the whole timed region by synchronisations
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    evs[0].record()
+    for k in range(args.steps):
         plan.step(workspace=ws)
+        evs[k + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = 1e3 * elapsed / args.steps
-    log(f"{ms_per_step:.3f} ms/step")
+    per_step = sorted(evs[k].elapsed_time(evs[k + 1]) for k in range(args.steps))
+    mid = len(per_step) // 2
+    median_ms = per_step[mid] if len(per_step) % 2 else 0.5 * (per_step[mid - 1] + per_step[mid])
+    mean_ms = 1e3 * elapsed / args.steps
+    log(f"median {median_ms:.3f} ms/step, mean {mean_ms:.3f} ms/step (wall clock)")
 
     # per-kernel-class durations with HIP events on the launch stream; while
     # timing is on, the grouped step runs every kernel in order on one stream
@@ -278,52 +280,55 @@ def main() -> int:
                           "avg_launch_ms": tot.value / n.value}
     L.check("timing", lib.mo_timing_enable(0))
 
-    # algorithmic work
+    # algorithmic work, per slice as the library runs it
     fused = plan.fuses_update()
     gspace = plan.gram_space()
     welt = w.params[0].dtype == "bf16" and 2 or 4
+    algos = plan.slice_algorithms()
     slices = [(r, c) for _, _, r, c in plan.slices()]
     elem = 2 if args.precision == "bf16" else 4
     muon_elems = sum(r * c for r, c in slices)
     adam_elems = sum(p.numel for p, r in zip(w.params, routes) if r[0] == L.MO_ALG_ADAMW)
-    small = [sc for sc in slices if args.precision == "bf16" and min(sc) <= SMALL_SIDE]
-    large = [sc for sc in slices if not (args.precision == "bf16" and min(sc) <= SMALL_SIDE)]
+    by_kernel = {"ns_gemm": [], "ns_small": []}
+    for (r, c), al in zip(slices, algos):
+        if al is not None:
+            by_kernel["ns_small" if al[1] == "resident" else "ns_gemm"].append((r, c) + al)
     peak = BF16_PEAK_TFLOPS if args.precision == "bf16" else FP32_PEAK_TFLOPS
     # the dominant Newton-Schulz kernel and the slices it processes
-    cands = [(name, part) for name, part in (("ns_gemm", large), ("ns_small", small))
-             if name in kern and part]
+    cands = [(name, part) for name, part in by_kernel.items() if name in kern and part]
     roofline = None
     if cands:
         kname, part = max(cands, key=lambda x: kern[x[0]]["ms_per_step"])
         g = kern[kname]
-        dense, exe, nbytes = ns_work(part, coeffs, elem, welt if fused else None,
-                                     gram_space=gspace, sxs_on_chip=kname == "ns_small")
+        work = ns_work(part, coeffs, elem, welt if fused else None)
         n = g["launches_per_step"]
         t = g["avg_launch_ms"] * 1e-3
         # the binding roof is the one with the longer ideal time: for the
-        # GEMM launches on the method's dense count, for the slice-resident
-        # kernel on the flops it executes (in Gram space its s x s work is
-        # small next to its passes over X)
-        flops = dense if kname == "ns_gemm" else exe
-        mfma_bound = flops / (peak * 1e12) >= nbytes / (HBM_PEAK_GBS * 1e9)
+        # GEMM launches on the method's flops, for the slice-resident kernel
+        # on the flops it executes (in Gram space its s x s work is small
+        # next to its passes over X)
+        flops = work["method"] if kname == "ns_gemm" else work["executed"]
+        mfma_bound = flops / (peak * 1e12) >= work["bytes"] / (HBM_PEAK_GBS * 1e9)
         if mfma_bound:
-            achieved = dense / n / t / 1e12
+            achieved = work["method"] / n / t / 1e12
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                         "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
         else:
-            achieved = nbytes / n / t / 1e9
+            achieved = work["bytes"] / n / t / 1e9
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
         roofline.update({
             "traffic": None, "kernel": "k_" + kname, "avg_launch_ms": g["avg_launch_ms"],
             "launches_per_step": n, "slices": len(part),
-            "dense_flops_per_launch": dense / n, "dense_tflops": round(dense / n / t / 1e12, 2),
-            "executed_tflops": round(exe / n / t / 1e12, 2),
-            "algorithmic_bytes_per_launch": nbytes / n,
-            "algorithmic_gbs": round(nbytes / n / t / 1e9, 1),
-            "executed_frac": round(exe / n / t / 1e12 / peak, 4),
-            "symmetry_exploited": kname == "ns_gemm",
-            "algorithm": "gram_space" if gspace else "plain"})
+            "method_flops_per_launch": work["method"] / n,
+            "method_tflops": round(work["method"] / n / t / 1e12, 2),
+            "dense_count_tflops": round(work["dense"] / n / t / 1e12, 2),
+            "executed_tflops": round(work["executed"] / n / t / 1e12, 2),
+            "executed_frac": round(work["executed"] / n / t / 1e12 / peak, 4),
+            "algorithmic_bytes_per_launch": work["bytes"] / n,
+            "algorithmic_gbs": round(work["bytes"] / n / t / 1e9, 1),
+            "gram_space_slices": sum(1 for x in part if x[2]),
+            "algorithm": "gram_space" if any(x[2] for x in part) else "plain"})
     hbm = {}
     elt = w.params[0].dtype == "bf16" and 2 or 4
     if "momentum" in kern:
@@ -385,10 +390,12 @@ def main() -> int:
         log("timing the fp64 oracle on a bounded sample")
         cpu = cpu_baseline(w, coeffs, w.normuon, args.cpu_budget)
 
-    value = 1e3 / ms_per_step
+    value = 1e3 / median_ms
     out = {
         "metric": METRIC, "value": round(value, 4), "unit": "steps/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(median_ms, 4),
+        "timing": "median of per-step HIP-event times on the launch stream",
+        "mean_ms_per_step": round(mean_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": args.precision, "data": "synthetic",
         "config": {"workload": w.key, "muon_params": muon_elems, "adamw_params": adam_elems,
@@ -397,8 +404,7 @@ def main() -> int:
                    "fused_update": fused, "gram_space": gspace,
                    "param_dtype": w.params[0].dtype, "state_dtype": "f32"},
         "roofline": roofline,
-        "ns_dense_tflops_pct_of_peak": (round(100 * roofline["dense_tflops"] / peak, 2)
-                                        if roofline else None),
+        "ns_mfma_util_pct": roofline.get("mfma_util_pct") if roofline else None,
         "adamw_hbm_gbs": hbm.get("adamw"),
         "hbm_gbs": hbm,
         "hbm_gbs_counted": hbm_counted,

@@ -64,7 +64,8 @@ const char* mo_last_error(void);
 const char* mo_version(void);
 /* sizeof() of the ABI structs, for binding self-checks: 0 mo_momentum_item,
  * 1 mo_ns_item, 2 mo_adamw_item, 3 mo_param_desc, 4 mo_route_out, 5 mo_param,
- * 6 mo_hparams, 7 mo_step_args, 8 mo_lr_schedule; 0 for any other index. */
+ * 6 mo_hparams, 7 mo_step_args, 8 mo_lr_schedule, 9 mo_ns_options,
+ * 10 mo_plan_options; 0 for any other index. */
 size_t mo_abi_struct_size(int32_t which);
 
 /* ------------------------------------------------------------------------
@@ -97,6 +98,47 @@ mo_status muon_momentum(const mo_momentum_item* items, int32_t n, float mu, int3
                         void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Newton-Schulz options (every field has a default; see mo_ns_options_default).
+ *
+ *   gram_space         1: run slices in Gram space where the library's rule
+ *                      admits it (the default); 0: the plain iteration
+ *                      everywhere.  Gram space: the iteration X <- a X + b A X
+ *                      (+ c A^2 X), A = X X^T, keeps every iterate of the form
+ *                      Q X0 with Q a polynomial in A0 = X0 X0^T, so the
+ *                      iterations can run on s x s matrices (A_{k+1} =
+ *                      P_k A_k P_k, Q_{k+1} = P_k Q_k) and X0 is multiplied
+ *                      once, by Q_N.  Equal to the plain iteration up to
+ *                      rounding.  Rule: bf16 path only, and the table's
+ *                      small-singular-value gain prod_k a_k^2 at most 1024
+ *                      (Gram space carries A, whose small eigenvalues are the
+ *                      squares of X's, so its bf16 rounding grows with that
+ *                      gain where the plain iteration's grows with its square
+ *                      root: the cubic set qualifies up to 8 iterations, the
+ *                      quintic up to 5); then slices with a short side of 64
+ *                      to 128 (slice-resident kernel, any rows) and GEMM-path
+ *                      slices whose long side is at least 1.25 times the short
+ *                      side and whose every row has c = 0.
+ *   big_tile_min_work  GEMM-path slices with a short side of at least 512
+ *                      use 256 x 256 tiles when the batch holds at least this
+ *                      many such upper-triangle Gram tiles (-1: 512, two per
+ *                      CU; 0: always); otherwise 128 x 128 tiles.
+ *   few_tile_max       bf16 launches of fewer 128 x 128 tiles than this split
+ *                      each tile over 8 waves (-1: 512; 0: never).
+ * The choices change launch shapes and rounding order only; every choice
+ * meets the same tolerances.
+ * ------------------------------------------------------------------------ */
+typedef struct mo_ns_options {
+  int32_t gram_space;
+  int32_t big_tile_min_work;
+  int32_t few_tile_max;
+  int32_t reserved;
+} mo_ns_options;
+
+/* Fills *o with the defaults (gram_space 1, big_tile_min_work -1,
+ * few_tile_max -1).  No-op for NULL. */
+void mo_ns_options_default(mo_ns_options* o);
+
+/* ------------------------------------------------------------------------
  * ns_orthogonalize_batched - Newton-Schulz orthogonalisation of many
  * independent matrices.
  *
@@ -116,10 +158,12 @@ mo_status muon_momentum(const mo_momentum_item* items, int32_t n, float mu, int3
  *   items[i].out  device, out_dtype, rows x cols with row stride ld_out; may
  *                 alias `in` (the input is fully consumed first).
  *   coeffs        host, [steps][3] floats (a, b, c) per iteration,
- *                 1 <= steps <= MO_NS_MAX_STEPS.
+ *                 1 <= steps <= MO_NS_MAX_STEPS, all finite.
  *   precision     mo_ns_precision.
- * Workspace: ns_workspace_bytes(items, n, precision).  All sizes must be >= 1
- * and cols, rows <= 65536.
+ *   opts          host, nullable (NULL = mo_ns_options_default).
+ * Workspace: ns_workspace_bytes(items, n, coeffs, steps, precision, opts);
+ * with coeffs == NULL the query returns the most any table can need.  All
+ * sizes must be >= 1 and cols, rows <= 65536.
  * ------------------------------------------------------------------------ */
 typedef struct mo_ns_item {
   const void* in;
@@ -132,10 +176,11 @@ typedef struct mo_ns_item {
   int32_t out_dtype;
 } mo_ns_item;
 
-size_t ns_workspace_bytes(const mo_ns_item* items, int32_t n, int32_t precision);
+size_t ns_workspace_bytes(const mo_ns_item* items, int32_t n, const float* coeffs, int32_t steps,
+                          int32_t precision, const mo_ns_options* opts);
 mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const float* coeffs,
-                                   int32_t steps, int32_t precision, void* ws, size_t ws_bytes,
-                                   void* stream);
+                                   int32_t steps, int32_t precision, const mo_ns_options* opts,
+                                   void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * normuon_rownorm - NorMuon per-row second-moment normalisation, in place.
@@ -353,8 +398,19 @@ typedef struct mo_step_args {
 
 typedef struct mo_plan mo_plan;
 
+/* Plan options: the Newton-Schulz options (mo_ns_options) of every Muon
+ * slice of the plan, and keep_ns_output (0 / 1, as mo_plan_keep_ns_output).
+ * NULL = mo_plan_options_default. */
+typedef struct mo_plan_options {
+  mo_ns_options ns;
+  int32_t keep_ns_output;
+  int32_t reserved;
+} mo_plan_options;
+
+void mo_plan_options_default(mo_plan_options* o);
+
 mo_status mo_plan_create(const mo_param* params, int32_t n, const mo_hparams* hp,
-                         mo_plan** out);
+                         const mo_plan_options* opts, mo_plan** out);
 void mo_plan_destroy(mo_plan* plan);
 size_t mo_plan_workspace_bytes(const mo_plan* plan);
 /* Host queries for tests: routing of each param and the slice table. */
@@ -393,21 +449,16 @@ mo_status mo_plan_keep_ns_output(mo_plan* plan, int32_t keep);
 /* 1 if the next grouped step will apply the update inside the last
  * Newton-Schulz launch (see mo_plan_keep_ns_output), else 0 (also for NULL). */
 int32_t mo_plan_fuses_update(const mo_plan* plan);
-/* 1 if the plan runs its GEMM-path slices in Gram space, else 0 (also for
- * NULL).  The Newton-Schulz iteration of the NorMuon paper section 2.2,
- * eq. (5), X <- a X + b A X with A = X X^T, keeps every iterate of the form
- * Q X0 with Q a polynomial in A0 = X0 X0^T; the plan then forms A0 once,
- * runs the iterations on s x s matrices (A_{k+1} = P_k A_k P_k,
- * Q_{k+1} = P_k Q_k) and multiplies X0 once, by Q_N.  Chosen at plan
- * creation for the bf16 path, for rectangular GEMM-path slices (long side at
- * least 1.25 times the short side: on square ones it saves no work) when
- * every coefficient row has c = 0 and the environment does not set
- * MO_NS_GRAM_SPACE=0; equal to the plain iteration up to rounding.  The slice-resident kernel (padded short side 128) runs
- * the same sequence with its 128 x 128 matrices in LDS, two passes over X
- * instead of N + 1, for bf16 slices with a short side of at least 64 and
- * any coefficient rows (P_k = a_k I + b_k A_k + c_k A_k^2); smaller ones
- * keep the plain iteration, where it is the more accurate in bf16. */
+/* 1 if the plan runs any slice in Gram space, else 0 (also for NULL).  The
+ * choice is made at plan creation by the rule of mo_ns_options (gram_space
+ * option, bf16 path, coefficient-table gain, slice shape). */
 int32_t mo_plan_gram_space(const mo_plan* plan);
+/* How each slice of mo_plan_slices' table runs its Newton-Schulz iterations,
+ * one int per slice: bit 0 set when in Gram space; bits 1-2 the kernel,
+ * 0 = batched GEMM on 128 x 128 tiles, 1 = batched GEMM on 256 x 256 tiles,
+ * 2 = slice-resident kernel; -1 for a slice whose param has no gradient.
+ * Host only.  MO_EINVAL for a NULL pointer or n below the slice count. */
+mo_status mo_plan_slice_algorithms(const mo_plan* plan, int32_t* out, int32_t n);
 
 /* ------------------------------------------------------------------------
  * Kernel timing (diagnostics).  While enabled, every kernel launch of this

@@ -18,6 +18,7 @@ import torch
 
 import workloads as wl
 from oracle import bf16 as obf16
+from oracle.routing import descs_from_specs
 
 NS_BF16_MAXABS = 2e-2
 NS_BF16_RELFRO = 1.5e-2
@@ -80,3 +81,47 @@ def assert_ns_close(got: np.ndarray, ref: np.ndarray, precision: str,
 
 def storage_draw(seed: int, step: int, idx: int, shape, std: float, dtype: str) -> np.ndarray:
     return wl.to_storage(wl.draw_f32(seed, step, idx, shape, std), dtype)
+
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def build_entries(w: wl.Workload, normuon: bool, init=None):
+    """Plan entries (api.Plan) for a workload: device W from the seeded init
+    (or ``init``), zero grads and zero optimizer states."""
+    from adamw_optimizer_step_amd import _lib as L
+    from adamw_optimizer_step_amd import api
+    entries = []
+    routes, _ = api.route([api.make_desc(p.name, p.shape, p.role, p.no_decay,
+                                         p.requires_grad, i, p.view, p.split,
+                                         p.exclude)
+                           for i, p in enumerate(w.params)])
+    for i, (p, r) in enumerate(zip(w.params, routes)):
+        W0 = wl.init_weight(w, i) if init is None else init[i]
+        e = {"desc": api.make_desc(p.name, p.shape, p.role, p.no_decay, p.requires_grad, i,
+                                   p.view, p.split, p.exclude),
+             "param": to_dev(W0, p.dtype),
+             "grad": torch.zeros(p.shape, dtype=TORCH_DT[p.dtype], device="cuda"),
+             "route": r}
+        if r[0] == L.MO_ALG_MUON:
+            e["momentum"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
+            if normuon:
+                e["normuon_v"] = torch.zeros(p.shape[0], dtype=torch.float32, device="cuda")
+        if r[0] == L.MO_ALG_ADAMW or (r[0] == L.MO_ALG_MUON and p.exclude):
+            e["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
+            e["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
+        entries.append(e)
+    return entries
+
+
+def oracle_descs(w: wl.Workload):
+    """Routing descriptors of a workload for oracle.hybrid, with dtypes."""
+    descs = descs_from_specs(w.params)
+    for d, p in zip(descs, w.params):
+        d["dtype"] = p.dtype
+    return descs
+
+
+def relfro(got: np.ndarray, ref: np.ndarray) -> float:
+    nr = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / nr) if nr > 0 else float(np.linalg.norm(got))

@@ -28,23 +28,27 @@ def test_sweep_workload_names_carry_the_coefficients():
     assert bench.workload_by_name("dense_decoder_1p2b").key == "dense_decoder_1p2b"
 
 
-def test_ns_work_applies_gram_space_per_slice():
-    """Gram space covers rectangular GEMM slices and slice-resident ones with
-    a short side of 64 or more; the others count as the plain iteration."""
+def test_ns_work_counts_per_slice():
+    """Work counts follow each slice's own algorithm: the method's flops do
+    not depend on it; Gram space changes only the executed flops and bytes."""
     import workloads as wl
     co = wl.coeff_table("cubic")
-    sq, rect = [(2048, 2048)] * 3, [(5632, 2048)] * 2
-    plain_sq = bench.ns_work(sq, co, 2)
-    assert bench.ns_work(sq, co, 2, gram_space=True) == plain_sq
-    gs_rect = bench.ns_work(rect, co, 2, gram_space=True)
-    assert gs_rect != bench.ns_work(rect, co, 2)
-    mixed = bench.ns_work(sq + rect, co, 2, gram_space=True)
-    assert mixed == tuple(a + b for a, b in zip(plain_sq, gs_rect))
-    # square slices execute the same flops in either form (N = 5, cubic)
-    s = 2048.0
-    assert plain_sq[1] == 3 * 15 * s ** 3
-    small = [(32, 512), (128, 512)]
-    got = bench.ns_work(small, co, 2, gram_space=True, sxs_on_chip=True)
-    want = [bench.ns_work([small[0]], co, 2), bench.ns_work([small[1]], co, 2, gram_space=True,
-                                                             sxs_on_chip=True)]
-    assert got == tuple(a + b for a, b in zip(*want))
+    s, l = 2048.0, 5632.0
+    sq = [(2048, 2048, False, "gemm128")] * 3
+    rect_gs = [(5632, 2048, True, "gemm256")] * 2
+    rect_plain = [(5632, 2048, False, "gemm256")] * 2
+    a, b, c = bench.ns_work(sq, co, 2), bench.ns_work(rect_gs, co, 2), \
+        bench.ns_work(rect_plain, co, 2)
+    assert a["method"] == 3 * 5 * 3 * s ** 3 and a["dense"] == 3 * 5 * 4 * s ** 3
+    assert a["executed"] == a["method"]
+    assert b["method"] == c["method"] == 2 * 5 * 3 * s * s * l
+    assert b["executed"] == 2 * (3 * s * s * l + 12 * s ** 3) < c["executed"]
+    assert c["bytes"] == 2 * 2 * s * l * 11
+    mixed = bench.ns_work(sq + rect_gs, co, 2)
+    assert all(mixed[k] == a[k] + b[k] for k in mixed)
+    # a quintic row adds s^3 to the method count and 2 s^3 to the dense one
+    q = bench.ns_work([(128, 512, True, "resident")], wl.coeff_table("quintic"), 2)
+    assert q["method"] == 5 * (3 * 128 * 128 * 512 + 128 ** 3)
+    assert q["executed"] == 3 * 128 * 128 * 512 + (12 + 5) * 128 ** 3
+    # the fused update replaces the last write by a read and a write of W
+    assert bench.ns_work(sq, co, 2, 2)["bytes"] - a["bytes"] == 3 * 2 * s * s

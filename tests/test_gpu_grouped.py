@@ -12,17 +12,13 @@ from adamw_optimizer_step_amd import _lib as L
 from adamw_optimizer_step_amd import api
 from oracle import muon as omuon
 from oracle.hybrid import HybridState, HyperParams, hybrid_step
-from oracle.routing import descs_from_specs
 from oracle.views import expand, expand_pieces
 
-from gpu_common import (NS_BF16_MAXABS, NS_BF16_RELFRO, NS_F32_MAXABS, REL_F32,
-                        assert_bf16_close, assert_ns_close, bf16_ulp, f64, rel_inf, require_gpu,
-                        to_dev)
+from gpu_common import (NS_BF16_MAXABS, NS_F32_MAXABS, REL_F32,
+                        assert_bf16_close, assert_ns_close, bf16_ulp, build_entries, f64,
+                        oracle_descs, rel_inf, require_gpu, to_dev)
 
 pytestmark = pytest.mark.gpu
-
-TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
-
 
 @pytest.fixture(autouse=True)
 def _gpu():
@@ -31,45 +27,13 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def build_entries(w: wl.Workload, normuon: bool, init=None):
-    """Device tensors for a workload: W from the seeded init, zero states."""
-    entries = []
-    routes, _ = api.route([api.make_desc(p.name, p.shape, p.role, p.no_decay,
-                                         p.requires_grad, i, p.view, p.split,
-                                         p.exclude)
-                           for i, p in enumerate(w.params)])
-    for i, (p, r) in enumerate(zip(w.params, routes)):
-        W0 = wl.init_weight(w, i) if init is None else init[i]
-        e = {"desc": api.make_desc(p.name, p.shape, p.role, p.no_decay, p.requires_grad, i,
-                                   p.view, p.split, p.exclude),
-             "param": to_dev(W0, p.dtype),
-             "grad": torch.zeros(p.shape, dtype=TORCH_DT[p.dtype], device="cuda"),
-             "route": r}
-        if r[0] == L.MO_ALG_MUON:
-            e["momentum"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
-            if normuon:
-                e["normuon_v"] = torch.zeros(p.shape[0], dtype=torch.float32, device="cuda")
-        if r[0] == L.MO_ALG_ADAMW or (r[0] == L.MO_ALG_MUON and p.exclude):
-            e["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
-            e["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
-        entries.append(e)
-    return entries
-
-
-def _oracle_setup(w):
-    descs = descs_from_specs(w.params)
-    for d, p in zip(descs, w.params):
-        d["dtype"] = p.dtype
-    return descs
-
-
 @pytest.mark.parametrize("precision", ["fp32", "bf16"])
 def test_grouped_tiny_three_steps(precision):
     w = wl.tiny_routing()
     ents = build_entries(w, normuon=False)
     coeffs = wl.coeff_table("cubic")
     plan = api.Plan(ents, api.make_hparams(coeffs=coeffs, ns_precision=precision))
-    descs = _oracle_setup(w)
+    descs = oracle_descs(w)
     st = HybridState()
     hp = HyperParams(coeffs=coeffs)
     Wref = {p.name: f64(e["param"]) for p, e in zip(w.params, ents)}
@@ -154,39 +118,55 @@ def test_fused_gate_up_equals_separate(normuon):
 
 @pytest.mark.parametrize("precision", ["bf16", "fp32"])
 def test_grouped_normuon_parity(precision):
-    steps = 2
-    w, ents, init, grads = _run_small(False, True, steps=steps, precision=precision)
-    descs = _oracle_setup(w)
+    """NorMuon in the grouped step (NorMuon paper section 3.1), over two
+    steps: each slice's Newton-Schulz output O element-wise against the
+    oracle's (1e-4 fp32 path, 2e-2 bf16 path); then, from the GPU's own O,
+    the row second moment v (EMA of the row mean square) and the weights
+    W (1 - lr wd) - lr scale O / (sqrt(v) + eps).  Momentum and the AdamW
+    params against the oracle as usual."""
+    w = _small_decoder(False, True)
+    ents = build_entries(w, normuon=True)
+    plan = api.Plan(ents, api.make_hparams(ns_precision=precision, normuon=True))
+    assert not plan.fuses_update()
+    descs = oracle_descs(w)
     st = HybridState()
     hp = HyperParams(normuon=True)
-    W = {p.name: wl.from_storage(init[i], p.dtype).astype(np.float64)
-         for i, p in enumerate(w.params)}
-    for t in range(1, steps + 1):
-        G = {p.name: wl.from_storage(grads[t][i], p.dtype).astype(np.float64)
-             for i, p in enumerate(w.params)}
-        out = hybrid_step(descs, W, G, st, hp, keep_outputs=True)
-        W = out["W"]
-    relfro = NS_BF16_RELFRO if precision == "bf16" else 1e-4
-    for i, (p, e) in enumerate(zip(w.params, ents)):
-        got = f64(e["param"])
-        W0 = wl.from_storage(init[i], p.dtype).astype(np.float64)
-        if p.name in st.B:
-            assert rel_inf(f64(e["momentum"]), st.B[p.name]) <= REL_F32
-            # NorMuon v follows the NS output's row norms: relative, per row
-            vr = st.nv[p.name]
-            assert np.max(np.abs(f64(e["normuon_v"]) - vr) / vr) <= 4 * relfro
-            dgot, dref = got - W0, W[p.name] - W0
-            # total update over the steps, relative Frobenius; bf16 storage
-            # of W adds at most half an ulp per step
-            assert np.linalg.norm(dgot - dref) / np.linalg.norm(dref) <= 2 * relfro + 2e-2
-        else:
-            assert_bf16_close(got, W[p.name], extra=bf16_extra(W[p.name]))
-
-
-def bf16_extra(x):
-    # two AdamW steps each rounded to bf16: allow one more ulp of drift
-    from gpu_common import bf16_ulp
-    return bf16_ulp(x)
+    Wref = {p.name: f64(e["param"]) for p, e in zip(w.params, ents)}
+    for t in (1, 2):
+        G = {}
+        for i, (p, e) in enumerate(zip(w.params, ents)):
+            g = wl.grad(w, i, t)
+            e["grad"].copy_(to_dev(g, p.dtype))
+            G[p.name] = wl.from_storage(g, p.dtype).astype(np.float64)
+        Wold = {p.name: f64(e["param"]) for p, e in zip(w.params, ents)}
+        vold = {p.name: f64(e["normuon_v"]) for p, e in zip(w.params, ents) if "normuon_v" in e}
+        plan.step()
+        torch.cuda.synchronize()
+        out = hybrid_step(descs, Wref, G, st, hp, keep_outputs=True)
+        slices = plan.slices()
+        for pi, (p, e) in enumerate(zip(w.params, ents)):
+            got = f64(e["param"])
+            if p.name not in out["muon"]:
+                assert_bf16_close(got, out["W"][p.name])
+                Wref[p.name] = got.copy()
+                continue
+            res = out["muon"][p.name]
+            assert rel_inf(f64(e["momentum"]), res["B"]) <= REL_F32
+            for k, (owner, off, r, c) in enumerate(slices):
+                if owner != pi:
+                    continue
+                rows = slice(off, off + r)
+                print(f"[normuon] {precision} step {t} {p.name} rows {off}:{off + r}", flush=True)
+                O = f64(plan.ns_output(k))
+                assert_ns_close(O, res["O"][rows], precision)
+                On, v_exp = omuon.normuon_rownorm(O, vold[p.name][rows], hp.normuon_beta2,
+                                                  hp.normuon_eps)
+                assert rel_inf(f64(e["normuon_v"])[rows], v_exp) <= 1e-5
+                sc = math.sqrt(max(1.0, r / c))
+                assert_bf16_close(got[rows], omuon.apply_update(Wold[p.name][rows], sc * On, 0.01),
+                                  extra=2e-6 * 0.01 * sc * np.abs(On))
+            Wref[p.name] = got.copy()
+    assert plan.get_steps() == [2, 2, 0, 0, 0, 0]
 
 
 def test_overlapped_step_equals_serial():
@@ -210,7 +190,7 @@ def test_overlapped_step_equals_serial():
 def _mixed_shapes():
     """Slices for every kernel that can finish a step: slice-resident (wide,
     tall, split view), 128 x 128 GEMM tiles (wide, tall), 256 x 256 tiles
-    (with MO_NS_BIG_TILE_MIN_WORK=0), fp32 weights, and AdamW params."""
+    (with big_tile_min_work = 0), fp32 weights, and AdamW params."""
     ps = [wl.ParamSpec("embed", (256, 64), "bf16", wl.ROLE_EMBEDDING, no_decay=True),
           wl.ParamSpec("norm", (64,), "bf16", wl.ROLE_NORM, no_decay=True),
           wl.ParamSpec("small_wide", (96, 256), "bf16"),
@@ -225,20 +205,17 @@ def _mixed_shapes():
 
 @pytest.mark.parametrize("mode", ["gram_space", "plain"])
 @pytest.mark.parametrize("big_tiles", [False, True])
-def test_fused_update_bit_identical(big_tiles, mode, monkeypatch):
+def test_fused_update_bit_identical(big_tiles, mode):
     """The Muon update applied inside the last Newton-Schulz launch (the
     default) gives the same bits as the separate row pass over the stored O,
     for every kernel that can end a step, over two steps, in the Gram-space
     sequence and in the plain iteration."""
-    if big_tiles:
-        monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0")
-    if mode == "plain":
-        monkeypatch.setenv("MO_NS_GRAM_SPACE", "0")
+    opts = {"big_tile_min_work": 0 if big_tiles else None, "gram_space": mode == "gram_space"}
     w = _mixed_shapes()
     runs = []
     for keep in (True, False):
         ents = build_entries(w, normuon=False)
-        plan = api.Plan(ents, api.make_hparams(muon_wd=0.1))
+        plan = api.Plan(ents, api.make_hparams(muon_wd=0.1), options=opts)
         plan.keep_ns_output(keep)
         assert plan.fuses_update() == (not keep)
         for t in (1, 2):
@@ -285,17 +262,17 @@ def _aligned_shapes():
 
 @pytest.mark.parametrize("coeffs", ["cubic", "quintic"])
 @pytest.mark.parametrize("exp2", [0, -35, 35, -60, 55])
-def test_first_iteration_in_place_and_range_fallback(exp2, coeffs, monkeypatch):
+def test_first_iteration_in_place_and_range_fallback(exp2, coeffs):
     """Iteration 0 reads the unscaled D in place, the normalisation scale
     folded into the products; a slice whose max|D| leaves [2^-50, 2^40] (here
     gradients scaled by 2^-60 or 2^55) falls back to the prepared X0.  The
     Newton-Schulz output meets the oracle's bound at every scale; the quintic
     cases put the 512-row slice on 256 x 256 tiles."""
-    monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0" if coeffs == "quintic" else "512")
     w = _aligned_shapes()
     cf = wl.coeff_table(coeffs)
     ents = build_entries(w, normuon=False)
-    plan = api.Plan(ents, api.make_hparams(coeffs=cf))
+    plan = api.Plan(ents, api.make_hparams(coeffs=cf),
+                    options={"big_tile_min_work": 0 if coeffs == "quintic" else 512})
     plan.keep_ns_output(True)
     for i, (e, p) in enumerate(zip(ents, w.params)):
         e["grad"].copy_(to_dev(wl.grad(w, i, 1), p.dtype))
@@ -312,16 +289,14 @@ def test_first_iteration_in_place_and_range_fallback(exp2, coeffs, monkeypatch):
 @pytest.mark.parametrize("steps", [1, 2, 3, 7])
 @pytest.mark.parametrize("mode", ["gram_space", "plain"])
 @pytest.mark.parametrize("row", ["cubic", "quintic"])
-def test_iteration_count_and_mode(steps, mode, row, monkeypatch):
+def test_iteration_count_and_mode(steps, mode, row):
     """The grouped step's Newton-Schulz output for 1, 2, 3 and 7 iterations,
     in Gram space (the default for the bf16 path: cubic rows on the GEMM
     path, any rows in the slice-resident kernel for short sides >= 64) and in
-    the plain iteration (MO_NS_GRAM_SPACE=0), against the oracle, over GEMM
+    the plain iteration (gram_space option off), against the oracle, over GEMM
     slices on both tile sizes and slice-resident slices on both sides of the
     64-row threshold."""
-    if mode == "plain":
-        monkeypatch.setenv("MO_NS_GRAM_SPACE", "0")
-    monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0")
+    opts = {"gram_space": mode == "gram_space", "big_tile_min_work": 0}
     base = _aligned_shapes()
     extra = [wl.ParamSpec("small_wide", (96, 256), "bf16"),
              wl.ParamSpec("small_tall", (392, 120), "bf16"),
@@ -329,7 +304,7 @@ def test_iteration_count_and_mode(steps, mode, row, monkeypatch):
     w = wl.Workload("iteration_shapes", 17, base.params + tuple(extra), grad_std=1e-3)
     cf = [(1.5, -0.5, 0.0) if row == "cubic" else (15 / 8, -5 / 4, 3 / 8)] * steps
     ents = build_entries(w, normuon=False)
-    plan = api.Plan(ents, api.make_hparams(coeffs=cf))
+    plan = api.Plan(ents, api.make_hparams(coeffs=cf), options=opts)
     plan.keep_ns_output(True)
     for i, (e, p) in enumerate(zip(ents, w.params)):
         e["grad"].copy_(to_dev(wl.grad(w, i, 1), p.dtype))
@@ -354,7 +329,7 @@ def test_grouped_excluded_pieces(normuon, precision):
     plan = api.Plan(ents, api.make_hparams(coeffs=coeffs, normuon=normuon,
                                            ns_precision=precision))
     tol_ns = NS_F32_MAXABS if precision == "fp32" else NS_BF16_MAXABS
-    descs = _oracle_setup(w)
+    descs = oracle_descs(w)
     st = HybridState()
     hp = HyperParams(coeffs=coeffs, normuon=normuon)
     Wref = {p.name: f64(e["param"]) for p, e in zip(w.params, ents)}

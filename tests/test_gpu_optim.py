@@ -1,0 +1,179 @@
+"""GPU tests of the ``MuonAdamW`` wrapper: a multi-step run against the
+oracle's hybrid step, a plan rebuild when a gradient tensor moves, the state
+dict, and the token-clock learning-rate schedule driving both optimizers
+(OMN "Dual-Manifold Optimization" page: one token clock steps both schedules,
+each from its own peak, through warmup, the stable phase, the square-root
+cooldown and the floor)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from adamw_optimizer_step_amd import api
+from adamw_optimizer_step_amd.optim import MuonAdamW
+from oracle import schedule as osched
+from oracle.hybrid import HybridState, HyperParams, hybrid_step
+from oracle.views import expand
+
+from gpu_common import (NS_BF16_MAXABS, NS_F32_MAXABS, REL_F32, TORCH_DT, bf16_ulp, f64,
+                        oracle_descs, rel_inf, require_gpu, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _model(dtype: str):
+    d, ffn = 64, 96
+    ps = (wl.ParamSpec("embed", (256, d), dtype, wl.ROLE_EMBEDDING, no_decay=True),
+          wl.ParamSpec("norm", (d,), dtype, wl.ROLE_NORM, no_decay=True),
+          wl.ParamSpec("q", (d, d), dtype),
+          wl.ParamSpec("gate_up", (2 * ffn, d), dtype, view=(2, ffn, d)),
+          wl.ParamSpec("down", (d, ffn), dtype))
+    return wl.Workload(f"optim_{dtype}", 23, ps, grad_std=1e-3)
+
+
+def _params(w):
+    out = []
+    for i, p in enumerate(w.params):
+        t = to_dev(wl.init_weight(w, i), p.dtype).requires_grad_(True)
+        out.append({"name": p.name, "param": t, "role": p.role, "no_decay": p.no_decay,
+                    "view": p.view, "split": p.split})
+    return out
+
+
+def _set_grads(w, named, step):
+    G = {}
+    for i, (p, e) in enumerate(zip(w.params, named)):
+        g = wl.grad(w, i, step)
+        if e["param"].grad is None:
+            e["param"].grad = torch.empty(p.shape, dtype=TORCH_DT[p.dtype], device="cuda")
+        e["param"].grad.copy_(to_dev(g, p.dtype))
+        G[p.name] = wl.from_storage(g, p.dtype).astype(np.float64)
+    return G
+
+
+def _compare(w, named, opt, out, Wold, st, muon_lr, tol_ns):
+    for p, e in zip(w.params, named):
+        got = f64(e["param"].detach())
+        if p.name in out["muon"]:
+            res = out["muon"][p.name]
+            ent = next(x for x in opt.entries if x["name"] == p.name)
+            assert rel_inf(f64(ent["momentum"]), res["B"]) <= REL_F32
+            dgot, dref = got - Wold[p.name], -muon_lr * res["U"]
+            for off, r, c in expand(p.shape, p.view, p.split):
+                sc = math.sqrt(max(1.0, r / c))
+                rows = slice(off, off + r)
+                ulp = bf16_ulp(Wold[p.name][rows]).max() if p.dtype == "bf16" else \
+                    2 ** -23 * np.abs(Wold[p.name][rows]).max()
+                err = np.abs(dgot[rows] - dref[rows]).max()
+                assert err <= muon_lr * sc * tol_ns + ulp, (p.name, off, err)
+        else:
+            want = out["W"][p.name]
+            if p.dtype == "bf16":
+                assert np.all(np.abs(got - want) <= bf16_ulp(want)), p.name
+            else:
+                d = want - Wold[p.name]
+                tol = REL_F32 * np.abs(d).max() + 2 ** -23 * np.abs(got).max()
+                assert np.max(np.abs(got - want)) <= tol, p.name
+            ent = next(x for x in opt.entries if x["name"] == p.name)
+            assert rel_inf(f64(ent["exp_avg"]), st.m[p.name]) <= REL_F32
+            assert rel_inf(f64(ent["exp_avg_sq"]), st.v[p.name]) <= REL_F32
+
+
+def test_muon_adamw_steps_rebuild_and_state():
+    """Three steps of MuonAdamW on bf16 params against the oracle; before
+    step 2 one gradient tensor is replaced (a new address), which rebuilds
+    the plan and keeps the AdamW step counters; the state dict round-trips."""
+    w = _model("bf16")
+    named = _params(w)
+    opt = MuonAdamW(named)
+    descs = oracle_descs(w)
+    st = HybridState()
+    hp = HyperParams()
+    Wref = {p.name: f64(e["param"].detach()) for p, e in zip(w.params, named)}
+    plans = []
+    for step in (1, 2, 3):
+        if step == 2:
+            old = named[1]["param"].grad
+            named[1]["param"].grad = torch.empty_like(old)     # moved gradient
+        G = _set_grads(w, named, step)
+        Wold = {p.name: f64(e["param"].detach()) for p, e in zip(w.params, named)}
+        opt.step()
+        torch.cuda.synchronize()
+        plans.append(opt._plan)
+        out = hybrid_step(descs, Wref, G, st, hp, keep_outputs=True)
+        _compare(w, named, opt, out, Wold, st, hp.muon_lr, NS_BF16_MAXABS)
+        for p, e in zip(w.params, named):
+            Wref[p.name] = f64(e["param"].detach())
+    assert plans[0] is not plans[1] and plans[1] is plans[2]
+    assert opt._plan.get_steps() == [3, 3, 0, 0, 0]
+    sd = opt.state_dict()
+    opt2 = MuonAdamW(_params(w))
+    opt2.load_state_dict(sd)
+    for a, b in zip(opt.entries, opt2.entries):
+        for k in ("momentum", "exp_avg", "exp_avg_sq"):
+            if k in a:
+                assert torch.equal(a[k], b[k]), (a["name"], k)
+    assert opt2._plan.get_steps() == [3, 3, 0, 0, 0]
+
+
+def test_muon_adamw_rejects_mismatched_grad():
+    """A gradient whose dtype or size differs from its parameter is refused
+    before anything is enqueued (the library reads G with W's dtype)."""
+    w = _model("bf16")
+    named = _params(w)
+    opt = MuonAdamW(named)
+    _set_grads(w, named, 1)
+    named[2]["param"].grad = torch.zeros(named[2]["param"].shape, dtype=torch.float32,
+                                         device="cuda")
+    with pytest.raises(TypeError):
+        opt.step()
+    named[2]["param"].grad = torch.zeros(10, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        opt.step()
+
+
+def test_token_clock_drives_both_rates():
+    """Seven steps with 80-token windows through a schedule with a 100-token
+    warmup, the peak to 300, a square-root cooldown to 500 and the floor
+    after it: the clock's rates reach mo_grouped_step (fp32 params and the
+    fp32 Newton-Schulz path, so that the tolerances are tight enough to tell
+    the rates apart) and match the oracle's hybrid step at the oracle's
+    schedule."""
+    phases = dict(warmup=100.0, stable_end=300.0, end=500.0, floor=1e-5)
+    w = _model("f32")
+    named = _params(w)
+    clock = api.TokenClock(muon_peak=0.01, adamw_peak=3e-4, **phases)
+    opt = MuonAdamW(named, clock=clock, ns_precision="fp32")
+    oclock = osched.TokenClock(muon_peak=0.01, adamw_peak=3e-4, **phases)
+    descs = oracle_descs(w)
+    st = HybridState()
+    Wref = {p.name: f64(e["param"].detach()) for p, e in zip(w.params, named)}
+    seen = set()
+    for step in range(1, 8):
+        G = _set_grads(w, named, step)
+        Wold = {p.name: f64(e["param"].detach()) for p, e in zip(w.params, named)}
+        opt.step(window_tokens=80.0)
+        torch.cuda.synchronize()
+        muon_lr, adamw_lr = oclock.advance(80.0)
+        tau = oclock.tokens
+        seen.add("warmup" if tau < 100 else "stable" if tau < 300 else
+                 "cooldown" if tau < 500 else "floor")
+        assert clock.tokens == tau
+        hp = HyperParams(muon_lr=muon_lr, adamw_lr=adamw_lr)
+        print(f"[clock] step {step} tokens {tau:.0f} lr {muon_lr:.6g} / {adamw_lr:.6g}",
+              flush=True)
+        out = hybrid_step(descs, Wref, G, st, hp, keep_outputs=True)
+        _compare(w, named, opt, out, Wold, st, muon_lr, NS_F32_MAXABS)
+        for p, e in zip(w.params, named):
+            Wref[p.name] = f64(e["param"].detach())
+    assert seen == {"warmup", "stable", "cooldown", "floor"}

@@ -108,15 +108,14 @@ def _ns_case(shapes, dtype, seed, std=1.0):
 @pytest.mark.parametrize("few_tiles", ["default", "0"])
 @pytest.mark.parametrize("precision", ["bf16", "fp32"])
 @pytest.mark.parametrize("kind", ["cubic", "quintic"])
-def test_ns_parity_ragged_shapes(precision, kind, few_tiles, monkeypatch):
+def test_ns_parity_ragged_shapes(precision, kind, few_tiles):
     # these launches have few tiles, so bf16 uses the 8-wave 128 x 128
-    # kernels; MO_NS_FEW_TILES=0 forces the 4-wave ones
-    if few_tiles != "default":
-        monkeypatch.setenv("MO_NS_FEW_TILES", few_tiles)
+    # kernels; few_tile_max = 0 forces the 4-wave ones
+    opts = None if few_tiles == "default" else {"few_tile_max": int(few_tiles)}
     dtype = "bf16" if precision == "bf16" else "f32"
     mats, dev = _ns_case(NS_SHAPES, dtype, 21)
     coeffs = wl.coeff_table(kind)
-    outs = api.ns_orthogonalize_batched(dev, coeffs=coeffs, precision=precision)
+    outs = api.ns_orthogonalize_batched(dev, coeffs=coeffs, precision=precision, options=opts)
     for m, o in zip(mats, outs):
         ref = omuon.newton_schulz(wl.from_storage(m, dtype).astype(np.float64), coeffs)
         assert_ns_close(f64(o), ref, precision)
@@ -168,14 +167,14 @@ NS_BIG_SHAPES = [(520, 600), (1100, 530), (512, 512), (768, 2050), (40, 90), (30
 
 @pytest.mark.parametrize("precision", ["bf16", "fp32"])
 @pytest.mark.parametrize("kind", ["cubic", "quintic"])
-def test_ns_parity_big_tiles(precision, kind, monkeypatch):
+def test_ns_parity_big_tiles(precision, kind):
     # force the 256 x 256 kernels for these few tiles (by default they are
     # used only when a launch has enough tiles to fill the chip)
-    monkeypatch.setenv("MO_NS_BIG_TILE_MIN_WORK", "0")
     dtype = "bf16" if precision == "bf16" else "f32"
     mats, dev = _ns_case(NS_BIG_SHAPES, dtype, 25)
     coeffs = wl.coeff_table(kind)
-    outs = api.ns_orthogonalize_batched(dev, coeffs=coeffs, precision=precision)
+    outs = api.ns_orthogonalize_batched(dev, coeffs=coeffs, precision=precision,
+                                        options={"big_tile_min_work": 0})
     for m, o in zip(mats, outs):
         ref = omuon.newton_schulz(wl.from_storage(m, dtype).astype(np.float64), coeffs)
         assert_ns_close(f64(o), ref, precision)
@@ -187,12 +186,7 @@ def test_ns_tile_choice_agrees():
     mats, dev = _ns_case([(600, 700), (520, 1030)], "bf16", 27)
     coeffs = wl.coeff_table("cubic")
     a = api.ns_orthogonalize_batched(dev, coeffs=coeffs)
-    import os
-    os.environ["MO_NS_BIG_TILE_MIN_WORK"] = "0"
-    try:
-        b = api.ns_orthogonalize_batched(dev, coeffs=coeffs)
-    finally:
-        del os.environ["MO_NS_BIG_TILE_MIN_WORK"]
+    b = api.ns_orthogonalize_batched(dev, coeffs=coeffs, options={"big_tile_min_work": 0})
     for m, x, y in zip(mats, a, b):
         ref = omuon.newton_schulz(wl.from_storage(m, "bf16").astype(np.float64), coeffs)
         assert_ns_close(f64(x), ref, "bf16")

@@ -143,7 +143,7 @@ def test_plan_slice_table_host_only(w):
     arr = _fake_entries(w.params)
     h = C.c_void_p()
     hp = api.make_hparams()
-    L.check("plan", L.lib().mo_plan_create(arr, len(w.params), C.byref(hp), C.byref(h)))
+    L.check("plan", L.lib().mo_plan_create(arr, len(w.params), C.byref(hp), None, C.byref(h)))
     try:
         k = L.lib().mo_plan_num_slices(h)
         out = (C.c_int64 * (4 * k))()
@@ -169,12 +169,12 @@ def test_plan_validation_errors():
     h = C.c_void_p()
     hp = api.make_hparams()
     hp.ns_steps = 0
-    assert L.lib().mo_plan_create(arr, len(w.params), C.byref(hp), C.byref(h)) == L.MO_EINVAL
+    assert L.lib().mo_plan_create(arr, len(w.params), C.byref(hp), None, C.byref(h)) == L.MO_EINVAL
     hp = api.make_hparams(normuon=True)      # NorMuon without v buffers
-    assert L.lib().mo_plan_create(arr, len(w.params), C.byref(hp), C.byref(h)) == L.MO_EINVAL
+    assert L.lib().mo_plan_create(arr, len(w.params), C.byref(hp), None, C.byref(h)) == L.MO_EINVAL
     hp = api.make_hparams()
     arr[1].momentum = None                   # Muon param without momentum
-    assert L.lib().mo_plan_create(arr, len(w.params), C.byref(hp), C.byref(h)) == L.MO_EINVAL
+    assert L.lib().mo_plan_create(arr, len(w.params), C.byref(hp), None, C.byref(h)) == L.MO_EINVAL
     assert not h.value
     assert L.lib().mo_grouped_step(None, None, None, 0, None) == L.MO_EINVAL
 
@@ -196,21 +196,34 @@ def test_entry_point_validation_before_enqueue():
     ns[0].inp, ns[0].out, ns[0].rows, ns[0].cols, ns[0].ld_in, ns[0].ld_out = (
         _fake_ptr(3), _fake_ptr(4), 0, 8, 8, 8)
     co = (C.c_float * 15)(*([1.5, -0.5, 0.0] * 5))
-    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 0, None, 0, None) == L.MO_ESHAPE
+    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 0, None, None, 0, None) == L.MO_ESHAPE
     ns[0].rows = 4
-    assert lib.ns_orthogonalize_batched(ns, 1, co, 0, 0, None, 0, None) == L.MO_EINVAL
-    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 9, None, 0, None) == L.MO_EINVAL
+    assert lib.ns_orthogonalize_batched(ns, 1, co, 0, 0, None, None, 0, None) == L.MO_EINVAL
+    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 9, None, None, 0, None) == L.MO_EINVAL
     bad = (C.c_float * 15)(*([float("nan")] * 15))
-    assert lib.ns_orthogonalize_batched(ns, 1, bad, 5, 0, None, 0, None) == L.MO_EINVAL
-    need = lib.ns_workspace_bytes(ns, 1, 0)      # sized for the quintic (A buffer) layout
+    assert lib.ns_orthogonalize_batched(ns, 1, bad, 5, 0, None, None, 0, None) == L.MO_EINVAL
+    # options out of range
+    opt = L.NsOptions()
+    lib.mo_ns_options_default(C.byref(opt))
+    assert (opt.gram_space, opt.big_tile_min_work, opt.few_tile_max) == (1, -1, -1)
+    opt.gram_space = 2
+    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 0, C.byref(opt), None, 0, None) == \
+        L.MO_EINVAL
+    opt.gram_space, opt.few_tile_max = 1, -2
+    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 0, C.byref(opt), None, 0, None) == \
+        L.MO_EINVAL
+    need = lib.ns_workspace_bytes(ns, 1, None, 0, 0, None)   # the most any table needs
     assert need > 0
     qu = (C.c_float * 15)(*([15 / 8, -10 / 8, 3 / 8] * 5))
-    assert lib.ns_orthogonalize_batched(ns, 1, qu, 5, 0, C.c_void_p(_fake_ptr(9)), need - 256,
-                                        None) == L.MO_EWORKSPACE
-    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 0, C.c_void_p(_fake_ptr(9) + 16), need,
-                                        None) == L.MO_EALIGN
+    assert lib.ns_workspace_bytes(ns, 1, qu, 5, 0, None) <= need
+    assert lib.ns_workspace_bytes(ns, 1, co, 5, 0, None) <= need
+    need_q = lib.ns_workspace_bytes(ns, 1, qu, 5, 0, None)
+    assert lib.ns_orthogonalize_batched(ns, 1, qu, 5, 0, None, C.c_void_p(_fake_ptr(9)),
+                                        need_q - 256, None) == L.MO_EWORKSPACE
+    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 0, None, C.c_void_p(_fake_ptr(9) + 16),
+                                        need, None) == L.MO_EALIGN
     ns[0].ld_in = 4
-    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 0, None, 0, None) == L.MO_ESHAPE
+    assert lib.ns_orthogonalize_batched(ns, 1, co, 5, 0, None, None, 0, None) == L.MO_ESHAPE
     # AdamW: step 0, bad betas, workspace
     ad = (L.AdamwItem * 1)()
     ad[0].param, ad[0].grad, ad[0].exp_avg, ad[0].exp_avg_sq = [_fake_ptr(k) for k in (5, 6, 7, 8)]
@@ -237,7 +250,7 @@ def _fuses(specs, normuon=False, precision="bf16", keep=False, offset=0):
                 arr[i].param = _fake_ptr(8 * i) + offset
     h = C.c_void_p()
     hp = api.make_hparams(ns_precision=precision, normuon=normuon)
-    L.check("plan", L.lib().mo_plan_create(arr, len(specs), C.byref(hp), C.byref(h)))
+    L.check("plan", L.lib().mo_plan_create(arr, len(specs), C.byref(hp), None, C.byref(h)))
     try:
         if keep:
             L.check("keep", L.lib().mo_plan_keep_ns_output(h, 1))
@@ -290,16 +303,16 @@ def test_excluded_piece_alignment_and_buffers():
     h = C.c_void_p()
     hp = api.make_hparams()
     arr = _fake_entries([ok])
-    L.check("plan", L.lib().mo_plan_create(arr, 1, C.byref(hp), C.byref(h)))
+    L.check("plan", L.lib().mo_plan_create(arr, 1, C.byref(hp), None, C.byref(h)))
     assert L.lib().mo_plan_num_slices(h) == 2
     L.lib().mo_plan_destroy(h)
     arr = _fake_entries([ok])
     arr[0].exp_avg = None
-    assert L.lib().mo_plan_create(arr, 1, C.byref(hp), C.byref(h)) == L.MO_EINVAL
+    assert L.lib().mo_plan_create(arr, 1, C.byref(hp), None, C.byref(h)) == L.MO_EINVAL
     # rows of 6 bf16 columns: the excluded piece at row 3 starts 36 bytes in
     bad = wl.ParamSpec("f", (12, 6), "bf16", view=(2, 6, 6), split=(3, 3), exclude=(1,))
     arr = _fake_entries([bad])
-    assert L.lib().mo_plan_create(arr, 1, C.byref(hp), C.byref(h)) == L.MO_EALIGN
+    assert L.lib().mo_plan_create(arr, 1, C.byref(hp), None, C.byref(h)) == L.MO_EALIGN
 
 
 def test_lr_schedule_matches_oracle():
@@ -326,3 +339,44 @@ def test_lr_schedule_matches_oracle():
     assert L.lib().mo_lr_at(C.byref(ok), -1.0, C.byref(out)) == L.MO_EINVAL
     assert L.lib().mo_lr_at(C.byref(ok), float("nan"), C.byref(out)) == L.MO_EINVAL
     assert L.lib().mo_lr_at(None, 1.0, C.byref(out)) == L.MO_EINVAL
+
+
+@pytest.mark.parametrize("table,rect,resident", [
+    ([wl.CUBIC] * 5, True, True),          # gain 58: both
+    ([wl.CUBIC] * 8, True, True),          # gain 657
+    ([wl.CUBIC] * 9, False, False),        # gain 1478: past the threshold
+    ([wl.QUINTIC] * 5, False, True),       # gain 537; c != 0 keeps the GEMM path plain
+    ([wl.QUINTIC] * 6, False, False),      # gain 1888
+    ([wl.CUBIC, wl.QUINTIC, wl.CUBIC], False, True),
+])
+@pytest.mark.parametrize("gram_option", [True, False])
+def test_gram_space_rule_host_only(table, rect, resident, gram_option):
+    """Which slices run in Gram space (mo_plan_slice_algorithms): bf16,
+    the table's gain prod a_k^2 <= 1024, then rectangular GEMM slices with
+    cubic-type rows only and slice-resident slices with short side >= 64;
+    square GEMM slices, short sides below 64 and the fp32 path never."""
+    specs = (wl.ParamSpec("rect", (256, 640), "bf16"), wl.ParamSpec("square", (256, 256), "bf16"),
+             wl.ParamSpec("resident", (128, 512), "bf16"), wl.ParamSpec("thin", (40, 512), "bf16"),
+             wl.ParamSpec("rect32", (256, 640), "f32"))
+    for precision in ("bf16", "fp32"):
+        arr = _fake_entries(specs)
+        hp = api.make_hparams(coeffs=table, ns_precision=precision)
+        opts = api.plan_options(gram_space=gram_option)
+        h = C.c_void_p()
+        L.check("plan", L.lib().mo_plan_create(arr, len(specs), C.byref(hp), C.byref(opts),
+                                               C.byref(h)))
+        try:
+            n = L.lib().mo_plan_num_slices(h)
+            out = (C.c_int32 * n)()
+            L.check("algos", L.lib().mo_plan_slice_algorithms(h, out, n))
+            on = gram_option and precision == "bf16"
+            want_gram = [on and rect, False, on and resident, False, on and rect]
+            assert [bool(v & 1) for v in out] == want_gram
+            kinds = [v >> 1 for v in out]
+            if precision == "bf16":
+                assert kinds == [0, 0, 2, 2, 0]
+            else:
+                assert kinds == [0, 0, 0, 0, 0]
+            assert L.lib().mo_plan_gram_space(h) == int(any(want_gram))
+        finally:
+            L.lib().mo_plan_destroy(h)

@@ -378,3 +378,19 @@ def spiked_grad(w: Workload, index: int, step: int, rank: int = 8,
     v = g.standard_normal((rank, c), dtype=np.float32)
     spike = (u @ v) * np.float32(amplitude * w.grad_std / np.sqrt(rank))
     return to_storage(base + spike, p.dtype)
+
+
+def prescribed_spectrum(config_seed: int, index: int, rows: int, cols: int,
+                        sigma_hi: float = 1.0, sigma_lo: float = 1e-4,
+                        dtype: str = "bf16") -> np.ndarray:
+    """Matrix U diag(sigma) V^T with orthonormal U, V from the QR factors of
+    seeded Gaussians and sigma spaced geometrically from ``sigma_hi`` down to
+    ``sigma_lo`` (condition number sigma_hi / sigma_lo), built in float64,
+    rounded to fp32 and then to the storage dtype.  A stand-in for the badly
+    conditioned momentum matrices the NorMuon paper describes."""
+    g = rng(config_seed, 0, 20_000 + index)
+    s = min(rows, cols)
+    U, _ = np.linalg.qr(g.standard_normal((rows, s)))
+    V, _ = np.linalg.qr(g.standard_normal((cols, s)))
+    sig = np.geomspace(sigma_hi, sigma_lo, s)
+    return to_storage(((U * sig) @ V.T).astype(np.float32), dtype)
