@@ -21,6 +21,7 @@ MO_ALG_SKIP, MO_ALG_ADAMW, MO_ALG_MUON = -1, 0, 1
 MO_MAX_NDIM = 8
 MO_MAX_SPLIT = 8
 MO_NS_MAX_STEPS = 64
+MO_MAX_GROUPS = 256
 
 ROLE_CODES = {"matrix": MO_ROLE_MATRIX, "embedding": MO_ROLE_EMBEDDING, "head": MO_ROLE_HEAD,
               "norm": MO_ROLE_NORM}
@@ -83,7 +84,13 @@ class PlanOptions(C.Structure):
 
 
 class StepArgs(C.Structure):
-    _fields_ = [("muon_lr", f32), ("adamw_lr", f32), ("norm_out", vp)]
+    _fields_ = [("muon_lr", f32), ("adamw_lr", f32), ("norm_out", vp), ("group_lr", C.POINTER(f32)),
+                ("n_group_lr", i32), ("reserved", i32)]
+
+
+class Group(C.Structure):
+    _fields_ = [("algorithm", i32), ("nparams", i32), ("params", C.POINTER(Param)),
+                ("hp", HParams)]
 
 
 class LrSchedule(C.Structure):
@@ -115,6 +122,10 @@ SIGNATURES = [
     ("mo_plan_options_default", None, [C.POINTER(PlanOptions)]),
     ("mo_plan_create", i32, [C.POINTER(Param), i32, C.POINTER(HParams), C.POINTER(PlanOptions),
                              C.POINTER(vp)]),
+    ("mo_plan_create_groups", i32, [C.POINTER(Group), i32, C.POINTER(PlanOptions),
+                                    C.POINTER(vp)]),
+    ("mo_plan_num_params", i32, [vp]),
+    ("mo_plan_num_groups", i32, [vp]),
     ("mo_plan_destroy", None, [vp]),
     ("mo_plan_workspace_bytes", C.c_size_t, [vp]),
     ("mo_plan_route", i32, [vp, C.POINTER(RouteOut), i32]),
@@ -140,7 +151,7 @@ KERNEL_CLASSES = ["momentum", "ns_stats", "ns_scale", "ns_prep", "ns_gemm", "ns_
 
 #: ctypes mirror of each struct, in the order of mo_abi_struct_size's index.
 ABI_STRUCTS = [MomentumItem, NsItem, AdamwItem, ParamDesc, RouteOut, Param, HParams, StepArgs,
-               LrSchedule, NsOptions, PlanOptions]
+               LrSchedule, NsOptions, PlanOptions, Group]
 
 
 class LibraryError(RuntimeError):

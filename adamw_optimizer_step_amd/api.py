@@ -397,9 +397,55 @@ class Plan:
     """
 
     def __init__(self, entries: Sequence[dict], hparams: L.HParams, options=None):
-        n = len(entries)
+        self._setup(entries, options)
+        arr = self._param_array(self._keep)
+        h = C.c_void_p()
+        L.check("mo_plan_create",
+                L.lib().mo_plan_create(arr, len(self._keep), C.byref(hparams),
+                                       None if self._opts is None else C.byref(self._opts),
+                                       C.byref(h)))
+        self._h = h
+
+    @classmethod
+    def from_groups(cls, groups: Sequence[dict], options=None) -> "Plan":
+        """Plan over a group table (mo_plan_create_groups).  ``groups``: dicts
+        with ``algorithm`` ('muon' or 'adamw'), ``entries`` (as for the
+        constructor) and ``hparams`` (``make_hparams(...)``: the group's own
+        learning rate, decay and, for Muon, momentum, coefficient table and
+        NorMuon setting).  Plan order is group by group."""
+        self = cls.__new__(cls)
+        self._setup([e for g in groups for e in g["entries"]], options)
+        garr = (L.Group * max(len(groups), 1))()
+        self._arrays = []
+        for gi, g in enumerate(groups):
+            arr = self._param_array(g["entries"])
+            self._arrays.append(arr)
+            garr[gi].algorithm = {"muon": L.MO_ALG_MUON, "adamw": L.MO_ALG_ADAMW}[g["algorithm"]]
+            garr[gi].nparams = len(g["entries"])
+            garr[gi].params = C.cast(arr, C.POINTER(L.Param))
+            garr[gi].hp = g["hparams"]
+        h = C.c_void_p()
+        L.check("mo_plan_create_groups",
+                L.lib().mo_plan_create_groups(garr, len(groups),
+                                              None if self._opts is None else
+                                              C.byref(self._opts), C.byref(h)))
+        self._h = h
+        return self
+
+    def _setup(self, entries, options) -> None:
         self._keep = list(entries)
-        arr = (L.Param * max(n, 1))()
+        if options is not None and not isinstance(options, L.PlanOptions):
+            options = plan_options(**options)
+        self._opts = options
+        # kept on the instance: __del__ may run after module globals are gone
+        self._destroy = L.lib().mo_plan_destroy
+        self.n = len(self._keep)
+        self._ws: Optional[torch.Tensor] = None
+        self._slices = None
+
+    @staticmethod
+    def _param_array(entries):
+        arr = (L.Param * max(len(entries), 1))()
         for i, e in enumerate(entries):
             _check_entry(i, e)
             arr[i].desc = e["desc"]
@@ -409,21 +455,11 @@ class Plan:
                 arr[i].dtype = _dt(e["param"])
             for k in ("momentum", "normuon_v", "exp_avg", "exp_avg_sq"):
                 setattr(arr[i], k, _ptr(e.get(k)))
-        self._hp = hparams
-        if options is not None and not isinstance(options, L.PlanOptions):
-            options = plan_options(**options)
-        self._opts = options
-        h = C.c_void_p()
-        # kept on the instance: __del__ may run after module globals are gone
-        self._destroy = L.lib().mo_plan_destroy
-        L.check("mo_plan_create",
-                L.lib().mo_plan_create(arr, n, C.byref(hparams),
-                                       None if options is None else C.byref(options),
-                                       C.byref(h)))
-        self._h = h
-        self.n = n
-        self._ws: Optional[torch.Tensor] = None
-        self._slices = None
+        return arr
+
+    @property
+    def num_groups(self) -> int:
+        return int(L.lib().mo_plan_num_groups(self._h))
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -512,11 +548,20 @@ class Plan:
 
     def step(self, muon_lr: Optional[float] = None, adamw_lr: Optional[float] = None,
              norm_out: Optional[torch.Tensor] = None, stream=None,
-             workspace: Optional[torch.Tensor] = None) -> None:
+             workspace: Optional[torch.Tensor] = None,
+             group_lr: Optional[Sequence[Optional[float]]] = None) -> None:
+        """One hybrid step.  ``muon_lr`` / ``adamw_lr`` set every Muon / AdamW
+        group's rate this step; ``group_lr[g]`` (None = keep) sets group g's,
+        with precedence."""
         a = L.StepArgs()
         a.muon_lr = -1.0 if muon_lr is None else float(muon_lr)
         a.adamw_lr = -1.0 if adamw_lr is None else float(adamw_lr)
         a.norm_out = _ptr(norm_out)
+        if group_lr is not None:
+            vals = (C.c_float * max(len(group_lr), 1))(
+                *[-1.0 if v is None else float(v) for v in group_lr])
+            a.group_lr = C.cast(vals, C.POINTER(C.c_float))
+            a.n_group_lr = len(group_lr)
         if workspace is None:
             dev = next(e["param"].device for e in self._keep if e.get("param") is not None)
             workspace = self.workspace(dev)

@@ -227,7 +227,7 @@ mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const flo
   if ((s = launch_ns_scale(dprep, n, partials, scale, nullptr, st)) != MO_OK) return s;
   if ((s = launch_ns_prep(dprep, n, L.prep_tiles, scale, pool, L.elem, st)) != MO_OK) return s;
   if ((s = ns_run_iterations(L, base + W.tab, W.tabs, pool, scale, coeffs, steps, nullptr, 0.f,
-                             nullptr, st)) != MO_OK)
+                             nullptr, nullptr, st)) != MO_OK)
     return s;
   return launch_ns_final(reinterpret_cast<const FinalItem*>(base + W.fin), n, rows, pool, L.elem,
                          st);
@@ -245,7 +245,7 @@ mo_status normuon_rownorm(void* O, int32_t dtype, int64_t rows, int64_t cols, in
   std::memset(&one, 0, sizeof(one));
   one.o = O; one.nv = v; one.ld_o = ld; one.rows = static_cast<int32_t>(rows);
   one.cols = static_cast<int32_t>(cols); one.o_dt = dtype; one.w_dt = dtype; one.scale = 1.f;
-  return launch_rows(kRowNormInPlace, nullptr, 0, one, rows, 0.f, beta2, eps,
+  return launch_rows(kRowNormInPlace, nullptr, 0, one, rows, 0.f, nullptr, beta2, eps,
                      as_stream(stream));
 }
 
@@ -265,7 +265,8 @@ mo_status muon_update(void* W, int32_t w_dtype, const void* U, int32_t u_dtype, 
   one.w = W; one.o = const_cast<void*>(U); one.ld_w = ld_w; one.ld_o = ld_u;
   one.rows = static_cast<int32_t>(rows); one.cols = static_cast<int32_t>(cols);
   one.w_dt = w_dtype; one.o_dt = u_dtype; one.scale = scale; one.wd = wd;
-  return launch_rows(kRowUpdate, nullptr, 0, one, rows, lr, 0.f, 0.f, as_stream(stream));
+  return launch_rows(kRowUpdate, nullptr, 0, one, rows, lr, nullptr, 0.f, 0.f,
+                     as_stream(stream));
 }
 
 size_t adamw_workspace_bytes(const mo_adamw_item* items, int32_t n) {
@@ -297,7 +298,8 @@ mo_status adamw_clip_step(const mo_adamw_item* items, int32_t n, float lr, float
       return fail(MO_EALIGN, "item %d: pointers must be 16-byte aligned", i);
     AdamSeg s;
     s.p = it.param; s.g = it.grad; s.m = it.exp_avg; s.v = it.exp_avg_sq; s.numel = it.numel;
-    s.start = nblocks; s.dt = it.dtype; s.t0 = it.step; s.wd = it.weight_decay; s.pad = 0.f;
+    s.start = nblocks; s.dt = it.dtype; s.t0 = it.step; s.wd = it.weight_decay;
+    s.beta1 = beta1; s.beta2 = beta2; s.eps = eps; s.lr_slot = 0; s.pad = 0;
     nblocks += ceil_div(it.numel, kEltPerBlock);
     segs.push_back(s);
   }
@@ -313,7 +315,7 @@ mo_status adamw_clip_step(const mo_adamw_item* items, int32_t n, float lr, float
   const int nseg = static_cast<int>(segs.size());
   if ((s = launch_adam_sumsq(dsegs, nseg, nblocks, partials, st)) != MO_OK) return s;
   if ((s = launch_adam_norm(partials, nblocks, max_norm, scal, norm_out, st)) != MO_OK) return s;
-  return launch_adam_apply(dsegs, nseg, nblocks, scal, lr, beta1, beta2, eps, 0, st);
+  return launch_adam_apply(dsegs, nseg, nblocks, scal, lr, nullptr, 0, st);
 }
 
 mo_status mo_diag_copy(const void* src, void* dst, int64_t bytes, void* stream) {

@@ -186,13 +186,16 @@ __global__ __launch_bounds__(kNormThreads) void k_adam_norm(const double* __rest
 }
 
 __global__ __launch_bounds__(kThreads) void k_adam_apply(const AdamSeg* __restrict__ segs, int nseg,
-                                                         const double* __restrict__ scal, float lr,
-                                                         float beta1, float beta2, float eps,
+                                                         const double* __restrict__ scal,
+                                                         float lr_arg,
+                                                         const float* __restrict__ lrs,
                                                          int32_t tdelta) {
   const int64_t blk = blockIdx.x;
   const AdamSeg sg = segs[find_segment(segs, nseg, blk)];
   const int64_t base = (blk - sg.start) * kEltPerBlock;
   const float kappa = reinterpret_cast<const float*>(scal + 1)[0];
+  const float lr = lrs ? lrs[sg.lr_slot] : lr_arg;
+  const float beta1 = sg.beta1, beta2 = sg.beta2, eps = sg.eps;
   const int t = sg.t0 + tdelta;
   const double bc1 = one_minus_pow(beta1, t);
   const double bc2 = one_minus_pow(beta2, t);
@@ -251,8 +254,9 @@ __global__ __launch_bounds__(kThreads) void k_adam_apply(const AdamSeg* __restri
 // ---------------------------------------------------------------------------
 template <int kMode>
 __global__ __launch_bounds__(kThreads) void k_rows(const RowSeg* __restrict__ segs, int nseg,
-                                                   RowSeg one, int64_t total_rows, float lr,
-                                                   float beta2, float eps) {
+                                                   RowSeg one, int64_t total_rows, float lr_arg,
+                                                   const float* __restrict__ lrs, float beta2,
+                                                   float eps) {
   const int lane = threadIdx.x & 63;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
   if (row >= total_rows) return;
@@ -305,6 +309,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowSeg* __restrict__ se
     }
     return;
   }
+  const float lr = lrs ? lrs[sg.lr_slot] : lr_arg;
   const float decay = 1.f - lr * sg.wd;
   const float coef = lr * sg.scale * inv;
   if (vec_o && vec_w) {
@@ -362,35 +367,58 @@ mo_status launch_adam_norm(const double* partials, int64_t nblocks, float max_no
 }
 
 mo_status launch_adam_apply(const AdamSeg* segs, int nseg, int64_t nblocks, const double* scal,
-                            float lr, float beta1, float beta2, float eps, int32_t tdelta,
-                            hipStream_t st) {
+                            float lr, const float* lrs, int32_t tdelta, hipStream_t st) {
   if (nblocks <= 0) return MO_OK;
   KTimer tm(MO_KC_ADAM_APPLY, st);
   k_adam_apply<<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(
-      segs, nseg, scal, lr, beta1, beta2, eps, tdelta);
+      segs, nseg, scal, lr, lrs, tdelta);
   MO_LAUNCH_CHECK("k_adam_apply");
   return MO_OK;
 }
 
 mo_status launch_rows(int32_t mode, const RowSeg* segs, int nseg, const RowSeg& one,
-                      int64_t total_rows, float lr, float beta2, float eps, hipStream_t st) {
+                      int64_t total_rows, float lr, const float* lrs, float beta2, float eps,
+                      hipStream_t st) {
   if (total_rows <= 0) return MO_OK;
   const unsigned grid = static_cast<unsigned>(ceil_div(total_rows, kThreads / 64));
   KTimer tm(MO_KC_ROWS, st);
   switch (mode) {
     case kRowUpdate:
-      k_rows<kRowUpdate><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, beta2, eps);
+      k_rows<kRowUpdate><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, lrs, beta2,
+                                                     eps);
       break;
     case kRowNormUpdate:
-      k_rows<kRowNormUpdate><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, beta2,
-                                                         eps);
+      k_rows<kRowNormUpdate><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, lrs,
+                                                         beta2, eps);
       break;
     default:
-      k_rows<kRowNormInPlace><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, beta2,
-                                                          eps);
+      k_rows<kRowNormInPlace><<<grid, kThreads, 0, st>>>(segs, nseg, one, total_rows, lr, lrs,
+                                                          beta2, eps);
       break;
   }
   MO_LAUNCH_CHECK("k_rows");
+  return MO_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Per-step learning-rate table, written from the kernel's arguments.
+// ---------------------------------------------------------------------------
+struct LrArgs {
+  float v[kMaxLrSlots];
+};
+
+__global__ __launch_bounds__(kThreads) void k_set_lrs(float* __restrict__ dst, LrArgs a, int n) {
+  for (int i = threadIdx.x; i < n; i += kThreads) dst[i] = a.v[i];
+}
+
+mo_status launch_set_lrs(float* dst, const float* vals, int n, hipStream_t st) {
+  if (n <= 0) return MO_OK;
+  if (n > kMaxLrSlots) return fail(MO_EINVAL, "%d learning-rate slots (at most %d)", n,
+                                   kMaxLrSlots);
+  LrArgs a;
+  for (int i = 0; i < kMaxLrSlots; ++i) a.v[i] = i < n ? vals[i] : 0.f;
+  k_set_lrs<<<1, kThreads, 0, st>>>(dst, a, n);
+  MO_LAUNCH_CHECK("k_set_lrs");
   return MO_OK;
 }
 

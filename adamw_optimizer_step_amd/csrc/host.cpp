@@ -207,6 +207,7 @@ size_t mo_abi_struct_size(int32_t which) {
     case 8: return sizeof(mo_lr_schedule);
     case 9: return sizeof(mo_ns_options);
     case 10: return sizeof(mo_plan_options);
+    case 11: return sizeof(mo_group);
   }
   return 0;
 }

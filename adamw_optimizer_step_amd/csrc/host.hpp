@@ -165,13 +165,14 @@ mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st)
 // Enqueue the Newton-Schulz iterations on the prepared pool.
 // `scale` holds the per-slice normalisation scales (the prep kernel's).
 // wt (nullable): per-slice weight rows; the last iteration then applies the
-// Muon update with learning rate lr to them instead of writing O (bf16 pool,
-// every slice eligible; see fused_apply_ok).
+// Muon update to them instead of writing O (bf16 pool, every slice eligible),
+// at learning rate lrs[row.lr_slot] (lrs given, device) or lr.
 // range_fb (nullable): the per-slice range flags of launch_ns_scale, which
 // send a slice's in-place iteration 0 back to the prepared X0.
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                            float lr, const int32_t* range_fb, hipStream_t st);
+                            float lr, const float* lrs, const int32_t* range_fb,
+                            hipStream_t st);
 
 // True while kernel timing (mo_timing_enable) is on.
 bool timing_enabled();

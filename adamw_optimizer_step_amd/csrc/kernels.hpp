@@ -59,8 +59,10 @@ struct AdamSeg {
   int64_t start;       // first block
   int32_t dt;
   int32_t t0;          // step number for tdelta == 0
-  float wd;
-  float pad;
+  float wd;            // decoupled decay of the item's group
+  float beta1, beta2, eps;
+  int32_t lr_slot;     // learning rate: lrs[lr_slot] when a table is given
+  int32_t pad;
 };
 
 mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, double* partials,
@@ -68,9 +70,15 @@ mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, doub
 // Reduces partials -> T (fp64) and kappa (fp32) at scal[0], (float*)&scal[1].
 mo_status launch_adam_norm(const double* partials, int64_t nblocks, float max_norm, double* scal,
                            double* norm_out, hipStream_t st);
+// lrs (nullable): per-slot learning rates in device memory, read at each
+// segment's lr_slot; NULL = `lr` for every segment.
 mo_status launch_adam_apply(const AdamSeg* segs, int nseg, int64_t nblocks, const double* scal,
-                            float lr, float beta1, float beta2, float eps, int32_t tdelta,
-                            hipStream_t st);
+                            float lr, const float* lrs, int32_t tdelta, hipStream_t st);
+
+// Per-step learning-rate table: dst[i] = vals[i] for i < n (n <= kMaxLrSlots),
+// written by a kernel from its arguments (no host copy, no memset node).
+constexpr int kMaxLrSlots = 2 * MO_MAX_GROUPS;
+mo_status launch_set_lrs(float* dst, const float* vals, int n, hipStream_t st);
 
 // ----- row kernels: NorMuon row normalisation and the scaled Muon update -----
 enum RowMode : int32_t {
@@ -89,12 +97,16 @@ struct RowSeg {
   int32_t w_dt, o_dt;
   float scale;             // shape scale
   float wd;                // decoupled decay of this matrix's group
+  int32_t lr_slot;         // learning rate: lrs[lr_slot] when a table is given
+  int32_t pad;
 };
 
 // nseg == 0: `one` is the only matrix (passed by value, no table needed).
 mo_status launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+// lrs (nullable): per-slot learning rates, read at each segment's lr_slot.
 mo_status launch_rows(int32_t mode, const RowSeg* segs, int nseg, const RowSeg& one,
-                      int64_t total_rows, float lr, float beta2, float eps, hipStream_t st);
+                      int64_t total_rows, float lr, const float* lrs, float beta2, float eps,
+                      hipStream_t st);
 
 // ----- Newton-Schulz ------------------------------------------------------------
 constexpr int kPrepTile = 64;   // prep / stats tile edge
@@ -191,14 +203,14 @@ constexpr int kSmallS = 128;
 // build_ns_layout), the result in the second iterate buffer.
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
                           const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                          float lr, hipStream_t st, int gspace = 0);
+                          float lr, const float* lrs, hipStream_t st, int gspace = 0);
 
 // C = c1 A B (+ c0 E) (+ cd I on diagonal tiles).  bk = 1: B is read K-major
 // (K x N row-major) through LDS transpose reads; no E term, and the output
 // goes straight from registers to c (or, transposed, to ct).
 // wt (nullable, bf16 with bk = 1 only): problems with item >= 0 apply the Muon
 // update to the weights of slice `item` (as launch_ns_small) instead of
-// writing their output.  pscale (nullable): problems with sitem >= 0 scale
+// writing their output, at learning rate lrs[wt[item].lr_slot] (lrs given) or lr.  pscale (nullable): problems with sitem >= 0 scale
 // c1 by pscale[sitem]^2 (bk = 0) or pscale[sitem] (bk = 1), unless
 // pfb[sitem] is set: they then read alt_off for the X operand(s), unscaled.
 // c1b, cdb: the constants of the second outputs (c2_off).
@@ -207,8 +219,8 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
                          int64_t few_max, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
-                         const RowSeg* wt, float lr, const float* pscale, const int32_t* pfb,
-                         hipStream_t st, float c1b = 0.f, float cdb = 0.f);
+                         const RowSeg* wt, float lr, const float* lrs, const float* pscale,
+                         const int32_t* pfb, hipStream_t st, float c1b = 0.f, float cdb = 0.f);
 mo_status launch_ns_final(const FinalItem* items, int n, int64_t total_rows, const void* pool,
                           int elem, hipStream_t st);
 

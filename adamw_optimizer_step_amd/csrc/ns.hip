@@ -517,9 +517,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
 template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK, int ST, int SRB>
 __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1_arg,
-    int has_e, float cd, const RowSeg* __restrict__ wt, float lr,
-    const float* __restrict__ pscale, const int32_t* __restrict__ pfb, float c1b_arg,
-    float cdb) {
+    int has_e, float cd, const RowSeg* __restrict__ wt, float lr_arg,
+    const float* __restrict__ lrs, const float* __restrict__ pscale,
+    const int32_t* __restrict__ pfb, float c1b_arg, float cdb) {
   using C = GemmCfg<T, BM, BN, WM, WN, BK, ST, SRB>;
   constexpr int NT = C::kThreads, FM = C::FM, FN = C::FN;
   __shared__ __attribute__((aligned(16))) char smem[C::kLdsBytes];
@@ -814,6 +814,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
         // (every weight load of the thread is issued before the first update)
         const RowSeg w = wt[pr.item];
         const int orow0 = to_c ? ti * BM : tj * BN, ocol0 = to_c ? tj * BN : ti * BM;
+        const float lr = lrs ? lrs[w.lr_slot] : lr_arg;
         const float decay = 1.f - lr * w.wd, coef = lr * w.scale;
         constexpr int NP = BM * NCH / NT;
         W8 wr[NP];
@@ -1189,7 +1190,8 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
                                                             const float* __restrict__ scale,
                                                             NsCoeffTable cf, int steps,
                                                             const RowSeg* __restrict__ wt,
-                                                            float lr) {
+                                                            float lr_arg,
+                                                            const float* __restrict__ lrs) {
   __shared__ __attribute__((aligned(16))) char smem[kSmTile * (2 + kSmStages)];
   char* const Ps = smem;             // P (A operand of the update)
   char* const Xn = smem + kSmTile;   // the new block X'_b (and A in a quintic step)
@@ -1383,6 +1385,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
         // apply the Muon step to the slice's weights (stored orientation,
         // clipped to the real extent) instead of writing O
         const RowSeg w = wt[pr.item];
+        const float lr = lrs ? lrs[w.lr_slot] : lr_arg;
         const float decay = 1.f - lr * w.wd, coef = lr * w.scale;
         // (one chunk at a time: holding all four weight chunks of a thread
         // in registers would spill in this kernel)
@@ -1576,22 +1579,22 @@ mo_status launch_ns_prep_fallback(const PrepItem* items, int n, const float* sca
 template <typename T, int BM, int WM, int WN, int ST = 4, int SRB = 64>
 void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
                        float c1, int has_e, float cd, const RowSeg* wt, float lr,
-                       const float* pscale, const int32_t* pfb, float c1b, float cdb,
-                       hipStream_t st) {
+                       const float* lrs, const float* pscale, const int32_t* pfb, float c1b,
+                       float cdb, hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
   if (bk)
     k_ns_gemm<T, BM, BM, WM, WN, 2, true, ST, SRB><<<grid, NT, 0, st>>>(
-        probs, n, pool, c0, c1, has_e, cd, wt, lr, pscale, pfb, c1b, cdb);
+        probs, n, pool, c0, c1, has_e, cd, wt, lr, lrs, pscale, pfb, c1b, cdb);
   else
     k_ns_gemm<T, BM, BM, WM, WN, 2, false, ST, SRB><<<grid, NT, 0, st>>>(
-        probs, n, pool, c0, c1, has_e, cd, wt, lr, pscale, pfb, c1b, cdb);
+        probs, n, pool, c0, c1, has_e, cd, wt, lr, lrs, pscale, pfb, c1b, cdb);
 }
 
 mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
                          int64_t few_max, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
-                         const RowSeg* wt, float lr, const float* pscale, const int32_t* pfb,
-                         hipStream_t st, float c1b, float cdb) {
+                         const RowSeg* wt, float lr, const float* lrs, const float* pscale,
+                         const int32_t* pfb, hipStream_t st, float c1b, float cdb) {
   if (ntiles <= 0) return MO_OK;
   if (bk && has_e) return fail(MO_EINVAL, "the K-major-B GEMM takes no E term");
   if (wt && (!bk || elem != 2))
@@ -1606,10 +1609,10 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     if (elem == 2)
       launch_gemm_shape<uint16_t, 256, 2, 4, 2, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, pscale, pfb, c1b, cdb, st);
+                                                     cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
     else
       launch_gemm_shape<float, 256, 2, 4>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, cd, wt, lr, pscale, pfb, c1b, cdb, st);
+                                          has_e, cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
   } else if (tile == 128) {
     // A launch with few tiles leaves most CUs idle and lasts as long as one
     // tile's K loop, whose length is set by the fixed cost of each K slab
@@ -1620,14 +1623,14 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     if (elem == 2 && ntiles < few_max)
       launch_gemm_shape<uint16_t, 128, 2, 4, 4, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, pscale, pfb, c1b, cdb, st);
+                                                     cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
     else if (elem == 2)  // 2 stages of 64-deep slabs, as for 256 x 256 tiles (64 KiB)
       launch_gemm_shape<uint16_t, 128, 2, 2, 2, 128>(probs, n, grid, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
-                                                     cd, wt, lr, pscale, pfb, c1b, cdb, st);
+                                                     cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
     else
       launch_gemm_shape<float, 128, 2, 2>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
-                                          has_e, cd, wt, lr, pscale, pfb, c1b, cdb, st);
+                                          has_e, cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
   } else {
     return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);
   }
@@ -1637,7 +1640,7 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
 
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
                           const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                          float lr, hipStream_t st, int gspace) {
+                          float lr, const float* lrs, hipStream_t st, int gspace) {
   if (n <= 0) return MO_OK;
   if (steps < 1 || steps > MO_NS_MAX_STEPS) return fail(MO_EINVAL, "bad step count %d", steps);
   NsCoeffTable cf;
@@ -1650,10 +1653,10 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
   KTimer tm(MO_KC_NS_SMALL, st);
   if (gspace)
     k_ns_small<true><<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
-        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr);
+        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr, lrs);
   else
     k_ns_small<false><<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
-        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr);
+        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr, lrs);
   MO_LAUNCH_CHECK("k_ns_small");
   return MO_OK;
 }

@@ -346,7 +346,8 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
 
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                            float lr, const int32_t* range_fb, hipStream_t st) {
+                            float lr, const float* lrs, const int32_t* range_fb,
+                            hipStream_t st) {
   auto tab = [dtab](size_t off) { return reinterpret_cast<const GemmProb*>(dtab + off); };
   for (int gsm = 0; gsm < 2; ++gsm) {
     const std::vector<SmallProb>& v = gsm ? L.small_gs : L.small;
@@ -354,7 +355,7 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
     mo_status s = launch_ns_small(
         reinterpret_cast<const SmallProb*>(dtab + (gsm ? T.small_gs : T.small)),
         static_cast<int>(v.size()), pool, reinterpret_cast<const PrepItem*>(dtab + T.prep),
-        scale, coeffs, steps, wt, lr, st, gsm);
+        scale, coeffs, steps, wt, lr, lrs, st, gsm);
     if (s != MO_OK) return s;
   }
   // Gram-space sequence (every GEMM slice of the layout, or none)
@@ -371,13 +372,13 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       mo_status s;
       if (B.gs_kind[j] == kGsGram)
         s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, 0.f, 1.f, 0, 0.f,
-                           nullptr, 0.f, scale, range_fb, st, b, a);
+                           nullptr, 0.f, nullptr, scale, range_fb, st, b, a);
       else if (B.gs_kind[j] == kGsProd)
         s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, a, b, 1, 0.f, nullptr,
-                           0.f, nullptr, nullptr, st);
+                           0.f, nullptr, nullptr, nullptr, st);
       else
         s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, wt,
-                           lr, scale, range_fb, st);
+                           lr, lrs, scale, range_fb, st);
       if (s != MO_OK) return s;
     }
   }
@@ -400,13 +401,13 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       mo_status s;
       if (cubic_step) {
         s = launch_ns_gemm(tab(first ? tb.gram_p0 : tb.gram_p[q]), n, B.gram_tiles, B.tile, L.few_tile_max, 0,
-                           pool, L.elem, 0.f, b, 0, a, nullptr, 0.f, ps, pfb, st);
+                           pool, L.elem, 0.f, b, 0, a, nullptr, 0.f, nullptr, ps, pfb, st);
       } else {
         s = launch_ns_gemm(tab(first ? tb.gram_a0 : tb.gram_a[q]), n, B.gram_tiles, B.tile, L.few_tile_max, 0,
-                           pool, L.elem, 0.f, 1.f, 0, 0.f, nullptr, 0.f, ps, pfb, st);
+                           pool, L.elem, 0.f, 1.f, 0, 0.f, nullptr, 0.f, nullptr, ps, pfb, st);
         if (s == MO_OK)
           s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, B.tile, L.few_tile_max, 0, pool, L.elem, b, c, 1,
-                             a, nullptr, 0.f, nullptr, nullptr, st);
+                             a, nullptr, 0.f, nullptr, nullptr, nullptr, st);
       }
       if (s != MO_OK) return s;
     }
@@ -419,7 +420,7 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const size_t off = fin ? (first ? tb.fin0 : tb.fin[q]) : (first ? tb.upd0 : tb.upd[q]);
       mo_status s = launch_ns_gemm(tab(off), static_cast<int>(B.upd[q].size()), B.upd_tiles,
                                    B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr,
-                                   lr, ps, pfb, st);
+                                   lr, lrs, ps, pfb, st);
       if (s != MO_OK) return s;
     }
   }

@@ -56,6 +56,7 @@ typedef enum mo_algorithm { MO_ALG_SKIP = -1, MO_ALG_ADAMW = 0, MO_ALG_MUON = 1 
 #define MO_MAX_NDIM 8
 #define MO_MAX_SPLIT 8
 #define MO_NS_MAX_STEPS 64
+#define MO_MAX_GROUPS 256
 
 const char* mo_status_str(mo_status s);
 /* Message of the last failing call on this thread ("" if none). */
@@ -65,7 +66,7 @@ const char* mo_version(void);
 /* sizeof() of the ABI structs, for binding self-checks: 0 mo_momentum_item,
  * 1 mo_ns_item, 2 mo_adamw_item, 3 mo_param_desc, 4 mo_route_out, 5 mo_param,
  * 6 mo_hparams, 7 mo_step_args, 8 mo_lr_schedule, 9 mo_ns_options,
- * 10 mo_plan_options; 0 for any other index. */
+ * 10 mo_plan_options, 11 mo_group; 0 for any other index. */
 size_t mo_abi_struct_size(int32_t which);
 
 /* ------------------------------------------------------------------------
@@ -335,26 +336,33 @@ mo_status mo_lr_at(const mo_lr_schedule* s, double tokens, double* lr);
 /* ------------------------------------------------------------------------
  * Plan + grouped hybrid step over a parameter-group table.
  *
- * mo_plan_create routes `params` (mo_route), expands Muon views into
- * independent slices and sizes the workspace; it is host-only.  The plan
- * keeps the tensor pointers given here; its small device-side descriptor
- * tables are allocated and uploaded on the first mo_grouped_step call and
- * freed by mo_plan_destroy.
+ * The group table follows the kimi-k3 "build_parameter_groups" page: each
+ * group lists its params with their algorithm and weight decay (plus, for
+ * Muon, the registered view and split sizes of each param).  A plan is made
+ * either from such a table (mo_plan_create_groups: each group with its own
+ * hyper-parameters) or from a flat parameter list that the library routes
+ * itself (mo_plan_create: mo_route's groups, all on one hyper-parameter
+ * block, decay where the routing key decays).  Plan creation is host-only;
+ * the plan keeps the tensor pointers given here; its small device-side
+ * descriptor tables are allocated and uploaded on the first mo_grouped_step
+ * call and freed by mo_plan_destroy.
  *
  * mo_grouped_step runs one full hybrid step on `stream`:
- *   Muon params with a grad: muon_momentum -> per-slice Newton-Schulz ->
- *     [NorMuon row normalisation] -> shape scale -> update (lr, wd if the
- *     routing key decays);
- *   AdamW params with a grad: adamw_clip_step over all of them jointly
- *     (decay only for decaying groups); the per-parameter step counter t is
- *     kept by the plan and incremented after each call.
+ *   Muon params with a grad: momentum -> per-slice Newton-Schulz ->
+ *     [NorMuon row normalisation] -> shape scale -> update, each with its
+ *     group's lr, decay, momentum, coefficient table and NorMuon setting;
+ *   AdamW params with a grad, over every AdamW group jointly: one global-norm
+ *     clip (the OMN page's clip over the AdamW parameters), then AdamW with
+ *     each group's lr, decay, betas and eps; the per-parameter step counter t
+ *     is kept by the plan and incremented after each call.
  *   Excluded pieces of a Muon param (exclude_mask) are AdamW parameters of
- *     their own: they join the clip norm and take the AdamW update with the
- *     param's step counter, reading and writing exp_avg / exp_avg_sq at the
- *     same element offsets as the param; Muon leaves their rows alone
- *     (momentum, direction and weight).  Such a param needs momentum,
- *     exp_avg and exp_avg_sq buffers of numel elements, and each excluded
- *     piece must start on a 16-byte boundary in all four (MO_EALIGN).
+ *     their own: they join the clip norm and take the AdamW update (the
+ *     group's adamw_lr, adamw_wd, betas, eps) with the param's step counter,
+ *     reading and writing exp_avg / exp_avg_sq at the same element offsets as
+ *     the param; Muon leaves their rows alone (momentum, direction and
+ *     weight).  Such a param needs momentum, exp_avg and exp_avg_sq buffers of
+ *     numel elements, and each excluded piece must start on a 16-byte
+ *     boundary in all four (MO_EALIGN).
  * Sources: as for the individual entry points above; the ordering of NorMuon
  * before the shape scale is this library's reading (the pages do not order
  * them).
@@ -390,10 +398,32 @@ typedef struct mo_hparams {
   float max_norm;
 } mo_hparams;
 
+/* One group of mo_plan_create_groups.  Muon groups read muon_lr, muon_wd,
+ * mu, nesterov, ns_steps, ns_precision, ns_coeffs and the normuon fields of
+ * `hp` (and the AdamW fields for excluded pieces); AdamW groups read
+ * adamw_lr, adamw_wd, beta1, beta2, eps.  max_norm must be the same in every
+ * group that has AdamW items (the clip norm is joint).  A Muon group's
+ * params must be 2-D. */
+typedef struct mo_group {
+  int32_t algorithm;      /* MO_ALG_MUON or MO_ALG_ADAMW */
+  int32_t nparams;
+  const mo_param* params; /* host array of nparams */
+  mo_hparams hp;
+} mo_group;
+
+/* Per-step arguments (NULL = none).  The learning rate of group g this step
+ * is group_lr[g] when g < n_group_lr and group_lr[g] >= 0; else muon_lr
+ * (Muon groups) or adamw_lr (AdamW groups, and the excluded pieces of Muon
+ * groups) when >= 0; else the group's own hp value.  A scheduler drives the
+ * rates through these fields (the OMN page steps both schedules from one
+ * token clock; see mo_lr_at). */
 typedef struct mo_step_args {
-  float muon_lr;          /* < 0: use the plan's hparams */
-  float adamw_lr;         /* < 0: use the plan's hparams */
+  float muon_lr;
+  float adamw_lr;
   double* norm_out;       /* device fp64 scalar receiving the AdamW pre-clip norm T (nullable) */
+  const float* group_lr;  /* host, n_group_lr entries (nullable) */
+  int32_t n_group_lr;
+  int32_t reserved;
 } mo_step_args;
 
 typedef struct mo_plan mo_plan;
@@ -409,10 +439,23 @@ typedef struct mo_plan_options {
 
 void mo_plan_options_default(mo_plan_options* o);
 
+/* Routes params (mo_route) and makes one group per routing key on `hp`.
+ * Plan order of the params is the order given. */
 mo_status mo_plan_create(const mo_param* params, int32_t n, const mo_hparams* hp,
                          const mo_plan_options* opts, mo_plan** out);
+/* Plan over a caller's group table (at most MO_MAX_GROUPS groups).  Plan
+ * order of the params is group by group, in table order; params with
+ * requires_grad == 0 are skipped.  MO_ECONFLICT when a parameter identity
+ * appears twice, MO_EEMPTY when nothing is trainable, MO_EINVAL for a bad
+ * algorithm or hyper-parameter (or differing max_norm), MO_ESHAPE for a Muon
+ * param that is not 2-D or a bad view. */
+mo_status mo_plan_create_groups(const mo_group* groups, int32_t ngroups,
+                                const mo_plan_options* opts, mo_plan** out);
 void mo_plan_destroy(mo_plan* plan);
 size_t mo_plan_workspace_bytes(const mo_plan* plan);
+/* Number of params (plan order) and of groups (0 for NULL). */
+int32_t mo_plan_num_params(const mo_plan* plan);
+int32_t mo_plan_num_groups(const mo_plan* plan);
 /* Host queries for tests: routing of each param and the slice table. */
 mo_status mo_plan_route(const mo_plan* plan, mo_route_out* out, int32_t n);
 int32_t mo_plan_num_slices(const mo_plan* plan);

@@ -126,22 +126,6 @@ def test_muon_adamw_steps_rebuild_and_state():
     assert opt2._plan.get_steps() == [3, 3, 0, 0, 0]
 
 
-def test_muon_adamw_rejects_mismatched_grad():
-    """A gradient whose dtype or size differs from its parameter is refused
-    before anything is enqueued (the library reads G with W's dtype)."""
-    w = _model("bf16")
-    named = _params(w)
-    opt = MuonAdamW(named)
-    _set_grads(w, named, 1)
-    named[2]["param"].grad = torch.zeros(named[2]["param"].shape, dtype=torch.float32,
-                                         device="cuda")
-    with pytest.raises(TypeError):
-        opt.step()
-    named[2]["param"].grad = torch.zeros(10, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(ValueError):
-        opt.step()
-
-
 def test_token_clock_drives_both_rates():
     """Seven steps with 80-token windows through a schedule with a 100-token
     warmup, the peak to 300, a square-root cooldown to 500 and the floor

@@ -380,3 +380,105 @@ def test_gram_space_rule_host_only(table, rect, resident, gram_option):
             assert L.lib().mo_plan_gram_space(h) == int(any(want_gram))
         finally:
             L.lib().mo_plan_destroy(h)
+
+
+def test_plan_entries_checked_before_the_library_sees_them():
+    """api.Plan refuses a gradient or state whose dtype, size, layout or
+    device does not match its parameter before calling mo_plan_create (the
+    library reads G with W's dtype and every buffer with W's element count,
+    so such an entry would read past an allocation).  CPU tensors only."""
+    import torch
+    spec = wl.ParamSpec("w", (8, 16), "bf16")
+    desc = api.make_desc(spec.name, spec.shape)
+
+    def entry(**over):
+        e = {"desc": desc, "param": torch.zeros(8, 16, dtype=torch.bfloat16),
+             "grad": torch.zeros(8, 16, dtype=torch.bfloat16),
+             "momentum": torch.zeros(8, 16)}
+        e.update(over)
+        return e
+
+    hp = api.make_hparams()
+    bad = [(TypeError, dict(grad=torch.zeros(8, 16))),                          # fp32 grad
+           (ValueError, dict(grad=torch.zeros(10, dtype=torch.bfloat16))),      # size
+           (ValueError, dict(grad=torch.zeros(16, 8, dtype=torch.bfloat16).t())),  # layout
+           (ValueError, dict(momentum=torch.zeros(8, 8))),                       # state size
+           (TypeError, dict(momentum=torch.zeros(8, 16, dtype=torch.bfloat16))),
+           (ValueError, dict(normuon_v=torch.zeros(16))),                         # rows
+           (ValueError, dict(grad=torch.zeros(8, 16, dtype=torch.bfloat16, device="meta"))),
+           (ValueError, dict(param=torch.zeros(4, 16, dtype=torch.bfloat16)))]
+    for exc, over in bad:
+        with pytest.raises(exc):
+            api.Plan([entry(**over)], hp)
+
+
+def _group(alg, specs, first, **hp):
+    arr = _fake_entries(specs, normuon=hp.get("normuon", False))
+    for i in range(len(specs)):
+        arr[i].desc.ident = first + i
+    g = L.Group()
+    g.algorithm = L.MO_ALG_MUON if alg == "muon" else L.MO_ALG_ADAMW
+    g.nparams = len(specs)
+    g.params = C.cast(arr, C.POINTER(L.Param))
+    g.hp = api.make_hparams(**hp)
+    return g, arr
+
+
+def test_group_table_host_only():
+    """mo_plan_create_groups: plan order is group by group, routes report each
+    group's algorithm and decay, slices come from each param's view; the
+    table is validated before anything is built."""
+    mat = wl.ParamSpec("q", (96, 96), "bf16")
+    heads = wl.ParamSpec("h", (256, 64), "bf16", view=(2, 128, 64))
+    emb = wl.ParamSpec("e", (64, 32), "bf16", wl.ROLE_EMBEDDING)
+    gain = wl.ParamSpec("n", (32,), "bf16", wl.ROLE_NORM)
+    keep = []
+    gs = [_group("muon", [mat], 0, muon_lr=0.02, muon_wd=0.1),
+          _group("muon", [heads], 10, muon_lr=0.005, coeffs=[wl.QUINTIC] * 5, normuon=True),
+          _group("adamw", [emb], 20, adamw_lr=1e-3, adamw_wd=0.01),
+          _group("adamw", [gain], 30, adamw_lr=3e-4, beta1=0.8)]
+    keep += [a for _, a in gs]
+    table = (L.Group * 4)(*[g for g, _ in gs])
+    h = C.c_void_p()
+    L.check("groups", L.lib().mo_plan_create_groups(table, 4, None, C.byref(h)))
+    try:
+        assert L.lib().mo_plan_num_groups(h) == 4 and L.lib().mo_plan_num_params(h) == 4
+        out = (L.RouteOut * 4)()
+        L.check("route", L.lib().mo_plan_route(h, out, 4))
+        got = [(o.algorithm, o.decay, o.group, o.nslices) for o in out]
+        assert got == [(L.MO_ALG_MUON, 1, 0, 1), (L.MO_ALG_MUON, 0, 1, 2),
+                       (L.MO_ALG_ADAMW, 1, 2, 0), (L.MO_ALG_ADAMW, 0, 3, 0)]
+        n = L.lib().mo_plan_num_slices(h)
+        sl = (C.c_int64 * (4 * n))()
+        L.check("slices", L.lib().mo_plan_slices(h, sl, n))
+        assert [tuple(sl[4 * k:4 * k + 4]) for k in range(n)] == \
+            [(0, 0, 96, 96), (1, 0, 128, 64), (1, 128, 128, 64)]
+    finally:
+        L.lib().mo_plan_destroy(h)
+
+    def create(groups):
+        t = (L.Group * len(groups))(*groups)
+        hh = C.c_void_p()
+        st = L.lib().mo_plan_create_groups(t, len(groups), None, C.byref(hh))
+        if st == L.MO_OK:
+            L.lib().mo_plan_destroy(hh)
+        return st
+
+    dup, a1 = _group("muon", [mat], 0)
+    dup2, a2 = _group("adamw", [gain], 0)             # same identity 0
+    assert create([dup, dup2]) == L.MO_ECONFLICT
+    flat, a3 = _group("muon", [gain], 40)             # a 1-D param in a Muon group
+    assert create([flat]) == L.MO_ESHAPE
+    n1, a4 = _group("adamw", [emb], 50, max_norm=1.0)
+    n2, a5 = _group("adamw", [gain], 60, max_norm=2.0)
+    assert create([n1, n2]) == L.MO_EINVAL            # the clip norm is joint
+    bad, a6 = _group("muon", [mat], 70)
+    bad.algorithm = 7
+    assert create([bad]) == L.MO_EINVAL
+    frozen = api.make_desc("f", (8, 8), requires_grad=False, ident=80)
+    arr = (L.Param * 1)()
+    arr[0].desc = frozen
+    g = L.Group()
+    g.algorithm, g.nparams, g.params = L.MO_ALG_MUON, 1, C.cast(arr, C.POINTER(L.Param))
+    g.hp = api.make_hparams()
+    assert create([g]) == L.MO_EEMPTY
