@@ -115,6 +115,42 @@ AdamWs adam_ws_layout(const mo_adamw_item* items, int32_t n) {
 
 }  // namespace
 
+namespace mo {
+
+mo_status adam_segments(const mo_adamw_item* items, int32_t n, float lr, float beta1, float beta2,
+                        float eps, float max_norm, AdamSeg* segs, int max_segs, int* nseg,
+                        int64_t* nblocks) {
+  if (n < 0 || (n > 0 && !items)) return fail(MO_EINVAL, "bad item list");
+  if (!std::isfinite(lr) || !std::isfinite(beta1) || !std::isfinite(beta2) ||
+      !std::isfinite(eps) || beta1 < 0.f || beta1 >= 1.f || beta2 < 0.f || beta2 >= 1.f ||
+      std::isnan(max_norm))
+    return fail(MO_EINVAL, "bad hyper-parameter");
+  *nseg = 0;
+  *nblocks = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const mo_adamw_item& it = items[i];
+    if (it.numel < 0) return fail(MO_EINVAL, "item %d: negative numel", i);
+    if (!it.grad || it.numel == 0) continue;
+    if (!it.param || !it.exp_avg || !it.exp_avg_sq) return fail(MO_EINVAL, "item %d: NULL", i);
+    if (!valid_dtype(it.dtype)) return fail(MO_EDTYPE, "item %d: bad dtype", i);
+    if (it.step < 1) return fail(MO_EINVAL, "item %d: step must be >= 1", i);
+    if (!std::isfinite(it.weight_decay)) return fail(MO_EINVAL, "item %d: bad decay", i);
+    if (!aligned16(it.param) || !aligned16(it.grad) || !aligned16(it.exp_avg) ||
+        !aligned16(it.exp_avg_sq))
+      return fail(MO_EALIGN, "item %d: pointers must be 16-byte aligned", i);
+    if (*nseg >= max_segs)
+      return fail(MO_EWORKSPACE, "more than %d items with a gradient", max_segs);
+    AdamSeg& s = segs[(*nseg)++];
+    s.p = it.param; s.g = it.grad; s.m = it.exp_avg; s.v = it.exp_avg_sq; s.numel = it.numel;
+    s.start = *nblocks; s.dt = it.dtype; s.t0 = it.step; s.wd = it.weight_decay;
+    s.beta1 = beta1; s.beta2 = beta2; s.eps = eps; s.lr_slot = 0; s.pad = 0;
+    *nblocks += ceil_div(it.numel, kEltPerBlock);
+  }
+  return MO_OK;
+}
+
+}  // namespace mo
+
 extern "C" {
 
 size_t muon_momentum_workspace_bytes(int32_t n) { return momentum_table_bytes(n); }
@@ -279,40 +315,20 @@ mo_status adamw_clip_step(const mo_adamw_item* items, int32_t n, float lr, float
                           size_t ws_bytes, void* stream) {
   clear_error();
   if (n < 0 || (n > 0 && !items)) return fail(MO_EINVAL, "bad item list");
-  if (!std::isfinite(lr) || !std::isfinite(beta1) || !std::isfinite(beta2) ||
-      !std::isfinite(eps) || beta1 < 0.f || beta1 >= 1.f || beta2 < 0.f || beta2 >= 1.f ||
-      std::isnan(max_norm))
-    return fail(MO_EINVAL, "bad hyper-parameter");
-  std::vector<AdamSeg> segs;
+  std::vector<AdamSeg> segs(static_cast<size_t>(n > 0 ? n : 1));
+  int nseg = 0;
   int64_t nblocks = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    const mo_adamw_item& it = items[i];
-    if (it.numel < 0) return fail(MO_EINVAL, "item %d: negative numel", i);
-    if (!it.grad || it.numel == 0) continue;
-    if (!it.param || !it.exp_avg || !it.exp_avg_sq) return fail(MO_EINVAL, "item %d: NULL", i);
-    if (!valid_dtype(it.dtype)) return fail(MO_EDTYPE, "item %d: bad dtype", i);
-    if (it.step < 1) return fail(MO_EINVAL, "item %d: step must be >= 1", i);
-    if (!std::isfinite(it.weight_decay)) return fail(MO_EINVAL, "item %d: bad decay", i);
-    if (!aligned16(it.param) || !aligned16(it.grad) || !aligned16(it.exp_avg) ||
-        !aligned16(it.exp_avg_sq))
-      return fail(MO_EALIGN, "item %d: pointers must be 16-byte aligned", i);
-    AdamSeg s;
-    s.p = it.param; s.g = it.grad; s.m = it.exp_avg; s.v = it.exp_avg_sq; s.numel = it.numel;
-    s.start = nblocks; s.dt = it.dtype; s.t0 = it.step; s.wd = it.weight_decay;
-    s.beta1 = beta1; s.beta2 = beta2; s.eps = eps; s.lr_slot = 0; s.pad = 0;
-    nblocks += ceil_div(it.numel, kEltPerBlock);
-    segs.push_back(s);
-  }
-  const AdamWs W = adam_ws_layout(items, n);
-  mo_status s = check_ws(ws, ws_bytes, W.total);
+  mo_status s = adam_segments(items, n, lr, beta1, beta2, eps, max_norm, segs.data(), n, &nseg,
+                              &nblocks);
   if (s != MO_OK) return s;
+  const AdamWs W = adam_ws_layout(items, n);
+  if ((s = check_ws(ws, ws_bytes, W.total)) != MO_OK) return s;
   hipStream_t st = as_stream(stream);
   char* base = static_cast<char*>(ws);
   double* partials = reinterpret_cast<double*>(base + W.partials);
   double* scal = reinterpret_cast<double*>(base + W.scal);
   const AdamSeg* dsegs = reinterpret_cast<const AdamSeg*>(base + W.tab);
-  if ((s = upload(base + W.tab, segs.data(), segs.size() * sizeof(AdamSeg), st)) != MO_OK) return s;
-  const int nseg = static_cast<int>(segs.size());
+  if ((s = upload(base + W.tab, segs.data(), nseg * sizeof(AdamSeg), st)) != MO_OK) return s;
   if ((s = launch_adam_sumsq(dsegs, nseg, nblocks, partials, st)) != MO_OK) return s;
   if ((s = launch_adam_norm(partials, nblocks, max_norm, scal, norm_out, st)) != MO_OK) return s;
   return launch_adam_apply(dsegs, nseg, nblocks, scal, lr, nullptr, 0, st);

@@ -174,6 +174,14 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
                             float lr, const float* lrs, const int32_t* range_fb,
                             hipStream_t st);
 
+// Validates an AdamW call (adamw_clip_step's arguments) and writes one
+// AdamSeg per item with a gradient into segs (capacity max_segs, host
+// memory); *nseg and *nblocks receive the counts.  MO_EWORKSPACE when more
+// than max_segs items have a gradient.
+mo_status adam_segments(const mo_adamw_item* items, int32_t n, float lr, float beta1, float beta2,
+                        float eps, float max_norm, AdamSeg* segs, int max_segs, int* nseg,
+                        int64_t* nblocks);
+
 // True while kernel timing (mo_timing_enable) is on.
 bool timing_enabled();
 

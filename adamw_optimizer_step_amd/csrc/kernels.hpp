@@ -28,6 +28,16 @@ class KTimer {
   bool active_ = false;
 };
 
+// While one exists on a thread, KTimer scopes on that thread record nothing
+// and create no events (launches that must not acquire resources).
+class KTimerOff {
+ public:
+  KTimerOff();
+  ~KTimerOff();
+  KTimerOff(const KTimerOff&) = delete;
+  KTimerOff& operator=(const KTimerOff&) = delete;
+};
+
 // ----- momentum (elementwise, 8192 elements per block) ----------------------
 constexpr int kEltPerThread = 8;
 constexpr int kEltIters = 1;

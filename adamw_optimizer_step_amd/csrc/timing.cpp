@@ -14,6 +14,7 @@ struct Record {
 std::mutex g_mu;
 bool g_on = false;
 std::vector<Record> g_recs;
+thread_local int g_quiet = 0;   // KTimerOff scopes on this thread
 
 void clear_locked() {
   for (Record& r : g_recs) {
@@ -24,7 +25,11 @@ void clear_locked() {
 }
 }  // namespace
 
+KTimerOff::KTimerOff() { ++g_quiet; }
+KTimerOff::~KTimerOff() { --g_quiet; }
+
 KTimer::KTimer(int cls, hipStream_t st) : cls_(cls), st_(st) {
+  if (g_quiet) return;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_on) return;
   if (hipEventCreate(&a_) != hipSuccess) return;
