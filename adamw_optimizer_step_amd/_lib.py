@@ -116,6 +116,8 @@ SIGNATURES = [
     ("adamw_workspace_bytes", C.c_size_t, [C.POINTER(AdamwItem), i32]),
     ("adamw_clip_step", i32, [C.POINTER(AdamwItem), i32, f32, f32, f32, f32, f32, vp, vp,
                               C.c_size_t, vp]),
+    ("adamw_clip_step_noalloc", i32, [C.POINTER(AdamwItem), i32, f32, f32, f32, f32, f32, vp,
+                                      vp]),
     ("mo_route", i32, [C.POINTER(ParamDesc), i32, C.POINTER(RouteOut), C.POINTER(i32)]),
     ("mo_expand_view", i32, [i64, i64, i32, C.POINTER(i64), i32, C.POINTER(i64),
                              C.POINTER(i64), i32, C.POINTER(i32)]),

@@ -186,12 +186,7 @@ def muon_update(W: torch.Tensor, U: torch.Tensor, lr: float, wd: float = 0.0,
                                 _stream(stream)))
 
 
-def adamw_clip_step(params: Sequence[torch.Tensor], grads: Sequence[Optional[torch.Tensor]],
-                    exp_avgs: Sequence[torch.Tensor], exp_avg_sqs: Sequence[torch.Tensor],
-                    steps: Sequence[int], lr: float, beta1: float = 0.9, beta2: float = 0.95,
-                    eps: float = 1e-8, weight_decay=0.0, max_norm: float = 1.0,
-                    norm_out: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Joint clipped AdamW step; ``weight_decay`` is a float or one per param."""
+def _adamw_items(params, grads, exp_avgs, exp_avg_sqs, steps, weight_decay, norm_out):
     n = len(params)
     wds = list(weight_decay) if isinstance(weight_decay, (list, tuple)) else [weight_decay] * n
     items = (L.AdamwItem * max(n, 1))()
@@ -201,6 +196,8 @@ def adamw_clip_step(params: Sequence[torch.Tensor], grads: Sequence[Optional[tor
             _dense(t, nm)
         if m.dtype != torch.float32 or v.dtype != torch.float32:
             raise TypeError("AdamW moments are fp32")
+        if m.numel() != p.numel() or v.numel() != p.numel():
+            raise ValueError("AdamW moments must match the param's size")
         items[i].param = _ptr(p)
         items[i].exp_avg = _ptr(m)
         items[i].exp_avg_sq = _ptr(v)
@@ -212,14 +209,42 @@ def adamw_clip_step(params: Sequence[torch.Tensor], grads: Sequence[Optional[tor
             _dense(g, "grad")
             if g.dtype != p.dtype:
                 raise TypeError("grad dtype must match the param dtype")
+            if g.numel() != p.numel():
+                raise ValueError("grad must match the param's size")
             items[i].grad = _ptr(g)
     if norm_out is not None and (norm_out.dtype != torch.float64 or norm_out.numel() < 1):
         raise TypeError("norm_out must be a float64 device tensor")
+    return items
+
+
+def adamw_clip_step(params: Sequence[torch.Tensor], grads: Sequence[Optional[torch.Tensor]],
+                    exp_avgs: Sequence[torch.Tensor], exp_avg_sqs: Sequence[torch.Tensor],
+                    steps: Sequence[int], lr: float, beta1: float = 0.9, beta2: float = 0.95,
+                    eps: float = 1e-8, weight_decay=0.0, max_norm: float = 1.0,
+                    norm_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Joint clipped AdamW step; ``weight_decay`` is a float or one per param."""
+    n = len(params)
+    items = _adamw_items(params, grads, exp_avgs, exp_avg_sqs, steps, weight_decay, norm_out)
     dev = params[0].device if n else torch.device("cuda")
     ws = _workspace(L.lib().adamw_workspace_bytes(items, n), dev)
     L.check("adamw_clip_step",
             L.lib().adamw_clip_step(items, n, lr, beta1, beta2, eps, max_norm, _ptr(norm_out),
                                     C.c_void_p(ws.data_ptr()), ws.numel(), _stream(stream)))
+
+
+def adamw_clip_step_noalloc(params: Sequence[torch.Tensor],
+                            grads: Sequence[Optional[torch.Tensor]],
+                            exp_avgs: Sequence[torch.Tensor], exp_avg_sqs: Sequence[torch.Tensor],
+                            steps: Sequence[int], lr: float, beta1: float = 0.9,
+                            beta2: float = 0.95, eps: float = 1e-8, weight_decay=0.0,
+                            max_norm: float = 1.0, norm_out: Optional[torch.Tensor] = None,
+                            stream=None) -> None:
+    """adamw_clip_step with the library's fixed device scratch instead of a
+    workspace: nothing is allocated (for code that cannot allocate)."""
+    items = _adamw_items(params, grads, exp_avgs, exp_avg_sqs, steps, weight_decay, norm_out)
+    L.check("adamw_clip_step_noalloc",
+            L.lib().adamw_clip_step_noalloc(items, len(params), lr, beta1, beta2, eps, max_norm,
+                                            _ptr(norm_out), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

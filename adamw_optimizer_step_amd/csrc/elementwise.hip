@@ -126,9 +126,9 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
 // apply kernel's partition, one 16-byte load of 8 elements per thread and
 // block, all issued before the reduction (four independent fp64 sums), and
 // writes one partial.
-constexpr int kSumsqSub = 4;
+constexpr int kSumsqSub = kSumsqBlocksPerPartial;
 __host__ __device__ constexpr int64_t sumsq_partials(int64_t nblocks) {
-  return (nblocks + kSumsqSub - 1) / kSumsqSub;
+  return sumsq_partial_count(nblocks);
 }
 
 __global__ __launch_bounds__(kThreads) void k_adam_sumsq(const AdamSeg* __restrict__ segs, int nseg,

@@ -75,6 +75,12 @@ struct AdamSeg {
   int32_t pad;
 };
 
+// k_adam_sumsq writes one fp64 partial sum per kSumsqBlocksPerPartial blocks
+// of kEltPerBlock elements: sumsq_partial_count(nblocks) partials in all.
+constexpr int kSumsqBlocksPerPartial = 4;
+__host__ __device__ constexpr int64_t sumsq_partial_count(int64_t nblocks) {
+  return (nblocks + kSumsqBlocksPerPartial - 1) / kSumsqBlocksPerPartial;
+}
 mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, double* partials,
                             hipStream_t st);
 // Reduces partials -> T (fp64) and kappa (fp32) at scal[0], (float*)&scal[1].

@@ -249,6 +249,28 @@ mo_status adamw_clip_step(const mo_adamw_item* items, int32_t n, float lr, float
                           size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * adamw_clip_step_noalloc - adamw_clip_step without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments (minus ws, ws_bytes), arithmetic, kernels and results as
+ * adamw_clip_step.  The scratch the step needs (segment table, fp64 partial
+ * sums, the norm and the clip factor) is a fixed 1 MiB array in device
+ * memory that the library holds on every GPU it runs on until the process
+ * ends; the call itself allocates nothing (no hipMalloc, no pinned staging,
+ * no timing events) and writes everything it reads from that array, so no
+ * clearing is needed between calls.  Limits: at most 64 items with a
+ * gradient and about 1.07e9 elements in all (ceil(numel / 2048) blocks per
+ * item, one partial per 4 blocks, 130,016 partials); beyond them MO_EWORKSPACE
+ * with the numbers in mo_last_error(), before anything is enqueued.  Calls
+ * that overlap on one GPU (different streams, unordered) share the array and
+ * race; order them on one stream.
+ * ------------------------------------------------------------------------ */
+mo_status adamw_clip_step_noalloc(const mo_adamw_item* items, int32_t n, float lr, float beta1,
+                                  float beta2, float eps, float max_norm, double* norm_out,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
  * Host-only: routing predicate and view expansion (no GPU needed).
  *
  * mo_route follows the kimi-k3 "build_parameter_groups" page ("Exclusion and

@@ -482,3 +482,24 @@ def test_group_table_host_only():
     g.algorithm, g.nparams, g.params = L.MO_ALG_MUON, 1, C.cast(arr, C.POINTER(L.Param))
     g.hp = api.make_hparams()
     assert create([g]) == L.MO_EEMPTY
+
+
+def test_noalloc_limits_refused_before_any_launch():
+    """adamw_clip_step_noalloc: more than 64 items with a gradient, or more
+    elements than its fixed scratch covers, is refused (MO_EWORKSPACE) on
+    the host, before the device is touched (no GPU here)."""
+    lib = L.lib()
+    items = (L.AdamwItem * 65)()
+    for i in range(65):
+        items[i].param, items[i].grad = _fake_ptr(4 * i), _fake_ptr(4 * i + 1)
+        items[i].exp_avg, items[i].exp_avg_sq = _fake_ptr(4 * i + 2), _fake_ptr(4 * i + 3)
+        items[i].numel, items[i].dtype, items[i].step = 1024, L.MO_BF16, 1
+    assert lib.adamw_clip_step_noalloc(items, 65, 1e-3, 0.9, 0.95, 1e-8, 1.0, None, None) == \
+        L.MO_EWORKSPACE
+    assert "64" in lib.mo_last_error().decode()
+    items[0].numel = 130016 * 4 * 2048 + 1          # one block past the partial capacity
+    assert lib.adamw_clip_step_noalloc(items, 1, 1e-3, 0.9, 0.95, 1e-8, 1.0, None, None) == \
+        L.MO_EWORKSPACE
+    items[0].numel, items[0].step = 1024, 0
+    assert lib.adamw_clip_step_noalloc(items, 1, 1e-3, 0.9, 0.95, 1e-8, 1.0, None, None) == \
+        L.MO_EINVAL
