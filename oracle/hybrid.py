@@ -35,6 +35,8 @@ class HyperParams:
     normuon: bool = False
     normuon_beta2: float = 0.95
     normuon_eps: float = 1e-8
+    spectral_cap: float = 0.0        # inactive by default (OMN page, Muon-path paragraph)
+    spectral_iters: int = 8
     adamw_lr: float = 3e-4
     beta1: float = 0.90
     beta2: float = 0.95
@@ -91,7 +93,8 @@ def hybrid_step(descs: List[dict], W: Dict[str, np.ndarray], G: Dict[str, Option
                     hp.coeffs, hp.muon_lr, hp.mu, hp.muon_wd if g["decay"] else 0.0,
                     hp.nesterov,
                     normuon_v=nv, normuon_beta2=hp.normuon_beta2,
-                    normuon_eps=hp.normuon_eps)
+                    normuon_eps=hp.normuon_eps, spectral_cap_value=hp.spectral_cap,
+                    spectral_iters=hp.spectral_iters)
                 Wm, Bm = res["W"], res["B"]
                 for off, r, _ in excl:   # rows that Muon does not own
                     Wm[off:off + r] = W[name][off:off + r]

@@ -17,6 +17,14 @@ Sources (page titles and sections):
 * MuonClip page, "Newton-Schulz Orthogonalization": the cubic set
   X <- 1.5 X - 0.5 X (X^T X).
 
+* OMN page, Muon-path paragraph: an optional spectral-cap guard on the
+  momentum buffer with a power-iteration estimate, inactive by default in
+  the recipe.  Its details are not printed; the reading used here: per
+  independent matrix, after B_t = mu B_{t-1} + G_t, K power iterations on
+  B^T B from v_0 = ones / sqrt(cols) give v_K, sigma = ||B v_K||; when sigma
+  exceeds the cap tau the buffer is rescaled to tau / sigma times itself
+  (the rescaled buffer is the state and feeds the Nesterov direction).
+
 Readings where the pages are silent (each listed in the design notes):
 the Frobenius epsilon is 1e-7 added to the norm; Nesterov uses the updated
 buffer, D = G + mu * B_t; NorMuon keeps v_0 = 0, no bias correction, epsilon
@@ -40,6 +48,30 @@ def momentum(B: np.ndarray, G: np.ndarray, mu: float, nesterov: bool = True):
     B_new = mu * B + G
     D = G + mu * B_new if nesterov else B_new.copy()
     return B_new, D
+
+
+def spectral_estimate(B: np.ndarray, iters: int) -> float:
+    """Power-iteration estimate of the largest singular value of B: v_0 =
+    ones(cols) / sqrt(cols); v_{k+1} = B^T B v_k / ||B^T B v_k|| for k < iters;
+    the estimate is ||B v_iters||.  Zero when B^T B v_k vanishes."""
+    B = np.asarray(B, dtype=np.float64)
+    v = np.ones(B.shape[1]) / math.sqrt(B.shape[1])
+    for _ in range(iters):
+        w = B.T @ (B @ v)
+        n = math.sqrt(float(np.sum(w * w)))
+        if n == 0.0:
+            return 0.0
+        v = w / n
+    return math.sqrt(float(np.sum((B @ v) ** 2)))
+
+
+def spectral_cap(B: np.ndarray, cap: float, iters: int) -> np.ndarray:
+    """The spectral-cap guard on one independent matrix of the buffer:
+    B (cap / sigma) when the estimate sigma exceeds cap > 0, else B."""
+    if not cap > 0.0:
+        return B
+    sigma = spectral_estimate(B, iters)
+    return B * (cap / sigma) if sigma > cap else B
 
 
 def normalise(D: np.ndarray) -> np.ndarray:
@@ -87,14 +119,22 @@ def apply_update(W: np.ndarray, U: np.ndarray, lr: float, wd: float = 0.0) -> np
 def muon_param_step(W: np.ndarray, G: np.ndarray, B: np.ndarray, slices,
                     coeffs, lr: float, mu: float, wd: float = 0.0,
                     nesterov: bool = True, normuon_v: Optional[np.ndarray] = None,
-                    normuon_beta2: float = 0.95, normuon_eps: float = 1e-8):
+                    normuon_beta2: float = 0.95, normuon_eps: float = 1e-8,
+                    spectral_cap_value: float = 0.0, spectral_iters: int = 8):
     """One Muon step for one stored weight with its slice table.
 
     ``slices`` is [(row_offset, rows, cols), ...]; every slice is processed
-    independently.  Returns dict with W, B, D, O (pre-NorMuon NS output laid
-    out like W), U (final scaled update) and v (NorMuon state or None).
+    independently.  With ``spectral_cap_value`` > 0 each slice of the buffer
+    passes the spectral-cap guard before the direction is formed.  Returns
+    dict with W, B, D, O (pre-NorMuon NS output laid out like W), U (final
+    scaled update) and v (NorMuon state or None).
     """
     B_new, D = momentum(B, G, mu, nesterov)
+    if spectral_cap_value > 0.0:
+        for off, r, _ in slices:
+            B_new[off:off + r] = spectral_cap(B_new[off:off + r], spectral_cap_value,
+                                              spectral_iters)
+        D = G + mu * B_new if nesterov else B_new.copy()
     O = np.zeros_like(D)
     U = np.zeros_like(D)
     v_new = None if normuon_v is None else normuon_v.copy()
