@@ -71,7 +71,11 @@ class HParams(C.Structure):
                 ("ns_coeffs", (f32 * 3) * MO_NS_MAX_STEPS), ("normuon", i32),
                 ("normuon_beta2", f32), ("normuon_eps", f32), ("adamw_lr", f32),
                 ("beta1", f32), ("beta2", f32), ("eps", f32), ("adamw_wd", f32),
-                ("max_norm", f32)]
+                ("max_norm", f32), ("spectral_cap", f32), ("spectral_iters", i32)]
+
+
+class SpectralItem(C.Structure):
+    _fields_ = [("b", vp), ("rows", i64), ("cols", i64), ("ld", i64)]
 
 
 class NsOptions(C.Structure):
@@ -111,6 +115,9 @@ SIGNATURES = [
                                         C.POINTER(NsOptions)]),
     ("ns_orthogonalize_batched", i32, [C.POINTER(NsItem), i32, C.POINTER(f32), i32, i32,
                                        C.POINTER(NsOptions), vp, C.c_size_t, vp]),
+    ("muon_spectral_workspace_bytes", C.c_size_t, [C.POINTER(SpectralItem), i32]),
+    ("muon_spectral_estimate", i32, [C.POINTER(SpectralItem), i32, i32, vp, vp, C.c_size_t,
+                                     vp]),
     ("normuon_rownorm", i32, [vp, i32, i64, i64, i64, vp, f32, f32, vp]),
     ("muon_update", i32, [vp, i32, vp, i32, i64, i64, i64, i64, f32, f32, f32, vp]),
     ("adamw_workspace_bytes", C.c_size_t, [C.POINTER(AdamwItem), i32]),
@@ -149,11 +156,11 @@ SIGNATURES = [
 ]
 
 KERNEL_CLASSES = ["momentum", "ns_stats", "ns_scale", "ns_prep", "ns_gemm", "ns_final", "rows",
-                  "adam_sumsq", "adam_norm", "adam_apply", "ns_small"]
+                  "adam_sumsq", "adam_norm", "adam_apply", "ns_small", "spectral"]
 
 #: ctypes mirror of each struct, in the order of mo_abi_struct_size's index.
 ABI_STRUCTS = [MomentumItem, NsItem, AdamwItem, ParamDesc, RouteOut, Param, HParams, StepArgs,
-               LrSchedule, NsOptions, PlanOptions, Group]
+               LrSchedule, NsOptions, PlanOptions, Group, SpectralItem]
 
 
 class LibraryError(RuntimeError):

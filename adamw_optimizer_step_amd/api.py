@@ -166,6 +166,27 @@ def ns_orthogonalize_batched(inputs: Sequence[torch.Tensor],
     return outputs
 
 
+def muon_spectral_estimate(mats: Sequence[torch.Tensor], iters: int = 8,
+                           stream=None) -> torch.Tensor:
+    """Power-iteration estimate of each fp32 matrix's largest singular value
+    (the spectral-cap guard's estimate); returns a float64 device tensor."""
+    n = len(mats)
+    items = (L.SpectralItem * max(n, 1))()
+    for i, m in enumerate(mats):
+        if m.dtype != torch.float32:
+            raise TypeError("the guard's matrices are fp32 buffers")
+        items[i].b = _ptr(m)
+        items[i].rows, items[i].cols = m.shape
+        items[i].ld = _matrix(m, "matrix")
+    out = torch.empty(max(n, 1), dtype=torch.float64, device=mats[0].device)
+    ws = _workspace(L.lib().muon_spectral_workspace_bytes(items, n), mats[0].device)
+    L.check("muon_spectral_estimate",
+            L.lib().muon_spectral_estimate(items, n, int(iters), _ptr(out),
+                                           C.c_void_p(ws.data_ptr()), ws.numel(),
+                                           _stream(stream)))
+    return out[:n]
+
+
 def normuon_rownorm(O: torch.Tensor, v: torch.Tensor, beta2: float = 0.95, eps: float = 1e-8,
                     stream=None) -> None:
     if v.dtype != torch.float32 or v.numel() != O.shape[0]:
@@ -346,7 +367,7 @@ class TokenClock:
 def make_hparams(muon_lr=0.01, muon_wd=0.0, mu=0.95, nesterov=True, coeffs=((1.5, -0.5, 0.0),) * 5,
                  ns_precision="bf16", normuon=False, normuon_beta2=0.95, normuon_eps=1e-8,
                  adamw_lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, adamw_wd=0.0,
-                 max_norm=1.0) -> L.HParams:
+                 max_norm=1.0, spectral_cap=0.0, spectral_iters=8) -> L.HParams:
     h = L.HParams()
     h.muon_lr, h.muon_wd, h.mu, h.nesterov = muon_lr, muon_wd, mu, int(bool(nesterov))
     rows = [tuple(r) for r in coeffs]
@@ -359,6 +380,7 @@ def make_hparams(muon_lr=0.01, muon_wd=0.0, mu=0.95, nesterov=True, coeffs=((1.5
     h.normuon, h.normuon_beta2, h.normuon_eps = int(bool(normuon)), normuon_beta2, normuon_eps
     h.adamw_lr, h.beta1, h.beta2, h.eps = adamw_lr, beta1, beta2, eps
     h.adamw_wd, h.max_norm = adamw_wd, max_norm
+    h.spectral_cap, h.spectral_iters = spectral_cap, int(spectral_iters)
     return h
 
 

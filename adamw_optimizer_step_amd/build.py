@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmuonadamw.so")
 SOURCES = ["host.cpp", "ns_host.cpp", "api.cpp", "plan.cpp", "timing.cpp", "staging.cpp",
-           "elementwise.hip", "ns.hip", "noalloc.hip"]
+           "elementwise.hip", "ns.hip", "noalloc.hip", "spectral.hip"]
 ARCH = "gfx950"
 
 

@@ -149,9 +149,116 @@ mo_status adam_segments(const mo_adamw_item* items, int32_t n, float lr, float b
   return MO_OK;
 }
 
+PowLayout pow_layout(const int64_t* rows, const int64_t* cols, int n, WsCursor& c) {
+  PowLayout L;
+  for (int i = 0; i < n; ++i) {
+    L.rows += rows[i];
+    L.cols += cols[i];
+    L.row_blocks += pow_row_blocks(rows[i]);
+    L.col_blocks += pow_col_blocks(cols[i]);
+  }
+  L.tab = c.take(sizeof(PowSeg) * n);
+  L.u = c.take(sizeof(double) * L.rows);
+  L.w = c.take(sizeof(double) * L.cols);
+  L.rpart = c.take(sizeof(double) * L.row_blocks);
+  L.cpart = c.take(sizeof(double) * L.col_blocks);
+  L.inv = c.take(sizeof(double) * n);
+  L.sigma = c.take(sizeof(double) * n);
+  L.kappa = c.take(sizeof(float) * n);
+  return L;
+}
+
+void pow_fill(PowSeg* segs, const int64_t* rows, const int64_t* cols, int n) {
+  int64_t rb = 0, cb = 0, uo = 0, wo = 0;
+  for (int i = 0; i < n; ++i) {
+    PowSeg& s = segs[i];
+    s.rblk0 = rb;
+    s.cblk0 = cb;
+    s.u_off = uo;
+    s.w_off = wo;
+    s.rows = static_cast<int32_t>(rows[i]);
+    s.cols = static_cast<int32_t>(cols[i]);
+    rb += pow_row_blocks(rows[i]);
+    cb += pow_col_blocks(cols[i]);
+    uo += rows[i];
+    wo += cols[i];
+  }
+}
+
+PowWork pow_work(const PowLayout& L, char* base) {
+  PowWork w;
+  w.u = reinterpret_cast<double*>(base + L.u);
+  w.w = reinterpret_cast<double*>(base + L.w);
+  w.rpart = reinterpret_cast<double*>(base + L.rpart);
+  w.cpart = reinterpret_cast<double*>(base + L.cpart);
+  w.inv = reinterpret_cast<double*>(base + L.inv);
+  w.sigma = reinterpret_cast<double*>(base + L.sigma);
+  w.kappa = reinterpret_cast<float*>(base + L.kappa);
+  return w;
+}
+
 }  // namespace mo
 
+namespace {
+
+mo_status spectral_items(const mo_spectral_item* items, int32_t n, std::vector<int64_t>& r,
+                         std::vector<int64_t>& c) {
+  if (n <= 0 || !items) return fail(MO_EINVAL, "no matrices");
+  r.resize(n);
+  c.resize(n);
+  for (int32_t i = 0; i < n; ++i) {
+    const mo_spectral_item& it = items[i];
+    if (!it.b) return fail(MO_EINVAL, "item %d: NULL matrix", i);
+    if (it.rows < 1 || it.cols < 1 || it.rows > 65536 || it.cols > 65536)
+      return fail(MO_ESHAPE, "item %d: shape (%lld, %lld) outside [1, 65536]", i,
+                  static_cast<long long>(it.rows), static_cast<long long>(it.cols));
+    if (it.ld < it.cols) return fail(MO_ESHAPE, "item %d: row stride smaller than cols", i);
+    r[i] = it.rows;
+    c[i] = it.cols;
+  }
+  return MO_OK;
+}
+
+}  // namespace
+
 extern "C" {
+
+size_t muon_spectral_workspace_bytes(const mo_spectral_item* items, int32_t n) {
+  std::vector<int64_t> r, c;
+  if (spectral_items(items, n, r, c) != MO_OK) return 0;
+  WsCursor cur;
+  pow_layout(r.data(), c.data(), n, cur);
+  return align_up(cur.off, 256);
+}
+
+mo_status muon_spectral_estimate(const mo_spectral_item* items, int32_t n, int32_t iters,
+                                 double* sigma_out, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  std::vector<int64_t> r, c;
+  mo_status s = spectral_items(items, n, r, c);
+  if (s != MO_OK) return s;
+  if (iters < 0 || iters > MO_NS_MAX_STEPS)
+    return fail(MO_EINVAL, "iters must be in [0, %d]", MO_NS_MAX_STEPS);
+  if (!sigma_out) return fail(MO_EINVAL, "NULL sigma_out");
+  WsCursor cur;
+  const PowLayout L = pow_layout(r.data(), c.data(), n, cur);
+  if ((s = check_ws(ws, ws_bytes, align_up(cur.off, 256))) != MO_OK) return s;
+  std::vector<PowSeg> segs(n);
+  pow_fill(segs.data(), r.data(), c.data(), n);
+  for (int32_t i = 0; i < n; ++i) {
+    segs[i].b = items[i].b;
+    segs[i].ld = items[i].ld;
+  }
+  char* base = static_cast<char*>(ws);
+  hipStream_t st = as_stream(stream);
+  if ((s = upload(base + L.tab, segs.data(), segs.size() * sizeof(PowSeg), st)) != MO_OK) return s;
+  PowWork wk = pow_work(L, base);
+  wk.sigma = sigma_out;
+  wk.kappa = nullptr;
+  return launch_power_iteration(reinterpret_cast<const PowSeg*>(base + L.tab), n, L.row_blocks,
+                                L.col_blocks, iters, wk, 0.f, st);
+}
+
 
 size_t muon_momentum_workspace_bytes(int32_t n) { return momentum_table_bytes(n); }
 

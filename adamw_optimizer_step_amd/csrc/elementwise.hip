@@ -66,12 +66,16 @@ __device__ double one_minus_pow(double beta, int t) {
 // Momentum: B <- mu B + G ; D <- G + mu B (Nesterov) or B.
 // (OMN "Dual-Manifold Optimization", Muon-path paragraph; NorMuon eq. (1).)
 // ---------------------------------------------------------------------------
-template <bool kStats>
+template <bool kStats, int kPhase>
 __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict__ segs, int nseg,
                                                        float mu, int nesterov,
-                                                       StatPartial* __restrict__ stats) {
+                                                       StatPartial* __restrict__ stats,
+                                                       const float* __restrict__ kappa) {
   const int64_t blk = blockIdx.x;
-  const MomSeg sg = segs[find_segment(segs, nseg, blk)];
+  const int si = find_segment(segs, nseg, blk);
+  const MomSeg sg = segs[si];
+  // phase 2: the spectral-cap factor of this segment (1 leaves B as stored)
+  const float kap = kPhase == 2 ? kappa[si] : 1.f;
   const int64_t base = (blk - sg.start) * kEltPerBlock;
   float amax = 0.f;
   double ss = 0.0;
@@ -93,16 +97,18 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      b[k] = mu * b[k] + g[k];
+      b[k] = kPhase == 2 ? kap * b[k] : mu * b[k] + g[k];
       d[k] = nesterov ? g[k] + mu * b[k] : b[k];
     }
+    const bool store_b = kPhase != 2 || kap != 1.f;
+    void* const dst = kPhase == 1 ? nullptr : sg.d;
     if (vec) {
-      store4<true>(sg.b, e0, MO_F32, b);
-      if (sg.d) store4<true>(sg.d, e0, sg.ddt, d);
+      if (store_b) store4<true>(sg.b, e0, MO_F32, b);
+      if (dst) store4<true>(dst, e0, sg.ddt, d);
     } else {
       for (int k = 0; k < cnt; ++k) {
-        sg.b[e0 + k] = b[k];
-        if (sg.d) store_from_f32(sg.d, e0 + k, sg.ddt, d[k]);
+        if (store_b) sg.b[e0 + k] = b[k];
+        if (dst) store_from_f32(dst, e0 + k, sg.ddt, d[k]);
       }
     }
     if (kStats) {
@@ -334,15 +340,25 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowSeg* __restrict__ se
 }  // namespace
 
 mo_status launch_momentum(const MomSeg* segs, int nseg, int64_t nblocks, float mu, int nesterov,
-                          StatPartial* stats, hipStream_t st) {
+                          StatPartial* stats, hipStream_t st, int phase, const float* kappa) {
   if (nblocks <= 0) return MO_OK;
+  if (phase == 2 && !kappa) return fail(MO_EINVAL, "momentum phase 2 needs the cap factors");
   KTimer tm(MO_KC_MOMENTUM, st);
-  if (stats)
-    k_momentum<true><<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(
-        segs, nseg, mu, nesterov, stats);
+  const dim3 grid(static_cast<unsigned>(nblocks));
+  if (phase == 1)
+    k_momentum<false, 1><<<grid, dim3(kThreads), 0, st>>>(segs, nseg, mu, nesterov, nullptr,
+                                                           nullptr);
+  else if (phase == 2 && stats)
+    k_momentum<true, 2><<<grid, dim3(kThreads), 0, st>>>(segs, nseg, mu, nesterov, stats, kappa);
+  else if (phase == 2)
+    k_momentum<false, 2><<<grid, dim3(kThreads), 0, st>>>(segs, nseg, mu, nesterov, nullptr,
+                                                           kappa);
+  else if (stats)
+    k_momentum<true, 0><<<grid, dim3(kThreads), 0, st>>>(segs, nseg, mu, nesterov, stats,
+                                                          nullptr);
   else
-    k_momentum<false><<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(
-        segs, nseg, mu, nesterov, nullptr);
+    k_momentum<false, 0><<<grid, dim3(kThreads), 0, st>>>(segs, nseg, mu, nesterov, nullptr,
+                                                           nullptr);
   MO_LAUNCH_CHECK("k_momentum");
   return MO_OK;
 }

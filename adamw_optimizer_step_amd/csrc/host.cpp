@@ -208,6 +208,7 @@ size_t mo_abi_struct_size(int32_t which) {
     case 9: return sizeof(mo_ns_options);
     case 10: return sizeof(mo_plan_options);
     case 11: return sizeof(mo_group);
+    case 12: return sizeof(mo_spectral_item);
   }
   return 0;
 }

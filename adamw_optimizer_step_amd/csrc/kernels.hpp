@@ -56,8 +56,42 @@ struct MomSeg {
 
 // stats != nullptr: per-block (amax, sum d^2) of the written direction, one
 // StatPartial per block at stats[block].
+// phase 0: B <- mu B + G, D from it (the default step);
+// phase 1: B <- mu B + G only (no D, no statistics: the buffer before the
+//          spectral-cap guard);
+// phase 2: B <- kappa[seg] B, then D from it (the guard's factor per segment,
+//          the buffer already accumulated by phase 1).
 mo_status launch_momentum(const MomSeg* segs, int nseg, int64_t nblocks, float mu, int nesterov,
-                          StatPartial* stats, hipStream_t st);
+                          StatPartial* stats, hipStream_t st, int phase = 0,
+                          const float* kappa = nullptr);
+
+// ----- spectral-cap guard: power iteration per matrix -------------------------
+struct PowSeg {
+  const float* b;          // fp32 matrix, rows x cols, row stride ld
+  int64_t ld;
+  int64_t rblk0;           // first block of the row pass
+  int64_t cblk0;           // first block of the column pass
+  int64_t u_off;           // offset of this matrix's u (rows entries)
+  int64_t w_off;           // offset of this matrix's w (cols entries)
+  int32_t rows, cols;
+};
+struct PowWork {
+  double* u;               // sum of rows
+  double* w;               // sum of cols
+  double* rpart;           // one per row-pass block
+  double* cpart;           // one per column-pass block
+  double* inv;             // per matrix
+  double* sigma;           // per matrix (nullable)
+  float* kappa;            // per matrix (nullable): cap / sigma above the cap, else 1
+};
+int64_t pow_row_blocks(int64_t rows);
+int64_t pow_col_blocks(int64_t cols);
+// `iters` power iterations on every matrix (B^T B from ones / sqrt(cols)),
+// then sigma = ||B v|| and the cap factor.  rblk0 / cblk0 of the table are
+// the running sums of pow_row_blocks / pow_col_blocks.
+mo_status launch_power_iteration(const PowSeg* segs, int nseg, int64_t row_blocks,
+                                 int64_t col_blocks, int iters, const PowWork& wk, float cap,
+                                 hipStream_t st);
 
 // ----- AdamW ------------------------------------------------------------------
 struct AdamSeg {

@@ -49,7 +49,8 @@ struct mo_plan {
     NsTables nst;
     size_t ws_stats = 0, ws_scale = 0, ws_fb = 0, ws_pool = 0;
     int64_t mom_blocks = 0, total_rows = 0;
-    size_t tab_mom = 0, tab_ns = 0, tab_rows = 0;
+    size_t tab_mom = 0, tab_ns = 0, tab_rows = 0, tab_pow = 0;
+    PowLayout pow;                    // spectral-cap guard (hp.spectral_cap > 0)
     // Muon update fused into the last Newton-Schulz launch (no O in the
     // workspace, no separate row pass): possible for every active slice
     bool fuse_ok = false;
@@ -109,6 +110,10 @@ mo_status check_hparams(const mo_hparams& hp, int g) {
   if (hp.beta1 < 0.f || hp.beta1 >= 1.f || hp.beta2 < 0.f || hp.beta2 >= 1.f)
     return fail(MO_EINVAL, "group %d: betas must be in [0, 1)", g);
   if (std::isnan(hp.max_norm)) return fail(MO_EINVAL, "group %d: max_norm is NaN", g);
+  if (!std::isfinite(hp.spectral_cap) || hp.spectral_cap < 0.f)
+    return fail(MO_EINVAL, "group %d: spectral_cap must be finite and >= 0", g);
+  if (hp.spectral_iters < 0 || hp.spectral_iters > MO_NS_MAX_STEPS)
+    return fail(MO_EINVAL, "group %d: spectral_iters must be in [0, %d]", g, MO_NS_MAX_STEPS);
   for (int k = 0; k < hp.ns_steps; ++k)
     for (int j = 0; j < 3; ++j)
       if (!std::isfinite(hp.ns_coeffs[k][j]))
@@ -122,6 +127,9 @@ bool same_launches(const mo_hparams& a, const mo_hparams& b) {
       a.ns_precision != b.ns_precision || (a.normuon != 0) != (b.normuon != 0))
     return false;
   if (a.normuon && (a.normuon_beta2 != b.normuon_beta2 || a.normuon_eps != b.normuon_eps))
+    return false;
+  if (a.spectral_cap != b.spectral_cap ||
+      (a.spectral_cap > 0.f && a.spectral_iters != b.spectral_iters))
     return false;
   for (int k = 0; k < a.ns_steps; ++k)
     for (int j = 0; j < 3; ++j)
@@ -250,6 +258,14 @@ mo_status build_plan(mo_plan* P) {
     B.ws_stats = ws.take(sizeof(StatPartial) * B.mom_blocks);
     B.ws_scale = ws.take(sizeof(float) * B.active.size());
     B.ws_fb = ws.take(sizeof(int32_t) * B.active.size());
+    if (P->bhp(B).spectral_cap > 0.f && !B.active.empty()) {
+      std::vector<int64_t> rr, cc;
+      for (const auto& a : B.active) {
+        rr.push_back(a.rows);
+        cc.push_back(a.cols);
+      }
+      B.pow = pow_layout(rr.data(), cc.data(), static_cast<int>(rr.size()), ws);
+    }
   }
   P->ws_adam_partials = ws.take(sizeof(double) * P->adam_blocks);
   P->ws_adam_scal = ws.take(2 * sizeof(double));
@@ -284,6 +300,7 @@ mo_status build_plan(mo_plan* P) {
     B.tab_mom = t.take(sizeof(MomSeg) * B.active.size());
     B.tab_ns = t.take(B.nst.bytes);
     B.tab_rows = t.take(sizeof(RowSeg) * B.active.size());
+    if (P->bhp(B).spectral_cap > 0.f) B.tab_pow = t.take(sizeof(PowSeg) * B.active.size());
   }
   P->tab_adam = t.take(sizeof(AdamSeg) * P->n_adam);
   P->tab_bytes = align_up(t.off, 256);
@@ -362,6 +379,21 @@ mo_status upload_tables(mo_plan* P, char* ws, hipStream_t st) {
     std::vector<char> nsbuf;
     ns_pack_tables(B.ns, B.nst, nsbuf);
     if (!nsbuf.empty()) std::memcpy(h + B.tab_ns, nsbuf.data(), nsbuf.size());
+    if (hp.spectral_cap > 0.f && !B.active.empty()) {
+      // the guard's matrices: each active slice's rows of the fp32 buffer
+      PowSeg* ps = reinterpret_cast<PowSeg*>(h + B.tab_pow);
+      std::vector<int64_t> rr, cc;
+      for (const auto& a : B.active) {
+        rr.push_back(a.rows);
+        cc.push_back(a.cols);
+      }
+      pow_fill(ps, rr.data(), cc.data(), static_cast<int>(rr.size()));
+      for (size_t k = 0; k < B.active.size(); ++k) {
+        const auto& a = B.active[k];
+        ps[k].b = P->params[a.param].momentum + a.off * a.cols;
+        ps[k].ld = a.cols;
+      }
+    }
   }
   AdamSeg* ad = reinterpret_cast<AdamSeg*>(h + P->tab_adam);
   const int ng = static_cast<int>(P->groups.size());
@@ -719,9 +751,25 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     StatPartial* stats = reinterpret_cast<StatPartial*>(base + B.ws_stats);
     float* scale = reinterpret_cast<float*>(base + B.ws_scale);
     const PrepItem* dprep = reinterpret_cast<const PrepItem*>(dns + B.nst.prep);
-    if ((s = launch_momentum(reinterpret_cast<const MomSeg*>(P->dtab + B.tab_mom), nsl,
-                             B.mom_blocks, hp.mu, hp.nesterov, stats, st)) != MO_OK)
+    const MomSeg* dmom = reinterpret_cast<const MomSeg*>(P->dtab + B.tab_mom);
+    if (hp.spectral_cap > 0.f) {
+      // spectral-cap guard: accumulate B, estimate each slice's top singular
+      // value, then rescale B where it exceeds the cap and form D from it
+      PowWork wk = pow_work(B.pow, base);
+      if ((s = launch_momentum(dmom, nsl, B.mom_blocks, hp.mu, hp.nesterov, nullptr, st, 1)) !=
+          MO_OK)
+        return s;
+      if ((s = launch_power_iteration(reinterpret_cast<const PowSeg*>(P->dtab + B.tab_pow), nsl,
+                                      B.pow.row_blocks, B.pow.col_blocks, hp.spectral_iters, wk,
+                                      hp.spectral_cap, st)) != MO_OK)
+        return s;
+      if ((s = launch_momentum(dmom, nsl, B.mom_blocks, hp.mu, hp.nesterov, stats, st, 2,
+                               wk.kappa)) != MO_OK)
+        return s;
+    } else if ((s = launch_momentum(dmom, nsl, B.mom_blocks, hp.mu, hp.nesterov, stats, st)) !=
+               MO_OK) {
       return s;
+    }
     int32_t* fb = reinterpret_cast<int32_t*>(base + B.ws_fb);
     if ((s = launch_ns_scale(dprep, nsl, stats, scale, fb, st)) != MO_OK) return s;
     if ((s = launch_ns_prep(dprep, nsl, B.ns.prep_tiles, scale, pool, B.ns.elem, st)) != MO_OK)

@@ -66,7 +66,7 @@ const char* mo_version(void);
 /* sizeof() of the ABI structs, for binding self-checks: 0 mo_momentum_item,
  * 1 mo_ns_item, 2 mo_adamw_item, 3 mo_param_desc, 4 mo_route_out, 5 mo_param,
  * 6 mo_hparams, 7 mo_step_args, 8 mo_lr_schedule, 9 mo_ns_options,
- * 10 mo_plan_options, 11 mo_group; 0 for any other index. */
+ * 10 mo_plan_options, 11 mo_group, 12 mo_spectral_item; 0 for any other index. */
 size_t mo_abi_struct_size(int32_t which);
 
 /* ------------------------------------------------------------------------
@@ -182,6 +182,35 @@ size_t ns_workspace_bytes(const mo_ns_item* items, int32_t n, const float* coeff
 mo_status ns_orthogonalize_batched(const mo_ns_item* items, int32_t n, const float* coeffs,
                                    int32_t steps, int32_t precision, const mo_ns_options* opts,
                                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * muon_spectral_estimate - power-iteration estimate of each matrix's largest
+ * singular value, as the spectral-cap guard on the Muon buffer computes it.
+ *
+ * OMN "Dual-Manifold Optimization" page, Muon-path paragraph: an optional
+ * spectral-cap guard with power-iteration estimation, inactive by default in
+ * the recipe.  The page prints no formula; this library's reading:
+ *   v_0 = ones(cols) / sqrt(cols);
+ *   v_{k+1} = B^T B v_k / ||B^T B v_k||   for k < iters (stops at 0 if it vanishes);
+ *   sigma = ||B v_iters||.
+ * In the grouped step (hparams spectral_cap > 0) each independent matrix of
+ * the buffer, after B <- mu B + G, is rescaled to (cap / sigma) B when sigma
+ * > cap, and the Nesterov direction is formed from the rescaled buffer.
+ *   items[i].b      device fp32, rows x cols, row stride ld (>= cols).
+ *   sigma_out       device fp64, n entries, written.
+ *   iters           0..64.
+ * Sums run in fp64.  Workspace: muon_spectral_workspace_bytes(items, n).
+ * ------------------------------------------------------------------------ */
+typedef struct mo_spectral_item {
+  const float* b;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld;
+} mo_spectral_item;
+
+size_t muon_spectral_workspace_bytes(const mo_spectral_item* items, int32_t n);
+mo_status muon_spectral_estimate(const mo_spectral_item* items, int32_t n, int32_t iters,
+                                 double* sigma_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * normuon_rownorm - NorMuon per-row second-moment normalisation, in place.
@@ -418,6 +447,8 @@ typedef struct mo_hparams {
   float eps;
   float adamw_wd;
   float max_norm;
+  float spectral_cap;     /* Muon: the spectral-cap guard's cap tau; 0 = off */
+  int32_t spectral_iters; /* Muon: power iterations of the guard's estimate, 0..64 */
 } mo_hparams;
 
 /* One group of mo_plan_create_groups.  Muon groups read muon_lr, muon_wd,
@@ -538,7 +569,8 @@ mo_status mo_plan_slice_algorithms(const mo_plan* plan, int32_t* out, int32_t n)
 typedef enum mo_kernel_class {
   MO_KC_MOMENTUM = 0, MO_KC_NS_STATS = 1, MO_KC_NS_SCALE = 2, MO_KC_NS_PREP = 3,
   MO_KC_NS_GEMM = 4, MO_KC_NS_FINAL = 5, MO_KC_ROWS = 6, MO_KC_ADAM_SUMSQ = 7,
-  MO_KC_ADAM_NORM = 8, MO_KC_ADAM_APPLY = 9, MO_KC_NS_SMALL = 10, MO_KC_COUNT = 11
+  MO_KC_ADAM_NORM = 8, MO_KC_ADAM_APPLY = 9, MO_KC_NS_SMALL = 10, MO_KC_SPECTRAL = 11,
+  MO_KC_COUNT = 12
 } mo_kernel_class;
 
 mo_status mo_timing_enable(int32_t on);
