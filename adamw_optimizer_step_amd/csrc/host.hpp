@@ -86,9 +86,12 @@ struct NsBucket {
 
 // Launch kinds of the Gram-space sequence.
 enum GsKind : int32_t {
-  kGsGram = 0,   // A0 = X0 X0^T, and Q1 = a0 I + b0 A0 as a second output
-  kGsProd = 1,   // C = a E + b (U V^T) over s x s operands (symmetric result)
-  kGsFinal = 2,  // X_N = Q_N X0 (K-major B), the last update
+  kGsGram = 0,       // A0 = X0 X0^T, and Q1 = a0 I + b0 A0 as a second output
+                     // (cubic-type row 0)
+  kGsProd = 1,       // C = a E + b (U V^T) over s x s operands (symmetric result)
+  kGsFinal = 2,      // X_N = Q_N X0 (K-major B), the last update
+  kGsProdP = 3,      // P = c (A A^T) + b A + a I (quintic-type row, E = A)
+  kGsProdPlain = 4,  // C = U V^T (quintic-type row: T = P A, A' = T P, Q' = P Q)
 };
 
 struct NsLayout {
@@ -131,10 +134,13 @@ struct NsLayout {
 //
 // Gram space on the GEMM path (rectangular slices, l >= 1.25 s; on a square
 // slice it executes the same flops as the plain iteration in one more
-// launch; cubic-type rows only): every iterate is P_k ... P_0 X0 with
-// P_k = a_k I + b_k A_k, A_{k+1} = P_k A_k P_k, so the iterations run on
-// s x s matrices (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q with P kept
-// implicit through the E term) and X0 is multiplied once, by Q_N, at the end.
+// launch): every iterate is P_k ... P_0 X0 with P_k = a_k I + b_k A_k +
+// c_k A_k^2, A_{k+1} = P_k A_k P_k, so the iterations run on s x s matrices
+// (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q) and X0 is multiplied
+// once, by Q_N, at the end.  A cubic-type row keeps P implicit through the E
+// term (T = a A + b A A, A' = a T + b T A, Q' = a Q + b A Q: three products);
+// a quintic-type row materialises P = c A A + b A + a I in one product with
+// an E term, then three plain products.
 // The slice-resident kernel does the same with its 128 x 128 matrices in LDS
 // (quintic-type rows included, P_k = a_k I + R_k with R_k = b_k A_k +
 // c_k A_k^2), for slices with a short side of at least kGramSpaceMinS: on

@@ -67,14 +67,13 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
                      const float* coeffs, int steps, const NsOpts& opt,
                      const uint8_t* direct_ok, bool stats_from_prep, const int64_t* in_off) {
   L = NsLayout();
-  bool need_a = false, cubic_rows = true;
+  bool need_a = false;
   for (int k = 0; k < steps; ++k)
     if (coeffs[3 * k + 2] != 0.f) need_a = true;
-  cubic_rows = !need_a;
   // Gram space (bf16): the table's small-singular-value gain bounded, see
-  // kGramSpaceMaxGain; the GEMM path also needs cubic-type rows
+  // kGramSpaceMaxGain
   const bool gram_ok = elem == 2 && opt.gram_space && gram_gain_ok(coeffs, steps);
-  const bool gspace_mode = gram_ok && cubic_rows;
+  const bool gspace_mode = gram_ok;
   L.few_tile_max = opt.few_tile_max;
   L.elem = elem;
   L.need_a = need_a;
@@ -171,10 +170,12 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       return g;
     };
     if (gs) {
-      // s x s buffers: A / T rotate through S[3] (A_k in S[2k % 3], T_k in
-      // S[(2k + 1) % 3], A_{k+1} in S[(2k + 2) % 3]); Q_k in Qb[(k - 1) % 2]
-      int64_t S[3], Qb[2];
-      for (auto& v : S) v = take(static_cast<int64_t>(sp) * sp);
+      // s x s buffers: A_k in Ab[k % 2], T_k in Tb, a quintic-type row's
+      // P_k in Pb (P_0 in Qb[0], which is Q_1), Q_k in Qb[(k - 1) % 2]
+      int64_t Ab[2], Tb, Pb, Qb[2];
+      for (auto& v : Ab) v = take(static_cast<int64_t>(sp) * sp);
+      Tb = take(static_cast<int64_t>(sp) * sp);
+      Pb = need_a ? take(static_cast<int64_t>(sp) * sp) : -1;
       for (auto& v : Qb) v = take(static_cast<int64_t>(sp) * sp);
       size_t stage = 0;
       auto add = [&](int32_t kind, int32_t k, const GemmProb& g) {
@@ -189,27 +190,45 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
         B.gs_k[stage] = k;
         B.gs_tiles[stage] += tiles_of(g.tiles_m, g.tiles_n, g.sym != 0);
       };
-      // C = a E + b (U V^T) over s x s symmetric operands; the result is
-      // symmetric too (all factors are polynomials in A_0)
+      // C = c0 E + c1 (U V^T) (+ cd I) over s x s symmetric operands; the
+      // result is symmetric too (all factors are polynomials in A_0)
       auto prod = [&](int64_t u, int64_t v, int64_t e, int64_t out) {
         return make_prob(u, v, out, out, e, sp, sp, sp, sp, sp, sp, ts, ts, 1, 0);
       };
-      GemmProb g = first(make_prob(x0, x0, S[0], S[0], -1, lp, lp, sp, sp, 0, lp, ts, ts, 1, 0));
-      g.c2_off = Qb[0];
+      const bool quintic0 = coeffs[2] != 0.f;
+      GemmProb g = first(make_prob(x0, x0, Ab[0], Ab[0], -1, lp, lp, sp, sp, 0, lp, ts, ts, 1, 0));
+      g.c2_off = quintic0 ? -1 : Qb[0];   // Q_1 = P_0 = a_0 I + b_0 A_0 (cubic-type row 0)
       add(kGsGram, 0, g);
       ++stage;
-      for (int k = 0; k + 1 < steps; ++k) {
-        const int64_t Ak = S[(2 * k) % 3], Tk = S[(2 * k + 1) % 3], An = S[(2 * k + 2) % 3];
-        add(kGsProd, k, prod(Ak, Ak, Ak, Tk));
-        if (k >= 1) add(kGsProd, k, prod(Ak, Qb[(k - 1) % 2], Qb[(k - 1) % 2], Qb[k % 2]));
-        ++stage;
-        add(kGsProd, k, prod(Tk, Ak, Tk, An));
-        ++stage;
-      }
-      if (steps >= 2) {
-        const int k = steps - 1;
-        add(kGsProd, k, prod(S[(2 * k) % 3], Qb[(k - 1) % 2], Qb[(k - 1) % 2], Qb[k % 2]));
-        ++stage;
+      for (int k = 0; k < steps; ++k) {
+        const bool last = k + 1 == steps;
+        const int64_t Ak = Ab[k % 2], An = Ab[(k + 1) % 2];
+        const int64_t Qk = k >= 1 ? Qb[(k - 1) % 2] : -1, Qn = Qb[k % 2];
+        if (coeffs[3 * k + 2] == 0.f) {
+          // cubic-type row, P_k = a I + b A_k kept implicit in the E term:
+          // T_k = a A_k + b A_k A_k, Q_{k+1} = a Q_k + b A_k Q_k,
+          // A_{k+1} = a T_k + b T_k A_k
+          if (!last) add(kGsProd, k, prod(Ak, Ak, Ak, Tb));
+          if (k >= 1) add(kGsProd, k, prod(Ak, Qk, Qk, Qn));
+          if (!last || k >= 1) ++stage;
+          if (!last) {
+            add(kGsProd, k, prod(Tb, Ak, Tb, An));
+            ++stage;
+          }
+        } else {
+          // quintic-type row: P_k = c A_k A_k + b A_k + a I materialised,
+          // then T_k = P_k A_k, Q_{k+1} = P_k Q_k, A_{k+1} = T_k P_k
+          const int64_t Pk = k == 0 ? Qb[0] : Pb;
+          add(kGsProdP, k, prod(Ak, Ak, Ak, Pk));
+          ++stage;
+          if (!last) add(kGsProdPlain, k, prod(Pk, Ak, -1, Tb));
+          if (k >= 1) add(kGsProdPlain, k, prod(Pk, Qk, -1, Qn));
+          if (!last || k >= 1) ++stage;
+          if (!last) {
+            add(kGsProdPlain, k, prod(Tb, Pk, -1, An));
+            ++stage;
+          }
+        }
       }
       // X_N = Q_N X0 into the second iterate buffer (transposed when tall)
       const int64_t qn = Qb[(steps - 1) % 2];
@@ -376,6 +395,12 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       else if (B.gs_kind[j] == kGsProd)
         s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, a, b, 1, 0.f, nullptr,
                            0.f, nullptr, nullptr, nullptr, st);
+      else if (B.gs_kind[j] == kGsProdP)
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, b,
+                           coeffs[3 * k + 2], 1, a, nullptr, 0.f, nullptr, nullptr, nullptr, st);
+      else if (B.gs_kind[j] == kGsProdPlain)
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, 0.f,
+                           1.f, 0, 0.f, nullptr, 0.f, nullptr, nullptr, nullptr, st);
       else
         s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, wt,
                            lr, lrs, scale, range_fb, st);

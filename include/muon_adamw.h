@@ -116,9 +116,9 @@ mo_status muon_momentum(const mo_momentum_item* items, int32_t n, float mu, int3
  *                      gain where the plain iteration's grows with its square
  *                      root: the cubic set qualifies up to 8 iterations, the
  *                      quintic up to 5); then slices with a short side of 64
- *                      to 128 (slice-resident kernel, any rows) and GEMM-path
- *                      slices whose long side is at least 1.25 times the short
- *                      side and whose every row has c = 0.
+ *                      to 128 (slice-resident kernel) and GEMM-path slices
+ *                      whose long side is at least 1.25 times the short side
+ *                      (on a square slice it saves no work).
  *   big_tile_min_work  GEMM-path slices with a short side of at least 512
  *                      use 256 x 256 tiles when the batch holds at least this
  *                      many such upper-triangle Gram tiles (-1: 512, two per

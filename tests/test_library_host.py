@@ -345,16 +345,16 @@ def test_lr_schedule_matches_oracle():
     ([wl.CUBIC] * 5, True, True),          # gain 58: both
     ([wl.CUBIC] * 8, True, True),          # gain 657
     ([wl.CUBIC] * 9, False, False),        # gain 1478: past the threshold
-    ([wl.QUINTIC] * 5, False, True),       # gain 537; c != 0 keeps the GEMM path plain
+    ([wl.QUINTIC] * 5, True, True),        # gain 537
     ([wl.QUINTIC] * 6, False, False),      # gain 1888
-    ([wl.CUBIC, wl.QUINTIC, wl.CUBIC], False, True),
+    ([wl.CUBIC, wl.QUINTIC, wl.CUBIC], True, True),
 ])
 @pytest.mark.parametrize("gram_option", [True, False])
 def test_gram_space_rule_host_only(table, rect, resident, gram_option):
     """Which slices run in Gram space (mo_plan_slice_algorithms): bf16,
-    the table's gain prod a_k^2 <= 1024, then rectangular GEMM slices with
-    cubic-type rows only and slice-resident slices with short side >= 64;
-    square GEMM slices, short sides below 64 and the fp32 path never."""
+    the table's gain prod a_k^2 <= 1024, then rectangular GEMM slices (any
+    rows) and slice-resident slices with short side >= 64; square GEMM
+    slices, short sides below 64 and the fp32 path never."""
     specs = (wl.ParamSpec("rect", (256, 640), "bf16"), wl.ParamSpec("square", (256, 256), "bf16"),
              wl.ParamSpec("resident", (128, 512), "bf16"), wl.ParamSpec("thin", (40, 512), "bf16"),
              wl.ParamSpec("rect32", (256, 640), "f32"))
