@@ -96,7 +96,7 @@ def ns_work(slices, coeffs, elem, w_elem=None):
     return t
 
 
-def build_plan(w, coeffs, precision, normuon):
+def build_plan(w, coeffs, precision, normuon, spectral_cap=0.0, spectral_iters=8):
     import torch
 
     import workloads as wl
@@ -121,12 +121,13 @@ def build_plan(w, coeffs, precision, normuon):
             e["exp_avg"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
             e["exp_avg_sq"] = torch.zeros(p.shape, dtype=torch.float32, device="cuda")
         ents.append(e)
-    hp = api.make_hparams(coeffs=coeffs, ns_precision=precision, normuon=normuon)
+    hp = api.make_hparams(coeffs=coeffs, ns_precision=precision, normuon=normuon,
+                          spectral_cap=spectral_cap, spectral_iters=spectral_iters)
     plan = api.Plan(ents, hp)
     return plan, ents, routes
 
 
-def cpu_baseline(w, coeffs, normuon, budget_s: float):
+def cpu_baseline(w, coeffs, normuon, budget_s: float, spectral_cap=0.0, spectral_iters=8):
     """The fp64 oracle on a bounded sample of the same workload, extrapolated
     to one full step: one Muon matrix of each distinct slice shape (every
     shape is measured; the sample is bounded by the number of shapes) and a
@@ -161,7 +162,8 @@ def cpu_baseline(w, coeffs, normuon, budget_s: float):
         t0 = time.perf_counter()
         omuon.muon_param_step(W, G, np.zeros_like(G), expand(p.shape, p.view, p.split), coeffs,
                               0.01, 0.95,
-                              normuon_v=np.zeros(p.shape[0]) if normuon else None)
+                              normuon_v=np.zeros(p.shape[0]) if normuon else None,
+                              spectral_cap_value=spectral_cap, spectral_iters=spectral_iters)
         dt = time.perf_counter() - t0
         spent += dt
         t_total += dt * count
@@ -207,6 +209,11 @@ def main() -> int:
     ap.add_argument("--separate-update", action="store_true",
                     help="keep O and apply the Muon update in its own row pass instead of "
                          "inside the last Newton-Schulz launch")
+    ap.add_argument("--spectral-cap", type=float, default=0.0, metavar="TAU",
+                    help="turn on the spectral-cap guard on the Muon buffer at cap TAU "
+                         "(0 = off, the default)")
+    ap.add_argument("--spectral-iters", type=int, default=8,
+                    help="power iterations of the guard's estimate")
     ap.add_argument("--cpu-budget", type=float, default=20.0,
                     help="seconds of oracle work for the cpu_baseline sample (0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=1024, metavar="MIB",
@@ -233,7 +240,8 @@ def main() -> int:
     w = workload_by_name(args.workload, args.coeffs)
     coeffs = wl.coeff_table(args.coeffs, w.ns_steps)
     log(f"building {w.key} on {torch.cuda.get_device_name(0)}")
-    plan, ents, routes = build_plan(w, coeffs, args.precision, w.normuon)
+    plan, ents, routes = build_plan(w, coeffs, args.precision, w.normuon, args.spectral_cap,
+                                    args.spectral_iters)
     if args.separate_update:
         plan.keep_ns_output(True)
     ws = plan.workspace(torch.device("cuda"))
@@ -332,8 +340,16 @@ def main() -> int:
     hbm = {}
     elt = w.params[0].dtype == "bf16" and 2 or 4
     if "momentum" in kern:
-        b = muon_elems * (elt + 4 + 4 + elt)
+        # with the guard on, two passes: B <- mu B + G, then D (and B <- kappa B
+        # where the cap binds, not counted here)
+        b = muon_elems * ((elt + 4 + 4 + elt) if args.spectral_cap <= 0
+                          else (elt + 4 + 4) + (elt + 4 + elt))
         hbm["momentum"] = round(b / (kern["momentum"]["ms_per_step"] * 1e-3) / 1e9, 1)
+    if "spectral" in kern:
+        # the power iteration reads the fp32 buffer twice per iteration and
+        # once more for the estimate
+        b = muon_elems * 4 * (2 * args.spectral_iters + 1)
+        hbm["spectral"] = round(b / (kern["spectral"]["ms_per_step"] * 1e-3) / 1e9, 1)
     if "adam_apply" in kern:
         t = sum(kern[k]["ms_per_step"] for k in ("adam_sumsq", "adam_norm", "adam_apply")
                 if k in kern)
@@ -364,7 +380,8 @@ def main() -> int:
         del src, dst
 
     # counter-based figures (committed rocprofv3 summaries; null when stale)
-    cnt = {k: counted(k, w.key, args.coeffs, args.precision)
+    # (the summaries are of the default step: none applies with the guard on)
+    cnt = {k: counted(k, w.key, args.coeffs, args.precision) if args.spectral_cap <= 0 else None
            for k in ("k_ns_gemm", "k_ns_small", "k_momentum", "k_rows", "k_adam_sumsq",
                      "k_adam_apply")}
     if roofline is not None:
@@ -388,7 +405,8 @@ def main() -> int:
     cpu = None
     if args.cpu_budget > 0:
         log("timing the fp64 oracle on a bounded sample")
-        cpu = cpu_baseline(w, coeffs, w.normuon, args.cpu_budget)
+        cpu = cpu_baseline(w, coeffs, w.normuon, args.cpu_budget, args.spectral_cap,
+                           args.spectral_iters)
 
     value = 1e3 / median_ms
     out = {
@@ -402,6 +420,7 @@ def main() -> int:
                    "muon_slices": len(slices), "ns_steps": len(coeffs), "coeffs": args.coeffs,
                    "ns_precision": args.precision, "normuon": bool(w.normuon),
                    "fused_update": fused, "gram_space": gspace,
+                   "spectral_cap": args.spectral_cap if args.spectral_cap > 0 else None,
                    "param_dtype": w.params[0].dtype, "state_dtype": "f32"},
         "roofline": roofline,
         "ns_mfma_util_pct": roofline.get("mfma_util_pct") if roofline else None,
