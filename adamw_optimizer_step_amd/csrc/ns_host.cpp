@@ -108,7 +108,7 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     const bool sgs = gram_ok && small && s_ >= kGramSpaceMinS;
     const int64_t x[2] = {take(static_cast<int64_t>(sp) * lp), take(static_cast<int64_t>(sp) * lp)};
     const int64_t p = small || gs ? -1 : take(static_cast<int64_t>(sp) * sp);
-    const int64_t a = need_a && !small ? take(static_cast<int64_t>(sp) * sp) : -1;
+    const int64_t a = need_a && !small && !gs ? take(static_cast<int64_t>(sp) * sp) : -1;
     L.gspace.push_back(gs || sgs);
     L.kind.push_back(small ? 2 : tile == kBigTile ? 1 : 0);
     L.x_off[0].push_back(x[0]);

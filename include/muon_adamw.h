@@ -452,11 +452,11 @@ typedef struct mo_hparams {
 } mo_hparams;
 
 /* One group of mo_plan_create_groups.  Muon groups read muon_lr, muon_wd,
- * mu, nesterov, ns_steps, ns_precision, ns_coeffs and the normuon fields of
- * `hp` (and the AdamW fields for excluded pieces); AdamW groups read
- * adamw_lr, adamw_wd, beta1, beta2, eps.  max_norm must be the same in every
- * group that has AdamW items (the clip norm is joint).  A Muon group's
- * params must be 2-D. */
+ * mu, nesterov, ns_steps, ns_precision, ns_coeffs, the normuon fields and the
+ * spectral-cap fields of `hp` (and the AdamW fields for excluded pieces);
+ * AdamW groups read adamw_lr, adamw_wd, beta1, beta2, eps.  max_norm must be
+ * the same in every group that has AdamW items (the clip norm is joint).  A
+ * Muon group's params must be 2-D. */
 typedef struct mo_group {
   int32_t algorithm;      /* MO_ALG_MUON or MO_ALG_ADAMW */
   int32_t nparams;
