@@ -1282,11 +1282,14 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   // of `cur` and have completed once those are waited for (vector memory
   // operations complete in order).
   // at_k: element at which element cur + k was issued (k = 0, 1, 2)
+  // (value selects, not a branch chain: the compiler turned the chain into a
+  // store at a computed index, which kept the three values in scratch memory,
+  // and every reload of them waited for all loads in flight)
   int next = 0, at_0 = 0, at_1 = 0, at_2 = 0;
   auto note_issue = [&](int e, int cur) __attribute__((always_inline)) {
-    if (e == cur) at_0 = cur;
-    else if (e == cur + 1) at_1 = cur;
-    else at_2 = cur;
+    at_0 = e == cur ? cur : at_0;
+    at_1 = e == cur + 1 ? cur : at_1;
+    at_2 = e != cur && e != cur + 1 ? cur : at_2;
   };
 
   // One element of the pipeline: block b of pass `pass`.  PC >= 0 fixes the
