@@ -1089,6 +1089,7 @@ __device__ __forceinline__ int sm_off(int row, int col) {
 // phase needs no registers beyond one accumulator block.
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 __device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_char* yb,
                                            const NsCoeffTable* cfp, int steps) {
@@ -1100,7 +1101,10 @@ __device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_ch
   };
   // x = U V over the wave's 64 x 32 block: U by rows, V by columns
   // (transpose reads of its 16-row slabs), so the product is exact whether
-  // or not the rounded factors are still exactly symmetric
+  // or not the rounded factors are still exactly symmetric.  The operands go
+  // into the MFMA swapped, which yields the transposed tile: each lane then
+  // holds 4 consecutive columns of one row, x[mi][4 q + e] = (U V)[rw(mi)]
+  // [cl(q) + e], so E terms and results move as 8-byte LDS accesses.
   const int g16 = lane >> 4, j16 = lane & 15;
   const int trow = 8 * (g16 >> 1) + (j16 >> 2);
   const int tcol = wn * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
@@ -1116,20 +1120,27 @@ __device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_ch
       const u32x2 hi = lds_read_tr16((const char*)(v + sm_off(16 * ks + trow + 4, tcol)));
       const u32x4 bf{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(frag(u, wm * 64 + mi * 32 + fr, ks), bf, x[mi]);
+      for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(bf, frag(u, wm * 64 + mi * 32 + fr, ks), x[mi]);
     }
   };
-  auto row = [&](int mi, int e) { return wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * fg + (e & 3); };
-  const int col = wn * 32 + fr;
+  auto rw = [&](int mi) { return wm * 64 + mi * 32 + fr; };
+  auto cl = [&](int q) { return wn * 32 + 8 * q + 4 * fg; };
   auto put = [&](lds_char* dst, const f32x16 (&x)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
-        *reinterpret_cast<lds_u16*>(dst + sm_off(row(mi, e), col)) = f32_to_bf16(x[mi][e]);
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<lds_u32x2*>(dst + sm_off(rw(mi), cl(q))) =
+            u32x2{pk_bf16(x[mi][4 * q], x[mi][4 * q + 1]),
+                  pk_bf16(x[mi][4 * q + 2], x[mi][4 * q + 3])};
   };
-  auto at = [&](const lds_char* src, int mi, int e) __attribute__((always_inline)) {
-    return bf16_to_f32(*reinterpret_cast<const lds_u16*>(src + sm_off(row(mi, e), col)));
+  // the 4 values of `src` at the place of x[mi][4 q .. 4 q + 3]
+  auto at4 = [&](const lds_char* src, int mi, int q, float (&e)[4]) __attribute__((always_inline)) {
+    const u32x2 w = *reinterpret_cast<const lds_u32x2*>(src + sm_off(rw(mi), cl(q)));
+    e[0] = __uint_as_float(w[0] << 16);
+    e[1] = __uint_as_float(w[0] & 0xffff0000u);
+    e[2] = __uint_as_float(w[1] << 16);
+    e[3] = __uint_as_float(w[1] & 0xffff0000u);
   };
   // x = alpha E + beta x, E from the tile `src` (read before any write)
   auto axpy = [&](f32x16 (&x)[2], float alpha, const lds_char* src, float beta)
@@ -1137,7 +1148,12 @@ __device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_ch
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[mi][e] = alpha * at(src, mi, e) + beta * x[mi][e];
+      for (int q = 0; q < 4; ++q) {
+        float e[4];
+        at4(src, mi, q, e);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) x[mi][4 * q + t] = alpha * e[t] + beta * x[mi][4 * q + t];
+      }
   };
   f32x16 x[2];
   for (int k = 0; k < steps; ++k) {
@@ -1156,8 +1172,13 @@ __device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_ch
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          x[mi][e] = rs * at(rt, mi, e) + (row(mi, e) == col ? ak : 0.f);
+        for (int q = 0; q < 4; ++q) {
+          float e[4];
+          at4(rt, mi, q, e);
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            x[mi][4 * q + t] = rs * e[t] + (rw(mi) == cl(q) + t ? ak : 0.f);
+        }
       put(qs, x);
     } else {            // Q' = a Q + rs (R Q)
       prod(rt, qs, x);
