@@ -239,8 +239,7 @@ struct SmallProb {
   int32_t tall;            // last iteration writes the result transposed (lp x 128)
   int32_t item;            // index of the slice's prep item and normalisation scale
   int32_t direct;          // the first two passes read the item's input D (bf16,
-                           // 128 x lp, row stride lp) and fold the scale into P,
-                           // instead of reading the prepared X0
+                           // 128 x lp, row stride lp) instead of the prepared X0
 };
 struct NsCoeffTable {
   float a[MO_NS_MAX_STEPS], b[MO_NS_MAX_STEPS], c[MO_NS_MAX_STEPS];
@@ -251,9 +250,13 @@ constexpr int kSmallS = 128;
 // of writing O.  Requires bf16 O, cols % 8 == 0 and 16-byte aligned rows.
 // gspace: run the iterations in Gram space (two passes over X; see
 // build_ns_layout), the result in the second iterate buffer.
+// range_fb (nullable): the per-slice range flags of launch_ns_scale; an
+// in-place slice whose flag is clear multiplies D unscaled and scales the
+// results (otherwise X0 = bf16(s D) is formed in LDS).
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
                           const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                          float lr, const float* lrs, hipStream_t st, int gspace = 0);
+                          float lr, const float* lrs, hipStream_t st, int gspace = 0,
+                          const int32_t* range_fb = nullptr);
 
 // C = c1 A B (+ c0 E) (+ cd I on diagonal tiles).  bk = 1: B is read K-major
 // (K x N row-major) through LDS transpose reads; no E term, and the output

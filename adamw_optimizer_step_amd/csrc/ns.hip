@@ -1212,7 +1212,8 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
                                                             NsCoeffTable cf, int steps,
                                                             const RowSeg* __restrict__ wt,
                                                             float lr_arg,
-                                                            const float* __restrict__ lrs) {
+                                                            const float* __restrict__ lrs,
+                                                            const int32_t* __restrict__ range_fb) {
   __shared__ __attribute__((aligned(16))) char smem[kSmTile * (2 + kSmStages)];
   char* const Ps = smem;             // P (A operand of the update)
   char* const Xn = smem + kSmTile;   // the new block X'_b (and A in a quintic step)
@@ -1222,6 +1223,13 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   const int wm = wave >> 2, wn = wave & 3;
   const int fr = lane & 31, fg = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
   const int NB = pr.lp / kSmallS;
+  // Workgroup w walks the column blocks starting at block w % NB: the
+  // workgroups that start together then read different column offsets of
+  // their row-strided slabs instead of all the same ones.
+  const int rot = static_cast<int>(blockIdx.x % static_cast<unsigned>(NB));
+  auto col_of = [&](int b) __attribute__((always_inline)) {
+    return b + rot >= NB ? b + rot - NB : b + rot;
+  };
   // passes over X: pass 0 forms the first Gram; pass k + 1 runs iteration k.
   // Gram space: pass 0, then all iterations on 128 x 128 matrices in LDS,
   // then one pass for X_N = Q_N X0.
@@ -1237,6 +1245,13 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   const u32x4 rs0 = buffer_rsrc(X0, kSmallS * ld_b), rs1 = buffer_rsrc(X1, kSmallS * ld_b);
   const u32x4 rsin = direct ? buffer_rsrc(items[pr.item].in, kSmallS * ld_b) : rs0;
   const float dscale = direct ? scale[pr.item] : 1.f;
+  // With range flags (grouped step), an in-place slice whose max|D| is in
+  // the range where unscaled products stay normal fp32 numbers (range flag
+  // clear) skips the conversion: the passes that read D multiply D instead
+  // of bf16(s D), and the scale is applied to the results, s^2 to the first
+  // Gram and s to the first update, as the batched GEMM's first iteration
+  // does.  Otherwise X0 = bf16(s D) is formed in LDS.
+  const bool fold = direct && range_fb != nullptr && range_fb[pr.item] == 0;
 
   // Direct-to-LDS loads of one 128 x 128 block: 32 instructions of 4 rows
   // (1 KiB), 4 per wave; lane i lands at row + i / 16, physical chunk i % 16
@@ -1252,7 +1267,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
   auto issue = [&](int e) __attribute__((always_inline)) {
-    const int pass = e / NB, b = e - pass * NB;
+    const int pass = e / NB, b = col_of(e - pass * NB);
     // iteration k reads X[k % 2]; passes 0 and 1 read X0 (or D in place).
     // Selected per 32-bit word: a select between whole descriptors made the
     // compiler keep them in scratch memory.
@@ -1319,6 +1334,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   auto element = [&](int cur, int pass_rt, auto pc) __attribute__((always_inline)) {
     constexpr int PC = decltype(pc)::value;
     const int pass = PC >= 0 ? PC : pass_rt, b = cur - pass * NB;
+    const int pb = col_of(b);   // the column block it covers
     int done;   // stores of elements <= done are complete after the wait below
     if (next == cur) {
       // not issued ahead (its block was written too recently): drain, then load
@@ -1346,7 +1362,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       done = a - 1;
     }
     __syncthreads();   // B1: block `cur` in LDS; element cur - 1 fully done
-    if (direct && cur < 2 * NB) {
+    if (direct && !fold && cur < 2 * NB) {
       // D block -> X0 block in place (16 bytes = 8 elements per access; the
       // chunk swizzle does not matter for an elementwise pass)
       char* const blk = smem + (2 + cur % kSmStages) * kSmTile;
@@ -1390,6 +1406,12 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
           mma<uint16_t>(u32x4{lo[0], lo[1], hi[0], hi[1]}, bp, accu[mi]);
         }
       }
+      if (fold && pass == 1) {   // (s D)-based result: s times the product with D
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) accu[mi][v] *= dscale;
+      }
       // accu[mi][4 q + e] = X'_b[i][j0 + e], i = wn * 32 + fr,
       // j0 = wm * 64 + mi * 32 + 8 q + 4 fg: 8-byte E reads and X'_b writes
       // (a X_b is on P's diagonal: P = a I + b A + c A^2)
@@ -1422,7 +1444,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
             // group: every lane takes part, whatever its row
             const u32x2 lo = lds_read_tr16(Xn + sm_off(k0 + (j16 >> 2), n0 + 4 * (j16 & 3)));
             const u32x2 hi = lds_read_tr16(Xn + sm_off(k0 + 4 + (j16 >> 2), n0 + 4 * (j16 & 3)));
-            const int orow = b * kSmallS + n0 + j16;
+            const int orow = pb * kSmallS + n0 + j16;
             if (orow < w.rows && k0 < w.cols) {
               const int64_t at = static_cast<int64_t>(orow) * w.ld_w + k0;
               apply_w8(w.w, at, w.w_dt, load_w8(w.w, at, w.w_dt),
@@ -1435,7 +1457,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
           for (int q = 0; q < 4; ++q) {
             const int id = q * kSmThreads + tid;
             const int row = id >> 4, c = id & 15;
-            const int ocol = b * kSmallS + c * 8;
+            const int ocol = pb * kSmallS + c * 8;
             if (row < w.rows && ocol < w.cols)
               wr[q] = load_w8(w.w, static_cast<int64_t>(row) * w.ld_w + ocol, MO_BF16);
           }
@@ -1443,7 +1465,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
           for (int q = 0; q < 4; ++q) {
             const int id = q * kSmThreads + tid;
             const int row = id >> 4, c = id & 15;
-            const int ocol = b * kSmallS + c * 8;
+            const int ocol = pb * kSmallS + c * 8;
             if (row < w.rows && ocol < w.cols)
               apply_w8(w.w, static_cast<int64_t>(row) * w.ld_w + ocol, MO_BF16, wr[q],
                        *reinterpret_cast<const u32x4*>(Xn + row * 256 +
@@ -1455,7 +1477,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
           for (int q = 0; q < 4; ++q) {
             const int id = q * kSmThreads + tid;
             const int row = id >> 4, c = id & 15;
-            const int ocol = b * kSmallS + c * 8;
+            const int ocol = pb * kSmallS + c * 8;
             if (row < w.rows && ocol < w.cols) {
               const int64_t at = static_cast<int64_t>(row) * w.ld_w + ocol;
               apply_w8(w.w, at, w.w_dt, load_w8(w.w, at, w.w_dt),
@@ -1474,7 +1496,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
           const int n0 = 16 * (T & 7), k0 = 8 * (T >> 3);
           const u32x2 lo = lds_read_tr16(Xn + sm_off(k0 + (j16 >> 2), n0 + 4 * (j16 & 3)));
           const u32x2 hi = lds_read_tr16(Xn + sm_off(k0 + 4 + (j16 >> 2), n0 + 4 * (j16 & 3)));
-          *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(b * kSmallS + n0 + j16) * kSmallS +
+          *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(pb * kSmallS + n0 + j16) * kSmallS +
                                     k0) = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
       } else {
@@ -1485,11 +1507,18 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
           const int row = id >> 4, c = id & 15;
           const u32x4 v = *reinterpret_cast<const u32x4*>(Xn + row * 256 +
                                                          (((c ^ sm_swz(row)) & 15) << 4));
-          *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row) * pr.lp + b * kSmallS +
+          *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row) * pr.lp + pb * kSmallS +
                                     c * 8) = v;
         }
       }
       if (!last) gram_acc(Xn, Xn, accg);
+    }
+    if (fold && b == NB - 1 && pass == 0) {   // the first Gram: s^2 D D^T
+      const float s2 = dscale * dscale;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) accg[mi][v] *= s2;
     }
     if (GS && b == NB - 1 && pass == 0) {
       // Gram space: A_0 (as stored, bf16) into Xn, then every iteration on
@@ -1664,7 +1693,8 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
 
 mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepItem* items,
                           const float* scale, const float* coeffs, int steps, const RowSeg* wt,
-                          float lr, const float* lrs, hipStream_t st, int gspace) {
+                          float lr, const float* lrs, hipStream_t st, int gspace,
+                          const int32_t* range_fb) {
   if (n <= 0) return MO_OK;
   if (steps < 1 || steps > MO_NS_MAX_STEPS) return fail(MO_EINVAL, "bad step count %d", steps);
   NsCoeffTable cf;
@@ -1677,10 +1707,10 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
   KTimer tm(MO_KC_NS_SMALL, st);
   if (gspace)
     k_ns_small<true><<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
-        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr, lrs);
+        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr, lrs, range_fb);
   else
     k_ns_small<false><<<dim3(static_cast<unsigned>(n)), kSmThreads, 0, st>>>(
-        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr, lrs);
+        probs, static_cast<uint16_t*>(pool), items, scale, cf, steps, wt, lr, lrs, range_fb);
   MO_LAUNCH_CHECK("k_ns_small");
   return MO_OK;
 }

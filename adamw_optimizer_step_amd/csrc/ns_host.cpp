@@ -374,7 +374,7 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
     mo_status s = launch_ns_small(
         reinterpret_cast<const SmallProb*>(dtab + (gsm ? T.small_gs : T.small)),
         static_cast<int>(v.size()), pool, reinterpret_cast<const PrepItem*>(dtab + T.prep),
-        scale, coeffs, steps, wt, lr, lrs, st, gsm);
+        scale, coeffs, steps, wt, lr, lrs, st, gsm, range_fb);
     if (s != MO_OK) return s;
   }
   // Gram-space sequence (every GEMM slice of the layout, or none)

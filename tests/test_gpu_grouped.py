@@ -256,7 +256,10 @@ def _aligned_shapes():
           wl.ParamSpec("wide", (256, 640), "bf16"),
           wl.ParamSpec("big", (512, 768), "bf16"),
           wl.ParamSpec("tall", (512, 256), "bf16"),
-          wl.ParamSpec("padded", (200, 336), "bf16")]
+          wl.ParamSpec("padded", (200, 336), "bf16"),
+          # slice-resident and read in place (128 rows, columns a multiple of 128)
+          wl.ParamSpec("heads", (256, 512), "bf16", view=(2, 128, 512)),
+          wl.ParamSpec("head_wide", (128, 1024), "bf16")]
     return wl.Workload("aligned_shapes", 13, tuple(ps), grad_std=1e-3)
 
 
@@ -265,7 +268,8 @@ def _aligned_shapes():
 def test_first_iteration_in_place_and_range_fallback(exp2, coeffs):
     """Iteration 0 reads the unscaled D in place, the normalisation scale
     folded into the products; a slice whose max|D| leaves [2^-50, 2^40] (here
-    gradients scaled by 2^-60 or 2^55) falls back to the prepared X0.  The
+    gradients scaled by 2^-60 or 2^55) falls back to the prepared X0 (batched
+    GEMM) or to X0 = bf16(s D) formed in LDS (slice-resident kernel).  The
     Newton-Schulz output meets the oracle's bound at every scale; the quintic
     cases put the 512-row slice on 256 x 256 tiles."""
     w = _aligned_shapes()
