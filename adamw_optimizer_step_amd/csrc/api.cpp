@@ -154,14 +154,17 @@ PowLayout pow_layout(const int64_t* rows, const int64_t* cols, int n, WsCursor& 
   for (int i = 0; i < n; ++i) {
     L.rows += rows[i];
     L.cols += cols[i];
-    L.row_blocks += pow_row_blocks(rows[i]);
-    L.col_blocks += pow_col_blocks(cols[i]);
+    L.grid.row_blocks += pow_row_blocks(rows[i]);
+    L.grid.col_blocks += pow_col_blocks(rows[i], cols[i]);
+    L.grid.fold_blocks += pow_fold_blocks(cols[i]);
+    L.grid.wpart += align_up(pow_row_chunks(rows[i]) * cols[i], 4);   // 32-byte aligned shares
   }
   L.tab = c.take(sizeof(PowSeg) * n);
   L.u = c.take(sizeof(double) * L.rows);
   L.w = c.take(sizeof(double) * L.cols);
-  L.rpart = c.take(sizeof(double) * L.row_blocks);
-  L.cpart = c.take(sizeof(double) * L.col_blocks);
+  L.wpart = c.take(sizeof(double) * L.grid.wpart);
+  L.rpart = c.take(sizeof(double) * L.grid.row_blocks);
+  L.cpart = c.take(sizeof(double) * L.grid.fold_blocks);
   L.inv = c.take(sizeof(double) * n);
   L.sigma = c.take(sizeof(double) * n);
   L.kappa = c.take(sizeof(float) * n);
@@ -169,19 +172,23 @@ PowLayout pow_layout(const int64_t* rows, const int64_t* cols, int n, WsCursor& 
 }
 
 void pow_fill(PowSeg* segs, const int64_t* rows, const int64_t* cols, int n) {
-  int64_t rb = 0, cb = 0, uo = 0, wo = 0;
+  int64_t rb = 0, cb = 0, kb = 0, uo = 0, wo = 0, po = 0;
   for (int i = 0; i < n; ++i) {
     PowSeg& s = segs[i];
     s.rblk0 = rb;
     s.cblk0 = cb;
+    s.kblk0 = kb;
     s.u_off = uo;
     s.w_off = wo;
+    s.wp_off = po;
     s.rows = static_cast<int32_t>(rows[i]);
     s.cols = static_cast<int32_t>(cols[i]);
     rb += pow_row_blocks(rows[i]);
-    cb += pow_col_blocks(cols[i]);
+    cb += pow_col_blocks(rows[i], cols[i]);
+    kb += pow_fold_blocks(cols[i]);
     uo += rows[i];
     wo += cols[i];
+    po += align_up(pow_row_chunks(rows[i]) * cols[i], 4);
   }
 }
 
@@ -189,6 +196,7 @@ PowWork pow_work(const PowLayout& L, char* base) {
   PowWork w;
   w.u = reinterpret_cast<double*>(base + L.u);
   w.w = reinterpret_cast<double*>(base + L.w);
+  w.wpart = reinterpret_cast<double*>(base + L.wpart);
   w.rpart = reinterpret_cast<double*>(base + L.rpart);
   w.cpart = reinterpret_cast<double*>(base + L.cpart);
   w.inv = reinterpret_cast<double*>(base + L.inv);
@@ -255,8 +263,8 @@ mo_status muon_spectral_estimate(const mo_spectral_item* items, int32_t n, int32
   PowWork wk = pow_work(L, base);
   wk.sigma = sigma_out;
   wk.kappa = nullptr;
-  return launch_power_iteration(reinterpret_cast<const PowSeg*>(base + L.tab), n, L.row_blocks,
-                                L.col_blocks, iters, wk, 0.f, st);
+  return launch_power_iteration(reinterpret_cast<const PowSeg*>(base + L.tab), n, L.grid, iters,
+                                wk, 0.f, st);
 }
 
 

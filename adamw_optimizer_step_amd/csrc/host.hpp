@@ -192,8 +192,9 @@ mo_status adam_segments(const mo_adamw_item* items, int32_t n, float lr, float b
 // (byte offsets; the table of PowSeg first); pow_fill writes the table's
 // block starts and vector offsets.
 struct PowLayout {
-  size_t tab = 0, u = 0, w = 0, rpart = 0, cpart = 0, inv = 0, sigma = 0, kappa = 0;
-  int64_t rows = 0, cols = 0, row_blocks = 0, col_blocks = 0;
+  size_t tab = 0, u = 0, w = 0, wpart = 0, rpart = 0, cpart = 0, inv = 0, sigma = 0, kappa = 0;
+  int64_t rows = 0, cols = 0;
+  PowGrid grid;
 };
 PowLayout pow_layout(const int64_t* rows, const int64_t* cols, int n, WsCursor& c);
 void pow_fill(PowSeg* segs, const int64_t* rows, const int64_t* cols, int n);

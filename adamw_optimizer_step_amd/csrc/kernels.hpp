@@ -70,28 +70,38 @@ struct PowSeg {
   const float* b;          // fp32 matrix, rows x cols, row stride ld
   int64_t ld;
   int64_t rblk0;           // first block of the row pass
-  int64_t cblk0;           // first block of the column pass
+  int64_t cblk0;           // first block of the column pass (row chunks x column blocks)
+  int64_t kblk0;           // first block of the fold of the column pass's partials
   int64_t u_off;           // offset of this matrix's u (rows entries)
   int64_t w_off;           // offset of this matrix's w (cols entries)
+  int64_t wp_off;          // offset of its column-pass partials (row chunks x cols entries)
   int32_t rows, cols;
 };
 struct PowWork {
   double* u;               // sum of rows
   double* w;               // sum of cols
+  double* wpart;           // sum of row chunks x cols: B^T u per chunk of rows
   double* rpart;           // one per row-pass block
-  double* cpart;           // one per column-pass block
+  double* cpart;           // one per fold block
   double* inv;             // per matrix
   double* sigma;           // per matrix (nullable)
   float* kappa;            // per matrix (nullable): cap / sigma above the cap, else 1
 };
+// Grid sizes (sums over the matrices of the counts below) and the number of
+// column-pass partials.
+struct PowGrid {
+  int64_t row_blocks = 0, col_blocks = 0, fold_blocks = 0, wpart = 0;
+};
 int64_t pow_row_blocks(int64_t rows);
-int64_t pow_col_blocks(int64_t cols);
+int64_t pow_row_chunks(int64_t rows);
+int64_t pow_col_blocks(int64_t rows, int64_t cols);
+int64_t pow_fold_blocks(int64_t cols);
 // `iters` power iterations on every matrix (B^T B from ones / sqrt(cols)),
-// then sigma = ||B v|| and the cap factor.  rblk0 / cblk0 of the table are
-// the running sums of pow_row_blocks / pow_col_blocks.
-mo_status launch_power_iteration(const PowSeg* segs, int nseg, int64_t row_blocks,
-                                 int64_t col_blocks, int iters, const PowWork& wk, float cap,
-                                 hipStream_t st);
+// then sigma = ||B v|| and the cap factor.  rblk0 / cblk0 / kblk0 / wp_off
+// of the table are the running sums of the counts above (wp_off: row chunks
+// x cols).
+mo_status launch_power_iteration(const PowSeg* segs, int nseg, const PowGrid& g, int iters,
+                                 const PowWork& wk, float cap, hipStream_t st);
 
 // ----- AdamW ------------------------------------------------------------------
 struct AdamSeg {

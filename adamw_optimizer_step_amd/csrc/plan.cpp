@@ -760,8 +760,8 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
           MO_OK)
         return s;
       if ((s = launch_power_iteration(reinterpret_cast<const PowSeg*>(P->dtab + B.tab_pow), nsl,
-                                      B.pow.row_blocks, B.pow.col_blocks, hp.spectral_iters, wk,
-                                      hp.spectral_cap, st)) != MO_OK)
+                                      B.pow.grid, hp.spectral_iters, wk, hp.spectral_cap, st)) !=
+          MO_OK)
         return s;
       if ((s = launch_momentum(dmom, nsl, B.mom_blocks, hp.mu, hp.nesterov, stats, st, 2,
                                wk.kappa)) != MO_OK)
