@@ -268,9 +268,12 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
                           float lr, const float* lrs, hipStream_t st, int gspace = 0,
                           const int32_t* range_fb = nullptr);
 
-// C = c1 A B (+ c0 E) (+ cd I on diagonal tiles).  bk = 1: B is read K-major
-// (K x N row-major) through LDS transpose reads; no E term, and the output
-// goes straight from registers to c (or, transposed, to ct).
+// C = c1 A B (+ c0 E) (+ cd I on diagonal tiles).  has_e: 0 no E term; 1 E
+// read from e_off; 2 (bf16) E is the left operand itself (e_off = a_off in
+// every problem, square s x s products), added from its slabs in LDS (with
+// c1 != 0; else read as for 1).  bk = 1: B is read K-major (K x N row-major)
+// through LDS transpose reads; no E term, and the output goes straight from
+// registers to c (or, transposed, to ct).
 // wt (nullable, bf16 with bk = 1 only): problems with item >= 0 apply the Muon
 // update to the weights of slice `item` (as launch_ns_small) instead of
 // writing their output, at learning rate lrs[wt[item].lr_slot] (lrs given) or lr.  pscale (nullable): problems with sitem >= 0 scale

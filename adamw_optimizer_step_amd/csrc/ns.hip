@@ -734,7 +734,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   //   read frags ks0 of slab kt+1 | MFMAs ks1
   static_assert(C::kSub % 2 == 0, "an even number of substeps per slab");
   const int KT = pr.K / C::kSlabK;
-  auto main_loop = [&](auto swc) __attribute__((always_inline)) {
+  // slab_hook(kt, stage): called at the start of slab kt, whose stage is
+  // complete in LDS and stays intact until the barrier of that slab
+  auto main_loop = [&](auto swc, auto slab_hook) __attribute__((always_inline)) {
     const int pre = KT < C::kStages - 1 ? KT : C::kStages - 1;
     for (int k = 0; k < pre; ++k) issue(k, k);
     wait_slab(pre - 1);
@@ -744,6 +746,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
       const int stage = kt & (C::kStages - 1);
       if (kt + C::kStages - 1 < KT)
         issue(kt + C::kStages - 1, (kt + C::kStages - 1) & (C::kStages - 1));
+      slab_hook(kt, stage);
       __builtin_amdgcn_sched_barrier(0);
       // substep ks multiplies set ks & 1 while the next substep's fragments
       // load into the other set; before the last substep, wait for slab
@@ -777,10 +780,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     // fp32: 16-byte stores straight from registers.  The output is read only
     // by the next launch: streaming stores.
     const bool to_c = pr.ct_off < 0;
+    auto none = [](int, int) __attribute__((always_inline)) {};
     if (to_c)
-      main_loop(std::true_type{});
+      main_loop(std::true_type{}, none);
     else
-      main_loop(std::false_type{});
+      main_loop(std::false_type{}, none);
     // tile-local (row, col) of value 4q of acc[mi][ni] in the staged tile
     auto at = [&](int mi, int ni, int q, int& r, int& c) __attribute__((always_inline)) {
       const int m = wm * C::kWaveM + mi * 32, n = wn * C::kWaveN + ni * 32;
@@ -867,16 +871,54 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     return;
   } else {
     if constexpr (sizeof(T) == 2) {
-      if (!has_e) {
-        // Gram epilogue (bf16, no E term): with swapped operands each lane
-        // holds 4 consecutive columns of one row of the tile.  The tile
-        // c1 C + cd I is staged once in LDS as bf16 (layout as in the update
-        // epilogue); C's rows are stored as contiguous row segments, and the
-        // mirror (the transposed tile, for the lower triangle) is read with
-        // transpose reads: per 16-lane group, two reads give lane i 8
-        // consecutive elements of row n0 + i of C^T, and the 4 groups of a
-        // wave cover 32 consecutive columns, 64 contiguous bytes per row.
-        main_loop(std::true_type{});
+      // has_e == 2: the E term is the product's own left factor (E = U, as
+      // for T = a A + b A A), so E's tile (ti, tj) is the A operand's slab
+      // of columns tj * BN .. and passes through LDS in the K loop: each wave
+      // adds (c0 / c1) E to its accumulators from the one slab holding its
+      // columns, and the product takes the epilogue below.
+      // (compiled into the two-stage variants only: the few-tile variant's
+      // launches read E, and an extra copy of its K loop measured slower)
+      const bool e_in_loop = ST == 2 && has_e == 2 && c1 != 0.f && pr.c2_off < 0;
+      if (!has_e || e_in_loop) {
+        // Gram epilogue (bf16): with swapped operands each lane holds 4
+        // consecutive columns of one row of the tile.  The tile c1 C + cd I
+        // is staged once in LDS as bf16 (layout as in the update epilogue);
+        // C's rows are stored as contiguous row segments, and the mirror (the
+        // transposed tile, for the lower triangle) is read with transpose
+        // reads: per 16-lane group, two reads give lane i 8 consecutive
+        // elements of row n0 + i of C^T, and the 4 groups of a wave cover 32
+        // consecutive columns, 64 contiguous bytes per row.
+        if constexpr (ST != 2) {
+          main_loop(std::true_type{}, [](int, int) __attribute__((always_inline)) {});
+        } else if (e_in_loop) {
+          // (separate copies of the K loop for the two cases)
+          const float eratio = c0 / c1;
+          const int e_col0 = tj * BN + wn * C::kWaveN;   // the wave's first column
+          const int kt_e = e_col0 / C::kSlabK, kk0 = e_col0 - kt_e * C::kSlabK;
+          main_loop(std::true_type{}, [&](int kt, int stage) __attribute__((always_inline)) {
+            if (kt != kt_e) return;
+            const char* const slab = smem + stage * C::kStageBytes;   // A rows first
+#pragma unroll
+            for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+              for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  // acc[mi][ni][4 q + e] = C[r][c + e]: E[r][c + e] = U[row r][k = kk + e]
+                  const int r = wm * C::kWaveM + mi * 32 + fr;
+                  const int kk = kk0 + ni * 32 + 8 * q + 4 * fg;
+                  const u32x2 ev = *reinterpret_cast<const u32x2*>(
+                      slab + r * C::kRowB + ((((kk >> 3) ^ swz(r)) & (C::kChunks - 1)) << 4) +
+                      (kk & 7) * 2);
+                  acc[mi][ni][4 * q] += eratio * __uint_as_float(ev[0] << 16);
+                  acc[mi][ni][4 * q + 1] += eratio * __uint_as_float(ev[0] & 0xffff0000u);
+                  acc[mi][ni][4 * q + 2] += eratio * __uint_as_float(ev[1] << 16);
+                  acc[mi][ni][4 * q + 3] += eratio * __uint_as_float(ev[1] & 0xffff0000u);
+                }
+          });
+        } else {
+          main_loop(std::true_type{}, [](int, int) __attribute__((always_inline)) {});
+        }
         static_assert(BM == BN, "square output tiles");
         constexpr int RB = BN * 2, NCH = RB / 16;
         static_assert(BM * RB <= C::kLdsBytes, "staged output tile fits the stages");
@@ -939,7 +981,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
         return;
       }
     }
-    main_loop(std::false_type{});
+    main_loop(std::false_type{}, [](int, int) __attribute__((always_inline)) {});
   }
   __syncthreads();
 

@@ -191,7 +191,9 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
         B.gs_tiles[stage] += tiles_of(g.tiles_m, g.tiles_n, g.sym != 0);
       };
       // C = c0 E + c1 (U V^T) (+ cd I) over s x s symmetric operands; the
-      // result is symmetric too (all factors are polynomials in A_0)
+      // result is symmetric too (all factors are polynomials in A_0).  Every
+      // product with an E term has E = U, so that E passes through LDS with
+      // the left operand (see launch_ns_gemm's has_e).
       auto prod = [&](int64_t u, int64_t v, int64_t e, int64_t out) {
         return make_prob(u, v, out, out, e, sp, sp, sp, sp, sp, sp, ts, ts, 1, 0);
       };
@@ -206,10 +208,10 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
         const int64_t Qk = k >= 1 ? Qb[(k - 1) % 2] : -1, Qn = Qb[k % 2];
         if (coeffs[3 * k + 2] == 0.f) {
           // cubic-type row, P_k = a I + b A_k kept implicit in the E term:
-          // T_k = a A_k + b A_k A_k, Q_{k+1} = a Q_k + b A_k Q_k,
-          // A_{k+1} = a T_k + b T_k A_k
+          // T_k = a A_k + b A_k A_k, Q_{k+1} = a Q_k + b Q_k A_k (Q_k and A_k
+          // commute), A_{k+1} = a T_k + b T_k A_k
           if (!last) add(kGsProd, k, prod(Ak, Ak, Ak, Tb));
-          if (k >= 1) add(kGsProd, k, prod(Ak, Qk, Qk, Qn));
+          if (k >= 1) add(kGsProd, k, prod(Qk, Ak, Qk, Qn));
           if (!last || k >= 1) ++stage;
           if (!last) {
             add(kGsProd, k, prod(Tb, Ak, Tb, An));
@@ -388,16 +390,21 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const float a = coeffs[3 * k], b = coeffs[3 * k + 1];
       const GemmProb* t = tab(T.b[i].gs[j]);
       const int n = static_cast<int>(B.gs[j].size());
+      // E products: the E term from the left operand's slabs (has_e 2), except
+      // in launches of few tiles, whose short K loops pay more for the add
+      // than for reading E in the epilogue
+      const bool few = B.tile == kGemmTile && B.gs_tiles[j] < L.few_tile_max;
+      const int e_mode = L.elem == 2 && !few ? 2 : 1;
       mo_status s;
       if (B.gs_kind[j] == kGsGram)
         s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, 0.f, 1.f, 0, 0.f,
                            nullptr, 0.f, nullptr, scale, range_fb, st, b, a);
-      else if (B.gs_kind[j] == kGsProd)
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, a, b, 1, 0.f, nullptr,
-                           0.f, nullptr, nullptr, nullptr, st);
+      else if (B.gs_kind[j] == kGsProd)   // E = U in every problem (bf16: has_e 2)
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, a, b, e_mode,
+                           0.f, nullptr, 0.f, nullptr, nullptr, nullptr, st);
       else if (B.gs_kind[j] == kGsProdP)
         s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, b,
-                           coeffs[3 * k + 2], 1, a, nullptr, 0.f, nullptr, nullptr, nullptr, st);
+                           coeffs[3 * k + 2], e_mode, a, nullptr, 0.f, nullptr, nullptr, nullptr, st);
       else if (B.gs_kind[j] == kGsProdPlain)
         s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, 0.f,
                            1.f, 0, 0.f, nullptr, 0.f, nullptr, nullptr, nullptr, st);

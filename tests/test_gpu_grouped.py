@@ -320,6 +320,46 @@ def test_iteration_count_and_mode(steps, mode, row):
         assert_ns_close(f64(plan.ns_output(k)), omuon.newton_schulz(D[off:off + r], cf), "bf16")
 
 
+# the per-iteration tables of the schedule tests: eight distinct cubic-type
+# rows; cubic- and quintic-type rows mixed, identity rows (b = 0) included
+_SCHED8 = [(a, 1.0 - a, 0.0) for a in (2.0, 1.0, 1.8, 1.1, 1.6, 1.2, 1.4, 1.0)]
+_Q = (15 / 8, -10 / 8, 3 / 8)
+_MIXED6 = [(2.0, -1.0, 0.0), (1.0, 0.0, 0.0), _Q, (1.3, -0.3, 0.0), _Q, (1.0, 0.0, 0.0)]
+
+
+@pytest.mark.parametrize("row", ["cubic", "quintic", "sched8", "mixed6"])
+@pytest.mark.parametrize("big", [False, True])
+def test_gram_space_e_term_from_the_left_operand(row, big):
+    """Gram-space products with an E term (T = a A + b A A, A' = a T + b T A,
+    Q' = a Q + b Q A, the quintic P = b A + c A A + a I) take E from the left
+    operand's slabs as they pass through LDS, in launches of many tiles (rows
+    with b = 0 read E instead).  With the few-tile variant off, launches of
+    these small shapes take that path: the Newton-Schulz output against the
+    oracle, on both tile sizes, for repeated and per-iteration tables."""
+    opts = {"few_tile_max": 0, "big_tile_min_work": 0 if big else -1}
+    ps = [wl.ParamSpec("wide", (256, 640), "bf16"),
+          wl.ParamSpec("big", (512, 1280), "bf16"),
+          wl.ParamSpec("tall", (768, 256), "bf16"),
+          wl.ParamSpec("padded", (200, 336), "bf16")]
+    w = wl.Workload("e_term_shapes", 19, tuple(ps), grad_std=1e-3)
+    cf = {"cubic": wl.coeff_table("cubic"), "quintic": wl.coeff_table("quintic"),
+          "sched8": _SCHED8, "mixed6": _MIXED6}[row]
+    ents = build_entries(w, normuon=False)
+    plan = api.Plan(ents, api.make_hparams(coeffs=cf), options=opts)
+    plan.keep_ns_output(True)
+    algos = plan.slice_algorithms()
+    assert all(a is not None and a[0] for a in algos)   # every slice in Gram space
+    for i, (e, p) in enumerate(zip(ents, w.params)):
+        e["grad"].copy_(to_dev(wl.grad(w, i, 1), p.dtype))
+    G = [f64(e["grad"]) for e in ents]
+    plan.step()
+    torch.cuda.synchronize()
+    for k, (param, off, r, c) in enumerate(plan.slices()):
+        _, D = omuon.momentum(np.zeros_like(G[param]), G[param], wl.MUON_MU)
+        print(f"[e-term] {row} big={big} slice {k} ({r}, {c})", flush=True)
+        assert_ns_close(f64(plan.ns_output(k)), omuon.newton_schulz(D[off:off + r], cf), "bf16")
+
+
 @pytest.mark.parametrize("normuon,precision", [(False, "bf16"), (True, "bf16"), (False, "fp32")],
                          ids=["plain", "normuon", "plain_fp32ns"])
 def test_grouped_excluded_pieces(normuon, precision):
