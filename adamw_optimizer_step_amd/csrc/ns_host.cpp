@@ -365,10 +365,19 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
   }
 }
 
+bool ns_has_two_chains(const NsLayout& L) {
+  bool gs = false, plain = false;
+  for (const NsBucket& B : L.buckets) {
+    gs = gs || !B.gs.empty();
+    plain = plain || !B.gram_p[0].empty();
+  }
+  return gs && plain;
+}
+
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* scale, const float* coeffs, int steps, const RowSeg* wt,
                             float lr, const float* lrs, const int32_t* range_fb,
-                            hipStream_t st) {
+                            hipStream_t st, hipStream_t st2) {
   auto tab = [dtab](size_t off) { return reinterpret_cast<const GemmProb*>(dtab + off); };
   for (int gsm = 0; gsm < 2; ++gsm) {
     const std::vector<SmallProb>& v = gsm ? L.small_gs : L.small;
@@ -414,6 +423,8 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       if (s != MO_OK) return s;
     }
   }
+  // the plain iteration (on st2 when given)
+  hipStream_t ps_st = st2 ? st2 : st;
   for (int k = 0; k < steps; ++k) {
     const float a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
     const bool cubic_step = c == 0.f || !L.need_a;
@@ -433,13 +444,13 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       mo_status s;
       if (cubic_step) {
         s = launch_ns_gemm(tab(first ? tb.gram_p0 : tb.gram_p[q]), n, B.gram_tiles, B.tile, L.few_tile_max, 0,
-                           pool, L.elem, 0.f, b, 0, a, nullptr, 0.f, nullptr, ps, pfb, st);
+                           pool, L.elem, 0.f, b, 0, a, nullptr, 0.f, nullptr, ps, pfb, ps_st);
       } else {
         s = launch_ns_gemm(tab(first ? tb.gram_a0 : tb.gram_a[q]), n, B.gram_tiles, B.tile, L.few_tile_max, 0,
-                           pool, L.elem, 0.f, 1.f, 0, 0.f, nullptr, 0.f, nullptr, ps, pfb, st);
+                           pool, L.elem, 0.f, 1.f, 0, 0.f, nullptr, 0.f, nullptr, ps, pfb, ps_st);
         if (s == MO_OK)
           s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, B.tile, L.few_tile_max, 0, pool, L.elem, b, c, 1,
-                             a, nullptr, 0.f, nullptr, nullptr, nullptr, st);
+                             a, nullptr, 0.f, nullptr, nullptr, nullptr, ps_st);
       }
       if (s != MO_OK) return s;
     }
@@ -452,7 +463,7 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const size_t off = fin ? (first ? tb.fin0 : tb.fin[q]) : (first ? tb.upd0 : tb.upd[q]);
       mo_status s = launch_ns_gemm(tab(off), static_cast<int>(B.upd[q].size()), B.upd_tiles,
                                    B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr,
-                                   lr, lrs, ps, pfb, st);
+                                   lr, lrs, ps, pfb, ps_st);
       if (s != MO_OK) return s;
     }
   }

@@ -87,6 +87,10 @@ struct mo_plan {
   // caller's stream, so that it overlaps the Muon path (created on first use)
   hipStream_t side = nullptr;
   hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+  // a batch's plain-iteration launches run on a second stream beside its
+  // Gram-space sequence (created on first use)
+  hipStream_t side2 = nullptr;
+  hipEvent_t ev_ns_fork = nullptr, ev_ns_join = nullptr;
   bool dirty = true;
   int32_t tdelta = 0;
   bool keep_ns_output = false;
@@ -582,6 +586,9 @@ void mo_plan_destroy(mo_plan* plan) {
   if (plan->ev_fork) (void)hipEventDestroy(plan->ev_fork);
   if (plan->ev_join) (void)hipEventDestroy(plan->ev_join);
   if (plan->side) (void)hipStreamDestroy(plan->side);
+  if (plan->ev_ns_fork) (void)hipEventDestroy(plan->ev_ns_fork);
+  if (plan->ev_ns_join) (void)hipEventDestroy(plan->ev_ns_join);
+  if (plan->side2) (void)hipStreamDestroy(plan->side2);
   delete plan;
 }
 
@@ -827,11 +834,33 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
       // of the separate row pass
       const RowSeg* drows = reinterpret_cast<const RowSeg*>(P->dtab + B.tab_rows);
       const bool fuse = B.fuse_ok && !P->keep_ns_output;
-      if ((r = ns_run_iterations(B.ns, dns, B.nst, base + B.ws_pool,
-                                 reinterpret_cast<const float*>(base + B.ws_scale),
-                                 B.coeffs.data(), hp.ns_steps, fuse ? drows : nullptr, 0.f, lrs,
-                                 reinterpret_cast<const int32_t*>(base + B.ws_fb), st)) != MO_OK)
-        return r;
+      // The Gram-space sequence and the plain iteration share no data: the
+      // latter goes to the second stream, forked here and joined back on
+      // every path, so that each chain's launches fill the other's last,
+      // partly empty round of workgroups.  (In order on `st` while timing.)
+      const bool two = !timing_enabled() && ns_has_two_chains(B.ns);
+      if (two) {
+        if (!P->side2) {
+          MO_HIP_TRY(hipStreamCreateWithFlags(&P->side2, hipStreamNonBlocking));
+          MO_HIP_TRY(hipEventCreateWithFlags(&P->ev_ns_fork, hipEventDisableTiming));
+          MO_HIP_TRY(hipEventCreateWithFlags(&P->ev_ns_join, hipEventDisableTiming));
+        }
+        MO_HIP_TRY(hipEventRecord(P->ev_ns_fork, st));
+        MO_HIP_TRY(hipStreamWaitEvent(P->side2, P->ev_ns_fork, 0));
+      }
+      r = ns_run_iterations(B.ns, dns, B.nst, base + B.ws_pool,
+                            reinterpret_cast<const float*>(base + B.ws_scale), B.coeffs.data(),
+                            hp.ns_steps, fuse ? drows : nullptr, 0.f, lrs,
+                            reinterpret_cast<const int32_t*>(base + B.ws_fb), st,
+                            two ? P->side2 : nullptr);
+      if (two) {
+        const hipError_t e1 = hipEventRecord(P->ev_ns_join, P->side2);
+        const hipError_t e2 = e1 == hipSuccess ? hipStreamWaitEvent(st, P->ev_ns_join, 0) : e1;
+        if (r == MO_OK && e2 != hipSuccess)
+          return fail(MO_EHIP, "joining the second Newton-Schulz stream failed: %s",
+                      hipGetErrorString(e2));
+      }
+      if (r != MO_OK) return r;
       if (!fuse) {
         RowSeg none;
         std::memset(&none, 0, sizeof(none));
