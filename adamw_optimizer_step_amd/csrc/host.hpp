@@ -175,12 +175,14 @@ mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st)
 // at learning rate lrs[row.lr_slot] (lrs given, device) or lr.
 // range_fb (nullable): the per-slice range flags of launch_ns_scale, which
 // send a slice's in-place iteration 0 back to the prepared X0.
-// Whether the layout has both a Gram-space sequence and plain-iteration
-// GEMM launches (which ns_run_iterations can put on two streams).
+// Whether the layout has at least two of the independent chains of launches
+// (slice-resident kernel, Gram-space GEMM sequence, plain-iteration GEMM),
+// which ns_run_iterations can put on two streams.
 bool ns_has_two_chains(const NsLayout& L);
-// st2 (nullable): a second stream for the plain-iteration launches, which
-// share no data with the Gram-space sequence; the caller orders st2 after
-// the work `st` holds so far and joins it back afterwards.
+// st2 (nullable): a second stream.  The Gram-space sequence stays on `st`
+// and the slice-resident and plain-iteration launches go to st2 (without a
+// Gram-space sequence, the plain iteration stays on `st`).  The caller
+// orders st2 after the work `st` holds so far and joins it back afterwards.
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
                             const float* scale, const float* coeffs, int steps, const RowSeg* wt,
                             float lr, const float* lrs, const int32_t* range_fb,

@@ -365,13 +365,26 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
   }
 }
 
-bool ns_has_two_chains(const NsLayout& L) {
-  bool gs = false, plain = false;
+namespace {
+// Which of the three independent chains a layout has: slice-resident
+// launches, the Gram-space GEMM sequence, plain-iteration GEMM launches.
+struct Chains {
+  bool small = false, gs = false, plain = false;
+};
+Chains chains_of(const NsLayout& L) {
+  Chains c;
+  c.small = !L.small.empty() || !L.small_gs.empty();
   for (const NsBucket& B : L.buckets) {
-    gs = gs || !B.gs.empty();
-    plain = plain || !B.gram_p[0].empty();
+    c.gs = c.gs || !B.gs.empty();
+    c.plain = c.plain || !B.gram_p[0].empty();
   }
-  return gs && plain;
+  return c;
+}
+}  // namespace
+
+bool ns_has_two_chains(const NsLayout& L) {
+  const Chains c = chains_of(L);
+  return static_cast<int>(c.small) + static_cast<int>(c.gs) + static_cast<int>(c.plain) >= 2;
 }
 
 mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables& T, void* pool,
@@ -379,13 +392,19 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
                             float lr, const float* lrs, const int32_t* range_fb,
                             hipStream_t st, hipStream_t st2) {
   auto tab = [dtab](size_t off) { return reinterpret_cast<const GemmProb*>(dtab + off); };
+  // With st2: the Gram-space sequence stays on st, the slice-resident and
+  // plain-iteration launches go to st2; without a Gram-space sequence the
+  // plain iteration stays on st.
+  const Chains ch = chains_of(L);
+  hipStream_t sm_st = st2 ? st2 : st;
+  hipStream_t ps_st = st2 && ch.gs ? st2 : st;
   for (int gsm = 0; gsm < 2; ++gsm) {
     const std::vector<SmallProb>& v = gsm ? L.small_gs : L.small;
     if (v.empty()) continue;
     mo_status s = launch_ns_small(
         reinterpret_cast<const SmallProb*>(dtab + (gsm ? T.small_gs : T.small)),
         static_cast<int>(v.size()), pool, reinterpret_cast<const PrepItem*>(dtab + T.prep),
-        scale, coeffs, steps, wt, lr, lrs, st, gsm, range_fb);
+        scale, coeffs, steps, wt, lr, lrs, sm_st, gsm, range_fb);
     if (s != MO_OK) return s;
   }
   // Gram-space sequence (every GEMM slice of the layout, or none)
@@ -423,8 +442,7 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       if (s != MO_OK) return s;
     }
   }
-  // the plain iteration (on st2 when given)
-  hipStream_t ps_st = st2 ? st2 : st;
+  // the plain iteration
   for (int k = 0; k < steps; ++k) {
     const float a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
     const bool cubic_step = c == 0.f || !L.need_a;

@@ -834,10 +834,13 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
       // of the separate row pass
       const RowSeg* drows = reinterpret_cast<const RowSeg*>(P->dtab + B.tab_rows);
       const bool fuse = B.fuse_ok && !P->keep_ns_output;
-      // The Gram-space sequence and the plain iteration share no data: the
-      // latter goes to the second stream, forked here and joined back on
-      // every path, so that each chain's launches fill the other's last,
-      // partly empty round of workgroups.  (In order on `st` while timing.)
+      // The slice-resident launches, the Gram-space sequence and the plain
+      // iteration share no data: they are split over `st` and the second
+      // stream, forked here and joined back on every path, so that one
+      // chain's launches fill the CUs another leaves idle (the last, partly
+      // empty round of workgroups of a launch; the memory-bound slice-resident
+      // kernel beside latency-bound GEMM launches).  (In order on `st` while
+      // timing.)
       const bool two = !timing_enabled() && ns_has_two_chains(B.ns);
       if (two) {
         if (!P->side2) {
