@@ -169,15 +169,48 @@ def test_grouped_normuon_parity(precision):
     assert plan.get_steps() == [2, 2, 0, 0, 0, 0]
 
 
-def test_overlapped_step_equals_serial():
-    """AdamW on the side stream (the default) and every kernel in order on one
-    stream (what the step does while kernel timing is on) read and write
-    disjoint buffers in the same kernels: the results are bit-identical."""
-    _, over, _, _ = _run_small(False, False)
+def _three_chains():
+    """One batch whose Newton-Schulz launches form all three chains: a
+    Gram-space GEMM sequence (wide), the plain GEMM iteration (square) and
+    the slice-resident kernel (128 rows), beside AdamW params."""
+    ps = [wl.ParamSpec("embed", (256, 64), "bf16", wl.ROLE_EMBEDDING, no_decay=True),
+          wl.ParamSpec("norm", (64,), "bf16", wl.ROLE_NORM, no_decay=True),
+          wl.ParamSpec("square", (384, 384), "bf16"),
+          wl.ParamSpec("wide", (256, 640), "bf16"),
+          wl.ParamSpec("tall", (520, 200), "bf16"),
+          wl.ParamSpec("head", (128, 512), "bf16"),
+          wl.ParamSpec("heads", (192, 256), "bf16", view=(3, 64, 256))]
+    return wl.Workload("three_chains", 13, tuple(ps), grad_std=1e-3)
+
+
+def _run_chains(steps=2):
+    w = _three_chains()
+    ents = build_entries(w, normuon=False)
+    plan = api.Plan(ents, api.make_hparams(muon_wd=0.1))
+    kinds = {a for a in plan.slice_algorithms() if a is not None}
+    assert {(True, "gemm128"), (False, "gemm128"), (True, "resident")} <= kinds, kinds
+    for t in range(1, steps + 1):
+        for i, (e, p) in enumerate(zip(ents, w.params)):
+            e["grad"].copy_(to_dev(wl.grad(w, i, t), p.dtype))
+        plan.step()
+    return w, ents
+
+
+@pytest.mark.parametrize("case", ["small_decoder", "three_chains"])
+def test_overlapped_step_equals_serial(case):
+    """AdamW on one side stream and the batch's independent Newton-Schulz
+    chains split over the caller's stream and a second one (the default),
+    against every kernel in order on one stream (what the step does while
+    kernel timing is on): the same kernels read and write disjoint buffers,
+    so the results are bit-identical."""
+    run = (lambda: _run_small(False, False)[1]) if case == "small_decoder" else \
+        (lambda: _run_chains()[1])
+    over = run()
+    torch.cuda.synchronize()
     lib = L.lib()
     L.check("timing", lib.mo_timing_enable(1))
     try:
-        _, serial, _, _ = _run_small(False, False)
+        serial = run()
         torch.cuda.synchronize()
     finally:
         L.check("timing", lib.mo_timing_enable(0))
