@@ -129,10 +129,10 @@ def build_plan(w, coeffs, precision, normuon, spectral_cap=0.0, spectral_iters=8
 
 def cpu_baseline(w, coeffs, normuon, budget_s: float, spectral_cap=0.0, spectral_iters=8):
     """The fp64 oracle on a bounded sample of the same workload, extrapolated
-    to one full step: one Muon matrix of each distinct slice shape (every
-    shape is measured; the sample is bounded by the number of shapes) and a
-    contiguous slab of the AdamW elements.  ``budget_s`` is reported against
-    the time spent."""
+    to one full step: one Muon matrix of each distinct slice shape and a
+    contiguous slab of the AdamW elements, timed in rounds over all shapes
+    until about ``budget_s`` seconds of oracle work are spent (at least one
+    round); each shape's time is its mean over the rounds."""
     import numpy as np
 
     import workloads as wl
@@ -152,39 +152,50 @@ def cpu_baseline(w, coeffs, normuon, budget_s: float, spectral_cap=0.0, spectral
             shapes.setdefault(key, [i, 0])[1] += 1
         else:
             adam_elems += p.numel
-    t_total = 0.0
-    parts = []
-    spent = 0.0
+    inputs = []
     for key, (idx, count) in shapes.items():
         p = w.params[idx]
         G = wl.from_storage(wl.grad(w, idx, 1), p.dtype).astype(np.float64)
         W = wl.from_storage(wl.init_weight(w, idx), p.dtype).astype(np.float64)
-        t0 = time.perf_counter()
-        omuon.muon_param_step(W, G, np.zeros_like(G), expand(p.shape, p.view, p.split), coeffs,
-                              0.01, 0.95,
-                              normuon_v=np.zeros(p.shape[0]) if normuon else None,
-                              spectral_cap_value=spectral_cap, spectral_iters=spectral_iters)
-        dt = time.perf_counter() - t0
-        spent += dt
-        t_total += dt * count
-        parts.append(f"{count}x{p.shape}")
-    n_adam = 0
-    if adam_elems:
-        n = min(adam_elems, 1 << 22)
-        g = wl.draw_f32(w.seed, 1, 0, (n,), w.grad_std).astype(np.float64)
-        W = wl.draw_f32(w.seed, 0, 0, (n,), w.init_std).astype(np.float64)
-        t0 = time.perf_counter()
-        T = oadamw.global_norm([g])
-        oadamw.adamw_update(W, g, np.zeros(n), np.zeros(n), 1, 3e-4, 0.9, 0.95, 1e-8, 0.0,
-                            oadamw.clip_factor(T, 1.0))
-        dt = time.perf_counter() - t0
-        t_total += dt * adam_elems / n
-        n_adam = n
+        inputs.append((p, G, W, count))
+    n_adam = min(adam_elems, 1 << 22)
+    if n_adam:
+        ga = wl.draw_f32(w.seed, 1, 0, (n_adam,), w.grad_std).astype(np.float64)
+        wa = wl.draw_f32(w.seed, 0, 0, (n_adam,), w.init_std).astype(np.float64)
+    muon_s = [0.0] * len(inputs)
+    adam_s = 0.0
+    spent = 0.0
+    rounds = 0
+    while rounds == 0 or spent < budget_s:
+        for j, (p, G, W, _) in enumerate(inputs):
+            Wr, Br = W.copy(), np.zeros_like(G)
+            t0 = time.perf_counter()
+            omuon.muon_param_step(Wr, G, Br, expand(p.shape, p.view, p.split),
+                                  coeffs, 0.01, 0.95,
+                                  normuon_v=np.zeros(p.shape[0]) if normuon else None,
+                                  spectral_cap_value=spectral_cap, spectral_iters=spectral_iters)
+            dt = time.perf_counter() - t0
+            muon_s[j] += dt
+            spent += dt
+        if n_adam:
+            Wr, m0, v0 = wa.copy(), np.zeros(n_adam), np.zeros(n_adam)
+            t0 = time.perf_counter()
+            T = oadamw.global_norm([ga])
+            oadamw.adamw_update(Wr, ga, m0, v0, 1, 3e-4, 0.9, 0.95, 1e-8, 0.0,
+                                oadamw.clip_factor(T, 1.0))
+            dt = time.perf_counter() - t0
+            adam_s += dt
+            spent += dt
+        rounds += 1
+    t_total = sum(m / rounds * count for m, (_, _, _, count) in zip(muon_s, inputs))
+    if n_adam:
+        t_total += adam_s / rounds * adam_elems / n_adam
+    parts = [f"{count}x{p.shape}" for p, _, _, count in inputs]
     return {"value": 1.0 / t_total, "unit": "steps/s", "cores": threads, "kind": "oracle",
             "sample": (f"fp64 numpy oracle: one full Muon step of one matrix per distinct "
                        f"slice shape (weighted by count: {', '.join(parts)}) and AdamW on "
                        f"{n_adam} of {adam_elems} elements, extrapolated to one full step; "
-                       f"{spent:.1f}s of Muon work measured")}
+                       f"{rounds} rounds, {spent:.1f}s of oracle work measured")}
 
 
 def counted(kernel: str, workload: str, coeffs: str, precision: str):
