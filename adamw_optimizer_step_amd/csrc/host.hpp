@@ -138,7 +138,7 @@ struct NsLayout {
 // c_k A_k^2, A_{k+1} = P_k A_k P_k, so the iterations run on s x s matrices
 // (A_0 = X0 X0^T, then T = P A, A' = T P, Q' = P Q) and X0 is multiplied
 // once, by Q_N, at the end.  A cubic-type row keeps P implicit through the E
-// term (T = a A + b A A, A' = a T + b T A, Q' = a Q + b A Q: three products);
+// term (T = a A + b A A, A' = a T + b T A, Q' = a Q + b Q A: three products);
 // a quintic-type row materialises P = c A A + b A + a I in one product with
 // an E term, then three plain products.
 // The slice-resident kernel does the same with its 128 x 128 matrices in LDS
@@ -168,6 +168,11 @@ void ns_pack_tables(const NsLayout& L, const NsTables& T, std::vector<char>& buf
 // may be released when this returns.
 mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st);
 
+// Whether the layout has at least two of the independent chains of launches
+// (slice-resident kernel, Gram-space GEMM sequence, plain-iteration GEMM),
+// which ns_run_iterations can put on two streams.
+bool ns_has_two_chains(const NsLayout& L);
+
 // Enqueue the Newton-Schulz iterations on the prepared pool.
 // `scale` holds the per-slice normalisation scales (the prep kernel's).
 // wt (nullable): per-slice weight rows; the last iteration then applies the
@@ -175,10 +180,6 @@ mo_status stage_upload(void* dst, const void* src, size_t bytes, hipStream_t st)
 // at learning rate lrs[row.lr_slot] (lrs given, device) or lr.
 // range_fb (nullable): the per-slice range flags of launch_ns_scale, which
 // send a slice's in-place iteration 0 back to the prepared X0.
-// Whether the layout has at least two of the independent chains of launches
-// (slice-resident kernel, Gram-space GEMM sequence, plain-iteration GEMM),
-// which ns_run_iterations can put on two streams.
-bool ns_has_two_chains(const NsLayout& L);
 // st2 (nullable): a second stream.  The Gram-space sequence stays on `st`
 // and the slice-resident and plain-iteration launches go to st2 (without a
 // Gram-space sequence, the plain iteration stays on `st`).  The caller
