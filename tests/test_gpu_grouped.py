@@ -283,12 +283,15 @@ def test_ns_output_refused_after_fused_step():
 
 def _aligned_shapes():
     """Slices whose iteration 0 reads D in place (wide or square, sides
-    multiples of the tile) beside ones that keep the prep copy (tall, padded)."""
+    multiples of the tile) beside ones that keep the prep copy (tall, also
+    from fp32 gradients and inside a view; padded)."""
     ps = [wl.ParamSpec("norm", (64,), "bf16", wl.ROLE_NORM, no_decay=True),
           wl.ParamSpec("square", (256, 256), "bf16"),
           wl.ParamSpec("wide", (256, 640), "bf16"),
           wl.ParamSpec("big", (512, 768), "bf16"),
           wl.ParamSpec("tall", (512, 256), "bf16"),
+          wl.ParamSpec("tall_pair", (1024, 256), "bf16", view=(2, 512, 256)),
+          wl.ParamSpec("tall_f32", (384, 256), "f32"),
           wl.ParamSpec("padded", (200, 336), "bf16"),
           # slice-resident and read in place (128 rows, columns a multiple of 128)
           wl.ParamSpec("heads", (256, 512), "bf16", view=(2, 128, 512)),

@@ -61,7 +61,9 @@ def _workload(dtype):
           wl.ParamSpec("q", (d, d), dtype),
           wl.ParamSpec("gate_up", (192, d), dtype, view=(2, 96, d)),
           wl.ParamSpec("down", (d, 96), dtype),
-          wl.ParamSpec("heads", (256, 128), dtype, view=(2, 128, 128)))
+          wl.ParamSpec("heads", (256, 128), dtype, view=(2, 128, 128)),
+          # tall, on the batched GEMM path (prep copy from the capped D)
+          wl.ParamSpec("up_tall", (512, 256), dtype))
     return wl.Workload(f"spectral_{dtype}", 37, ps, grad_std=1e-3)
 
 
