@@ -57,9 +57,9 @@ def ns_work(slices, coeffs, elem, w_elem=None):
     'gemm128', 'gemm256', 'resident' (the library's own choice, from
     mo_plan_slice_algorithms).  With s the short side, l the long side and N
     the table's rows:
-    * method flops, the method's own work with the symmetric Gram (SURVEY
-      8(d)): 3 s^2 l per iteration (s^2 l for A = X X^T, 2 s^2 l for P X),
-      + s^3 for a quintic-type row (A^2);
+    * method flops, the method's own work with the symmetric Gram: 3 s^2 l
+      per iteration (s^2 l for A = X X^T, 2 s^2 l for P X), + s^3 for a
+      quintic-type row (A^2);
     * dense flops, the same without symmetry: 4 s^2 l (+ 2 s^3);
     * executed flops, what the kernels run: the plain iteration executes the
       method flops; the Gram-space sequence executes s^2 l for A0 = X0 X0^T,
