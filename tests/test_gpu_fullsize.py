@@ -39,13 +39,14 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def _run(w, coeffs_kind, precision, sample_params):
+def _run(w, coeffs_kind, precision, sample_params, spectral_cap=0.0, spectral_iters=8):
     """Build the benchmark's plan for `w`, keep host copies of what the checks
     need, run one step with O kept in the workspace.  Returns (plan, entries,
     routes, before, T_gpu); before["muon_w0"] holds device copies of every
     Muon weight as it was before the step."""
     coeffs = wl.coeff_table(coeffs_kind, w.ns_steps)
-    plan, ents, routes = bench.build_plan(w, coeffs, precision, w.normuon)
+    plan, ents, routes = bench.build_plan(w, coeffs, precision, w.normuon, spectral_cap,
+                                          spectral_iters)
     plan.keep_ns_output(True)      # the checks read O from the workspace
     ws = plan.workspace(torch.device("cuda"))
     before = {"muon_w0": {i: e["param"].clone() for i, (e, r) in enumerate(zip(ents, routes))
@@ -210,6 +211,44 @@ def test_dense_decoder_full():
     _check_adamw(w, ents, routes, before, T_gpu, sample, np.random.default_rng(3))
     _all_slices_bounded(plan, "bf16")
     _fused_equals_kept(plan, ents, before)
+
+
+def test_dense_decoder_spectral_cap_full():
+    """The dense decoder with the spectral-cap guard on (OMN page, Muon-path
+    paragraph), built as the benchmark builds it: tau = 0.1 lies between the
+    step-1 estimates of the square attention slices (about 0.09 for these
+    gradients) and of the rectangular MLP slices (about 0.12), so the cap
+    binds on some slices and not on others.  Sampled slices: the capped
+    buffer against the oracle's (1e-6), the Newton-Schulz output from the
+    capped D, and the weights given the GPU's own O."""
+    w = wl.dense_decoder()
+    tau, iters = 0.1, 8
+    sample = _dense_sample(w)
+    plan, ents, routes, before, T_gpu, cf = _run(w, "cubic", "bf16", sample, tau, iters)
+    bound = 0
+    for i in sample:
+        if routes[i][0] != L.MO_ALG_MUON:
+            continue
+        p = w.params[i]
+        G, W0 = before[i]["G"], before[i]["W"]
+        B_gpu, W_gpu = f64(ents[i]["momentum"]), f64(ents[i]["param"])
+        for off, r, c in expand(p.shape, p.view, p.split):
+            rows = slice(off, off + r)
+            B1, _ = omuon.momentum(np.zeros((r, c)), G[rows], wl.MUON_MU)
+            sigma = omuon.spectral_estimate(B1, iters)
+            bound += int(sigma > tau)
+            B_ref = omuon.spectral_cap(B1, tau, iters)
+            print(f"[fullsize] cap {p.name} rows {off}:{off + r} sigma {sigma:.4f}", flush=True)
+            assert rel_inf(B_gpu[rows], B_ref) <= REL_F32, (p.name, off)
+            D_ref = G[rows] + wl.MUON_MU * B_ref
+            O_gpu = f64(plan.ns_output(_slice_index(plan, i, off)))
+            assert_ns_close(O_gpu, omuon.newton_schulz(D_ref, cf), "bf16")
+            sc = omuon.shape_scale(r, c)
+            W_exp = omuon.apply_update(W0[rows], sc * O_gpu, wl.MUON_LR)
+            assert_bf16_close(W_gpu[rows], W_exp, extra=2e-6 * wl.MUON_LR * sc * np.abs(O_gpu))
+    assert 0 < bound < 4            # the cap bound on some sampled slices, not all
+    _check_adamw(w, ents, routes, before, T_gpu, sample, np.random.default_rng(5))
+    _all_slices_bounded(plan, "bf16")
 
 
 def test_dense_decoder_fused_normuon_full():
