@@ -200,10 +200,11 @@ def _dense_sample(w):
     return [w.index(n) for n in names]
 
 
-def test_dense_decoder_full():
+@pytest.mark.parametrize("coeffs", ["cubic", "quintic"])
+def test_dense_decoder_full(coeffs):
     w = wl.dense_decoder()
     sample = _dense_sample(w)
-    plan, ents, routes, before, T_gpu, cf = _run(w, "cubic", "bf16", sample)
+    plan, ents, routes, before, T_gpu, cf = _run(w, coeffs, "bf16", sample)
     assert len(plan.slices()) == 168
     for i in sample:
         if routes[i][0] == L.MO_ALG_MUON:
@@ -265,13 +266,14 @@ def test_dense_decoder_fused_normuon_full():
     assert not plan.fuses_update()
 
 
-def test_head_batched_full():
+@pytest.mark.parametrize("coeffs", ["cubic", "quintic"])
+def test_head_batched_full(coeffs):
     w = wl.head_batched()
     names = {"layers.0.attn.W_UQ.weight": [0, 31], "layers.15.attn.W_UQ.weight": [17],
              "layers.0.attn.W_UKV.weight": [0, 1, 63], "layers.15.attn.W_UKV.weight": [40],
              "layers.0.attn.QKV.weight": [0, 37, 95], "layers.15.attn.QKV.weight": [64]}
     sample = [w.index(n) for n in names]
-    plan, ents, routes, before, _, cf = _run(w, "cubic", "bf16", sample)
+    plan, ents, routes, before, _, cf = _run(w, coeffs, "bf16", sample)
     assert len(plan.slices()) == 3072
     for n, ks in names.items():
         i = w.index(n)
