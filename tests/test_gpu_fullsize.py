@@ -214,6 +214,19 @@ def test_dense_decoder_full(coeffs):
     _fused_equals_kept(plan, ents, before)
 
 
+def test_dense_decoder_fp32_path_full():
+    """The dense decoder with the fp32 Newton-Schulz path (the OMN page's
+    precision), sampled slices at the fp32 bound of 1e-4."""
+    w = wl.dense_decoder()
+    sample = _dense_sample(w)
+    plan, ents, routes, before, T_gpu, cf = _run(w, "cubic", "fp32", sample)
+    for i in sample:
+        if routes[i][0] == L.MO_ALG_MUON:
+            _check_muon_param(w, plan, ents, i, before, cf, "fp32")
+    _check_adamw(w, ents, routes, before, T_gpu, sample, np.random.default_rng(6))
+    _all_slices_bounded(plan, "fp32")
+
+
 def test_dense_decoder_spectral_cap_full():
     """The dense decoder with the spectral-cap guard on (OMN page, Muon-path
     paragraph), built as the benchmark builds it: tau = 0.1 lies between the
