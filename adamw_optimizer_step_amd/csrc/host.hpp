@@ -129,8 +129,10 @@ struct NsLayout {
 //  * it goes to the slice-resident kernel with 128 rows and a multiple of 128
 //    columns, or
 //  * in_off (nullable) gives its input's element offset from the pool base,
-//    it is not tall and both sides are multiples of its GEMM tile: iteration
-//    0 then reads D itself, the scale folded into the products.
+//    it is not tall, its long side is a multiple of its GEMM tile and its
+//    short side is that tile's multiple (or, in 128 x 128 tiles, 64's):
+//    iteration 0 then reads D itself, the scale folded into the products
+//    (the rows past a padded short side read zero, see GemmProb's a_rows).
 //
 // Gram space on the GEMM path (rectangular slices, l >= 1.25 s; on a square
 // slice it executes the same flops as the plain iteration in one more

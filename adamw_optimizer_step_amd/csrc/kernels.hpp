@@ -210,6 +210,12 @@ struct GemmProb {
                            // no scaling) when the slice's range flag is set
   int64_t c2_off;          // bf16 product without E only: a second output
                            // c1b C + cdb I (layout and mirror as c), -1 = none
+  int32_t a_rows, b_rows;  // > 0: rows of A (of B stored N x K) that hold data;
+                           // in 128 x 128 tiles the loads of later rows read
+                           // zero (the padding of a slice, or a slice read in
+                           // place whose padded rows are not stored); 0: all
+                           // rows.  (B stored K x N is read up to K, which
+                           // stops at its data.)
 };
 
 struct FinalItem {         // NS output copy (stored orientation)

@@ -573,15 +573,30 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   const uint32_t ldb_b = static_cast<uint32_t>(pr.ldb) * sizeof(T);
   const char* abase = reinterpret_cast<const char*>(pool + a_off) +
                       static_cast<size_t>(ti) * BM * lda_b;
-  const u32x4 rsa = buffer_rsrc(abase, BM * lda_b);
+  // In 128 x 128 tiles, A's resource (and B's, stored N x K) ends at the
+  // operand's last row that holds data (a_rows, b_rows): rows past it (a
+  // slice's padding) read zero without a memory access, and a slice read in
+  // place needs no padded copy.  (The K slab's offset goes in the scalar
+  // offset, outside the range check; rows are in the lane offset, inside it.)
+  // K-major B needs no such limit: K stops at the last slab holding data, and
+  // a slice read in place has a multiple of the slab depth as its K (no
+  // per-slab arithmetic in the loop, where it cost 1%).  The 256 x 256 tiles
+  // read whole tiles: their slices are read in place only unpadded, and the
+  // limit's scalar registers cost them 0.3%.
+  auto rows_in = [](int32_t valid, int first, int n) __attribute__((always_inline)) {
+    if constexpr (BM == kGemmTile) return valid > 0 ? max(0, min(n, valid - first)) : n;
+    else return n;
+  };
+  const u32x4 rsa = buffer_rsrc(abase, rows_in(pr.a_rows, ti * BM, BM) * lda_b);
   const char* bbase = BK ? reinterpret_cast<const char*>(pool + b_off + tj * BN)
                          : reinterpret_cast<const char*>(pool + b_off) +
                                static_cast<size_t>(tj) * BN * ldb_b;
+  const int rows_b = BK ? 0 : rows_in(pr.b_rows, tj * BN, BN);
   auto rsb_at = [&](int kt) __attribute__((always_inline)) {
     if constexpr (BK)
       return buffer_rsrc(bbase + static_cast<size_t>(kt) * C::kSlabK * ldb_b, C::kSlabK * ldb_b);
     else
-      return buffer_rsrc(bbase, BN * ldb_b);
+      return buffer_rsrc(bbase, rows_b * ldb_b);
   };
 
   // LDS slab layout (kRowB-byte rows): chunk c of row r at chunk

@@ -156,9 +156,20 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     // a 192-row slice's s x s products and final update take 3 slabs instead
     // of the 4 of its 256-row padding.
     const int32_t ks = static_cast<int32_t>(pad_to(s_, 64)), kl = static_cast<int32_t>(pad_to(l_, 64));
-    // iteration 0 reads D in place when it already has X0's layout (not
-    // tall, no padding): no prep copy, the scale folded into the products
-    const bool gdirect = in_off && direct_ok && direct_ok[i] && !tall && sp == s_ && lp == l_;
+    // Every operand of this slice's products has s rows of data (X: s x l,
+    // the s x s matrices): the loads of the padded rows read zero.
+    auto mk = [&](auto... args) {
+      GemmProb g = make_prob(args...);
+      g.a_rows = g.b_rows = static_cast<int32_t>(s_);
+      return g;
+    };
+    // iteration 0 reads D in place when it has X0's layout (not tall, the
+    // long side a multiple of the tile; in 128 x 128 tiles a padded short
+    // side reads zero past its last row, and is a multiple of 64, so that
+    // the K-major reads of the last product stop at its last row): no prep
+    // copy, the scale folded into the products
+    const bool gdirect = in_off && direct_ok && direct_ok[i] && !tall && lp == l_ &&
+                         (sp == s_ || (tile == kGemmTile && s_ % 64 == 0));
     if (gdirect) {
       // the prep copy stays available for slices whose range flag is set
       PrepItem fb = L.prep.back();
@@ -201,10 +212,10 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       // product with an E term has E = U, so that E passes through LDS with
       // the left operand (see launch_ns_gemm's has_e).
       auto prod = [&](int64_t u, int64_t v, int64_t e, int64_t out) {
-        return make_prob(u, v, out, out, e, sp, sp, sp, sp, sp, ks, ts, ts, 1, 0);
+        return mk(u, v, out, out, e, sp, sp, sp, sp, sp, ks, ts, ts, 1, 0);
       };
       const bool quintic0 = coeffs[2] != 0.f;
-      GemmProb g = first(make_prob(x0, x0, Ab[0], Ab[0], -1, lp, lp, sp, sp, 0, kl, ts, ts, 1, 0));
+      GemmProb g = first(mk(x0, x0, Ab[0], Ab[0], -1, lp, lp, sp, sp, 0, kl, ts, ts, 1, 0));
       g.c2_off = quintic0 ? -1 : Qb[0];   // Q_1 = P_0 = a_0 I + b_0 A_0 (cubic-type row 0)
       add(kGsGram, 0, g);
       ++stage;
@@ -240,22 +251,22 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       }
       // X_N = Q_N X0 into the second iterate buffer (transposed when tall)
       const int64_t qn = Qb[(steps - 1) % 2];
-      GemmProb f = first(tall ? make_prob(qn, x0, -1, x[1], -1, sp, lp, 0, sp, 0, ks, ts, tl, 0, 0)
-                              : make_prob(qn, x0, x[1], -1, -1, sp, lp, lp, 0, 0, ks, ts, tl, 0,
+      GemmProb f = first(tall ? mk(qn, x0, -1, x[1], -1, sp, lp, 0, sp, 0, ks, ts, tl, 0, 0)
+                              : mk(qn, x0, x[1], -1, -1, sp, lp, lp, 0, 0, ks, ts, tl, 0,
                                           0));
       f.item = i;
       add(kGsFinal, steps - 1, f);
       continue;
     }
     B.gram_p0.push_back(
-        first(make_prob(x0, x0, p, p, -1, lp, lp, sp, sp, 0, kl, ts, ts, 1, B.gram_tiles)));
+        first(mk(x0, x0, p, p, -1, lp, lp, sp, sp, 0, kl, ts, ts, 1, B.gram_tiles)));
     if (need_a)
       B.gram_a0.push_back(
-          first(make_prob(x0, x0, a, a, -1, lp, lp, sp, sp, 0, kl, ts, ts, 1, B.gram_tiles)));
+          first(mk(x0, x0, a, a, -1, lp, lp, sp, sp, 0, kl, ts, ts, 1, B.gram_tiles)));
     const GemmProb u0 =
-        first(make_prob(p, x0, x[1], -1, -1, sp, lp, lp, 0, 0, ks, ts, tl, 0, B.upd_tiles));
+        first(mk(p, x0, x[1], -1, -1, sp, lp, lp, 0, 0, ks, ts, tl, 0, B.upd_tiles));
     B.upd0.push_back(u0);
-    GemmProb f0 = tall ? first(make_prob(p, x0, -1, x[1], -1, sp, lp, 0, sp, 0, ks, ts, tl, 0,
+    GemmProb f0 = tall ? first(mk(p, x0, -1, x[1], -1, sp, lp, 0, sp, 0, ks, ts, tl, 0,
                                          B.upd_tiles))
                        : u0;
     f0.item = i;
@@ -264,18 +275,18 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
       const int64_t xc = x[q], xn = x[q ^ 1];
       // Gram X X^T (K = l), B = X read N x K: into P (scaled by b) or into A;
       // the lower triangle is written as the mirror through ct.
-      B.gram_p[q].push_back(make_prob(xc, xc, p, p, -1, lp, lp, sp, sp, 0, kl, ts, ts, 1,
+      B.gram_p[q].push_back(mk(xc, xc, p, p, -1, lp, lp, sp, sp, 0, kl, ts, ts, 1,
                                       B.gram_tiles));
       if (need_a)
-        B.gram_a[q].push_back(make_prob(xc, xc, a, a, -1, lp, lp, sp, sp, 0, kl, ts, ts, 1,
+        B.gram_a[q].push_back(mk(xc, xc, a, a, -1, lp, lp, sp, sp, 0, kl, ts, ts, 1,
                                         B.gram_tiles));
       // Update X' = P X (P = a I + b A + c A^2): A = P (s x s), B = X read
       // K-major (K = s); the next buffer receives the result.
-      B.upd[q].push_back(make_prob(p, xc, xn, -1, -1, sp, lp, lp, 0, 0, ks, ts, tl, 0,
+      B.upd[q].push_back(mk(p, xc, xn, -1, -1, sp, lp, lp, 0, 0, ks, ts, tl, 0,
                                    B.upd_tiles));
       // Last iteration: a tall matrix is written transposed (l x s, stored
       // orientation) instead.
-      B.fin[q].push_back(tall ? make_prob(p, xc, -1, xn, -1, sp, lp, 0, sp, 0, ks, ts, tl, 0,
+      B.fin[q].push_back(tall ? mk(p, xc, -1, xn, -1, sp, lp, 0, sp, 0, ks, ts, tl, 0,
                                           B.upd_tiles)
                               : B.upd[q].back());
       B.fin[q].back().item = i;
@@ -283,7 +294,7 @@ void build_ns_layout(NsLayout& L, const int64_t* rows, const int64_t* cols, int 
     if (need_a) {
       // P = b A + c A A; A is exactly symmetric, so it is its own transposed
       // operand and its own E term.
-      B.square.push_back(make_prob(a, a, p, p, a, sp, sp, sp, sp, sp, ks, ts, ts, 1,
+      B.square.push_back(mk(a, a, p, p, a, sp, sp, sp, sp, sp, ks, ts, ts, 1,
                                    B.square_tiles));
       B.square_tiles += tiles_of(ts, ts, true);
     }

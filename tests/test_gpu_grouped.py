@@ -282,9 +282,10 @@ def test_ns_output_refused_after_fused_step():
 
 
 def _aligned_shapes():
-    """Slices whose iteration 0 reads D in place (wide or square, sides
-    multiples of the tile) beside ones that keep the prep copy (tall, also
-    from fp32 gradients and inside a view; padded)."""
+    """Slices whose iteration 0 reads D in place (wide or square, the long
+    side a multiple of the tile; a padded short side reads zero past its last
+    row) beside ones that keep the prep copy (tall, also from fp32 gradients
+    and inside a view; a long side off the tile)."""
     ps = [wl.ParamSpec("norm", (64,), "bf16", wl.ROLE_NORM, no_decay=True),
           wl.ParamSpec("square", (256, 256), "bf16"),
           wl.ParamSpec("wide", (256, 640), "bf16"),
@@ -293,6 +294,8 @@ def _aligned_shapes():
           wl.ParamSpec("tall_pair", (1024, 256), "bf16", view=(2, 512, 256)),
           wl.ParamSpec("tall_f32", (384, 256), "f32"),
           wl.ParamSpec("padded", (200, 336), "bf16"),
+          wl.ParamSpec("short_pad", (192, 512), "bf16"),
+          wl.ParamSpec("short_ragged", (200, 512), "bf16"),
           # slice-resident and read in place (128 rows, columns a multiple of 128)
           wl.ParamSpec("heads", (256, 512), "bf16", view=(2, 128, 512)),
           wl.ParamSpec("head_wide", (128, 1024), "bf16")]
