@@ -919,6 +919,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
           // (separate copies of the K loop for the two cases)
           const float eratio = c0 / c1;
           const int e_col0 = tj * BN + wn * C::kWaveN;   // the wave's first column
+          static_assert(C::kSlabK % C::kWaveN == 0, "a wave's columns lie in one K slab");
           const int kt_e = e_col0 / C::kSlabK, kk0 = e_col0 - kt_e * C::kSlabK;
           main_loop(std::true_type{}, [&](int kt, int stage) __attribute__((always_inline)) {
             if (kt != kt_e) return;
