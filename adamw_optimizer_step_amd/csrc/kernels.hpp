@@ -287,8 +287,10 @@ mo_status launch_ns_small(const SmallProb* probs, int n, void* pool, const PrepI
 // pfb[sitem] is set: they then read alt_off for the X operand(s), unscaled.
 // c1b, cdb: the constants of the second outputs (c2_off).
 // few_max: bf16 launches of fewer 128 x 128 tiles than this use the 8-wave
-// variant.
-mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
+// variant.  persist: every problem has the same K (equal tile times), so the
+// launch may take only the workgroups that fit on the device at once, each
+// running several tiles in turn.
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, bool persist, int tile,
                          int64_t few_max, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
                          const RowSeg* wt, float lr, const float* lrs, const float* pscale,

@@ -17,6 +17,7 @@
 // of X), so no bounds checks are needed inside the GEMM.  Head-sized slices
 // (short side at most 128, bf16) run all iterations in one slice-resident
 // kernel instead.
+#include <atomic>
 #include <type_traits>
 
 #include <cstdlib>
@@ -514,8 +515,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK, int ST, int SRB>
-__global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
+// Logical tile `bid` of a launch of G logical tiles (k_ns_gemm's body).
+template <typename T, int BM, int BN, int WM, int WN, bool BK, int ST, int SRB>
+__device__ __forceinline__ void ns_gemm_tile(
+    const int bid, const int G,
     const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0, float c1_arg,
     int has_e, float cd, const RowSeg* __restrict__ wt, float lr_arg,
     const float* __restrict__ lrs, const float* __restrict__ pscale,
@@ -528,7 +531,6 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
   // (neighbouring tiles share operand panels in that XCD's L2), the chunks
   // dealt round-robin so that every XCD gets a similar mix of long and short
   // problems; the last partial round is split into contiguous runs.
-  const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid & 7, ord = bid >> 3;
   const int full = G / (8 * kXcdChunk);
   int tile;
@@ -558,7 +560,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
     }
   }
 
-  const int tid = threadIdx.x;
+  // (opaque per tile in a persistent kernel, which then recomputes the
+  // per-lane offsets below for each tile rather than holding them in
+  // registers across the whole tile)
+  int tid = threadIdx.x;
+  if constexpr (BM == kGemmTile) asm volatile("" : "+v"(tid));
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / WN, wn = wave % WN;
   const int fr = lane & 31, fg = lane >> 5;
@@ -1112,6 +1118,35 @@ __global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
       }
     }
     __syncthreads();
+  }
+}
+
+// Batched GEMM over a problem table (GemmProb), one 64 WM x 64 WN-thread
+// workgroup per output tile at a time.  128 x 128 tiles: with gridDim.x
+// below ntiles the launch is persistent, workgroup b taking logical tiles b,
+// b + gridDim.x, ... (gridDim.x a multiple of 8, so each keeps its XCD,
+// b mod 8, and the workgroups of one round hold consecutive logical tiles as
+// one workgroup per tile would), without a workgroup launch per tile.
+// 256 x 256 tiles: one per workgroup (the tile loop's registers cost the
+// dense-decoder launches 1.6%).
+template <typename T, int BM, int BN, int WM, int WN, int MINW, bool BK, int ST, int SRB>
+__global__ __launch_bounds__(64 * WM * WN, MINW) void k_ns_gemm(
+    const GemmProb* __restrict__ probs, int nprob, T* __restrict__ pool, float c0,
+    float c1_arg, int has_e, float cd, const RowSeg* __restrict__ wt, float lr_arg,
+    const float* __restrict__ lrs, const float* __restrict__ pscale,
+    const int32_t* __restrict__ pfb, float c1b_arg, float cdb, int ntiles) {
+  if constexpr (BM == kGemmTile) {
+    for (int vb = blockIdx.x; vb < ntiles; vb += gridDim.x) {
+      // the previous tile's reads of LDS are done before its stages refill
+      if (vb != static_cast<int>(blockIdx.x)) __syncthreads();
+      ns_gemm_tile<T, BM, BN, WM, WN, BK, ST, SRB>(vb, ntiles, probs, nprob, pool, c0, c1_arg,
+                                                    has_e, cd, wt, lr_arg, lrs, pscale, pfb,
+                                                    c1b_arg, cdb);
+    }
+  } else {
+    ns_gemm_tile<T, BM, BN, WM, WN, BK, ST, SRB>(blockIdx.x, gridDim.x, probs, nprob, pool, c0,
+                                                  c1_arg, has_e, cd, wt, lr_arg, lrs, pscale,
+                                                  pfb, c1b_arg, cdb);
   }
 }
 
@@ -1697,21 +1732,48 @@ mo_status launch_ns_prep_fallback(const PrepItem* items, int n, const float* sca
   return MO_OK;
 }
 
+// Workgroups of `kernel` (nt threads) resident on the current device at once:
+// CUs x workgroups per CU, rounded down to a multiple of the 8 XCDs; 0 when
+// the runtime cannot tell.  Cached per kernel and device.
+template <typename K>
+int resident_wgs(K kernel, int nt) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int ncu = 0, occ = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, nt, 0) != hipSuccess)
+      return 0;
+    v = (ncu * occ) & ~7;
+    if (v <= 0) return 0;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 template <typename T, int BM, int WM, int WN, int ST = 4, int SRB = 64>
-void launch_gemm_shape(const GemmProb* probs, int n, const dim3& grid, int bk, T* pool, float c0,
-                       float c1, int has_e, float cd, const RowSeg* wt, float lr,
+void launch_gemm_shape(const GemmProb* probs, int n, int ntiles, bool persist, int bk, T* pool,
+                       float c0, float c1, int has_e, float cd, const RowSeg* wt, float lr,
                        const float* lrs, const float* pscale, const int32_t* pfb, float c1b,
                        float cdb, hipStream_t st) {
   constexpr int NT = 64 * WM * WN;
+  auto run = [&](auto kernel) {
+    // (only 128 x 128 tiles loop over tiles; others take one per workgroup)
+    const int res = persist && BM == kGemmTile ? resident_wgs(kernel, NT) : 0;
+    const dim3 grid(static_cast<unsigned>(res > 0 && res < ntiles ? res : ntiles));
+    kernel<<<grid, NT, 0, st>>>(probs, n, pool, c0, c1, has_e, cd, wt, lr, lrs, pscale, pfb,
+                                c1b, cdb, ntiles);
+  };
   if (bk)
-    k_ns_gemm<T, BM, BM, WM, WN, 2, true, ST, SRB><<<grid, NT, 0, st>>>(
-        probs, n, pool, c0, c1, has_e, cd, wt, lr, lrs, pscale, pfb, c1b, cdb);
+    run(k_ns_gemm<T, BM, BM, WM, WN, 2, true, ST, SRB>);
   else
-    k_ns_gemm<T, BM, BM, WM, WN, 2, false, ST, SRB><<<grid, NT, 0, st>>>(
-        probs, n, pool, c0, c1, has_e, cd, wt, lr, lrs, pscale, pfb, c1b, cdb);
+    run(k_ns_gemm<T, BM, BM, WM, WN, 2, false, ST, SRB>);
 }
 
-mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
+mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, bool persist, int tile,
                          int64_t few_max, int bk,
                          void* pool, int elem, float c0, float c1, int has_e, float cd,
                          const RowSeg* wt, float lr, const float* lrs, const float* pscale,
@@ -1720,21 +1782,27 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
   if (bk && has_e) return fail(MO_EINVAL, "the K-major-B GEMM takes no E term");
   if (wt && (!bk || elem != 2))
     return fail(MO_EINVAL, "the fused weight update needs the bf16 K-major-B GEMM");
+  if (ntiles > INT32_MAX) return fail(MO_EINVAL, "%lld GEMM tiles in one launch", static_cast<long long>(ntiles));
   KTimer tm(MO_KC_NS_GEMM, st);
-  const dim3 grid(static_cast<unsigned>(ntiles));
+  const int nt = static_cast<int>(ntiles);
   if (tile == 256) {
     // bf16: 64-deep K slabs (128-byte rows) in 2 stages (128 KiB), one slab
     // in flight while the other is multiplied: half the waits and barriers
     // per unit of k of 4 stages of 32-deep slabs, and 2% faster on the
-    // dense-decoder batch.
+    // dense-decoder batch.  One workgroup per tile: persistent launches of
+    // these long tiles ran no faster alone, and left no CU to a concurrent
+    // launch on another stream (the dense-decoder step: 1.2 ms slower).
     if (elem == 2)
-      launch_gemm_shape<uint16_t, 256, 2, 4, 2, 128>(probs, n, grid, bk,
+      launch_gemm_shape<uint16_t, 256, 2, 4, 2, 128>(probs, n, nt, persist, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
                                                      cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
     else
-      launch_gemm_shape<float, 256, 2, 4>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
+      launch_gemm_shape<float, 256, 2, 4>(probs, n, nt, persist, bk, static_cast<float*>(pool), c0, c1,
                                           has_e, cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
   } else if (tile == 128) {
+    // Persistent when every problem has one K: a workgroup launch per tile
+    // left the CU idle for about 3 us between two tiles, a large share of
+    // these short tiles (the head-batched set's launches: 2-8% faster).
     // A launch with few tiles leaves most CUs idle and lasts as long as one
     // tile's K loop, whose length is set by the fixed cost of each K slab
     // (wait, barrier, fragment reads): split each tile over 8 waves of
@@ -1742,15 +1810,15 @@ mo_status launch_ns_gemm(const GemmProb* probs, int n, int64_t ntiles, int tile,
     // rows; 4 stages, 128 KiB) instead of 32-deep ones.  15-20% faster on the
     // single-matrix sweeps; 8 stages of 32-deep slabs were slower.
     if (elem == 2 && ntiles < few_max)
-      launch_gemm_shape<uint16_t, 128, 2, 4, 4, 128>(probs, n, grid, bk,
+      launch_gemm_shape<uint16_t, 128, 2, 4, 4, 128>(probs, n, nt, persist, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
                                                      cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
     else if (elem == 2)  // 2 stages of 64-deep slabs, as for 256 x 256 tiles (64 KiB)
-      launch_gemm_shape<uint16_t, 128, 2, 2, 2, 128>(probs, n, grid, bk,
+      launch_gemm_shape<uint16_t, 128, 2, 2, 2, 128>(probs, n, nt, persist, bk,
                                                      static_cast<uint16_t*>(pool), c0, c1, has_e,
                                                      cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
     else
-      launch_gemm_shape<float, 128, 2, 2>(probs, n, grid, bk, static_cast<float*>(pool), c0, c1,
+      launch_gemm_shape<float, 128, 2, 2>(probs, n, nt, persist, bk, static_cast<float*>(pool), c0, c1,
                                           has_e, cd, wt, lr, lrs, pscale, pfb, c1b, cdb, st);
   } else {
     return fail(MO_EINVAL, "unsupported GEMM tile %d", tile);

@@ -397,6 +397,15 @@ Chains chains_of(const NsLayout& L) {
   }
   return c;
 }
+
+// Every problem of a launch has the same K: its tiles take the same time, and
+// the launch can run persistent (a workgroup per resident slot, several tiles
+// each) with no workgroup left holding the long tiles.
+bool one_k(const std::vector<GemmProb>& probs) {
+  for (const GemmProb& g : probs)
+    if (g.K != probs.front().K) return false;
+  return true;
+}
 }  // namespace
 
 bool ns_has_two_chains(const NsLayout& L) {
@@ -442,19 +451,19 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const int e_mode = L.elem == 2 && !few ? 2 : 1;
       mo_status s;
       if (B.gs_kind[j] == kGsGram)
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, 0.f, 1.f, 0, 0.f,
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], one_k(B.gs[j]), B.tile, L.few_tile_max, 0, pool, L.elem, 0.f, 1.f, 0, 0.f,
                            nullptr, 0.f, nullptr, scale, range_fb, st, b, a);
       else if (B.gs_kind[j] == kGsProd)   // E = U in every problem (bf16: has_e 2)
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, a, b, e_mode,
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], one_k(B.gs[j]), B.tile, L.few_tile_max, 0, pool, L.elem, a, b, e_mode,
                            0.f, nullptr, 0.f, nullptr, nullptr, nullptr, st);
       else if (B.gs_kind[j] == kGsProdP)
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, b,
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], one_k(B.gs[j]), B.tile, L.few_tile_max, 0, pool, L.elem, b,
                            coeffs[3 * k + 2], e_mode, a, nullptr, 0.f, nullptr, nullptr, nullptr, st);
       else if (B.gs_kind[j] == kGsProdPlain)
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 0, pool, L.elem, 0.f,
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], one_k(B.gs[j]), B.tile, L.few_tile_max, 0, pool, L.elem, 0.f,
                            1.f, 0, 0.f, nullptr, 0.f, nullptr, nullptr, nullptr, st);
       else
-        s = launch_ns_gemm(t, n, B.gs_tiles[j], B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, wt,
+        s = launch_ns_gemm(t, n, B.gs_tiles[j], one_k(B.gs[j]), B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, wt,
                            lr, lrs, scale, range_fb, st);
       if (s != MO_OK) return s;
     }
@@ -476,15 +485,16 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       if (B.gram_p[q].empty()) continue;
       const NsBucketTables& tb = T.b[i];
       const int n = static_cast<int>(B.gram_p[q].size());
+      const bool uk = one_k(first ? B.gram_p0 : B.gram_p[q]);
       mo_status s;
       if (cubic_step) {
-        s = launch_ns_gemm(tab(first ? tb.gram_p0 : tb.gram_p[q]), n, B.gram_tiles, B.tile, L.few_tile_max, 0,
+        s = launch_ns_gemm(tab(first ? tb.gram_p0 : tb.gram_p[q]), n, B.gram_tiles, uk, B.tile, L.few_tile_max, 0,
                            pool, L.elem, 0.f, b, 0, a, nullptr, 0.f, nullptr, ps, pfb, ps_st);
       } else {
-        s = launch_ns_gemm(tab(first ? tb.gram_a0 : tb.gram_a[q]), n, B.gram_tiles, B.tile, L.few_tile_max, 0,
+        s = launch_ns_gemm(tab(first ? tb.gram_a0 : tb.gram_a[q]), n, B.gram_tiles, uk, B.tile, L.few_tile_max, 0,
                            pool, L.elem, 0.f, 1.f, 0, 0.f, nullptr, 0.f, nullptr, ps, pfb, ps_st);
         if (s == MO_OK)
-          s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, B.tile, L.few_tile_max, 0, pool, L.elem, b, c, 1,
+          s = launch_ns_gemm(tab(tb.square), n, B.square_tiles, one_k(B.square), B.tile, L.few_tile_max, 0, pool, L.elem, b, c, 1,
                              a, nullptr, 0.f, nullptr, nullptr, nullptr, ps_st);
       }
       if (s != MO_OK) return s;
@@ -496,8 +506,9 @@ mo_status ns_run_iterations(const NsLayout& L, const char* dtab, const NsTables&
       const NsBucketTables& tb = T.b[i];
       const bool fin = k + 1 == steps;
       const size_t off = fin ? (first ? tb.fin0 : tb.fin[q]) : (first ? tb.upd0 : tb.upd[q]);
+      const std::vector<GemmProb>& probs = fin ? (first ? B.fin0 : B.fin[q]) : (first ? B.upd0 : B.upd[q]);
       mo_status s = launch_ns_gemm(tab(off), static_cast<int>(B.upd[q].size()), B.upd_tiles,
-                                   B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr,
+                                   one_k(probs), B.tile, L.few_tile_max, 1, pool, L.elem, 0.f, 1.f, 0, 0.f, fin ? wt : nullptr,
                                    lr, lrs, ps, pfb, ps_st);
       if (s != MO_OK) return s;
     }
