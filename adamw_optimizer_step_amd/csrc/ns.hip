@@ -1425,6 +1425,18 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   // store at a computed index, which kept the three values in scratch memory,
   // and every reload of them waited for all loads in flight)
   int next = 0, at_0 = 0, at_1 = 0, at_2 = 0;
+  // Stores per wave of an update element, as the waits below count them: 4
+  // (one 16-byte store per q; the fp32 weight update's 8 are counted as 4, a
+  // smaller count only makes a wait stronger).  A fused weight update whose
+  // weight rows (tall: rows or columns) do not fill the 128 x 128 blocks
+  // leaves some waves without a valid row in some q, and their stores may
+  // then not be issued at all: none are counted.
+  int st_upd = 4;
+  if (wt != nullptr) {
+    const RowSeg& w = wt[pr.item];
+    const bool full = pr.tall ? w.rows % kSmallS == 0 && w.cols >= kSmallS : w.rows >= kSmallS;
+    if (!full) st_upd = 0;
+  }
   auto note_issue = [&](int e, int cur) __attribute__((always_inline)) {
     at_0 = e == cur ? cur : at_0;
     at_1 = e == cur + 1 ? cur : at_1;
@@ -1450,11 +1462,12 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       done = cur - 1;
     } else {
       // operations of this wave younger than the loads of `cur`: loads of
-      // later elements (4 each) and the stores (4 each) of update elements
-      // processed since those loads were issued
+      // later elements (4 each) and the stores (st_upd each) of update
+      // elements processed since those loads were issued
       const int a = at_0;
       const int first_store = a > NB ? a : NB;
-      const int young = 4 * (next - 1 - cur) + 4 * (cur > first_store ? cur - first_store : 0);
+      const int young =
+          4 * (next - 1 - cur) + st_upd * (cur > first_store ? cur - first_store : 0);
       switch (young >> 2) {
         case 0: __builtin_amdgcn_s_waitcnt(vm_wait_imm(0)); break;
         case 1: __builtin_amdgcn_s_waitcnt(vm_wait_imm(4)); break;
