@@ -85,19 +85,27 @@ __device__ __forceinline__ void store_from_f32(void* p, int64_t i, int32_t dt, f
 
 // 8 consecutive elements <-> 8 floats.  Pointers must be 16-byte aligned.
 // NT = non-temporal (streaming) access, for data a launch touches once.
+// Device memory only, never LDS: through a global-address-space pointer the
+// access is a global instruction, counted by the vector-memory counter alone
+// (a flat one, which a pointer read from memory would otherwise give, also
+// counts as an LDS access, so that every wait on LDS accesses waited for it).
+template <typename V>
+using gptr = __attribute__((address_space(1))) V*;
 template <typename V, bool NT>
 __device__ __forceinline__ V ldv(const V* q) {
+  const gptr<const V> g = (gptr<const V>)(q);
   if constexpr (NT)
-    return __builtin_nontemporal_load(q);
+    return __builtin_nontemporal_load(g);
   else
-    return *q;
+    return *g;
 }
 template <typename V, bool NT>
 __device__ __forceinline__ void stv(V* q, const V& v) {
+  const gptr<V> g = (gptr<V>)(q);
   if constexpr (NT)
-    __builtin_nontemporal_store(v, q);
+    __builtin_nontemporal_store(v, g);
   else
-    *q = v;
+    *g = v;
 }
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
