@@ -1450,6 +1450,24 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
     constexpr int PC = decltype(pc)::value;
     const int pass = PC >= 0 ? PC : pass_rt, b = cur - pass * NB;
     const int pb = col_of(b);   // the column block it covers
+    // A fused bf16 weight update (not tall) loads its weights here, before
+    // the block wait, so that they arrive while the block's MFMAs run rather
+    // than after them (the kernel: 1.45 -> 1.41 ms on the head-batched set).
+    // The wait below counts these loads (when every wave issues all four).
+    const bool wpre = wt != nullptr && !pr.tall && pass >= 1 && (GS || pass == npass) &&
+                      wt[pr.item].w_dt == MO_BF16;
+    W8 wrp[4];
+    if (wpre) {
+      const RowSeg& w = wt[pr.item];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int id = q * kSmThreads + tid;
+        const int row = id >> 4, c = id & 15;
+        const int ocol = pb * kSmallS + c * 8;
+        if (row < w.rows && ocol < w.cols)
+          wrp[q] = load_w8(w.w, static_cast<int64_t>(row) * w.ld_w + ocol, MO_BF16);
+      }
+    }
     int done;   // stores of elements <= done are complete after the wait below
     if (next == cur) {
       // not issued ahead (its block was written too recently): drain, then load
@@ -1466,8 +1484,9 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       // elements processed since those loads were issued
       const int a = at_0;
       const int first_store = a > NB ? a : NB;
-      const int young =
-          4 * (next - 1 - cur) + st_upd * (cur > first_store ? cur - first_store : 0);
+      const int young = 4 * (next - 1 - cur) +
+                        st_upd * (cur > first_store ? cur - first_store : 0) +
+                        (wpre && st_upd == 4 ? 4 : 0);
       switch (young >> 2) {
         case 0: __builtin_amdgcn_s_waitcnt(vm_wait_imm(0)); break;
         case 1: __builtin_amdgcn_s_waitcnt(vm_wait_imm(4)); break;
@@ -1568,15 +1587,7 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
             }
           }
         } else if (w.w_dt == MO_BF16) {
-          W8 wr[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int id = q * kSmThreads + tid;
-            const int row = id >> 4, c = id & 15;
-            const int ocol = pb * kSmallS + c * 8;
-            if (row < w.rows && ocol < w.cols)
-              wr[q] = load_w8(w.w, static_cast<int64_t>(row) * w.ld_w + ocol, MO_BF16);
-          }
+          W8 (&wr)[4] = wrp;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int id = q * kSmThreads + tid;
