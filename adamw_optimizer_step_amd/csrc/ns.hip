@@ -639,16 +639,23 @@ __device__ __forceinline__ void ns_gemm_tile(
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem))));
   // all direct-to-LDS loads of slab kt into `stage` (kInst per wave)
-  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+  auto issue_a = [&](int kt, int stage) __attribute__((always_inline)) {
     const uint32_t sb = lds0 + stage * C::kStageBytes;
 #pragma unroll
     for (int q = 0; q < C::kInstA; ++q)
       lds_dma16(rsa, sb + (wv * C::kInstA + q) * 1024, voa[q], kt * C::kRowB);
+  };
+  auto issue_b = [&](int kt, int stage) __attribute__((always_inline)) {
+    const uint32_t sb = lds0 + stage * C::kStageBytes;
     const u32x4 rsb = rsb_at(kt);
 #pragma unroll
     for (int q = 0; q < C::kInstB; ++q)
       lds_dma16(rsb, sb + BM * C::kRowB + (wv * C::kInstB + q) * 1024, vob[q],
                 BK ? 0 : kt * C::kRowB);
+  };
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    issue_a(kt, stage);
+    issue_b(kt, stage);
   };
 
   // Fragment reads.  A / NxK B: lane reads row (wave row base + fr), logical
@@ -761,6 +768,13 @@ __device__ __forceinline__ void ns_gemm_tile(
   // few tiles ran 2.5% slower that way and keep the issue at the slab start).
   static_assert(C::kSub % 2 == 0, "an even number of substeps per slab");
   constexpr bool kEarly = C::kStages == 2;
+  // 256 x 256 tiles issue those loads in two halves: A's right after the
+  // barrier, B's at the start of the next slab, once the slab's last MFMAs
+  // are issued.  The dense-decoder launches ran 4% faster than with all of a
+  // wave's loads issued at the barrier (B a substep later, or the loads in
+  // four parts, were no faster or slower); the 128 x 128 tiles gained
+  // nothing and issue them together.
+  constexpr bool kSplitIssue = kEarly && BM == 256;
   const int KT = pr.K / C::kSlabK;
   // slab_hook(kt, stage): called at the start of slab kt, whose stage is
   // complete in LDS and stays intact until the barrier of that slab
@@ -771,8 +785,13 @@ __device__ __forceinline__ void ns_gemm_tile(
     __syncthreads();
     if (kEarly && C::kStages - 1 < KT) issue(C::kStages - 1, C::kStages - 1);
     fload(0, 0, Int<0>{});
+    int pend_b = -1;   // slab whose B half is still to be issued (split issue)
     for (int kt = 0; kt < KT; ++kt) {
       const int stage = kt & (C::kStages - 1);
+      if (kSplitIssue && pend_b >= 0) {
+        issue_b(pend_b, pend_b & (C::kStages - 1));
+        pend_b = -1;
+      }
       if (!kEarly && kt + C::kStages - 1 < KT)
         issue(kt + C::kStages - 1, (kt + C::kStages - 1) & (C::kStages - 1));
       slab_hook(kt, stage);
@@ -789,7 +808,14 @@ __device__ __forceinline__ void ns_gemm_tile(
           wait_slab(last - (kt + 1));
           __syncthreads();
           // slab kt's stage is free from here: it takes slab kt + S
-          if (kEarly && kt + C::kStages < KT) issue(kt + C::kStages, stage);
+          if (kEarly && kt + C::kStages < KT) {
+            if constexpr (kSplitIssue) {
+              issue_a(kt + C::kStages, stage);
+              pend_b = kt + C::kStages;
+            } else {
+              issue(kt + C::kStages, stage);
+            }
+          }
           if (kt + 1 < KT) fload((kt + 1) & (C::kStages - 1), 0, Int<0>{});
         }
         __builtin_amdgcn_sched_barrier(0);
