@@ -818,8 +818,23 @@ __device__ __forceinline__ void ns_gemm_tile(
           }
           if (kt + 1 < KT) fload((kt + 1) & (C::kStages - 1), 0, Int<0>{});
         }
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_block(Int<ks & 1>{}, swc);
+        if constexpr (ks + 1 < C::kSub && sizeof(T) == 2) {
+          // (bf16) the next substep's fragment reads interleaved with this
+          // one's MFMAs, one read after each MFMA, rather than all reads
+          // first: the dense decoder's GEMM launches 1.3% faster
+          constexpr int kReads = FM + (BK ? 2 * FN : FN), kMf = FM * FN;
+          constexpr int kPairs = kReads < kMf ? kReads : kMf;
+          mfma_block(Int<ks & 1>{}, swc);
+          static_for<0, kPairs>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          });
+          if constexpr (kReads > kPairs) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kPairs, 0);
+          if constexpr (kMf > kPairs) __builtin_amdgcn_sched_group_barrier(0x008, kMf - kPairs, 0);
+        } else {
+          __builtin_amdgcn_sched_barrier(0);
+          mfma_block(Int<ks & 1>{}, swc);
+        }
         __builtin_amdgcn_sched_barrier(0);
       });
     }
