@@ -1258,14 +1258,23 @@ __device__ __forceinline__ void sm_gram_space(lds_char* qs, lds_char* xa, lds_ch
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[mi][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    u32x4 fv[2], fu[2][2];
+    auto load = [&](int set, int ks) __attribute__((always_inline)) {
       const u32x2 lo = lds_read_tr16((const char*)(v + sm_off(16 * ks + trow, tcol)));
       const u32x2 hi = lds_read_tr16((const char*)(v + sm_off(16 * ks + trow + 4, tcol)));
-      const u32x4 bf{lo[0], lo[1], hi[0], hi[1]};
+      fv[set] = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(bf, frag(u, wm * 64 + mi * 32 + fr, ks), x[mi]);
-    }
+      for (int mi = 0; mi < 2; ++mi) fu[set][mi] = frag(u, wm * 64 + mi * 32 + fr, ks);
+    };
+    load(0, 0);
+    static_for<0, 8>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value, c = ks & 1;
+      if constexpr (ks + 1 < 8) load(c ^ 1, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(fv[c], fu[c][mi], x[mi]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   auto rw = [&](int mi) { return wm * 64 + mi * 32 + fr; };
   auto cl = [&](int q) { return wn * 32 + 8 * q + 4 * fg; };
@@ -1435,13 +1444,25 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
   };
   const int trow = 8 * (g16 >> 1) + (j16 >> 2);
   // C[m][n] += sum_k A[m][k] B[n][k] over a 128-wide K, both operands NT
+  // (the fragments of step ks + 1 are read while step ks is multiplied: two
+  // register sets, as in the batched GEMM; here and in the update and the
+  // Gram-space products: 1% on the head-batched set)
   auto gram_acc = [&](const char* ta, const char* tb, f32x16 (&acc)[2]) __attribute__((always_inline)) {
+    u32x4 fb[2], fa[2][2];
+    auto load = [&](int set, int ks) __attribute__((always_inline)) {
+      fb[set] = nt_frag(tb, wn * 32 + fr, ks);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const u32x4 b = nt_frag(tb, wn * 32 + fr, ks);
+      for (int mi = 0; mi < 2; ++mi) fa[set][mi] = nt_frag(ta, wm * 64 + mi * 32 + fr, ks);
+    };
+    load(0, 0);
+    static_for<0, 8>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value, c = ks & 1;
+      if constexpr (ks + 1 < 8) load(c ^ 1, ks + 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(nt_frag(ta, wm * 64 + mi * 32 + fr, ks), b, acc[mi]);
-    }
+      for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(fa[c][mi], fb[c], acc[mi]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
   auto zero = [](f32x16 (&acc)[2]) __attribute__((always_inline)) {
 #pragma unroll
@@ -1571,16 +1592,27 @@ __global__ __launch_bounds__(kSmThreads, 1) void k_ns_small(const SmallProb* __r
       // X'_b.  A operand X_b^T: rows = block columns, read K-major (transpose
       // reads); B operand P: rows read as stored.
       zero(accu);
+      {
+        u32x4 fp[2], fx[2][2];
+        auto load = [&](int set, int ks) __attribute__((always_inline)) {
+          fp[set] = nt_frag(Ps, wn * 32 + fr, ks);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const u32x4 bp = nt_frag(Ps, wn * 32 + fr, ks);
+          for (int mi = 0; mi < 2; ++mi) {
+            const int c0 = wm * 64 + mi * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
+            const u32x2 lo = lds_read_tr16(stg + sm_off(16 * ks + trow, c0));
+            const u32x2 hi = lds_read_tr16(stg + sm_off(16 * ks + trow + 4, c0));
+            fx[set][mi] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          }
+        };
+        load(0, 0);
+        static_for<0, 8>([&](auto ksc) {
+          constexpr int ks = decltype(ksc)::value, c = ks & 1;
+          if constexpr (ks + 1 < 8) load(c ^ 1, ks + 1);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) {
-          const int c0 = wm * 64 + mi * 32 + 16 * (g16 & 1) + 4 * (j16 & 3);
-          const u32x2 lo = lds_read_tr16(stg + sm_off(16 * ks + trow, c0));
-          const u32x2 hi = lds_read_tr16(stg + sm_off(16 * ks + trow + 4, c0));
-          mma<uint16_t>(u32x4{lo[0], lo[1], hi[0], hi[1]}, bp, accu[mi]);
-        }
+          for (int mi = 0; mi < 2; ++mi) mma<uint16_t>(fx[c][mi], fp[c], accu[mi]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
       if (fold && pass == 1) {   // (s D)-based result: s times the product with D
 #pragma unroll
