@@ -820,8 +820,9 @@ __device__ __forceinline__ void ns_gemm_tile(
         }
         if constexpr (ks + 1 < C::kSub && sizeof(T) == 2) {
           // (bf16) the next substep's fragment reads interleaved with this
-          // one's MFMAs, one read after each MFMA, rather than all reads
-          // first: the dense decoder's GEMM launches 1.3% faster
+          // one's MFMAs, alternately one LDS read (scheduling group 0x100)
+          // and one MFMA (0x008), rather than all reads first: the dense
+          // decoder's GEMM launches 1.3% faster
           constexpr int kReads = FM + (BK ? 2 * FN : FN), kMf = FM * FN;
           constexpr int kPairs = kReads < kMf ? kReads : kMf;
           mfma_block(Int<ks & 1>{}, swc);
