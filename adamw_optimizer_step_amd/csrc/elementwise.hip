@@ -195,9 +195,14 @@ __global__ __launch_bounds__(kThreads) void k_adam_apply(const AdamSeg* __restri
                                                          const double* __restrict__ scal,
                                                          float lr_arg,
                                                          const float* __restrict__ lrs,
-                                                         int32_t tdelta) {
+                                                         int32_t tdelta,
+                                                         const int32_t* __restrict__ tcount) {
   const int64_t blk = blockIdx.x;
   const AdamSeg sg = segs[find_segment(segs, nseg, blk)];
+  // steps since the tables were built: the device counter (advanced at the
+  // start of every grouped step, so that a step replayed from a graph still
+  // takes the next step's bias correction), else the argument
+  if (tcount != nullptr) tdelta = *tcount - 1;
   const int64_t base = (blk - sg.start) * kEltPerBlock;
   const float kappa = reinterpret_cast<const float*>(scal + 1)[0];
   const float lr = lrs ? lrs[sg.lr_slot] : lr_arg;
@@ -383,11 +388,12 @@ mo_status launch_adam_norm(const double* partials, int64_t nblocks, float max_no
 }
 
 mo_status launch_adam_apply(const AdamSeg* segs, int nseg, int64_t nblocks, const double* scal,
-                            float lr, const float* lrs, int32_t tdelta, hipStream_t st) {
+                            float lr, const float* lrs, int32_t tdelta, hipStream_t st,
+                            const int32_t* tcount) {
   if (nblocks <= 0) return MO_OK;
   KTimer tm(MO_KC_ADAM_APPLY, st);
   k_adam_apply<<<dim3(static_cast<unsigned>(nblocks)), dim3(kThreads), 0, st>>>(
-      segs, nseg, scal, lr, lrs, tdelta);
+      segs, nseg, scal, lr, lrs, tdelta, tcount);
   MO_LAUNCH_CHECK("k_adam_apply");
   return MO_OK;
 }
@@ -423,17 +429,19 @@ struct LrArgs {
   float v[kMaxLrSlots];
 };
 
-__global__ __launch_bounds__(kThreads) void k_set_lrs(float* __restrict__ dst, LrArgs a, int n) {
+__global__ __launch_bounds__(kThreads) void k_set_lrs(float* __restrict__ dst, LrArgs a, int n,
+                                                      int32_t* __restrict__ tcount) {
   for (int i = threadIdx.x; i < n; i += kThreads) dst[i] = a.v[i];
+  if (tcount != nullptr && threadIdx.x == 0) *tcount += 1;
 }
 
-mo_status launch_set_lrs(float* dst, const float* vals, int n, hipStream_t st) {
-  if (n <= 0) return MO_OK;
+mo_status launch_set_lrs(float* dst, const float* vals, int n, hipStream_t st, int32_t* tcount) {
+  if (n <= 0 && tcount == nullptr) return MO_OK;
   if (n > kMaxLrSlots) return fail(MO_EINVAL, "%d learning-rate slots (at most %d)", n,
                                    kMaxLrSlots);
   LrArgs a;
   for (int i = 0; i < kMaxLrSlots; ++i) a.v[i] = i < n ? vals[i] : 0.f;
-  k_set_lrs<<<1, kThreads, 0, st>>>(dst, a, n);
+  k_set_lrs<<<1, kThreads, 0, st>>>(dst, a, n, tcount);
   MO_LAUNCH_CHECK("k_set_lrs");
   return MO_OK;
 }

@@ -131,14 +131,18 @@ mo_status launch_adam_sumsq(const AdamSeg* segs, int nseg, int64_t nblocks, doub
 mo_status launch_adam_norm(const double* partials, int64_t nblocks, float max_norm, double* scal,
                            double* norm_out, hipStream_t st);
 // lrs (nullable): per-slot learning rates in device memory, read at each
-// segment's lr_slot; NULL = `lr` for every segment.
+// segment's lr_slot; NULL = `lr` for every segment.  Step t of a segment is
+// t0 + tdelta, or t0 + *tcount - 1 with tcount (nullable) given.
 mo_status launch_adam_apply(const AdamSeg* segs, int nseg, int64_t nblocks, const double* scal,
-                            float lr, const float* lrs, int32_t tdelta, hipStream_t st);
+                            float lr, const float* lrs, int32_t tdelta, hipStream_t st,
+                            const int32_t* tcount = nullptr);
 
 // Per-step learning-rate table: dst[i] = vals[i] for i < n (n <= kMaxLrSlots),
-// written by a kernel from its arguments (no host copy, no memset node).
+// written by a kernel from its arguments (no host copy, no memset node); the
+// same kernel adds 1 to *tcount (nullable), the grouped step's device count.
 constexpr int kMaxLrSlots = 2 * MO_MAX_GROUPS;
-mo_status launch_set_lrs(float* dst, const float* vals, int n, hipStream_t st);
+mo_status launch_set_lrs(float* dst, const float* vals, int n, hipStream_t st,
+                         int32_t* tcount = nullptr);
 
 // ----- row kernels: NorMuon row normalisation and the scaled Muon update -----
 enum RowMode : int32_t {

@@ -78,7 +78,7 @@ struct mo_plan {
   int n_adam = 0;
 
   // plan-owned device tables
-  size_t tab_adam = 0, tab_bytes = 0;
+  size_t tab_adam = 0, tab_tcount = 0, tab_bytes = 0;
   char* dtab = nullptr;
   int device = -1;
   std::vector<char> htab;
@@ -307,6 +307,9 @@ mo_status build_plan(mo_plan* P) {
     if (P->bhp(B).spectral_cap > 0.f) B.tab_pow = t.take(sizeof(PowSeg) * B.active.size());
   }
   P->tab_adam = t.take(sizeof(AdamSeg) * P->n_adam);
+  // grouped steps since the upload (AdamW's bias correction), on the device:
+  // uploaded as 0 with the tables, advanced by every step's k_set_lrs
+  P->tab_tcount = t.take(sizeof(int32_t));
   P->tab_bytes = align_up(t.off, 256);
   return MO_OK;
 }
@@ -745,7 +748,8 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
     if ((s = upload_tables(P, base, st)) != MO_OK) return s;
   }
   float* lrs = reinterpret_cast<float*>(base + P->ws_lr);
-  if ((s = launch_set_lrs(lrs, lr.data(), P->nslots(), st)) != MO_OK) return s;
+  int32_t* tcount = reinterpret_cast<int32_t*>(P->dtab + P->tab_tcount);
+  if ((s = launch_set_lrs(lrs, lr.data(), P->nslots(), st, tcount)) != MO_OK) return s;
   // Muon: momentum and the Newton-Schulz input (HBM-bound) first
   int nsl_total = 0;
   for (mo_plan::Batch& B : P->batches) {
@@ -818,7 +822,7 @@ mo_status mo_grouped_step(mo_plan* P, const mo_step_args* args, void* ws, size_t
                                 args ? args->norm_out : nullptr, ast)) != MO_OK)
         return r;
       if ((r = launch_adam_apply(dad, P->n_adam, P->adam_blocks, scal, 0.f, lrs, P->tdelta,
-                                 ast)) != MO_OK)
+                                 ast, tcount)) != MO_OK)
         return r;
     } else if (args && args->norm_out) {
       // no AdamW gradient: report T = 0 (a kernel write, not a memset node)
