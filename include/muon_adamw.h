@@ -406,6 +406,11 @@ mo_status mo_lr_at(const mo_lr_schedule* s, double tokens, double* lr);
  *     clip (the OMN page's clip over the AdamW parameters), then AdamW with
  *     each group's lr, decay, betas and eps; the per-parameter step counter t
  *     is kept by the plan and incremented after each call.
+ *   A call made under HIP stream capture (after one ordinary call on the same
+ *     workspace, which uploads the tables) records the whole step; each
+ *     replay of the graph runs it with the learning rates of the capture and
+ *     AdamW's next step count (kept on the device); mo_plan_get_steps counts
+ *     calls, not replays.
  *   Excluded pieces of a Muon param (exclude_mask) are AdamW parameters of
  *     their own: they join the clip norm and take the AdamW update (the
  *     group's adamw_lr, adamw_wd, betas, eps) with the param's step counter,
