@@ -133,6 +133,8 @@ __global__ __launch_bounds__(kThreads) void k_momentum(const MomSeg* __restrict_
 // block, all issued before the reduction (four independent fp64 sums), and
 // writes one partial.
 constexpr int kSumsqSub = kSumsqBlocksPerPartial;
+static_assert(kEltPerBlock == kThreads * 8,
+              "k_adam_sumsq covers a block with one 8-element chunk per thread");
 __host__ __device__ constexpr int64_t sumsq_partials(int64_t nblocks) {
   return sumsq_partial_count(nblocks);
 }

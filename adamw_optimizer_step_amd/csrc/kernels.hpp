@@ -38,7 +38,7 @@ class KTimerOff {
   KTimerOff& operator=(const KTimerOff&) = delete;
 };
 
-// ----- momentum (elementwise, 8192 elements per block) ----------------------
+// ----- momentum (elementwise, 2048 elements per block) ----------------------
 constexpr int kEltPerThread = 8;
 constexpr int kEltIters = 1;
 constexpr int kEltPerBlock = kThreads * kEltPerThread * kEltIters;
